@@ -1,0 +1,14 @@
+"""MI355X (gfx950) fused attention: split-K GQA/MLA decode and causal GQA prefill.
+
+The compute runs in the HIP kernels of ``libattn_mi355x.so`` (C ABI declared
+in ``include/attn_mi355x.h``); this package is its thin ctypes binding.
+"""
+from ._lib import (ATTN_BF16, ATTN_ERR_ARG, ATTN_ERR_HIP, ATTN_ERR_UNSUPPORTED,
+                   ATTN_ERR_WORKSPACE, ATTN_F32, ATTN_OK, EXPORTED, KERNEL_NAMES, AttnError,
+                   AttnPlan, AttnProblem, attn_combine, attn_decode_plan, attn_decode_split,
+                   attn_prefill, decode, load, make_problem, prefill, workspace)
+
+__all__ = ["ATTN_BF16", "ATTN_ERR_ARG", "ATTN_ERR_HIP", "ATTN_ERR_UNSUPPORTED",
+           "ATTN_ERR_WORKSPACE", "ATTN_F32", "ATTN_OK", "EXPORTED", "KERNEL_NAMES", "AttnError",
+           "AttnPlan", "AttnProblem", "attn_combine", "attn_decode_plan", "attn_decode_split",
+           "attn_prefill", "decode", "load", "make_problem", "prefill", "workspace"]

@@ -1,0 +1,322 @@
+// C-ABI front end: argument checks, the split planner, kernel selection and launch.
+// Every check runs before anything is enqueued; no exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "attn_internal.hpp"
+#include "attn_mi355x.h"
+
+namespace attn {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Compute units of the current device, cached per device id.
+int device_cu_count(int* out) {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -1;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return -1;
+    cache[dev] = n;
+  }
+  *out = cache[dev];
+  return 0;
+}
+
+int check_problem(const attn_problem* p) {
+  if (!p) return fail(ATTN_ERR_ARG, "problem is NULL");
+  if (p->reserved0 != 0) return fail(ATTN_ERR_ARG, "reserved0 must be 0");
+  if ((p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) ||
+      (p->o_dtype != ATTN_F32 && p->o_dtype != ATTN_BF16))
+    return fail(ATTN_ERR_ARG, "dtype/o_dtype must be ATTN_F32 or ATTN_BF16");
+  if (p->batch < 0) return fail(ATTN_ERR_ARG, "batch < 0");
+  if (p->q_heads < 1 || p->kv_heads < 1) return fail(ATTN_ERR_ARG, "head counts must be >= 1");
+  if (p->q_heads % p->kv_heads != 0)
+    return fail(ATTN_ERR_ARG, "q_heads (%d) is not a multiple of kv_heads (%d)", p->q_heads,
+                p->kv_heads);
+  if (p->head_dim_qk < 1 || p->head_dim_v < 1) return fail(ATTN_ERR_ARG, "head dims must be >= 1");
+  if (p->q_len < 1) return fail(ATTN_ERR_ARG, "q_len < 1");
+  if (p->kv_len_max < 0) return fail(ATTN_ERR_ARG, "kv_len_max < 0");
+  if (p->causal != 0 && p->causal != 1) return fail(ATTN_ERR_ARG, "causal must be 0 or 1");
+  if (!std::isfinite(p->scale)) return fail(ATTN_ERR_ARG, "scale is not finite");
+  for (int a = 0; a < 3; ++a)
+    if (p->q_stride[a] < 0 || p->k_stride[a] < 0 || p->v_stride[a] < 0 || p->o_stride[a] < 0)
+      return fail(ATTN_ERR_ARG, "strides must be >= 0");
+  if (p->head_dim_qk > 768 || p->head_dim_v > 512)
+    return fail(ATTN_ERR_UNSUPPORTED, "head_dim_qk > 768 or head_dim_v > 512");
+  return ATTN_OK;
+}
+
+uint64_t problem_key(const attn_problem* p) {
+  // The output dtype is not part of the key: the split partials are fp32 either way.
+  const int32_t f[] = {p->dtype, p->batch, p->q_heads, p->kv_heads, p->head_dim_qk,
+                       p->head_dim_v, p->q_len, p->kv_len_max, p->causal};
+  uint64_t h = 1469598103934665603ull;
+  for (int32_t x : f) {
+    for (int s = 0; s < 32; s += 8) {
+      h ^= (uint64_t)((x >> s) & 0xff);
+      h *= 1099511628211ull;
+    }
+  }
+  return h | 1ull;  // never 0, so a zeroed plan is always rejected
+}
+
+float scale_of(const attn_problem* p) {
+  return p->scale > 0.f ? p->scale : 1.0f / std::sqrt((float)p->head_dim_qk);
+}
+
+KParams base_params(const attn_problem* p) {
+  KParams k;
+  std::memset(&k, 0, sizeof(k));
+  k.kv_lens = p->kv_lens;
+  k.qs_b = p->q_stride[0]; k.qs_t = p->q_stride[1]; k.qs_h = p->q_stride[2];
+  k.ks_b = p->k_stride[0]; k.ks_t = p->k_stride[1]; k.ks_h = p->k_stride[2];
+  k.vs_b = p->v_stride[0]; k.vs_t = p->v_stride[1]; k.vs_h = p->v_stride[2];
+  k.os_b = p->o_stride[0]; k.os_t = p->o_stride[1]; k.os_h = p->o_stride[2];
+  k.B = p->batch; k.Hq = p->q_heads; k.Hkv = p->kv_heads; k.G = p->q_heads / p->kv_heads;
+  k.Dqk = p->head_dim_qk; k.Dv = p->head_dim_v; k.Lq = p->q_len; k.Lcap = p->kv_len_max;
+  k.causal = p->causal;
+  k.in_bf16 = p->dtype == ATTN_BF16;
+  k.o_bf16 = p->o_dtype == ATTN_BF16;
+  k.rows = k.G * k.Lq;
+  k.row_tile = kGenericRowTile;
+  k.scale_log2 = scale_of(p) * 1.44269504088896340736f;
+  return k;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
+
+// Shape-level kernel choice for decode (pointers are checked at launch).
+int decode_family(const attn_problem* p) {
+  const int rows = (p->q_heads / p->kv_heads) * p->q_len;
+  if (p->dtype == ATTN_BF16 && p->head_dim_qk == 128 && p->head_dim_v == 128 && rows <= kGqaMaxRows)
+    return ATTN_KERNEL_GQA_D128;
+  return ATTN_KERNEL_GENERIC;
+}
+
+int tile_n_of(int family) {
+  switch (family) {
+    case ATTN_KERNEL_GQA_D128: return kGqaTileN;
+    case ATTN_KERNEL_MLA: return kMlaTileN;
+    default: return kGenericTileN;
+  }
+}
+
+// Can the MFMA GQA kernel run on these pointers/strides?  (16-byte rows,
+// 32-bit buffer offsets.)
+bool gqa_d128_fits(const attn_problem* p, const void* q, const void* k, const void* v) {
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return false;
+  for (int a = 0; a < 3; ++a)
+    if ((p->q_stride[a] | p->k_stride[a] | p->v_stride[a]) & 7) return false;
+  const int64_t kbytes = (int64_t)p->kv_len_max * p->k_stride[1] * 2 + 256;
+  const int64_t vbytes = (int64_t)p->kv_len_max * p->v_stride[1] * 2 + 256;
+  return kbytes < (1ll << 31) && vbytes < (1ll << 31);
+}
+
+int check_ptrs(const void* a, const char* na, const void* b, const char* nb, const void* c,
+               const char* nc) {
+  if (!a) return fail(ATTN_ERR_ARG, "%s is NULL", na);
+  if (!b) return fail(ATTN_ERR_ARG, "%s is NULL", nb);
+  if (!c) return fail(ATTN_ERR_ARG, "%s is NULL", nc);
+  return ATTN_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(ATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+}  // namespace
+}  // namespace attn
+
+using namespace attn;
+
+extern "C" {
+
+int attn_version(void) { return ATTN_MI355X_VERSION; }
+
+const char* attn_status_str(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_ERR_ARG: return "invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "unsupported problem";
+    case ATTN_ERR_WORKSPACE: return "workspace too small";
+    case ATTN_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_err; }
+
+int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32_t* kv_lens_host,
+                     int32_t num_cus, attn_plan* out) {
+  g_err[0] = 0;
+  if (!out) return fail(ATTN_ERR_ARG, "plan output is NULL");
+  std::memset(out, 0, sizeof(*out));
+  if (int st = check_problem(problem)) return st;
+  const attn_problem* p = problem;
+  int cus = num_cus;
+  if (cus <= 0 && device_cu_count(&cus) != 0)
+    return fail(ATTN_ERR_HIP, "cannot query the compute-unit count of the current device");
+
+  const int family = decode_family(p);
+  const int tile_n = tile_n_of(family);
+  const int G = p->q_heads / p->kv_heads;
+  const int rows = G * p->q_len;
+  const int row_tiles = family == ATTN_KERNEL_GENERIC ? (int)ceil_div(rows, kGenericRowTile) : 1;
+  const int64_t units_per_req = (int64_t)p->kv_heads * row_tiles;
+
+  // Lengths as the kernels will see them.
+  int64_t lmax = 0, tiles_total = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    int64_t n = kv_lens_host ? kv_lens_host[b] : p->kv_len_max;
+    n = std::min<int64_t>(std::max<int64_t>(n, 0), p->kv_len_max);
+    lmax = std::max(lmax, n);
+    tiles_total += ceil_div(n, tile_n);
+  }
+
+  int64_t s_max = 1, chunk = tile_n;
+  if (lmax > 0) {
+    const int64_t max_tiles = ceil_div(lmax, tile_n);
+    if (s_request > 0) {
+      s_max = std::min<int64_t>(s_request, max_tiles);
+      chunk = ceil_div(ceil_div(lmax, s_max), tile_n) * tile_n;
+    } else {
+      // Aim for about four workgroups per compute unit in total, with at least
+      // two tiles per split so the per-split prologue and epilogue stay small.
+      const int64_t target_wgs = (int64_t)cus * 4;
+      const int64_t work_tiles = tiles_total * units_per_req;
+      int64_t chunk_tiles = ceil_div(work_tiles, target_wgs);
+      chunk_tiles = std::max<int64_t>(chunk_tiles, 2);
+      chunk_tiles = std::min<int64_t>(chunk_tiles, max_tiles);
+      chunk = chunk_tiles * tile_n;
+    }
+    s_max = ceil_div(lmax, chunk);
+  }
+  if (s_max > 65535) return fail(ATTN_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)s_max);
+
+  out->kernel = family;
+  out->s_max = (int32_t)s_max;
+  out->chunk = (int32_t)chunk;
+  out->tile_n = tile_n;
+  out->rows_per_unit = rows;
+  out->row_tiles = row_tiles;
+  if (family == ATTN_KERNEL_GENERIC) {
+    out->grid[0] = (uint32_t)s_max;
+    out->grid[1] = (uint32_t)row_tiles;
+    out->grid[2] = (uint32_t)((int64_t)p->batch * p->kv_heads);
+    out->block = kGenericBlock;
+  } else {
+    out->grid[0] = (uint32_t)s_max;
+    out->grid[1] = (uint32_t)p->kv_heads;
+    out->grid[2] = (uint32_t)p->batch;
+    out->block = kGqaBlock;
+  }
+  const uint64_t nrows = (uint64_t)p->batch * p->q_len * p->q_heads;
+  out->ws_o_bytes = (uint64_t)s_max * nrows * p->head_dim_v * sizeof(float);
+  out->ws_lse_bytes = (uint64_t)s_max * nrows * sizeof(float);
+  out->problem_key = problem_key(p);
+  return ATTN_OK;
+}
+
+int attn_decode_split(const attn_problem* problem, const attn_plan* plan, const void* q,
+                      const void* k, const void* v, float* ws_o, size_t ws_o_bytes, float* ws_lse,
+                      size_t ws_lse_bytes, void* stream) {
+  g_err[0] = 0;
+  if (int st = check_problem(problem)) return st;
+  const attn_problem* p = problem;
+  if (!plan) return fail(ATTN_ERR_ARG, "plan is NULL");
+  if (plan->problem_key != problem_key(p))
+    return fail(ATTN_ERR_ARG, "plan was made for a different problem");
+  if (plan->s_max < 1 || plan->chunk < 1) return fail(ATTN_ERR_ARG, "corrupt plan");
+  if (p->batch == 0) return ATTN_OK;
+  if (int st = check_ptrs(q, "q", k, "k", v, "v")) return st;
+  if (!ws_o || !ws_lse) return fail(ATTN_ERR_ARG, "workspace pointer is NULL");
+  if (ws_o_bytes < plan->ws_o_bytes || ws_lse_bytes < plan->ws_lse_bytes)
+    return fail(ATTN_ERR_WORKSPACE, "workspace too small: need %llu + %llu bytes",
+                (unsigned long long)plan->ws_o_bytes, (unsigned long long)plan->ws_lse_bytes);
+
+  KParams kp = base_params(p);
+  kp.q = q; kp.k = k; kp.v = v;
+  kp.ws_o = ws_o; kp.ws_lse = ws_lse;
+  kp.chunk = plan->chunk;
+  kp.s_max = plan->s_max;
+  kp.split_mode = 1;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+  if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_fits(p, q, k, v)) {
+    return hip_status(launch_decode_gqa_d128(kp, dim3(plan->s_max, p->kv_heads, p->batch), s),
+                      "decode_gqa_d128 launch");
+  }
+  const int row_tiles = (int)ceil_div(kp.rows, kGenericRowTile);
+  const dim3 grid(plan->s_max, row_tiles, (unsigned)((int64_t)p->batch * p->kv_heads));
+  return hip_status(launch_generic(kp, grid, dim3(kGenericBlock), s), "generic split launch");
+}
+
+int attn_combine(const attn_problem* problem, const attn_plan* plan, const float* ws_o,
+                 const float* ws_lse, void* o, float* lse_out, void* stream) {
+  g_err[0] = 0;
+  if (int st = check_problem(problem)) return st;
+  const attn_problem* p = problem;
+  if (!plan) return fail(ATTN_ERR_ARG, "plan is NULL");
+  if (plan->problem_key != problem_key(p))
+    return fail(ATTN_ERR_ARG, "plan was made for a different problem");
+  if (plan->s_max < 1 || plan->chunk < 1) return fail(ATTN_ERR_ARG, "corrupt plan");
+  if (p->batch == 0) return ATTN_OK;
+  if (!ws_o || !ws_lse) return fail(ATTN_ERR_ARG, "workspace pointer is NULL");
+  if (!o) return fail(ATTN_ERR_ARG, "o is NULL");
+  KParams kp = base_params(p);
+  kp.ws_o = const_cast<float*>(ws_o);
+  kp.ws_lse = const_cast<float*>(ws_lse);
+  kp.o = o;
+  kp.lse_out = lse_out;
+  kp.chunk = plan->chunk;
+  kp.s_max = plan->s_max;
+  return hip_status(launch_combine(kp, reinterpret_cast<hipStream_t>(stream)), "combine launch");
+}
+
+int attn_prefill(const attn_problem* problem, const void* q, const void* k, const void* v, void* o,
+                 float* lse_out, void* stream) {
+  g_err[0] = 0;
+  if (int st = check_problem(problem)) return st;
+  const attn_problem* p = problem;
+  if (p->batch == 0) return ATTN_OK;
+  if (int st = check_ptrs(q, "q", k, "k", v, "v")) return st;
+  if (!o) return fail(ATTN_ERR_ARG, "o is NULL");
+  KParams kp = base_params(p);
+  kp.q = q; kp.k = k; kp.v = v; kp.o = o;
+  kp.lse_out = lse_out;
+  kp.chunk = p->kv_len_max;
+  kp.s_max = 1;
+  kp.split_mode = 0;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int row_tiles = (int)ceil_div(kp.rows, kGenericRowTile);
+  if (row_tiles > 65535) return fail(ATTN_ERR_UNSUPPORTED, "too many query rows per KV head");
+  const dim3 grid(1, row_tiles, (unsigned)((int64_t)p->batch * p->kv_heads));
+  return hip_status(launch_generic(kp, grid, dim3(kGenericBlock), s), "generic prefill launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Host-side internals shared by the C-ABI front end and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn_mi355x.h"
+
+namespace attn {
+
+// Everything a kernel needs, passed by value.  Strides are in elements.
+struct KParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;              // final output (prefill / combine)
+  float* ws_o;          // split partials [s_max, B, Lq, Hq, Dv]
+  float* ws_lse;        // split log-sum-exp [s_max, B, Lq, Hq]
+  float* lse_out;       // optional [B, Lq, Hq]
+  const int32_t* kv_lens;  // device, may be null
+  int64_t qs_b, qs_t, qs_h;
+  int64_t ks_b, ks_t, ks_h;
+  int64_t vs_b, vs_t, vs_h;
+  int64_t os_b, os_t, os_h;
+  int32_t B, Hq, Hkv, G, Dqk, Dv, Lq, Lcap;
+  int32_t causal;
+  int32_t in_bf16;      // Q/K/V element type
+  int32_t o_bf16;       // O element type
+  int32_t chunk;        // keys per split
+  int32_t s_max;        // split slots
+  int32_t rows;         // G * Lq rows per (request, KV head)
+  int32_t row_tile;     // rows per workgroup (generic kernel)
+  int32_t split_mode;   // 1: write ws_o/ws_lse; 0: write o (+ lse_out)
+  float scale_log2;     // tau * log2(e): scores are kept in base-2 units
+};
+
+// Launchers (one per kernel family).  Each returns a hipError_t.
+hipError_t launch_generic(const KParams& p, dim3 grid, dim3 block, hipStream_t s);
+hipError_t launch_combine(const KParams& p, hipStream_t s);
+hipError_t launch_decode_gqa_d128(const KParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_decode_mla(const KParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_prefill_d128(const KParams& p, hipStream_t s);
+
+// Tile geometry of the kernels, used by the planner.
+constexpr int kGenericRowTile = 16;    // rows per generic workgroup
+constexpr int kGenericTileN = 64;      // keys per generic tile
+constexpr int kGenericBlock = 256;
+constexpr int kGqaTileN = 128;         // keys per GQA-D128 workgroup round (4 waves x 32)
+constexpr int kGqaBlock = 256;
+constexpr int kGqaMaxRows = 16;
+constexpr int kMlaTileN = 32;          // keys per MLA tile
+constexpr int kMlaBlock = 256;
+constexpr int kMlaRows = 128;          // query rows per MLA workgroup
+
+}  // namespace attn

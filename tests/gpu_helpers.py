@@ -1,0 +1,127 @@
+"""Helpers for the GPU parity tests: device placement and error reports.
+
+Inputs come from ``synthetic.inputs`` (seeded); expected values come from the
+fp64 oracle only.  Nothing here computes attention.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import reduction_attention_gqa_amd as ra  # noqa: E402
+
+DEV = "cuda"
+
+
+def torch_dtype(code: str):
+    return torch.bfloat16 if code == "bf16" else torch.float32
+
+
+class DeviceProblem:
+    """A synthetic Problem placed on the GPU.
+
+    layout "token": K/V buffers [B, Lcap, Hkv, D]; "head": [B, Hkv, Lcap, D]
+    exposed as a [B, Lcap, Hkv, D] view.  Padding rows past each length hold
+    ``pad``.  For MLA, v is a view of k's first Dv columns.
+    """
+
+    def __init__(self, prob, layout="token", pad=float("nan"), o_dtype=None, lcap=None):
+        self.prob = prob
+        dt = torch_dtype(prob.dtype)
+        b, lq, hq, dqk = prob.q.shape
+        self.lcap = prob.lcap if lcap is None else lcap
+        self.q = torch.from_numpy(prob.q).to(DEV).to(dt)
+        self.k = self._kv(prob.k, prob.hkv, dqk, dt, layout, pad)
+        if prob.v_aliases_k:
+            self.v = self.k[..., : prob.dv]
+        else:
+            self.v = self._kv(prob.v, prob.hkv, prob.dv, dt, layout, pad)
+        self.lens = torch.tensor(prob.lens, dtype=torch.int32, device=DEV)
+        od = dt if o_dtype is None else torch_dtype(o_dtype)
+        self.o_dtype = od
+        self.o = torch.full((b, lq, hq, prob.dv), float("nan"), dtype=od, device=DEV)
+        self.lse = torch.full((b, lq, hq), float("nan"), dtype=torch.float32, device=DEV)
+
+    def _kv(self, rows, hkv, d, dt, layout, pad):
+        b = len(rows)
+        if layout == "token":
+            buf = torch.full((b, self.lcap, hkv, d), pad, dtype=dt, device=DEV)
+            view = buf
+        elif layout == "head":
+            buf = torch.full((b, hkv, self.lcap, d), pad, dtype=dt, device=DEV)
+            view = buf.permute(0, 2, 1, 3)
+        else:
+            raise ValueError(layout)
+        for i, r in enumerate(rows):
+            if r.shape[0]:
+                view[i, : r.shape[0]] = torch.from_numpy(np.ascontiguousarray(r)).to(DEV).to(dt)
+        return view
+
+    def problem(self):
+        p = self.prob
+        return ra.make_problem(self.q, self.k, self.v, self.o, kv_lens=self.lens,
+                               kv_len_max=self.lcap, causal=p.causal, scale=p.scale)
+
+    def decode(self, s_request=0, plan=None):
+        prob = self.problem()
+        if plan is None:
+            plan = ra.attn_decode_plan(prob, s_request, list(self.prob.lens))
+        ws_o, ws_lse = ra.workspace(plan, DEV)
+        ra.attn_decode_split(prob, plan, self.q, self.k, self.v, ws_o, ws_lse)
+        ra.attn_combine(prob, plan, ws_o, ws_lse, self.o, self.lse)
+        torch.cuda.synchronize()
+        return plan
+
+    def prefill(self):
+        ra.attn_prefill(self.problem(), self.q, self.k, self.v, self.o, self.lse)
+        torch.cuda.synchronize()
+
+    def out(self):
+        return self.o.float().cpu().numpy().astype(np.float64)
+
+    def lse_out(self):
+        return self.lse.cpu().numpy().astype(np.float64)
+
+
+def v_rows(prob):
+    return [prob.v_rows(b) for b in range(prob.batch)]
+
+
+def report(name, got, want):
+    err = np.abs(got - want)
+    mx = float(err.max()) if err.size else 0.0
+    mean = float(err.mean()) if err.size else 0.0
+    print(f"[parity] {name}: max_abs={mx:.3e} mean_abs={mean:.3e} n={err.size}", flush=True)
+    return mx, mean
+
+
+def assert_close(name, got, want, max_tol, mean_tol):
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert not np.isnan(got).any(), f"{name}: NaN in GPU output"
+    mx, mean = report(name, got, want)
+    assert mx <= max_tol, f"{name}: max abs error {mx} > {max_tol}"
+    assert mean <= mean_tol, f"{name}: mean abs error {mean} > {mean_tol}"
+
+
+def assert_lse_close(name, got, want, tol=1e-3):
+    fin = np.isfinite(want)
+    assert np.array_equal(fin, np.isfinite(got)), f"{name}: -inf pattern of LSE differs"
+    if fin.any():
+        mx = float(np.abs(got[fin] - want[fin]).max())
+        print(f"[parity] {name} lse: max_abs={mx:.3e}", flush=True)
+        assert mx <= tol
+
+
+def bf16_round(x: torch.Tensor) -> torch.Tensor:
+    return x.to(torch.bfloat16)
+
+
+BF16_MAX, BF16_MEAN = 1e-2, 1e-3
+F32_MAX, F32_MEAN = 1e-5, 1e-5

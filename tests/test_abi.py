@@ -1,0 +1,234 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares,
+rejects bad arguments before enqueueing anything, and plans splits.
+
+No compute call is made here (there is no GPU in this environment); the
+checks below return before the library touches the device.
+"""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import reduction_attention_gqa_amd as ra
+from reduction_attention_gqa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_mi355x.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from reduction_attention_gqa_amd.build import build
+        build()
+    return ra.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_version_matches_header(lib):
+    m = re.search(r"#define ATTN_MI355X_VERSION (\d+)", open(HEADER).read())
+    assert lib.attn_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert lib.attn_status_str(code)
+    assert lib.attn_status_str(99) == b"unknown status"
+
+
+def test_struct_layout_matches_c():
+    # attn_problem: 12 int32/float fields, a pointer, 12 int64 strides.
+    assert ctypes.sizeof(_lib.AttnProblem) == 12 * 4 + 8 + 12 * 8
+    assert _lib.AttnProblem.kv_lens.offset == 48
+    assert ctypes.sizeof(_lib.AttnPlan) == 6 * 4 + 3 * 4 + 4 + 3 * 8
+
+
+def problem(**kw):
+    """A token-major [B, L, H, D] problem with fake (never dereferenced) pointers."""
+    f = dict(dtype=ra.ATTN_BF16, o_dtype=ra.ATTN_BF16, batch=32, q_heads=32, kv_heads=8,
+             head_dim_qk=128, head_dim_v=128, q_len=1, kv_len_max=4096, causal=0, scale=0.0)
+    f.update(kw)
+    p = _lib.AttnProblem()
+    for k, v in f.items():
+        setattr(p, k, v)
+    hq, hkv, dqk, dv, lq, lk = (p.q_heads, p.kv_heads, p.head_dim_qk, p.head_dim_v, p.q_len,
+                                p.kv_len_max)
+    for dst, (l, h, d) in ((p.q_stride, (lq, hq, dqk)), (p.k_stride, (lk, hkv, dqk)),
+                           (p.v_stride, (lk, hkv, dv)), (p.o_stride, (lq, hq, dv))):
+        dst[0], dst[1], dst[2] = l * h * d, h * d, d
+    return p
+
+
+def plan_status(lib, p, s_request=0, lens=None, num_cus=256):
+    plan = _lib.AttnPlan()
+    arr = None if lens is None else (ctypes.c_int32 * len(lens))(*lens)
+    st = lib.attn_decode_plan(ctypes.byref(p) if p is not None else None, s_request, arr, num_cus,
+                              ctypes.byref(plan))
+    return st, plan
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("q_heads", 30, ra.ATTN_ERR_ARG),            # 30 % 8 != 0
+    ("batch", -1, ra.ATTN_ERR_ARG),
+    ("q_len", 0, ra.ATTN_ERR_ARG),
+    ("kv_len_max", -5, ra.ATTN_ERR_ARG),
+    ("dtype", 7, ra.ATTN_ERR_ARG),
+    ("o_dtype", -1, ra.ATTN_ERR_ARG),
+    ("causal", 2, ra.ATTN_ERR_ARG),
+    ("kv_heads", 0, ra.ATTN_ERR_ARG),
+    ("head_dim_qk", 0, ra.ATTN_ERR_ARG),
+    ("reserved0", 1, ra.ATTN_ERR_ARG),
+    ("head_dim_qk", 1024, ra.ATTN_ERR_UNSUPPORTED),
+    ("head_dim_v", 600, ra.ATTN_ERR_UNSUPPORTED),
+])
+def test_invalid_problem_is_rejected_everywhere(lib, field, value, code):
+    p = problem(**{field: value})
+    fake = ctypes.c_void_p(0x1000)
+    st, _ = plan_status(lib, p)
+    assert st == code
+    assert lib.attn_last_error()
+    assert lib.attn_prefill(ctypes.byref(p), fake, fake, fake, fake, None, None) == code
+    plan = _lib.AttnPlan()
+    assert lib.attn_decode_split(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, fake,
+                                 1 << 30, fake, 1 << 30, None) == code
+    assert lib.attn_combine(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, None,
+                            None) == code
+
+
+def test_negative_stride_and_nonfinite_scale(lib):
+    p = problem()
+    p.k_stride[1] = -1
+    assert plan_status(lib, p)[0] == ra.ATTN_ERR_ARG
+    p = problem(scale=float("nan"))
+    assert plan_status(lib, p)[0] == ra.ATTN_ERR_ARG
+
+
+def test_null_arguments(lib):
+    st, _ = plan_status(lib, None)
+    assert st == ra.ATTN_ERR_ARG
+    p = problem()
+    assert lib.attn_decode_plan(ctypes.byref(p), 0, None, 256, None) == ra.ATTN_ERR_ARG
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.attn_prefill(ctypes.byref(p), None, fake, fake, fake, None, None) == ra.ATTN_ERR_ARG
+    assert lib.attn_prefill(ctypes.byref(p), fake, fake, fake, None, None, None) == ra.ATTN_ERR_ARG
+    st, plan = plan_status(lib, p)
+    assert st == 0
+    assert lib.attn_decode_split(ctypes.byref(p), None, fake, fake, fake, fake, 1 << 30, fake,
+                                 1 << 30, None) == ra.ATTN_ERR_ARG
+    assert lib.attn_decode_split(ctypes.byref(p), ctypes.byref(plan), fake, None, fake, fake,
+                                 1 << 30, fake, 1 << 30, None) == ra.ATTN_ERR_ARG
+    assert lib.attn_combine(ctypes.byref(p), ctypes.byref(plan), fake, fake, None, None,
+                            None) == ra.ATTN_ERR_ARG
+
+
+def test_workspace_too_small_and_plan_mismatch(lib):
+    p = problem()
+    st, plan = plan_status(lib, p)
+    assert st == 0
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.attn_decode_split(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, fake,
+                                 plan.ws_o_bytes - 4, fake, plan.ws_lse_bytes,
+                                 None) == ra.ATTN_ERR_WORKSPACE
+    assert lib.attn_decode_split(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, fake,
+                                 plan.ws_o_bytes, fake, plan.ws_lse_bytes - 4,
+                                 None) == ra.ATTN_ERR_WORKSPACE
+    other = problem(batch=31)
+    assert lib.attn_decode_split(ctypes.byref(other), ctypes.byref(plan), fake, fake, fake, fake,
+                                 plan.ws_o_bytes, fake, plan.ws_lse_bytes,
+                                 None) == ra.ATTN_ERR_ARG
+    assert lib.attn_combine(ctypes.byref(other), ctypes.byref(plan), fake, fake, fake, None,
+                            None) == ra.ATTN_ERR_ARG
+    zeroed = _lib.AttnPlan()
+    assert lib.attn_combine(ctypes.byref(p), ctypes.byref(zeroed), fake, fake, fake, None,
+                            None) == ra.ATTN_ERR_ARG
+
+
+def test_empty_batch_is_a_no_op(lib):
+    p = problem(batch=0)
+    st, plan = plan_status(lib, p)
+    assert st == 0 and plan.s_max == 1
+    assert lib.attn_prefill(ctypes.byref(p), None, None, None, None, None, None) == 0
+    assert lib.attn_decode_split(ctypes.byref(p), ctypes.byref(plan), None, None, None, None, 0,
+                                 None, 0, None) == 0
+
+
+# ---------------------------------------------------------------- planner
+
+def _check_plan_invariants(p, plan, lens):
+    lmax = max(lens) if lens else 0
+    assert plan.chunk % plan.tile_n == 0 and plan.chunk >= plan.tile_n
+    assert plan.s_max == max(1, math.ceil(lmax / plan.chunk))
+    assert plan.s_max * plan.chunk >= lmax
+    nrows = p.batch * p.q_len * p.q_heads
+    assert plan.ws_o_bytes == plan.s_max * nrows * p.head_dim_v * 4
+    assert plan.ws_lse_bytes == plan.s_max * nrows * 4
+    assert plan.grid[0] == plan.s_max
+
+
+def test_plan_tiny_fp32_decode_fixed_s4(lib):
+    # 256 keys split 4 ways: Split(A:[m, k], dim=1) -> [s, m, k/s] (Cleave §4), k/s = 64.
+    p = problem(dtype=ra.ATTN_F32, o_dtype=ra.ATTN_F32, batch=1, q_heads=8, kv_heads=2,
+                head_dim_qk=64, head_dim_v=64, kv_len_max=256)
+    st, plan = plan_status(lib, p, s_request=4)
+    assert st == 0
+    assert plan.kernel == 0 and plan.s_max == 4 and plan.chunk == 64
+    _check_plan_invariants(p, plan, [256])
+
+
+def test_plan_llama_decode_uses_gqa_kernel_and_fills_the_gpu(lib):
+    p = problem()
+    st, plan = plan_status(lib, p)
+    assert st == 0
+    assert ra.KERNEL_NAMES[plan.kernel] == "gqa_d128"
+    _check_plan_invariants(p, plan, [4096] * 32)
+    wgs = plan.s_max * p.kv_heads * p.batch
+    assert wgs >= 256          # at least one workgroup per compute unit
+    assert plan.s_max > 1      # one query row per request: the key axis must be split
+
+
+@pytest.mark.parametrize("s_req", [1, 2, 3, 7, 8, 16, 10_000])
+def test_plan_honours_requested_split(lib, s_req):
+    p = problem()
+    st, plan = plan_status(lib, p, s_request=s_req)
+    assert st == 0
+    assert plan.s_max <= s_req
+    _check_plan_invariants(p, plan, [4096] * 32)
+
+
+def test_plan_ragged_uses_host_lengths(lib):
+    lens = [128, 32768, 5000, 0] + [300] * 60
+    p = problem(batch=64, q_heads=64, kv_heads=8, kv_len_max=32768)
+    st, plan = plan_status(lib, p, lens=lens)
+    assert st == 0
+    _check_plan_invariants(p, plan, lens)
+    # lengths above capacity are clamped, not trusted
+    st2, plan2 = plan_status(lib, p, lens=lens[:1] + [10 ** 9] + lens[2:])
+    assert st2 == 0 and plan2.s_max == plan.s_max
+
+
+def test_plan_generic_for_other_shapes(lib):
+    p = problem(head_dim_qk=64, head_dim_v=64)
+    st, plan = plan_status(lib, p)
+    assert st == 0 and ra.KERNEL_NAMES[plan.kernel] == "generic"
+    _check_plan_invariants(p, plan, [4096] * 32)

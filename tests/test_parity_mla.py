@@ -1,0 +1,39 @@
+"""GPU parity of MLA-style decode (one latent KV head, V = K[..., :512]) against the oracle."""
+import numpy as np
+import pytest
+
+from gpu_helpers import BF16_MAX, BF16_MEAN, DeviceProblem, assert_close, assert_lse_close, v_rows
+from oracle import attention, attention_rows
+from synthetic.inputs import make_problem, workload
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("s", [0, 1, 3])
+def test_mla_small(s):
+    p = make_problem(dtype="bf16", batch=2, lq=1, hq=128, hkv=1, dqk=576, dv=512,
+                     kv_len=[300, 1000], lcap=1024, seed=41, mla=True)
+    d = DeviceProblem(p)
+    assert d.v.data_ptr() == d.k.data_ptr()
+    plan = d.decode(s_request=s)
+    o, lse = attention(p.q, p.k, v_rows(p), False, p.scale)
+    assert_close(f"mla s={s} kernel={plan.kernel}", d.out(), o, BF16_MAX, BF16_MEAN)
+    assert_lse_close(f"mla s={s}", d.lse_out(), lse)
+
+
+def test_mla_full_size_sampled_rows():
+    p = workload("mla_decode")
+    d = DeviceProblem(p)
+    plan = d.decode()
+    print(f"[plan] mla_decode: kernel={plan.kernel} s_max={plan.s_max} chunk={plan.chunk}",
+          flush=True)
+    out, lse_g = d.out(), d.lse_out()
+    assert not np.isnan(out).any()
+    rng = np.random.default_rng(43)
+    rows = {(0, 0, 0), (63, 0, 127)}
+    while len(rows) < 48:
+        rows.add((int(rng.integers(64)), 0, int(rng.integers(128))))
+    rows = sorted(rows)
+    o, lse = attention_rows(p.q, p.k, v_rows(p), False, p.scale, rows)
+    assert_close("mla full sampled", np.stack([out[r] for r in rows]), o, BF16_MAX, BF16_MEAN)
+    assert_lse_close("mla full sampled", np.array([lse_g[r] for r in rows]), lse)

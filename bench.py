@@ -1,0 +1,413 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+Default run (N = 1):
+  * value: split-K decode throughput in algorithmic HBM GB/s on the
+    Llama-3-8B-shaped GQA decode (B=32, 32/8 heads, D=128, 4096 keys, bf16);
+    one step = plan + split kernel + combine kernel over the whole batch.
+  * prefill: causal GQA prefill (B=4, L=4096, 32/8 heads, D=128, bf16) in
+    algorithmic TFLOP/s; one step = one fused prefill launch.
+  * roofline of the dominant kernel of each (per-launch HIP-event times on the
+    launch stream), the split-off (s = 1) ablation, and the fp64 oracle timed
+    on the host cores over a bounded sample of the same workload.
+Inputs are synthetic (seeded i.i.d. N(0,1), rounded to bf16) and resident in
+HBM before timing.  Several copies of the inputs are rotated so that a step
+never finds its K/V in the 256 MB Infinity Cache from the previous step.
+
+Algorithmic work: bytes = unique Q, K and V reads + O write (the split
+workspace is not counted); flops = 2 (Dqk + Dv) per visible (query, key) pair.
+
+--workload NAME benches one of the other named workloads instead (its own
+JSON line, decode or prefill by shape).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "decode attn HBM GB/s + prefill TFLOP/s (fraction of MI355X peak), 1 GPU"
+INFINITY_CACHE_BYTES = 256 << 20
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--s", type=int, default=0, help="force the split count (0 = planner)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------- inputs
+
+def device_copies(prob, n_copies, dev):
+    """n_copies independent device copies of one synthetic problem (zero padding)."""
+    import numpy as np
+    import torch
+    dt = torch.bfloat16 if prob.dtype == "bf16" else torch.float32
+    q = torch.from_numpy(prob.q).to(dev).to(dt)
+    k = torch.zeros((prob.batch, prob.lcap, prob.hkv, prob.dqk), dtype=dt, device=dev)
+    v = None if prob.v_aliases_k else torch.zeros((prob.batch, prob.lcap, prob.hkv, prob.dv),
+                                                   dtype=dt, device=dev)
+    for b in range(prob.batch):
+        n = int(prob.lens[b])
+        if n:
+            k[b, :n] = torch.from_numpy(np.ascontiguousarray(prob.k[b])).to(dev).to(dt)
+            if v is not None:
+                v[b, :n] = torch.from_numpy(np.ascontiguousarray(prob.v[b])).to(dev).to(dt)
+    copies = []
+    for c in range(n_copies):
+        qc, kc = (q, k) if c == 0 else (q.clone(), k.clone())
+        vc = kc[..., : prob.dv] if v is None else (v if c == 0 else v.clone())
+        copies.append((qc, kc, vc))
+    lens = torch.tensor(prob.lens, dtype=torch.int32, device=dev)
+    return copies, lens
+
+
+def n_copies_for(step_bytes):
+    return max(2, math.ceil((INFINITY_CACHE_BYTES * 4) / max(step_bytes, 1)) + 1)
+
+
+# ------------------------------------------------------------------- algorithmic
+
+def decode_bytes(prob):
+    e = 2 if prob.dtype == "bf16" else 4
+    sum_l = int(prob.lens.sum())
+    q = prob.batch * prob.lq * prob.hq * prob.dqk * e
+    o = prob.batch * prob.lq * prob.hq * prob.dv * e
+    kv = sum_l * prob.hkv * (prob.dqk if prob.v_aliases_k else prob.dqk + prob.dv) * e
+    return q, kv, o
+
+
+def visible_pairs(prob):
+    total = 0
+    for n in prob.lens:
+        n = int(n)
+        if prob.causal:
+            for i in range(prob.lq):
+                total += max(0, min(n, i + n - prob.lq + 1))
+        else:
+            total += prob.lq * n
+    return total * prob.hq
+
+
+def attention_flops(prob):
+    return 2 * (prob.dqk + prob.dv) * visible_pairs(prob)
+
+
+def source_sha(relpath):
+    with open(os.path.join(ROOT, relpath), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(kernel_src, launches_key):
+    """HBM bytes per launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    ent = data.get(launches_key)
+    if not ent or ent.get("source_sha") != source_sha(kernel_src):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ----------------------------------------------------------------------- timing
+
+def time_decode(prob, steps, warmup, s_request, dev):
+    import torch
+    import reduction_attention_gqa_amd as ra
+    qb, kvb, ob = decode_bytes(prob)
+    copies, lens = device_copies(prob, n_copies_for(qb + kvb + ob), dev)
+    dt = copies[0][0].dtype
+    o = torch.empty((prob.batch, prob.lq, prob.hq, prob.dv), dtype=dt, device=dev)
+    lens_host = [int(x) for x in prob.lens]
+    probs = [ra.make_problem(q, k, v, o, kv_lens=lens, kv_len_max=prob.lcap, causal=prob.causal,
+                             scale=prob.scale) for q, k, v in copies]
+    plan = ra.attn_decode_plan(probs[0], s_request, lens_host)
+    ws_o, ws_lse = ra.workspace(plan, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        q, k, v = copies[i % len(copies)]
+        pr = probs[i % len(copies)]
+        pl = ra.attn_decode_plan(pr, s_request, lens_host)
+        if ev is not None:
+            ev[0].record(stream)
+        ra.attn_decode_split(pr, pl, q, k, v, ws_o, ws_lse, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        ra.attn_combine(pr, pl, ws_o, ws_lse, o, None, stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # Timed region: exactly `steps` steps, synchronised on both sides.
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # Per-kernel durations, with events on the launch stream.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    split_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    comb_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    del copies, probs
+    return dict(plan=plan, wall_s=wall, split_ms=split_ms, combine_ms=comb_ms,
+                bytes=(qb, kvb, ob))
+
+
+def time_prefill(prob, steps, warmup, dev):
+    import torch
+    import reduction_attention_gqa_amd as ra
+    qb, kvb, ob = decode_bytes(prob)
+    copies, lens = device_copies(prob, n_copies_for(qb + kvb + ob), dev)
+    dt = copies[0][0].dtype
+    o = torch.empty((prob.batch, prob.lq, prob.hq, prob.dv), dtype=dt, device=dev)
+    probs = [ra.make_problem(q, k, v, o, kv_lens=lens, kv_len_max=prob.lcap, causal=prob.causal,
+                             scale=prob.scale) for q, k, v in copies]
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        q, k, v = copies[i % len(copies)]
+        if ev is not None:
+            ev[0].record(stream)
+        ra.attn_prefill(probs[i % len(copies)], q, k, v, o, None, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    k_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    del copies, probs
+    return dict(wall_s=wall, kernel_ms=k_ms, bytes=(qb, kvb, ob))
+
+
+def stats(ms):
+    n = len(ms)
+    return dict(mean_ms=sum(ms) / n, median_ms=ms[n // 2], min_ms=ms[0], p10_ms=ms[n // 10],
+                p90_ms=ms[min(n - 1, (9 * n) // 10)])
+
+
+# ------------------------------------------------------------------ CPU oracle
+
+def cpu_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def oracle_decode_baseline(prob, budget_s=10.0):
+    """The fp64 oracle, as it stands, over the whole decode batch, repeated for ~budget_s."""
+    from threadpoolctl import threadpool_limits
+    from oracle import attention
+    cores = cpu_cores()
+    qb, kvb, ob = decode_bytes(prob)
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            attention(prob.q, prob.k, [prob.v_rows(b) for b in range(prob.batch)], prob.causal,
+                      prob.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 1000:
+                break
+    gbs = (qb + kvb + ob) * reps / el / 1e9
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"whole batch ({prob.batch} requests) x {reps} repetitions, {el:.1f} s, "
+                      f"numpy fp64 with {cores} BLAS threads"}
+
+
+def oracle_prefill_baseline(prob, groups=6):
+    """The fp64 oracle on `groups` (request, KV-head) groups of the prefill workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import attention
+    cores = cpu_cores()
+    g = prob.hq // prob.hkv
+    done = 0
+    flops = 0
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        for idx in range(groups):
+            b, kvh = idx % prob.batch, (idx // prob.batch) % prob.hkv
+            heads = slice(kvh * g, (kvh + 1) * g)
+            q = np.ascontiguousarray(prob.q[b:b + 1, :, heads, :])
+            k = [prob.k[b][:, kvh:kvh + 1, :]]
+            v = [prob.v_rows(b)[:, kvh:kvh + 1, :]]
+            attention(q, k, v, prob.causal, prob.scale)
+            done += 1
+        el = time.perf_counter() - t0
+    n = int(prob.lens[0])
+    pairs = (n * (n + 1) // 2 if prob.causal else n * n) * g * done
+    flops = 2 * (prob.dqk + prob.dv) * pairs
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{done} of {prob.batch * prob.hkv} (request, KV head) groups "
+                      f"({g} heads x {prob.lq} queries each), {el:.1f} s, numpy fp64"}
+
+
+# ------------------------------------------------------------------------ main
+
+def decode_record(prob, r, steps, warmup, extra_src):
+    qb, kvb, ob = r["bytes"]
+    total = qb + kvb + ob
+    ms_step = r["wall_s"] * 1e3 / steps
+    split = stats(r["split_ms"])
+    comb = stats(r["combine_ms"])
+    split_bytes = qb + kvb
+    achieved = split_bytes / (split["mean_ms"] * 1e-3) / 1e9
+    plan = r["plan"]
+    traffic = traffic_for(extra_src, f"decode_split:{prob.name}")
+    return dict(
+        value=round(total / (ms_step * 1e-3) / 1e9, 2), ms_per_step=round(ms_step, 5),
+        plan=dict(kernel=plan.kernel, s_max=plan.s_max, chunk=plan.chunk,
+                  grid=list(plan.grid), ws_bytes=int(plan.ws_o_bytes + plan.ws_lse_bytes)),
+        roofline={"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                  "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                  "traffic": traffic, "kernel": "decode split kernel",
+                  "algorithmic_bytes_per_launch": split_bytes,
+                  "launch_ms": split},
+        combine=comb, algorithmic_bytes_per_step=total)
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import reduction_attention_gqa_amd as ra
+    ra.load()
+    from synthetic.inputs import WORKLOADS, workload
+    dev = "cuda:0"
+    name = a.workload or "llama3_8b_gqa_decode"
+    if name not in WORKLOADS:
+        sys.exit(f"unknown workload {name}; choose from {sorted(WORKLOADS)}")
+    log(f"generating {name}")
+    prob = workload(name)
+    is_prefill = prob.lq > 1
+    out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "bf16" if prob.dtype == "bf16" else "f32",
+           "data": "synthetic (seeded i.i.d. N(0,1), bf16-rounded; no model weights needed)"}
+    if not is_prefill:
+        log("timing decode")
+        r = time_decode(prob, a.steps, a.warmup, a.s, dev)
+        rec = decode_record(prob, r, a.steps, a.warmup,
+                            "reduction_attention_gqa_amd/csrc/kernels/"
+                            + {0: "generic.hip", 1: "decode_gqa_d128.hip",
+                               2: "decode_mla.hip"}[r["plan"].kernel])
+        out["unit"] = "GB/s"
+        out["value"] = rec["value"]
+        out["ms_per_step"] = rec["ms_per_step"]
+        out["config"] = {"workload": name, "batch": prob.batch, "q_heads": prob.hq,
+                         "kv_heads": prob.hkv, "head_dim_qk": prob.dqk, "head_dim_v": prob.dv,
+                         "kv_len_total": int(prob.lens.sum()), "kv_len_max": int(prob.lens.max()),
+                         "q_len": prob.lq, "split_s": rec["plan"]["s_max"],
+                         "chunk": rec["plan"]["chunk"],
+                         "kernel": ra.KERNEL_NAMES[rec["plan"]["kernel"]]}
+        out["roofline"] = rec["roofline"]
+        out["decode_detail"] = {"plan": rec["plan"], "combine_launch_ms": rec["combine"],
+                                "algorithmic_bytes_per_step": rec["algorithmic_bytes_per_step"],
+                                "wall_s_timed": round(r["wall_s"], 4)}
+        if not a.no_ablation and a.s == 0:
+            log("timing split-off ablation (s = 1)")
+            r1 = time_decode(prob, max(10, a.steps // 5), 3, 1, dev)
+            rec1 = decode_record(prob, r1, max(10, a.steps // 5), 3, "bench.py")
+            out["split_off"] = {"value": rec1["value"], "unit": "GB/s",
+                                "ms_per_step": rec1["ms_per_step"],
+                                "speedup_of_split": round(rec["value"] / rec1["value"], 3)}
+        if not a.no_cpu:
+            log("timing the fp64 oracle on the host")
+            out["cpu_baseline"] = oracle_decode_baseline(prob)
+    else:
+        out["unit"] = "TFLOP/s"
+    if is_prefill or (a.workload is None and not a.no_prefill):
+        pname = name if is_prefill else "gqa_causal_prefill"
+        pprob = prob if is_prefill else workload(pname)
+        log(f"timing prefill {pname}")
+        steps = a.steps
+        r = time_prefill(pprob, steps, a.warmup, dev)
+        flops = attention_flops(pprob)
+        ks = stats(r["kernel_ms"])
+        ms_step = r["wall_s"] * 1e3 / steps
+        achieved = flops / (ks["mean_ms"] * 1e-3) / 1e12
+        pre = {"value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+               "ms_per_step": round(ms_step, 5),
+               "config": {"workload": pname, "batch": pprob.batch, "q_len": pprob.lq,
+                          "kv_len": int(pprob.lens.max()), "q_heads": pprob.hq,
+                          "kv_heads": pprob.hkv, "head_dim": pprob.dqk,
+                          "causal": bool(pprob.causal)},
+               "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                            "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/"
+                                                   "prefill_d128.hip", f"prefill:{pname}")
+                            if os.path.exists(os.path.join(
+                                ROOT, "reduction_attention_gqa_amd/csrc/kernels/prefill_d128.hip"))
+                            else None,
+                            "kernel": "prefill kernel",
+                            "algorithmic_flops_per_launch": flops, "launch_ms": ks}}
+        if not a.no_cpu:
+            log("timing the fp64 oracle on prefill groups")
+            pre["cpu_baseline"] = oracle_prefill_baseline(pprob)
+        if is_prefill:
+            out.update({k: pre[k] for k in ("value", "ms_per_step", "config", "roofline")})
+            if "cpu_baseline" in pre:
+                out["cpu_baseline"] = pre["cpu_baseline"]
+        else:
+            out["prefill"] = pre
+    line = json.dumps(out)
+    print(line, flush=True)
+    if a.json_out:
+        with open(a.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -258,7 +258,7 @@ def oracle_decode_baseline(prob, budget_s=10.0):
                       f"numpy fp64 with {cores} BLAS threads"}
 
 
-def oracle_prefill_baseline(prob, groups=6):
+def oracle_prefill_baseline(prob, groups=24):
     """The fp64 oracle on `groups` (request, KV-head) groups of the prefill workload."""
     import numpy as np
     from threadpoolctl import threadpool_limits

@@ -23,6 +23,7 @@ SOURCES = [
     "kernels/generic.hip",
     "kernels/combine.hip",
     "kernels/decode_gqa_d128.hip",
+    "kernels/prefill_d128.hip",
 ]
 
 # Packed-fp32 VALU forms are switched off for all device code.

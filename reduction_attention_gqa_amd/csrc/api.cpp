@@ -136,6 +136,19 @@ bool gqa_d128_fits(const attn_problem* p, const void* q, const void* k, const vo
   return kbytes < (1ll << 31) && vbytes < (1ll << 31);
 }
 
+// Can the MFMA prefill kernel run on these pointers/strides?
+bool prefill_d128_fits(const attn_problem* p, const void* q, const void* k, const void* v,
+                       const void* o) {
+  if (p->dtype != ATTN_BF16 || p->head_dim_qk != 128 || p->head_dim_v != 128) return false;
+  if (!gqa_d128_fits(p, q, k, v)) return false;
+  const int oal = p->o_dtype == ATTN_BF16 ? 8 : 16;
+  if ((reinterpret_cast<uintptr_t>(o) & (oal - 1)) != 0) return false;
+  for (int a = 0; a < 3; ++a)
+    if (p->o_stride[a] & 3) return false;
+  const int64_t rows = (int64_t)(p->q_heads / p->kv_heads) * p->q_len;
+  return rows < (1ll << 30);
+}
+
 int check_ptrs(const void* a, const char* na, const void* b, const char* nb, const void* c,
                const char* nc) {
   if (!a) return fail(ATTN_ERR_ARG, "%s is NULL", na);
@@ -313,6 +326,8 @@ int attn_prefill(const attn_problem* problem, const void* q, const void* k, cons
   kp.s_max = 1;
   kp.split_mode = 0;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (prefill_d128_fits(p, q, k, v, o))
+    return hip_status(launch_prefill_d128(kp, s), "prefill_d128 launch");
   const int row_tiles = (int)ceil_div(kp.rows, kGenericRowTile);
   if (row_tiles > 65535) return fail(ATTN_ERR_UNSUPPORTED, "too many query rows per KV head");
   const dim3 grid(1, row_tiles, (unsigned)((int64_t)p->batch * p->kv_heads));

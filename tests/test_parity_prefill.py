@@ -106,3 +106,13 @@ def test_prefill_deterministic_bitwise():
     d.o.fill_(0)
     d.prefill()
     assert torch.equal(first, d.o)
+
+
+@pytest.mark.parametrize("hq,hkv,lq,lk", [(12, 4, 131, 131), (16, 2, 77, 200), (32, 2, 40, 40),
+                                          (2, 2, 513, 513)])
+def test_prefill_group_sizes_and_ragged_tiles(hq, hkv, lq, lk):
+    # G = 3, 8, 16, 1: rows (query, head) do not align with the 32-row waves
+    # or the 256-row workgroup tiles; key counts end mid-tile.
+    p = make_problem(dtype="bf16", batch=2, lq=lq, hq=hq, hkv=hkv, dqk=128, dv=128, kv_len=lk,
+                     seed=27 + hq, causal=True)
+    _gate(f"prefill G={hq // hkv} lq={lq} lk={lk}", p)

@@ -24,6 +24,7 @@ SOURCES = [
     "kernels/combine.hip",
     "kernels/decode_gqa_d128.hip",
     "kernels/prefill_d128.hip",
+    "kernels/decode_mla.hip",
 ]
 
 # Packed-fp32 VALU forms are switched off for all device code.

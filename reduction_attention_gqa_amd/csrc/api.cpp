@@ -114,7 +114,18 @@ int decode_family(const attn_problem* p) {
   const int rows = (p->q_heads / p->kv_heads) * p->q_len;
   if (p->dtype == ATTN_BF16 && p->head_dim_qk == 128 && p->head_dim_v == 128 && rows <= kGqaMaxRows)
     return ATTN_KERNEL_GQA_D128;
+  if (p->dtype == ATTN_BF16 && p->head_dim_qk == 576 && p->head_dim_v == 512 && rows <= kMlaRows)
+    return ATTN_KERNEL_MLA;
   return ATTN_KERNEL_GENERIC;
+}
+
+// Workgroups per compute unit the planner aims for, by kernel family.
+int target_wgs_per_cu(int family) {
+  switch (family) {
+    case ATTN_KERNEL_GQA_D128: return 4;
+    case ATTN_KERNEL_MLA: return 1;  // one 4-wave workgroup fills a CU's register file
+    default: return 4;
+  }
 }
 
 int tile_n_of(int family) {
@@ -134,6 +145,15 @@ bool gqa_d128_fits(const attn_problem* p, const void* q, const void* k, const vo
   const int64_t kbytes = (int64_t)p->kv_len_max * p->k_stride[1] * 2 + 256;
   const int64_t vbytes = (int64_t)p->kv_len_max * p->v_stride[1] * 2 + 256;
   return kbytes < (1ll << 31) && vbytes < (1ll << 31);
+}
+
+// Can the MLA kernel run?  V must be the first Dv columns of K (same pointer
+// and strides), with 16-byte rows and 32-bit buffer offsets.
+bool mla_fits(const attn_problem* p, const void* q, const void* k, const void* v) {
+  if (v != k) return false;
+  for (int a = 0; a < 3; ++a)
+    if (p->v_stride[a] != p->k_stride[a]) return false;
+  return gqa_d128_fits(p, q, k, v);
 }
 
 // Can the MFMA prefill kernel run on these pointers/strides?
@@ -218,9 +238,9 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
       s_max = std::min<int64_t>(s_request, max_tiles);
       chunk = ceil_div(ceil_div(lmax, s_max), tile_n) * tile_n;
     } else {
-      // Aim for about four workgroups per compute unit in total, with at least
-      // two tiles per split so the per-split prologue and epilogue stay small.
-      const int64_t target_wgs = (int64_t)cus * 4;
+      // Aim for a family-specific number of workgroups per compute unit, with at
+      // least two tiles per split so the per-split prologue and epilogue stay small.
+      const int64_t target_wgs = (int64_t)cus * target_wgs_per_cu(family);
       const int64_t work_tiles = tiles_total * units_per_req;
       int64_t chunk_tiles = ceil_div(work_tiles, target_wgs);
       chunk_tiles = std::max<int64_t>(chunk_tiles, 2);
@@ -246,7 +266,7 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
     out->grid[0] = (uint32_t)s_max;
     out->grid[1] = (uint32_t)p->kv_heads;
     out->grid[2] = (uint32_t)p->batch;
-    out->block = kGqaBlock;
+    out->block = family == ATTN_KERNEL_MLA ? kMlaBlock : kGqaBlock;
   }
   const uint64_t nrows = (uint64_t)p->batch * p->q_len * p->q_heads;
   out->ws_o_bytes = (uint64_t)s_max * nrows * p->head_dim_v * sizeof(float);
@@ -280,10 +300,11 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan, const 
   kp.split_mode = 1;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
-  if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_fits(p, q, k, v)) {
-    return hip_status(launch_decode_gqa_d128(kp, dim3(plan->s_max, p->kv_heads, p->batch), s),
-                      "decode_gqa_d128 launch");
-  }
+  const dim3 unit_grid(plan->s_max, p->kv_heads, p->batch);
+  if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_fits(p, q, k, v))
+    return hip_status(launch_decode_gqa_d128(kp, unit_grid, s), "decode_gqa_d128 launch");
+  if (plan->kernel == ATTN_KERNEL_MLA && mla_fits(p, q, k, v))
+    return hip_status(launch_decode_mla(kp, unit_grid, s), "decode_mla launch");
   const int row_tiles = (int)ceil_div(kp.rows, kGenericRowTile);
   const dim3 grid(plan->s_max, row_tiles, (unsigned)((int64_t)p->batch * p->kv_heads));
   return hip_status(launch_generic(kp, grid, dim3(kGenericBlock), s), "generic split launch");

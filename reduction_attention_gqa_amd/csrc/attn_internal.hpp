@@ -49,7 +49,7 @@ constexpr int kGqaTileN = 128;         // keys per GQA-D128 workgroup round (4 w
 constexpr int kGqaBlock = 256;
 constexpr int kGqaMaxRows = 16;
 constexpr int kMlaTileN = 32;          // keys per MLA tile
-constexpr int kMlaBlock = 256;
+constexpr int kMlaBlock = 512;         // 8 waves: 4 row groups x 2 halves
 constexpr int kMlaRows = 128;          // query rows per MLA workgroup
 
 }  // namespace attn

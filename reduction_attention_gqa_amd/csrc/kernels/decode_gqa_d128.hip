@@ -25,16 +25,35 @@ namespace {
 
 constexpr int NW = 4;            // waves per workgroup
 constexpr int KB = 32;           // keys per wave block
+constexpr int STEP = KB * NW;    // keys per workgroup round
 constexpr int D = 128;
-constexpr int VT_STRIDE = 36;    // u16 per LDS row of V^T (32 keys + 4 pad)
+constexpr int VROW = 288;        // bytes per V row in LDS (256 + 32 pad)
+constexpr int VTILE = KB * VROW; // one wave's V tile
 
-__global__ __launch_bounds__(NW * 64) void decode_gqa_d128_kernel(KParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_raw[NW * D * VT_STRIDE];  // 36 KiB
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4
+// of the 8 bytes addressed by lanes 4e + i / 4 (e = 0..3) as its element e.
+__device__ __forceinline__ i32x2_t ds_read_tr(const char* lds) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds));
+  return __builtin_bit_cast(i32x2_t, v);
+}
+
+// One wave's 32-key block in registers: K in the MFMA A-operand layout, V rows.
+struct Block {
+  i32x4_t k[8];
+  i32x4_t v[8];
+};
+
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_gqa_d128_kernel(KParams p) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[NW * VTILE];  // 36 KiB
   __shared__ float m_w[NW][16];
   __shared__ float l_w[NW][16];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  // Wave index, made visibly wave-uniform so the key loop below is a scalar loop.
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
@@ -62,12 +81,15 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_d128_kernel(KParams p) {
     }
   }
 
+  // The buffer ranges end at this split's last key: loads past it return zero
+  // without touching memory, so every load below is unconditional (which lets
+  // the compiler wait only for the block about to be used).
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
   const uint32_t kst = (uint32_t)(p.ks_t * 2);  // bytes between consecutive keys
   const uint32_t vst = (uint32_t)(p.vs_t * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)L * kst);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)L * vst);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)hi * kst);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)hi * vst);
 
   // Per-lane load offsets inside a block (bytes), independent of the block start.
   //   K: sub-block sb, d-block db -> key 16*sb + r, d = 32*db + 8*h4
@@ -75,7 +97,9 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_d128_kernel(KParams p) {
   const uint32_t k_lane = (uint32_t)r * kst + (uint32_t)(16 * h4);
   const uint32_t v_lane = (uint32_t)h4 * vst + (uint32_t)(16 * r);
 
-  uint16_t* vt = lds_raw + w * D * VT_STRIDE;  // this wave's V^T tile [128][VT_STRIDE]
+  char* vt = lds_raw + w * VTILE;  // this wave's row-major V tile [32][VROW]
+  // ds_read_tr addresses: lane l reads row l/4 (+16), columns 16*db + 4*(l%4).
+  const char* vt_rd = vt + (lane >> 2) * VROW + 8 * (lane & 3);
 
   f32x4_t oacc[8];
 #pragma unroll
@@ -85,36 +109,24 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_d128_kernel(KParams p) {
   const float sl2 = p.scale_log2;
   const int qlim = qi + L - p.Lq;  // causal: keys <= qlim are visible
 
-  i32x4_t kc[8], vc[8];
-  int kb = lo + KB * w;
-  auto load_block = [&](int kb0, i32x4_t* kr, i32x4_t* vr) {
-    const uint32_t kbase = (uint32_t)kb0 * kst;
-    const uint32_t vbase = (uint32_t)kb0 * vst;
+  auto load_block = [&](Block& x, int kb0) {
+    const uint32_t kbc = (uint32_t)min(kb0, hi);
+    const uint32_t kbase = kbc * kst;
+    const uint32_t vbase = kbc * vst;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int db = 0; db < 4; ++db)
-        kr[sb * 4 + db] = buf_load16(krs, kbase + k_lane + (uint32_t)(16 * sb) * kst + 64 * db);
+        x.k[sb * 4 + db] = buf_load16(krs, kbase + k_lane + (uint32_t)(16 * sb) * kst + 64 * db);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) vr[c] = buf_load16(vrs, vbase + v_lane + (uint32_t)(4 * c) * vst);
+    for (int c = 0; c < 8; ++c) x.v[c] = buf_load16(vrs, vbase + v_lane + (uint32_t)(4 * c) * vst);
   };
-  if (kb < hi) load_block(kb, kc, vc);
 
-  for (; kb < hi; kb += KB * NW) {
-    i32x4_t kn[8], vn[8];
-    const int kbn = kb + KB * NW;
-    if (kbn < hi) load_block(kbn, kn, vn);
-
-    // V^T into LDS: element e of load c is V[key 4c + h4][d 8r + e].
+  auto process_block = [&](const Block& x, int kb) {
+    // V rows into the wave's LDS tile: load c is row 4c + h4, bytes 16r .. 16r + 15.
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        const uint32_t wv = (uint32_t)vc[c][q2];
-        vt[(8 * r + 2 * q2) * VT_STRIDE + 4 * c + h4] = (uint16_t)(wv & 0xffff);
-        vt[(8 * r + 2 * q2 + 1) * VT_STRIDE + 4 * c + h4] = (uint16_t)(wv >> 16);
-      }
-    }
+    for (int c = 0; c < 8; ++c)
+      *reinterpret_cast<i32x4_t*>(vt + (4 * c + h4) * VROW + 16 * r) = x.v[c];
 
     // S^T = K Q^T for the two 16-key sub-blocks.
     f32x4_t s[2];
@@ -122,11 +134,11 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_d128_kernel(KParams p) {
     for (int sb = 0; sb < 2; ++sb) {
       f32x4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int db = 0; db < 4; ++db) a = mfma16x16x32(as_bf16x8(kc[sb * 4 + db]), qf[db], a);
+      for (int db = 0; db < 4; ++db) a = mfma16x16x32(as_bf16x8(x.k[sb * 4 + db]), qf[db], a);
       s[sb] = a;
     }
     // Scale to base-2 units and mask: lane holds keys kb + 16*sb + 4*h4 + i.
-    float x[8];
+    float xs[8];
     float mt = kNegInf;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -135,7 +147,7 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_d128_kernel(KParams p) {
         const int key = kb + 16 * sb + 4 * h4 + i;
         const bool vis = key < hi && (!p.causal || key <= qlim);
         const float v = vis ? s[sb][i] * sl2 : kNegInf;
-        x[sb * 4 + i] = v;
+        xs[sb * 4 + i] = v;
         mt = fmaxf(mt, v);
       }
     mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
@@ -149,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_d128_kernel(KParams p) {
     } else {
       alpha = fast_exp2(m_run - m_new);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(x[e] - m_new);
+      for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(xs[e] - m_new);
     }
     m_run = m_new;
     float ps = 0.f;
@@ -167,25 +179,35 @@ __global__ __launch_bounds__(NW * 64) void decode_gqa_d128_kernel(KParams p) {
     pk[3] = (int)pack_bf16x2(pv[6], pv[7]);
     const bf16x8_t pb = as_bf16x8(pk);
 
-    // O^T += V^T P^T: A lane holds V^T[d = 16*db + r][the same key slots].
+    // O^T += V^T P^T.  A lane holds V^T[d = 16*db + r][the same key slots]: the
+    // transposed LDS reads give keys 4*h4 + e (rows l/4) and 16 + 4*h4 + e.
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
-      const uint16_t* row = vt + (16 * db + r) * VT_STRIDE;
-      const i32x2_t lo4 = *reinterpret_cast<const i32x2_t*>(row + 4 * h4);
-      const i32x2_t hi4 = *reinterpret_cast<const i32x2_t*>(row + 16 + 4 * h4);
+      const i32x2_t v0 = ds_read_tr(vt_rd + 32 * db);
+      const i32x2_t v1 = ds_read_tr(vt_rd + 16 * VROW + 32 * db);
       i32x4_t va;
-      va[0] = lo4[0];
-      va[1] = lo4[1];
-      va[2] = hi4[0];
-      va[3] = hi4[1];
+      va[0] = v0[0];
+      va[1] = v0[1];
+      va[2] = v1[0];
+      va[3] = v1[1];
       oacc[db] = mfma16x16x32(as_bf16x8(va), pb, oacc[db]);
     }
+  };
 
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      kc[c] = kn[c];
-      vc[c] = vn[c];
-    }
+  // Ping-pong over two register blocks: while one block is processed, the
+  // next one is in flight.  Wave w takes blocks lo + 32*w + 128*i.
+  Block A, Bk;
+  int kb = lo + KB * w;
+  load_block(A, kb);
+  // The scheduling barriers keep each block's loads issued before the wait for
+  // the block being processed.
+  for (; kb < hi; kb += 2 * STEP) {
+    load_block(Bk, kb + STEP);
+    __builtin_amdgcn_sched_barrier(0);
+    process_block(A, kb);
+    load_block(A, kb + 2 * STEP);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kb + STEP < hi) process_block(Bk, kb + STEP);
   }
 
   // Merge the four waves' partial states.

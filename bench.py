@@ -4,7 +4,10 @@
 Default run (N = 1):
   * value: split-K decode throughput in algorithmic HBM GB/s on the
     Llama-3-8B-shaped GQA decode (B=32, 32/8 heads, D=128, 4096 keys, bf16);
-    one step = plan + split kernel + combine kernel over the whole batch.
+    one step = plan + one attn_decode call over the whole batch (for this
+    kernel family a single launch whose last split per (request, KV head)
+    merges the partials); the two-launch form (split kernel + combine kernel)
+    is timed beside it as an ablation.
   * prefill: causal GQA prefill (B=4, L=4096, 32/8 heads, D=128, bf16) in
     algorithmic TFLOP/s; one step = one fused prefill launch.
   * roofline of the dominant kernel of each (per-launch HIP-event times on the
@@ -53,6 +56,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--two-launch", action="store_true",
+                    help="time decode as split kernel + combine kernel instead of one launch")
     ap.add_argument("--json-out", default=None)
     return ap.parse_args()
 
@@ -137,7 +142,10 @@ def traffic_for(kernel_src, launches_key):
 
 # ----------------------------------------------------------------------- timing
 
-def time_decode(prob, steps, warmup, s_request, dev):
+def time_decode(prob, steps, warmup, s_request, dev, fused):
+    """Time `steps` decode steps.  fused: one attn_decode call per step (for the
+    GQA family a single launch that merges its own splits); otherwise the split
+    launch and the combine launch, timed separately."""
     import torch
     import reduction_attention_gqa_amd as ra
     qb, kvb, ob = decode_bytes(prob)
@@ -148,7 +156,7 @@ def time_decode(prob, steps, warmup, s_request, dev):
     probs = [ra.make_problem(q, k, v, o, kv_lens=lens, kv_len_max=prob.lcap, causal=prob.causal,
                              scale=prob.scale) for q, k, v in copies]
     plan = ra.attn_decode_plan(probs[0], s_request, lens_host)
-    ws_o, ws_lse = ra.workspace(plan, dev)
+    ws_o, ws_lse, ws_cnt = ra.workspace(plan, dev)
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
@@ -157,6 +165,11 @@ def time_decode(prob, steps, warmup, s_request, dev):
         pl = ra.attn_decode_plan(pr, s_request, lens_host)
         if ev is not None:
             ev[0].record(stream)
+        if fused:
+            ra.attn_decode(pr, pl, q, k, v, ws_o, ws_lse, ws_cnt, o, None, stream)
+            if ev is not None:
+                ev[1].record(stream)
+            return
         ra.attn_decode_split(pr, pl, q, k, v, ws_o, ws_lse, stream)
         if ev is not None:
             ev[1].record(stream)
@@ -179,10 +192,10 @@ def time_decode(prob, steps, warmup, s_request, dev):
         step(i, evs[i])
     torch.cuda.synchronize()
     split_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
-    comb_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
+    comb_ms = None if fused else sorted(e[1].elapsed_time(e[2]) for e in evs)
     del copies, probs
     return dict(plan=plan, wall_s=wall, split_ms=split_ms, combine_ms=comb_ms,
-                bytes=(qb, kvb, ob))
+                bytes=(qb, kvb, ob), fused=fused)
 
 
 def time_prefill(prob, steps, warmup, dev):
@@ -294,21 +307,25 @@ def decode_record(prob, r, steps, warmup, extra_src):
     total = qb + kvb + ob
     ms_step = r["wall_s"] * 1e3 / steps
     split = stats(r["split_ms"])
-    comb = stats(r["combine_ms"])
-    split_bytes = qb + kvb
-    achieved = split_bytes / (split["mean_ms"] * 1e-3) / 1e9
+    # The dominant kernel: the single fused launch (Q, K, V read + O written) or
+    # the split launch of the two-launch path (Q, K, V read).
+    kern_bytes = total if r["fused"] else qb + kvb
+    achieved = kern_bytes / (split["mean_ms"] * 1e-3) / 1e9
     plan = r["plan"]
-    traffic = traffic_for(extra_src, f"decode_split:{prob.name}")
+    traffic = traffic_for(extra_src, ("decode:" if r["fused"] else "decode_split:") + prob.name)
     return dict(
         value=round(total / (ms_step * 1e-3) / 1e9, 2), ms_per_step=round(ms_step, 5),
-        plan=dict(kernel=plan.kernel, s_max=plan.s_max, chunk=plan.chunk,
+        plan=dict(kernel=plan.kernel, s_max=plan.s_max, chunk=plan.chunk, n_items=plan.n_items,
                   grid=list(plan.grid), ws_bytes=int(plan.ws_o_bytes + plan.ws_lse_bytes)),
         roofline={"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                  "traffic": traffic, "kernel": "decode split kernel",
-                  "algorithmic_bytes_per_launch": split_bytes,
+                  "traffic": traffic,
+                  "kernel": ("decode kernel, single launch with in-kernel merge" if r["fused"]
+                             else "decode split kernel"),
+                  "algorithmic_bytes_per_launch": kern_bytes,
                   "launch_ms": split},
-        combine=comb, algorithmic_bytes_per_step=total)
+        combine=None if r["combine_ms"] is None else stats(r["combine_ms"]),
+        algorithmic_bytes_per_step=total)
 
 
 def main():
@@ -336,12 +353,13 @@ def main():
            "dtype": "bf16" if prob.dtype == "bf16" else "f32",
            "data": "synthetic (seeded i.i.d. N(0,1), bf16-rounded; no model weights needed)"}
     if not is_prefill:
-        log("timing decode")
-        r = time_decode(prob, a.steps, a.warmup, a.s, dev)
-        rec = decode_record(prob, r, a.steps, a.warmup,
-                            "reduction_attention_gqa_amd/csrc/kernels/"
-                            + {0: "generic.hip", 1: "decode_gqa_d128.hip",
-                               2: "decode_mla.hip"}[r["plan"].kernel])
+        # The GQA family runs as one fused launch; the others as split + combine.
+        fused = prob.dtype == "bf16" and prob.dqk == 128 and prob.dv == 128 and not a.two_launch
+        log(f"timing decode ({'single launch' if fused else 'split + combine'})")
+        r = time_decode(prob, a.steps, a.warmup, a.s, dev, fused)
+        src = ("reduction_attention_gqa_amd/csrc/kernels/"
+               + {0: "generic.hip", 1: "decode_gqa_d128.hip", 2: "decode_mla.hip"}[r["plan"].kernel])
+        rec = decode_record(prob, r, a.steps, a.warmup, src)
         out["unit"] = "GB/s"
         out["value"] = rec["value"]
         out["ms_per_step"] = rec["ms_per_step"]
@@ -352,13 +370,25 @@ def main():
                          "chunk": rec["plan"]["chunk"],
                          "kernel": ra.KERNEL_NAMES[rec["plan"]["kernel"]]}
         out["roofline"] = rec["roofline"]
-        out["decode_detail"] = {"plan": rec["plan"], "combine_launch_ms": rec["combine"],
+        out["decode_detail"] = {"plan": rec["plan"], "single_launch": fused,
+                                "combine_launch_ms": rec["combine"],
                                 "algorithmic_bytes_per_step": rec["algorithmic_bytes_per_step"],
                                 "wall_s_timed": round(r["wall_s"], 4)}
         if not a.no_ablation and a.s == 0:
+            n_abl = max(10, a.steps // 5)
+            if fused:
+                log("timing the two-launch ablation (split kernel + combine kernel)")
+                r2 = time_decode(prob, n_abl, 3, 0, dev, False)
+                rec2 = decode_record(prob, r2, n_abl, 3, src)
+                out["two_launch"] = {"value": rec2["value"], "unit": "GB/s",
+                                     "ms_per_step": rec2["ms_per_step"],
+                                     "split_launch_ms": rec2["roofline"]["launch_ms"]["mean_ms"],
+                                     "combine_launch_ms": rec2["combine"]["mean_ms"],
+                                     "speedup_of_single_launch":
+                                         round(rec["value"] / rec2["value"], 3)}
             log("timing split-off ablation (s = 1)")
-            r1 = time_decode(prob, max(10, a.steps // 5), 3, 1, dev)
-            rec1 = decode_record(prob, r1, max(10, a.steps // 5), 3, "bench.py")
+            r1 = time_decode(prob, n_abl, 3, 1, dev, fused)
+            rec1 = decode_record(prob, r1, n_abl, 3, src)
             out["split_off"] = {"value": rec1["value"], "unit": "GB/s",
                                 "ms_per_step": rec1["ms_per_step"],
                                 "speedup_of_split": round(rec["value"] / rec1["value"], 3)}

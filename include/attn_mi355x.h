@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ATTN_MI355X_VERSION 1
+#define ATTN_MI355X_VERSION 2
 
 typedef enum attn_dtype {
   ATTN_F32 = 0,   /* IEEE binary32 */
@@ -106,6 +106,9 @@ typedef struct attn_plan {
   uint32_t block;         /* split-kernel threads per workgroup */
   uint64_t ws_o_bytes;    /* bytes needed for ws_o: s_max*B*Lq*Hq*Dv floats */
   uint64_t ws_lse_bytes;  /* bytes needed for ws_lse: s_max*B*Lq*Hq floats */
+  uint64_t ws_cnt_bytes;  /* bytes needed for ws_cnt (attn_decode): B*Hkv int32 */
+  int64_t n_items;        /* (request, KV head, split) work items from kv_lens_host:
+                             Hkv * max(1, s_b) summed over requests */
   uint64_t problem_key;   /* fingerprint of the planned problem */
 } attn_plan;
 
@@ -150,6 +153,31 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan,
                       const void* q, const void* k, const void* v,
                       float* ws_o, size_t ws_o_bytes,
                       float* ws_lse, size_t ws_lse_bytes, void* stream);
+
+/*
+ * attn_decode - split decode in one call, in as few launches as the kernel
+ * family allows.  The result equals attn_decode_split followed by
+ * attn_combine (same O and LSE definitions).
+ *
+ * For the GQA D=128 family this is a single launch: when s_max == 1 each
+ * workgroup writes O directly; otherwise every split writes its partial to
+ * ws_o / ws_lse, and the last split of each (request, KV head) to finish
+ * (counted with an atomic in ws_cnt) merges the partials and writes O -- the
+ * combine of Cleave §4 without the second launch (the cost the pages' §7.4
+ * attributes to the two-launch design).  Requests with one split write O
+ * directly.  Other families run the split launch and then the combine launch.
+ *
+ * ws_cnt  DEVICE int32 [B * Hkv] (plan->ws_cnt_bytes).  It must be all zero
+ *         before the first call; every call leaves it all zero again.  One
+ *         workspace (ws_o, ws_lse, ws_cnt) serves one call at a time: calls
+ *         that overlap on the same workspace race.
+ * o, lse_out as for attn_combine.  Errors as for attn_decode_split.
+ */
+int attn_decode(const attn_problem* problem, const attn_plan* plan,
+                const void* q, const void* k, const void* v,
+                float* ws_o, size_t ws_o_bytes, float* ws_lse, size_t ws_lse_bytes,
+                int32_t* ws_cnt, size_t ws_cnt_bytes, void* o, float* lse_out,
+                void* stream);
 
 /*
  * attn_combine - the combine kernel (Cleave §4, Fig. 5(b)): reduces the

@@ -5,10 +5,11 @@ in ``include/attn_mi355x.h``); this package is its thin ctypes binding.
 """
 from ._lib import (ATTN_BF16, ATTN_ERR_ARG, ATTN_ERR_HIP, ATTN_ERR_UNSUPPORTED,
                    ATTN_ERR_WORKSPACE, ATTN_F32, ATTN_OK, EXPORTED, KERNEL_NAMES, AttnError,
-                   AttnPlan, AttnProblem, attn_combine, attn_decode_plan, attn_decode_split,
-                   attn_prefill, decode, load, make_problem, prefill, workspace)
+                   AttnPlan, AttnProblem, attn_combine, attn_decode, attn_decode_plan,
+                   attn_decode_split, attn_prefill, decode, load, make_problem, prefill, workspace)
 
 __all__ = ["ATTN_BF16", "ATTN_ERR_ARG", "ATTN_ERR_HIP", "ATTN_ERR_UNSUPPORTED",
            "ATTN_ERR_WORKSPACE", "ATTN_F32", "ATTN_OK", "EXPORTED", "KERNEL_NAMES", "AttnError",
-           "AttnPlan", "AttnProblem", "attn_combine", "attn_decode_plan", "attn_decode_split",
+           "AttnPlan", "AttnProblem", "attn_combine", "attn_decode", "attn_decode_plan",
+           "attn_decode_split",
            "attn_prefill", "decode", "load", "make_problem", "prefill", "workspace"]

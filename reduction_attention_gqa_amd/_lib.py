@@ -24,7 +24,7 @@ ATTN_ERR_WORKSPACE = 3
 ATTN_ERR_HIP = 4
 KERNEL_NAMES = {0: "generic", 1: "gqa_d128", 2: "mla"}
 
-EXPORTED = ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_prefill",
+EXPORTED = ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_decode", "attn_prefill",
             "attn_status_str", "attn_last_error", "attn_version")
 
 
@@ -47,6 +47,7 @@ class AttnPlan(ctypes.Structure):
         ("tile_n", ctypes.c_int32), ("rows_per_unit", ctypes.c_int32),
         ("row_tiles", ctypes.c_int32), ("grid", ctypes.c_uint32 * 3), ("block", ctypes.c_uint32),
         ("ws_o_bytes", ctypes.c_uint64), ("ws_lse_bytes", ctypes.c_uint64),
+        ("ws_cnt_bytes", ctypes.c_uint64), ("n_items", ctypes.c_int64),
         ("problem_key", ctypes.c_uint64),
     ]
 
@@ -74,8 +75,11 @@ def load() -> ctypes.CDLL:
                                      ctypes.c_int32, PL]
     lib.attn_decode_split.argtypes = [P, PL, V, V, V, V, ctypes.c_size_t, V, ctypes.c_size_t, V]
     lib.attn_combine.argtypes = [P, PL, V, V, V, V, V]
+    lib.attn_decode.argtypes = [P, PL, V, V, V, V, ctypes.c_size_t, V, ctypes.c_size_t, V,
+                                ctypes.c_size_t, V, V, V]
     lib.attn_prefill.argtypes = [P, V, V, V, V, V, V]
-    for f in ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_prefill"):
+    for f in ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_decode",
+              "attn_prefill"):
         getattr(lib, f).restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -173,6 +177,16 @@ def attn_combine(problem: AttnProblem, plan: AttnPlan, ws_o, ws_lse, o, lse_out=
                             _ptr(o), _ptr(lse_out), _stream(stream)))
 
 
+def attn_decode(problem: AttnProblem, plan: AttnPlan, q, k, v, ws_o, ws_lse, ws_cnt, o,
+                lse_out=None, stream=None) -> None:
+    lib = load()
+    _check(lib.attn_decode(ctypes.byref(problem), ctypes.byref(plan), _ptr(q), _ptr(k), _ptr(v),
+                           _ptr(ws_o), ws_o.numel() * ws_o.element_size(),
+                           _ptr(ws_lse), ws_lse.numel() * ws_lse.element_size(),
+                           _ptr(ws_cnt), ws_cnt.numel() * ws_cnt.element_size(),
+                           _ptr(o), _ptr(lse_out), _stream(stream)))
+
+
 def attn_prefill(problem: AttnProblem, q, k, v, o, lse_out=None, stream=None) -> None:
     lib = load()
     _check(lib.attn_prefill(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
@@ -180,23 +194,31 @@ def attn_prefill(problem: AttnProblem, q, k, v, o, lse_out=None, stream=None) ->
 
 
 def workspace(plan: AttnPlan, device):
-    """Allocate the split workspace a plan asks for (torch owns the memory)."""
+    """Allocate the workspace a plan asks for (torch owns the memory):
+    (ws_o, ws_lse, ws_cnt); the arrival counters start at zero, as attn_decode
+    requires, and every attn_decode call leaves them at zero."""
     import torch
     ws_o = torch.empty(max(1, plan.ws_o_bytes // 4), dtype=torch.float32, device=device)
     ws_lse = torch.empty(max(1, plan.ws_lse_bytes // 4), dtype=torch.float32, device=device)
-    return ws_o, ws_lse
+    ws_cnt = torch.zeros(max(1, plan.ws_cnt_bytes // 4), dtype=torch.int32, device=device)
+    return ws_o, ws_lse, ws_cnt
 
 
 def decode(q, k, v, o, *, kv_lens=None, kv_lens_host=None, causal=False, scale=0.0,
-           s_request=0, lse_out=None, stream=None, plan=None, ws=None):
-    """Split + combine in two launches; returns the plan used."""
+           s_request=0, lse_out=None, stream=None, plan=None, ws=None, fused=True):
+    """Split decode; returns the plan used.  fused=True calls attn_decode (one
+    launch where the kernel family allows), fused=False the split launch
+    followed by the combine launch."""
     prob = make_problem(q, k, v, o, kv_lens=kv_lens, causal=causal, scale=scale)
     if plan is None:
         plan = attn_decode_plan(prob, s_request, kv_lens_host)
     if ws is None:
         ws = workspace(plan, q.device)
-    attn_decode_split(prob, plan, q, k, v, ws[0], ws[1], stream)
-    attn_combine(prob, plan, ws[0], ws[1], o, lse_out, stream)
+    if fused:
+        attn_decode(prob, plan, q, k, v, ws[0], ws[1], ws[2], o, lse_out, stream)
+    else:
+        attn_decode_split(prob, plan, q, k, v, ws[0], ws[1], stream)
+        attn_combine(prob, plan, ws[0], ws[1], o, lse_out, stream)
     return plan
 
 

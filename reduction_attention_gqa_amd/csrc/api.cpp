@@ -122,7 +122,7 @@ int decode_family(const attn_problem* p) {
 // Workgroups per compute unit the planner aims for, by kernel family.
 int target_wgs_per_cu(int family) {
   switch (family) {
-    case ATTN_KERNEL_GQA_D128: return 4;
+    case ATTN_KERNEL_GQA_D128: return kGqaItemsPerCu;
     case ATTN_KERNEL_MLA: return 1;  // one 4-wave workgroup fills a CU's register file
     default: return 4;
   }
@@ -142,8 +142,9 @@ bool gqa_d128_fits(const attn_problem* p, const void* q, const void* k, const vo
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return false;
   for (int a = 0; a < 3; ++a)
     if ((p->q_stride[a] | p->k_stride[a] | p->v_stride[a]) & 7) return false;
-  const int64_t kbytes = (int64_t)p->kv_len_max * p->k_stride[1] * 2 + 256;
-  const int64_t vbytes = (int64_t)p->kv_len_max * p->v_stride[1] * 2 + 256;
+  // Buffer offsets reach up to 64 rows past the last key (clamped block starts).
+  const int64_t kbytes = ((int64_t)p->kv_len_max + 64) * p->k_stride[1] * 2 + 256;
+  const int64_t vbytes = ((int64_t)p->kv_len_max + 64) * p->v_stride[1] * 2 + 256;
   return kbytes < (1ll << 31) && vbytes < (1ll << 31);
 }
 
@@ -216,25 +217,43 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
     return fail(ATTN_ERR_HIP, "cannot query the compute-unit count of the current device");
 
   const int family = decode_family(p);
-  const int tile_n = tile_n_of(family);
+  int tile_n = tile_n_of(family);
   const int G = p->q_heads / p->kv_heads;
   const int rows = G * p->q_len;
   const int row_tiles = family == ATTN_KERNEL_GENERIC ? (int)ceil_div(rows, kGenericRowTile) : 1;
   const int64_t units_per_req = (int64_t)p->kv_heads * row_tiles;
 
   // Lengths as the kernels will see them.
-  int64_t lmax = 0, tiles_total = 0;
+  int64_t lmax = 0, tiles_total = 0, keys_total = 0;
   for (int b = 0; b < p->batch; ++b) {
     int64_t n = kv_lens_host ? kv_lens_host[b] : p->kv_len_max;
     n = std::min<int64_t>(std::max<int64_t>(n, 0), p->kv_len_max);
     lmax = std::max(lmax, n);
+    keys_total += n;
     tiles_total += ceil_div(n, tile_n);
+  }
+
+  // GQA D=128: when there are at least as many (request, KV head) units as
+  // compute units and no request is much longer than the mean, one split per
+  // request (no partials, no merge) with 8-wave workgroups; otherwise 4-wave
+  // workgroups and the key axis split to about kGqaItemsPerCu items per CU.
+  int waves = 4;
+  if (family == ATTN_KERNEL_GQA_D128 && p->batch > 0) {
+    const bool balanced = lmax * 4 * p->batch <= keys_total * 5;
+    const bool one_split = s_request == 1 ||
+        (s_request <= 0 && (int64_t)p->batch * p->kv_heads >= cus && balanced);
+    if (one_split) {
+      waves = 8;
+      tile_n = kGqaTileN * 2;
+    }
   }
 
   int64_t s_max = 1, chunk = tile_n;
   if (lmax > 0) {
     const int64_t max_tiles = ceil_div(lmax, tile_n);
-    if (s_request > 0) {
+    if (waves == 8) {
+      chunk = max_tiles * tile_n;
+    } else if (s_request > 0) {
       s_max = std::min<int64_t>(s_request, max_tiles);
       chunk = ceil_div(ceil_div(lmax, s_max), tile_n) * tile_n;
     } else {
@@ -250,6 +269,16 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
     s_max = ceil_div(lmax, chunk);
   }
   if (s_max > 65535) return fail(ATTN_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)s_max);
+  // Work items (request, KV head, split) of the one-dimensional GQA grid; an
+  // empty request still owns one item per KV head (it writes O = 0).
+  int64_t n_items = 0;
+  for (int b = 0; b < p->batch; ++b) {
+    int64_t n = kv_lens_host ? kv_lens_host[b] : p->kv_len_max;
+    n = std::min<int64_t>(std::max<int64_t>(n, 0), p->kv_len_max);
+    n_items += (int64_t)p->kv_heads * std::max<int64_t>(1, ceil_div(n, chunk));
+  }
+  if (n_items > (1ll << 31) - 64)
+    return fail(ATTN_ERR_UNSUPPORTED, "too many work items (%lld)", (long long)n_items);
 
   out->kernel = family;
   out->s_max = (int32_t)s_max;
@@ -262,15 +291,22 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
     out->grid[1] = (uint32_t)row_tiles;
     out->grid[2] = (uint32_t)((int64_t)p->batch * p->kv_heads);
     out->block = kGenericBlock;
+  } else if (family == ATTN_KERNEL_GQA_D128) {
+    out->grid[0] = (uint32_t)(ceil_div(n_items, 8) * 8);  // workgroup x runs on XCD x % 8
+    out->grid[1] = 1;
+    out->grid[2] = 1;
+    out->block = 64 * waves;
   } else {
     out->grid[0] = (uint32_t)s_max;
     out->grid[1] = (uint32_t)p->kv_heads;
     out->grid[2] = (uint32_t)p->batch;
-    out->block = family == ATTN_KERNEL_MLA ? kMlaBlock : kGqaBlock;
+    out->block = kMlaBlock;
   }
+  out->n_items = n_items;
   const uint64_t nrows = (uint64_t)p->batch * p->q_len * p->q_heads;
   out->ws_o_bytes = (uint64_t)s_max * nrows * p->head_dim_v * sizeof(float);
   out->ws_lse_bytes = (uint64_t)s_max * nrows * sizeof(float);
+  out->ws_cnt_bytes = (uint64_t)p->batch * p->kv_heads * sizeof(int32_t);
   out->problem_key = problem_key(p);
   return ATTN_OK;
 }
@@ -301,13 +337,54 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan, const 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
   const dim3 unit_grid(plan->s_max, p->kv_heads, p->batch);
+  kp.n_items = plan->n_items;
+  kp.waves = plan->block == 512 ? 8 : 4;
   if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_fits(p, q, k, v))
-    return hip_status(launch_decode_gqa_d128(kp, unit_grid, s), "decode_gqa_d128 launch");
+    return hip_status(launch_decode_gqa_d128(kp, s), "decode_gqa_d128 launch");
   if (plan->kernel == ATTN_KERNEL_MLA && mla_fits(p, q, k, v))
     return hip_status(launch_decode_mla(kp, unit_grid, s), "decode_mla launch");
   const int row_tiles = (int)ceil_div(kp.rows, kGenericRowTile);
   const dim3 grid(plan->s_max, row_tiles, (unsigned)((int64_t)p->batch * p->kv_heads));
   return hip_status(launch_generic(kp, grid, dim3(kGenericBlock), s), "generic split launch");
+}
+
+int attn_decode(const attn_problem* problem, const attn_plan* plan, const void* q, const void* k,
+                const void* v, float* ws_o, size_t ws_o_bytes, float* ws_lse, size_t ws_lse_bytes,
+                int32_t* ws_cnt, size_t ws_cnt_bytes, void* o, float* lse_out, void* stream) {
+  g_err[0] = 0;
+  if (int st = check_problem(problem)) return st;
+  const attn_problem* p = problem;
+  if (!plan) return fail(ATTN_ERR_ARG, "plan is NULL");
+  if (plan->problem_key != problem_key(p))
+    return fail(ATTN_ERR_ARG, "plan was made for a different problem");
+  if (plan->s_max < 1 || plan->chunk < 1) return fail(ATTN_ERR_ARG, "corrupt plan");
+  if (p->batch == 0) return ATTN_OK;
+  if (int st = check_ptrs(q, "q", k, "k", v, "v")) return st;
+  if (!o) return fail(ATTN_ERR_ARG, "o is NULL");
+  if (!ws_o || !ws_lse || !ws_cnt) return fail(ATTN_ERR_ARG, "workspace pointer is NULL");
+  if (ws_o_bytes < plan->ws_o_bytes || ws_lse_bytes < plan->ws_lse_bytes ||
+      ws_cnt_bytes < plan->ws_cnt_bytes)
+    return fail(ATTN_ERR_WORKSPACE, "workspace too small: need %llu + %llu + %llu bytes",
+                (unsigned long long)plan->ws_o_bytes, (unsigned long long)plan->ws_lse_bytes,
+                (unsigned long long)plan->ws_cnt_bytes);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_fits(p, q, k, v)) {
+    KParams kp = base_params(p);
+    kp.q = q; kp.k = k; kp.v = v; kp.o = o;
+    kp.ws_o = ws_o; kp.ws_lse = ws_lse; kp.lse_out = lse_out;
+    kp.counters = ws_cnt;
+    kp.chunk = plan->chunk;
+    kp.s_max = plan->s_max;
+    kp.n_items = plan->n_items;
+    kp.waves = plan->block == 512 ? 8 : 4;
+    kp.split_mode = plan->s_max == 1 ? 0 : 2;
+    return hip_status(launch_decode_gqa_d128(kp, s), "decode_gqa_d128 launch");
+  }
+  // Other kernel families: the split launch, then the combine launch.
+  if (int st = attn_decode_split(problem, plan, q, k, v, ws_o, ws_o_bytes, ws_lse, ws_lse_bytes,
+                                 stream))
+    return st;
+  return attn_combine(problem, plan, ws_o, ws_lse, o, lse_out, stream);
 }
 
 int attn_combine(const attn_problem* problem, const attn_plan* plan, const float* ws_o,

@@ -17,7 +17,9 @@ struct KParams {
   float* ws_o;          // split partials [s_max, B, Lq, Hq, Dv]
   float* ws_lse;        // split log-sum-exp [s_max, B, Lq, Hq]
   float* lse_out;       // optional [B, Lq, Hq]
+  int32_t* counters;    // split arrivals per (request, KV head), zero between calls (mode 2)
   const int32_t* kv_lens;  // device, may be null
+  int64_t n_items;      // (request, KV head, split) work items of the 1-D decode grid
   int64_t qs_b, qs_t, qs_h;
   int64_t ks_b, ks_t, ks_h;
   int64_t vs_b, vs_t, vs_h;
@@ -30,14 +32,15 @@ struct KParams {
   int32_t s_max;        // split slots
   int32_t rows;         // G * Lq rows per (request, KV head)
   int32_t row_tile;     // rows per workgroup (generic kernel)
-  int32_t split_mode;   // 1: write ws_o/ws_lse; 0: write o (+ lse_out)
+  int32_t split_mode;   // 0: write o (+ lse_out); 1: write ws_o/ws_lse; 2: 1 + in-kernel merge
+  int32_t waves;        // waves per workgroup of the GQA decode kernel (4 or 8)
   float scale_log2;     // tau * log2(e): scores are kept in base-2 units
 };
 
 // Launchers (one per kernel family).  Each returns a hipError_t.
 hipError_t launch_generic(const KParams& p, dim3 grid, dim3 block, hipStream_t s);
 hipError_t launch_combine(const KParams& p, hipStream_t s);
-hipError_t launch_decode_gqa_d128(const KParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_decode_gqa_d128(const KParams& p, hipStream_t s);  // 1-D item grid
 hipError_t launch_decode_mla(const KParams& p, dim3 grid, hipStream_t s);
 hipError_t launch_prefill_d128(const KParams& p, hipStream_t s);
 
@@ -46,6 +49,8 @@ constexpr int kGenericRowTile = 16;    // rows per generic workgroup
 constexpr int kGenericTileN = 64;      // keys per generic tile
 constexpr int kGenericBlock = 256;
 constexpr int kGqaTileN = 128;         // keys per GQA-D128 workgroup round (4 waves x 32)
+constexpr int kGqaItemsPerCu = 8;      // planner target: work items per compute unit
+constexpr int kGqaMinChunk = 256;      // planner floor on keys per split
 constexpr int kGqaBlock = 256;
 constexpr int kGqaMaxRows = 16;
 constexpr int kMlaTileN = 32;          // keys per MLA tile

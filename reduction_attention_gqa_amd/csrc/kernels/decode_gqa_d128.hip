@@ -2,9 +2,16 @@
 //
 // Decode has one query row per request, so output tiles are too few to fill
 // the GPU; the key axis is split into chunks that run as separate workgroups
-// (Cleave §2.2 "Split-K", §7.3 decode setting).  A workgroup owns one
-// (split, KV head, request) unit and packs the G query heads that share the KV
+// (Cleave §2.2 "Split-K", §7.3 decode setting).  A workgroup owns one work
+// item (request, KV head, split) and packs the G query heads that share the KV
 // head into the MFMA column dimension, so every K/V byte is read from HBM once.
+//
+// Work items are numbered with the split fastest, then the KV head, then the
+// request; XCD x (workgroups x, x + 8, ...) takes one contiguous range of
+// them, so each XCD streams a compact region of the K/V cache (all heads of
+// the same tokens together).  The item of a workgroup is found on the device
+// from the per-request key counts, so one compiled kernel serves any mix of
+// lengths.
 //
 // Within the workgroup the four waves take interleaved 32-key blocks of the
 // split and each keeps its own running max / sum / output (a second, on-chip
@@ -15,17 +22,22 @@
 //   online softmax on S^T columns (one query row per lane column)
 //   O^T[128 x 16] += V^T[128 x 32] * P^T[32 x 16]   8 MFMA 16x16x32
 // K arrives from HBM straight in the A-operand layout (16 bytes per lane);
-// V is transposed through a wave-private LDS tile.  Out-of-range keys are
-// zero-filled by the buffer loads (num_records bound) and masked to -inf.
+// V goes row-major into a wave-private LDS tile and comes back transposed.
+//
+// Epilogues (KParams::split_mode):
+//   0  one split per request: O = U / l straight to the output;
+//   1  every split writes its partial (O_j = U_j / l_j, LSE_j) to the
+//      workspace for the combine kernel (Cleave §4, Fig. 5(b));
+//   2  as 1, then the last split of each (request, KV head) to finish merges
+//      the partials itself (single launch); a request with one split writes
+//      O directly.
 #include "../attn_internal.hpp"
 #include "common.hpp"
 
 namespace attn {
 namespace {
 
-constexpr int NW = 4;            // waves per workgroup
 constexpr int KB = 32;           // keys per wave block
-constexpr int STEP = KB * NW;    // keys per workgroup round
 constexpr int D = 128;
 constexpr int VROW = 288;        // bytes per V row in LDS (256 + 32 pad)
 constexpr int VTILE = KB * VROW; // one wave's V tile
@@ -45,21 +57,133 @@ struct Block {
   i32x4_t v[8];
 };
 
+__device__ __forceinline__ int wave_incl_scan(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// The work item of this workgroup: request b, KV head kvh, split j (of sb) and
+// the request's key count L.  Returns false when the workgroup has none.
+// Every wave computes the same answer.
+__device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, int& kvh, int& j,
+                                          int& sb, int& L) {
+  const int64_t N = p.n_items;
+  const int x = blockIdx.x & 7;
+  const int64_t k = blockIdx.x >> 3;
+  const int64_t s0 = ((int64_t)x * N) >> 3, s1 = ((int64_t)(x + 1) * N) >> 3;
+  if (k >= s1 - s0) return false;
+  const int64_t item = s0 + k;
+  // Splits per request: s_b = ceil(L_b / chunk), at least 1 (an empty request
+  // still owns one item, which writes O = 0 and LSE = -inf), and at most the
+  // plan's s_max (the workspace has s_max slots; keys past s_max * chunk are
+  // outside the plan).
+  if (p.kv_lens == nullptr) {
+    sb = max(1, min((p.Lcap + p.chunk - 1) / p.chunk, p.s_max));
+    const int64_t per = (int64_t)p.Hkv * sb;
+    if (per == 0 || item >= per * p.B) return false;
+    b = (int)(item / per);
+    const int local = (int)(item - (int64_t)b * per);
+    kvh = local / sb;
+    j = local - kvh * sb;
+    L = p.Lcap;
+    return true;
+  }
+  // Items per request are Hkv * s_b; scan them 64 requests at a time.
+  int64_t base = 0;
+  for (int c = 0; c < p.B; c += 64) {
+    const int bb = c + lane;
+    int n = 0;
+    if (bb < p.B)
+      n = p.Hkv * max(1, min((kv_len_of(p.kv_lens, bb, p.Lcap) + p.chunk - 1) / p.chunk, p.s_max));
+    const int incl = wave_incl_scan(n, lane);
+    const int total = __shfl(incl, 63, 64);
+    if (item < base + total) {
+      const int rel = (int)(item - base);
+      const int idx = __builtin_amdgcn_readfirstlane(__popcll(__ballot(incl <= rel)));
+      const int excl = __builtin_amdgcn_readfirstlane(__shfl(incl - n, idx, 64));
+      const int nb = __builtin_amdgcn_readfirstlane(__shfl(n, idx, 64));
+      b = c + idx;
+      sb = nb / p.Hkv;
+      const int local = rel - excl;
+      kvh = local / sb;
+      j = local - kvh * sb;
+      L = kv_len_of(p.kv_lens, b, p.Lcap);
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+
+// Device-coherent (sc1) stores and loads of the single-launch merge.  They do
+// not stay dirty in one XCD's L2 and do not hit stale lines there, so a
+// partial published by one workgroup and read by another after the arrival
+// counter needs no whole-L2 write-back or invalidate (which a device-scope
+// release/acquire fence would issue for ordinary stores and loads).
+__device__ __forceinline__ void store_dev(float* ptr, float v) {
+  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* ptr) {
+  return __hip_atomic_load(const_cast<float*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Eight consecutive output values of one row to O (bf16 or f32), 16-byte
+// stores when the address allows.
+__device__ __forceinline__ void store_o8(const KParams& p, int64_t off, const f32x4_t& a,
+                                         const f32x4_t& c) {
+  if (p.o_bf16) {
+    uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + off;
+    uint4 pk;
+    pk.x = pack_bf16x2(a[0], a[1]);
+    pk.y = pack_bf16x2(a[2], a[3]);
+    pk.z = pack_bf16x2(c[0], c[1]);
+    pk.w = pack_bf16x2(c[2], c[3]);
+    if ((reinterpret_cast<uintptr_t>(op) & 15) == 0) {
+      *reinterpret_cast<uint4*>(op) = pk;
+    } else {
+      const uint32_t wv[4] = {pk.x, pk.y, pk.z, pk.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        op[2 * e] = (uint16_t)(wv[e] & 0xffff);
+        op[2 * e + 1] = (uint16_t)(wv[e] >> 16);
+      }
+    }
+  } else {
+    float* op = reinterpret_cast<float*>(p.o) + off;
+    if ((reinterpret_cast<uintptr_t>(op) & 15) == 0) {
+      reinterpret_cast<f32x4_t*>(op)[0] = a;
+      reinterpret_cast<f32x4_t*>(op)[1] = c;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        op[e] = a[e];
+        op[4 + e] = c[e];
+      }
+    }
+  }
+}
+
+// NW waves per workgroup (4 or 8); a workgroup round covers KB * NW keys.
+template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_gqa_d128_kernel(KParams p) {
-  __shared__ __attribute__((aligned(16))) char lds_raw[NW * VTILE];  // 36 KiB
+  constexpr int STEP = KB * NW;
+  __shared__ __attribute__((aligned(16))) char lds_raw[NW * VTILE];  // 36 or 72 KiB
   __shared__ float m_w[NW][16];
   __shared__ float l_w[NW][16];
 
   const int lane = threadIdx.x & 63;
   // Wave index, made visibly wave-uniform so the key loop below is a scalar loop.
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int j = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
-  const int L = kv_len_of(p.kv_lens, b, p.Lcap);
+  int b, kvh, j, sb, L;
+  if (!find_item(p, lane, b, kvh, j, sb, L)) return;
   const int lo = j * p.chunk;
-  if (lo >= L) return;
   const int hi = min(lo + p.chunk, L);
 
   const int r = lane & 15;   // MFMA column: query row within the KV group
@@ -223,14 +347,14 @@ void decode_gqa_d128_kernel(KParams p) {
 #pragma unroll
   for (int u = 0; u < NW; ++u) M = fmaxf(M, m_w[u][r]);
   const float fw = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - M);
-  float* osum = reinterpret_cast<float*>(lds_raw);  // [NW][16][128] floats (32 KiB)
+  float* osum = reinterpret_cast<float*>(lds_raw);  // [NW][16][128] floats
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
     for (int i = 0; i < 4; ++i) osum[(w * 16 + r) * D + 16 * db + 4 * h4 + i] = oacc[db][i] * fw;
   __syncthreads();
 
-  // 256 threads write 16 rows x 128 columns: thread -> row t/16, columns 8*(t%16) .. +7.
+  // Threads 0..255 write 16 rows x 128 columns: row t/16, columns 8*(t%16) .. +7.
   const int t = threadIdx.x;
   const int orow = t >> 4;
   const int oc = (t & 15) * 8;
@@ -257,18 +381,87 @@ void decode_gqa_d128_kernel(KParams p) {
     o1 *= inv;
     const int i = orow / p.G;
     const int h = kvh * p.G + orow % p.G;
-    const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + ((int64_t)b * p.Lq + i) * p.Hq + h;
-    f32x4_t* dst = reinterpret_cast<f32x4_t*>(p.ws_o + slot * D + oc);
-    dst[0] = o0;
-    dst[1] = o1;
-    if (oc == 0) p.ws_lse[slot] = Lt > 0.f ? (Mr + fast_log2(Lt)) * kLn2 : kNegInf;
+    const float lse = Lt > 0.f ? (Mr + fast_log2(Lt)) * kLn2 : kNegInf;
+    if (p.split_mode == 0 || (p.split_mode == 2 && sb == 1)) {
+      store_o8(p, (int64_t)b * p.os_b + (int64_t)i * p.os_t + (int64_t)h * p.os_h + oc, o0, o1);
+      if (oc == 0 && p.lse_out) p.lse_out[((int64_t)b * p.Lq + i) * p.Hq + h] = lse;
+    } else {
+      const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + ((int64_t)b * p.Lq + i) * p.Hq + h;
+      float* dst = p.ws_o + slot * D + oc;
+      if (p.split_mode == 1) {
+        reinterpret_cast<f32x4_t*>(dst)[0] = o0;
+        reinterpret_cast<f32x4_t*>(dst)[1] = o1;
+        if (oc == 0) p.ws_lse[slot] = lse;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          store_dev(dst + e, o0[e]);
+          store_dev(dst + 4 + e, o1[e]);
+        }
+        if (oc == 0) store_dev(p.ws_lse + slot, lse);
+      }
+    }
   }
+  if (p.split_mode != 2 || sb == 1) return;
+
+  // Single-launch merge: the last split of this (request, KV head) to arrive
+  // reduces the sb partials (the combine of Cleave §4, done in place).  Each
+  // wave waits until its device-coherent partial stores have completed, the
+  // barrier gathers the waves, and thread 0 counts the arrival; the last
+  // arrival reads the partials back with device-coherent loads issued after
+  // its counter update returned.
+  __shared__ int s_last;
+  wait_vmem();
+  __syncthreads();
+  const int unit = b * p.Hkv + kvh;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(p.counters + unit, 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == sb - 1;
+  __syncthreads();
+  if (!s_last) return;
+  if (orow < R) {
+    const int i = orow / p.G;
+    const int h = kvh * p.G + orow % p.G;
+    const int64_t nrows = (int64_t)p.B * p.Lq * p.Hq;
+    const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
+    float M = kNegInf;
+    for (int jj = 0; jj < sb; ++jj) M = fmaxf(M, load_dev(p.ws_lse + jj * nrows + row));
+    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (M != kNegInf) {
+      const float m2 = M * kLog2e;
+      for (int jj = 0; jj < sb; ++jj) {
+        const int64_t slot = jj * nrows + row;
+        const float wgt = fast_exp2(load_dev(p.ws_lse + slot) * kLog2e - m2);
+        const float* src = p.ws_o + slot * D + oc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a0[e] += wgt * load_dev(src + e);
+          a1[e] += wgt * load_dev(src + 4 + e);
+        }
+        wsum += wgt;
+      }
+      const float inv = 1.f / wsum;
+      a0 *= inv;
+      a1 *= inv;
+    }
+    store_o8(p, (int64_t)b * p.os_b + (int64_t)i * p.os_t + (int64_t)h * p.os_h + oc, a0, a1);
+    if (oc == 0 && p.lse_out)
+      p.lse_out[row] = M == kNegInf ? kNegInf : M + fast_log2(wsum) * kLn2;
+  }
+  if (threadIdx.x == 0)  // leave the counter zeroed for the next call
+    __hip_atomic_store(p.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
 
-hipError_t launch_decode_gqa_d128(const KParams& p, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL(decode_gqa_d128_kernel, grid, dim3(NW * 64), 0, s, p);
+hipError_t launch_decode_gqa_d128(const KParams& p, hipStream_t s) {
+  const int64_t nwg = (p.n_items + 7) / 8 * 8;
+  if (nwg == 0) return hipSuccess;
+  if (p.waves == 8)
+    hipLaunchKernelGGL(decode_gqa_d128_kernel<8>, dim3((unsigned)nwg), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL(decode_gqa_d128_kernel<4>, dim3((unsigned)nwg), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

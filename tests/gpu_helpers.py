@@ -69,13 +69,19 @@ class DeviceProblem:
         return ra.make_problem(self.q, self.k, self.v, self.o, kv_lens=self.lens,
                                kv_len_max=self.lcap, causal=p.causal, scale=p.scale)
 
-    def decode(self, s_request=0, plan=None):
+    def decode(self, s_request=0, plan=None, fused=True, ws=None):
+        """fused: attn_decode (one launch where the kernel family allows);
+        otherwise attn_decode_split then attn_combine."""
         prob = self.problem()
         if plan is None:
             plan = ra.attn_decode_plan(prob, s_request, list(self.prob.lens))
-        ws_o, ws_lse = ra.workspace(plan, DEV)
-        ra.attn_decode_split(prob, plan, self.q, self.k, self.v, ws_o, ws_lse)
-        ra.attn_combine(prob, plan, ws_o, ws_lse, self.o, self.lse)
+        ws_o, ws_lse, ws_cnt = ra.workspace(plan, DEV) if ws is None else ws
+        if fused:
+            ra.attn_decode(prob, plan, self.q, self.k, self.v, ws_o, ws_lse, ws_cnt, self.o,
+                           self.lse)
+        else:
+            ra.attn_decode_split(prob, plan, self.q, self.k, self.v, ws_o, ws_lse)
+            ra.attn_combine(prob, plan, ws_o, ws_lse, self.o, self.lse)
         torch.cuda.synchronize()
         return plan
 

@@ -61,7 +61,8 @@ def test_struct_layout_matches_c():
     # attn_problem: 12 int32/float fields, a pointer, 12 int64 strides.
     assert ctypes.sizeof(_lib.AttnProblem) == 12 * 4 + 8 + 12 * 8
     assert _lib.AttnProblem.kv_lens.offset == 48
-    assert ctypes.sizeof(_lib.AttnPlan) == 6 * 4 + 3 * 4 + 4 + 3 * 8
+    assert ctypes.sizeof(_lib.AttnPlan) == 6 * 4 + 3 * 4 + 4 + 5 * 8
+    assert _lib.AttnPlan.problem_key.offset == 40 + 4 * 8
 
 
 def problem(**kw):
@@ -114,6 +115,8 @@ def test_invalid_problem_is_rejected_everywhere(lib, field, value, code):
                                  1 << 30, fake, 1 << 30, None) == code
     assert lib.attn_combine(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, None,
                             None) == code
+    assert lib.attn_decode(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, fake, 1 << 30,
+                           fake, 1 << 30, fake, 1 << 30, fake, None, None) == code
 
 
 def test_negative_stride_and_nonfinite_scale(lib):
@@ -162,6 +165,19 @@ def test_workspace_too_small_and_plan_mismatch(lib):
     zeroed = _lib.AttnPlan()
     assert lib.attn_combine(ctypes.byref(p), ctypes.byref(zeroed), fake, fake, fake, None,
                             None) == ra.ATTN_ERR_ARG
+    # attn_decode: each of the three workspace buffers is checked, and o must be given.
+    big = 1 << 40
+    for sizes in ((plan.ws_o_bytes - 4, big, big), (big, plan.ws_lse_bytes - 4, big),
+                  (big, big, plan.ws_cnt_bytes - 4)):
+        assert lib.attn_decode(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake,
+                               fake, sizes[0], fake, sizes[1], fake, sizes[2], fake, None,
+                               None) == ra.ATTN_ERR_WORKSPACE
+    assert lib.attn_decode(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, fake, big,
+                           fake, big, None, big, fake, None, None) == ra.ATTN_ERR_ARG
+    assert lib.attn_decode(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, fake, big,
+                           fake, big, fake, big, None, None, None) == ra.ATTN_ERR_ARG
+    assert lib.attn_decode(ctypes.byref(other), ctypes.byref(plan), fake, fake, fake, fake, big,
+                           fake, big, fake, big, fake, None, None) == ra.ATTN_ERR_ARG
 
 
 def test_empty_batch_is_a_no_op(lib):
@@ -171,6 +187,8 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.attn_prefill(ctypes.byref(p), None, None, None, None, None, None) == 0
     assert lib.attn_decode_split(ctypes.byref(p), ctypes.byref(plan), None, None, None, None, 0,
                                  None, 0, None) == 0
+    assert lib.attn_decode(ctypes.byref(p), ctypes.byref(plan), None, None, None, None, 0,
+                           None, 0, None, 0, None, None, None) == 0
 
 
 # ---------------------------------------------------------------- planner
@@ -183,7 +201,18 @@ def _check_plan_invariants(p, plan, lens):
     nrows = p.batch * p.q_len * p.q_heads
     assert plan.ws_o_bytes == plan.s_max * nrows * p.head_dim_v * 4
     assert plan.ws_lse_bytes == plan.s_max * nrows * 4
-    assert plan.grid[0] == plan.s_max
+    assert plan.ws_cnt_bytes == p.batch * p.kv_heads * 4
+    # Work items (request, KV head, split), counted from the clamped host lengths;
+    # an empty request owns one item per KV head.
+    cap = p.kv_len_max
+    assert plan.n_items == sum(p.kv_heads * max(1, math.ceil(min(max(n, 0), cap) / plan.chunk))
+                               for n in lens)
+    if ra.KERNEL_NAMES[plan.kernel] == "gqa_d128":
+        # One-dimensional grid, a whole number of rounds over the 8 XCDs.
+        assert plan.grid[0] == 8 * math.ceil(plan.n_items / 8)
+        assert plan.grid[1] == plan.grid[2] == 1
+    else:
+        assert plan.grid[0] == plan.s_max
 
 
 def test_plan_tiny_fp32_decode_fixed_s4(lib):
@@ -202,9 +231,25 @@ def test_plan_llama_decode_uses_gqa_kernel_and_fills_the_gpu(lib):
     assert st == 0
     assert ra.KERNEL_NAMES[plan.kernel] == "gqa_d128"
     _check_plan_invariants(p, plan, [4096] * 32)
-    wgs = plan.s_max * p.kv_heads * p.batch
-    assert wgs >= 256          # at least one workgroup per compute unit
-    assert plan.s_max > 1      # one query row per request: the key axis must be split
+    assert plan.n_items >= 256  # at least one workgroup per compute unit
+    # 32 x 8 = 256 (request, KV head) units fill 256 CUs and the lengths are
+    # equal: one split per request, the key axis split across the 8 waves of
+    # each workgroup instead (no partials, no merge).
+    assert plan.s_max == 1 and plan.block == 512 and plan.tile_n == 256
+    # With more compute units than units the key axis is split across workgroups.
+    st, plan2 = plan_status(lib, p, num_cus=1024)
+    assert st == 0 and plan2.s_max > 1 and plan2.block == 256
+    _check_plan_invariants(p, plan2, [4096] * 32)
+
+
+def test_plan_unbalanced_lengths_split_across_workgroups(lib):
+    # One long request among short ones: a single split per request would leave
+    # the long one's workgroup running alone, so the key axis is split.
+    lens = [32768] + [1024] * 511
+    p = problem(batch=512, kv_len_max=32768)
+    st, plan = plan_status(lib, p, lens=lens)
+    assert st == 0 and plan.s_max > 1 and plan.block == 256
+    _check_plan_invariants(p, plan, lens)
 
 
 @pytest.mark.parametrize("s_req", [1, 2, 3, 7, 8, 16, 10_000])

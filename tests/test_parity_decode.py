@@ -1,4 +1,6 @@
-"""GPU parity of split decode + combine against the fp64 oracle (through the C ABI).
+"""GPU parity of split decode against the fp64 oracle (through the C ABI), both
+as two launches (attn_decode_split + attn_combine) and as attn_decode (one
+launch: the last split of each (request, KV head) merges the partials).
 
 Tolerances: bf16 inputs with fp32 accumulation, max abs 1e-2 and mean abs
 1e-3; the fp32 workload, 1e-5.  K/V rows past each request's length hold NaN,
@@ -30,27 +32,29 @@ def test_tiny_gqa_decode_f32_s4():
     assert_lse_close("tiny_gqa_decode_f32", d.lse_out(), lse, 1e-5)
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("s", [0, 1, 2, 3, 4, 7, 8, 16, 1000])
-def test_gqa_d128_split_sweep(s):
+def test_gqa_d128_split_sweep(s, fused):
     # Llama-3-8B heads (32/8, D=128) at reduced batch and ragged lengths that
     # end mid-tile; every split count must give the same answer within tolerance.
     p = make_problem(dtype="bf16", batch=3, lq=1, hq=32, hkv=8, dqk=128, dv=128,
                      kv_len=[1000, 2311, 37], lcap=2400, seed=1)
     d = DeviceProblem(p)
-    plan = d.decode(s_request=s)
+    plan = d.decode(s_request=s, fused=fused)
     o, lse = _oracle(p)
-    assert_close(f"gqa_d128 s={s} (kernel {plan.kernel}, s_max {plan.s_max})", d.out(), o,
-                 BF16_MAX, BF16_MEAN)
-    assert_lse_close(f"gqa_d128 s={s}", d.lse_out(), lse)
+    assert_close(f"gqa_d128 s={s} fused={fused} (kernel {plan.kernel}, s_max {plan.s_max})",
+                 d.out(), o, BF16_MAX, BF16_MEAN)
+    assert_lse_close(f"gqa_d128 s={s} fused={fused}", d.lse_out(), lse)
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("layout", ["token", "head"])
-def test_gqa_g8_ragged_log_uniform(layout):
+def test_gqa_g8_ragged_log_uniform(layout, fused):
     # Qwen3-32B heads (64/8): G = 8 query heads per KV head.
     p = make_problem(dtype="bf16", batch=6, lq=1, hq=64, hkv=8, dqk=128, dv=128,
                      kv_len=(128, 3000), lcap=3000, seed=2)
     d = DeviceProblem(p, layout=layout)
-    d.decode()
+    d.decode(fused=fused)
     o, lse = _oracle(p)
     assert_close(f"gqa_g8 {layout}", d.out(), o, BF16_MAX, BF16_MEAN)
     assert_lse_close(f"gqa_g8 {layout}", d.lse_out(), lse)
@@ -105,15 +109,38 @@ def test_generic_kernel_bf16_head_dim_64():
     assert_close("generic d64", d.out(), o, BF16_MAX, BF16_MEAN)
 
 
-def test_deterministic_bitwise():
+@pytest.mark.parametrize("fused", [False, True])
+def test_deterministic_bitwise(fused):
+    # The single-launch merge always sums the splits in split order, whichever
+    # split arrives last, so repeated calls agree bit for bit.
     p = make_problem(dtype="bf16", batch=2, lq=1, hq=32, hkv=8, dqk=128, dv=128,
                      kv_len=[2048, 999], seed=7)
     d = DeviceProblem(p)
-    plan = d.decode()
+    plan = d.decode(fused=fused)
     first = d.o.clone()
-    d.o.fill_(0)
-    d.decode(plan=plan)
-    assert torch.equal(first, d.o)
+    for _ in range(3):
+        d.o.fill_(0)
+        d.decode(plan=plan, fused=fused)
+        assert torch.equal(first, d.o)
+
+
+def test_fused_decode_reuses_workspace_and_leaves_counters_zero():
+    # One problem (ragged, with a one-key request) twice through one workspace:
+    # the arrival counters must be back at zero after every call.
+    import reduction_attention_gqa_amd as ra
+    p = make_problem(dtype="bf16", batch=4, lq=1, hq=32, hkv=8, dqk=128, dv=128,
+                     kv_len=[4000, 300, 1, 2500], lcap=4096, seed=8)
+    d = DeviceProblem(p)
+    plan = ra.attn_decode_plan(d.problem(), 8, list(p.lens))
+    assert plan.s_max > 1
+    ws = ra.workspace(plan, "cuda")
+    o, lse = _oracle(p)
+    for _ in range(2):
+        d.o.fill_(float("nan"))
+        d.decode(plan=plan, ws=ws)
+        assert int(ws[2].abs().sum()) == 0
+        assert_close("fused reuse", d.out(), o, BF16_MAX, BF16_MEAN)
+        assert_lse_close("fused reuse", d.lse_out(), lse)
 
 
 def _sample_rows(p, n, seed):
@@ -124,13 +151,14 @@ def _sample_rows(p, n, seed):
     return sorted(rows)
 
 
+@pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name", ["llama3_8b_gqa_decode", "ragged_decode_qwen3_32b"])
-def test_full_size_decode_sampled_rows(name):
+def test_full_size_decode_sampled_rows(name, fused):
     # The full workload in the launch configuration the benchmark times
-    # (planner-chosen s); the oracle checks sampled outputs one by one.
+    # (planner-chosen s, attn_decode); the oracle checks sampled outputs one by one.
     p = workload(name)
     d = DeviceProblem(p)
-    plan = d.decode()
+    plan = d.decode(fused=fused)
     print(f"[plan] {name}: kernel={plan.kernel} s_max={plan.s_max} chunk={plan.chunk}", flush=True)
     out, lse_g = d.out(), d.lse_out()
     assert not np.isnan(out).any()

@@ -1,21 +1,35 @@
 // Fused causal / non-causal GQA prefill for bf16, Dqk = Dv = 128.
 //
-// One workgroup (8 waves) computes one 256-row tile of one (request, KV head)
+// One workgroup (4 waves) computes one 256-row tile of one (request, KV head)
 // group; a row is a (query position, head of the group) pair, so the G query
 // heads that share a KV head share every K/V tile staged in LDS.  This is the
 // inter-threadblock output tiling of Cleave §5.1 / §5.3 ([b_O, d] output tiles,
 // one per workgroup) with GQA packing added.  Inside, the key axis is tiled in
-// 64-key steps (iterative tiling, §5.1 and §5.3); the exp tile feeds both the
+// 32-key steps (iterative tiling, §5.1 and §5.3); the exp tile feeds both the
 // row sum and the V-matmul in the same step (horizontal fusion, §5.1); the
 // division by the row sum comes after the V-matmul (§2.2, Fig. 2); the Q tile
-// is loaded once, outside the key loop (§6.1).  The running max rescaling is
-// the online-softmax update.
+// is loaded once, outside the key loop (§6.1).
 //
-// Per wave (32 rows) and 64-key tile, keys on the MFMA rows:
-//   S^T[64 x 32]  = K[64 x 128] Q^T[128 x 32]     2 x 8 MFMA 32x32x16 bf16
-//   O^T[128 x 32] += V^T[128 x 64] P^T[64 x 32]   4 x 4 MFMA 32x32x16 bf16
-// K is read from LDS in the A-operand layout (16 bytes per lane); V is read
-// transposed from its row-major LDS tile with ds_read_b64_tr_b16.
+// Each wave owns 64 rows as two 32-row MFMA column blocks, so every K or V
+// fragment read from LDS feeds two MFMAs.  Per wave and 32-key tile, keys on
+// the MFMA rows:
+//   S^T[32 x 64]  = K[32 x 128] Q^T[128 x 64]     2 x 8 MFMA 32x32x16 bf16
+//   O^T[128 x 64] += V^T[128 x 32] P^T[32 x 64]   2 x 8 MFMA 32x32x16 bf16
+// One wave per SIMD (512 registers each): the matrix cores are kept busy by
+// interleaving, within the wave, the scores of tile i + 1 with the
+// exponentials of tile i, and the V-matmul of tile i with the max of tile
+// i + 1 (fixed interleaves pinned with scheduling barriers).
+//
+// The running max is updated lazily: a row's reference max moves (and its
+// accumulator and row sum are rescaled) only when the row's max grows by more
+// than 2^8; otherwise P = 2^(s - m_ref) <= 256 is used as is.  Row sum and
+// accumulator always share one reference, so O = U / l is unchanged.
+//
+// K/V tiles go HBM -> LDS by buffer loads that write LDS directly, four stages
+// deep (tile i + 3 is in flight while tile i is consumed).  A tile row is 256
+// bytes, and the 16-byte chunk c of row r sits at chunk c ^ swz(r), which keeps
+// both the K operand reads (16 keys, one chunk each) and the transposed V reads
+// (4 keys, 4 chunks each) free of bank conflicts.
 //
 // Causal tiles beyond a tile's diagonal are never loaded; masking runs only on
 // tiles that straddle the diagonal or the end of the keys.  Workgroups are
@@ -28,17 +42,17 @@
 namespace attn {
 namespace {
 
-constexpr int NW = 8;                 // waves per workgroup
+constexpr int NW = 4;                 // waves per workgroup
 constexpr int NT = NW * 64;
-constexpr int ROWS = NW * 32;         // rows per workgroup
-constexpr int TK = 64;                // keys per tile
-constexpr int D = 128;
-constexpr int K_STRIDE = 272;         // bytes per K row in LDS (256 + 16 pad)
-constexpr int V_STRIDE = 288;         // bytes per V row in LDS (256 + 32 pad)
-constexpr int K_TILE = TK * K_STRIDE;
-constexpr int V_TILE = TK * V_STRIDE;
-constexpr int STAGE = K_TILE + V_TILE;
-constexpr int LDS_BYTES = 2 * STAGE;  // double buffered
+constexpr int RPW = 64;               // rows per wave (two 32-row column blocks)
+constexpr int ROWS = NW * RPW;        // rows per workgroup
+constexpr int TK = 32;                // keys per tile
+constexpr int RB = 256;               // bytes per K or V row (128 bf16)
+constexpr int KT = TK * RB;           // 8 KiB: one K (or V) tile
+constexpr int STAGE = 2 * KT;         // K tile then V tile
+constexpr int NSTAGE = 4;
+constexpr int LDS_BYTES = NSTAGE * STAGE;  // 64 KiB
+constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -49,11 +63,16 @@ __device__ __forceinline__ i32x2_t ds_read_tr(const char* lds) {
   return __builtin_bit_cast(i32x2_t, v);
 }
 
-__global__ __launch_bounds__(NT) void prefill_d128_kernel(KParams p, int nrt) {
+// Chunk swizzle: swap the two 2-bit fields of r mod 16.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Byte offset of (row, 16-byte chunk c) inside a K or V tile.
+__device__ __forceinline__ int tile_off(int row, int c) { return row * RB + 16 * (c ^ swz(row)); }
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void prefill_d128_kernel(KParams p, int nrt) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   // Workgroup -> (group, row tile): heaviest row tiles first; per-XCD groups.
   const int ngroups = p.B * p.Hkv;
@@ -75,195 +94,322 @@ __global__ __launch_bounds__(NT) void prefill_d128_kernel(KParams p, int nrt) {
   const int r0 = rt * ROWS;
   const int off = L - p.Lq;        // causal: row position i sees keys <= i + off
 
-  // This wave's rows and key range.
-  const int c = lane & 31;          // MFMA column = row of this lane
-  const int h = lane >> 5;          // lane half
-  const int rw0 = r0 + 32 * w;
-  const int r = rw0 + c;
-  const int qi = r / G;
-  const int wave_rows = max(0, min(32, R - rw0));
-  int kend_w = 0;                  // keys [0, kend_w) can be visible to this wave
-  if (wave_rows > 0) {
-    kend_w = L;
-    if (p.causal) kend_w = min(L, (rw0 + wave_rows - 1) / G + off + 1);
-    kend_w = max(kend_w, 0);
+  // This wave's rows: lane (c, h) holds row rw0 + 32*cb + c of column block cb.
+  const int c = lane & 31;
+  const int h = lane >> 5;
+  const int rw0 = r0 + RPW * w;
+  int qi[2], qlim[2];
+  bool row_ok[2];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int r = rw0 + 32 * cb + c;
+    qi[cb] = r / G;
+    row_ok[cb] = r < R;
+    qlim[cb] = qi[cb] + off;       // last visible key of this row (causal)
   }
   const int wg_rows = max(0, min(ROWS, R - r0));
-  int kend = L;
+  int kend = L;                    // keys [0, kend) are visible to some row of the workgroup
   if (p.causal) kend = min(L, (r0 + wg_rows - 1) / G + off + 1);
   kend = max(kend, 0);
-  // First key that some row of the wave cannot see (causal diagonal).
-  const int kfull_w = p.causal ? max(0, rw0 / G + off + 1) : L;
+  // Keys below kfull_w are visible to every row of this wave.
+  const int kfull_w = p.causal ? max(0, min(L, rw0 / G + off + 1)) : L;
 
-  // Q^T as the B operand (hoisted): lane holds Q[row r][16*ks + 8*h .. +7].
-  bf16x8_t qf[8];
+  // Q^T as the B operand (hoisted): lane holds Q[row][16*ks + 8*h .. +7].
+  bf16x8_t qf[2][8];
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
-    const int qh = kvh * G + (r % G);
-    const int64_t qoff = (int64_t)b * p.qs_b + (int64_t)qi * p.qs_t + (int64_t)qh * p.qs_h;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      i32x4_t v = {0, 0, 0, 0};
-      if (r < R) v = *reinterpret_cast<const i32x4_t*>(qp + qoff + 16 * ks + 8 * h);
-      qf[ks] = as_bf16x8(v);
+    for (int cb = 0; cb < 2; ++cb) {
+      const int r = rw0 + 32 * cb + c;
+      const int qh = kvh * G + (r % G);
+      const int64_t qoff = (int64_t)b * p.qs_b + (int64_t)qi[cb] * p.qs_t + (int64_t)qh * p.qs_h;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        i32x4_t v = {0, 0, 0, 0};
+        if (row_ok[cb]) v = *reinterpret_cast<const i32x4_t*>(qp + qoff + 16 * ks + 8 * h);
+        qf[cb][ks] = as_bf16x8(v);
+      }
     }
+    // Wait for Q here, once, rather than at the loop head on every tile.
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[cb][ks]));
   }
 
-  // K/V global -> LDS copy: thread t moves chunks t and t + NT of each tile
-  // (chunk x: key x / 16, 16-byte column x % 16).
+  // Tile copy HBM -> LDS without registers: each wave fills rows 4*(2w + u) ..
+  // + 3 (u = 0, 1) of the K tile and of the V tile; lane l writes the 16-byte
+  // slot (row 4*(2w+u) + l/16, position l%16), which holds chunk (l%16) ^ swz(row).
+  // The buffer ranges end at the last key, so rows past it are zero.
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
   const uint32_t kst = (uint32_t)(p.ks_t * 2), vst = (uint32_t)(p.vs_t * 2);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)L * kst);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)L * vst);
-  const int ck0 = t >> 4, cc = t & 15;  // chunk t: key ck0, column cc; chunk t+NT: key ck0+32
-  i32x4_t stg[4];
-  auto gload = [&](int k0) {
-    stg[0] = buf_load16(krs, (uint32_t)(k0 + ck0) * kst + 16 * cc);
-    stg[1] = buf_load16(krs, (uint32_t)(k0 + ck0 + 32) * kst + 16 * cc);
-    stg[2] = buf_load16(vrs, (uint32_t)(k0 + ck0) * vst + 16 * cc);
-    stg[3] = buf_load16(vrs, (uint32_t)(k0 + ck0 + 32) * vst + 16 * cc);
-  };
-  auto lstore = [&](int stage) {
-    char* kl = smem + stage * STAGE;
-    char* vl = kl + K_TILE;
-    *reinterpret_cast<i32x4_t*>(kl + ck0 * K_STRIDE + 16 * cc) = stg[0];
-    *reinterpret_cast<i32x4_t*>(kl + (ck0 + 32) * K_STRIDE + 16 * cc) = stg[1];
-    *reinterpret_cast<i32x4_t*>(vl + ck0 * V_STRIDE + 16 * cc) = stg[2];
-    *reinterpret_cast<i32x4_t*>(vl + (ck0 + 32) * V_STRIDE + 16 * cc) = stg[3];
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(smem);
+  uint32_t k_voff[2], v_voff[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int row = 4 * (2 * w + u) + (lane >> 4);
+    const int chunk = (lane & 15) ^ swz(row);
+    k_voff[u] = (uint32_t)row * kst + 16 * chunk;
+    v_voff[u] = (uint32_t)row * vst + 16 * chunk;
+  }
+  // The whole byte offset goes in the per-lane offset, which the buffer range
+  // check covers.  The DMA is issued from inline asm so the compiler does not
+  // pair it with conservative waits; its completion is awaited explicitly
+  // before each barrier that publishes a tile.
+  auto dma_tile = [&](int k0, int stage) {
+    const uint32_t base = smem_lds + (uint32_t)(stage * STAGE);
+    const uint32_t ksoff = (uint32_t)k0 * kst, vsoff = (uint32_t)k0 * vst;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t m0k = base + (uint32_t)((2 * w + u) * 1024);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(m0k), "v"(k_voff[u] + ksoff), "s"(krs) : "memory", "m0");
+      const uint32_t m0v = m0k + KT;
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :: "s"(m0v), "v"(v_voff[u] + vsoff), "s"(vrs) : "memory", "m0");
+    }
   };
 
-  f32x16_t oacc[4];
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
-  float m_run = kNegInf, l_part = 0.f;
-  const float sl2 = p.scale_log2;
-  const int qlim = qi + off;  // last visible key of this lane's row (causal)
-
-  // Per-lane LDS byte offsets that do not depend on the tile.
-  const int k_rd = c * K_STRIDE + 16 * h;                     // + 32*ks + 32*kb*K_STRIDE
+  // Transposed V read: 16-lane group gq reads keys 4*(gq>>1) + li/4 (+8), element
+  // columns 32*db + 16*(gq&1) + 4*(li&3) .. +3.
   const int gq = lane >> 4, li = lane & 15;
-  const int v_rd = (4 * (gq >> 1) + (li >> 2)) * V_STRIDE + 2 * (16 * (gq & 1) + 4 * (li & 3));
+  const int vkey = 4 * (gq >> 1) + (li >> 2);
+  const int vcol = 16 * (gq & 1) + 4 * (li & 3);
+
+  f32x16_t oacc[2][4];
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[cb][db][e] = 0.f;
+  float m_ref[2] = {kNegInf, kNegInf};   // reference max per row (base-2 units)
+  float l_part[2] = {0.f, 0.f};
+  const float sl2 = p.scale_log2;
 
   const int ntiles = (kend + TK - 1) / TK;
+  // Leading tiles that need no mask for any row of this wave; the remaining
+  // ones (the diagonal, the ragged end, rows past R) are masked.
+  const int n_clean = (rw0 + RPW <= R) ? min(kfull_w, L) / TK : 0;
+
+  auto kread = [&](int stage, int ks) {  // K fragment: key c, 16-wide k-step ks
+    return *reinterpret_cast<const i32x4_t*>(smem + stage * STAGE + tile_off(c, 2 * ks + h));
+  };
+  // Masked scores are set to -inf.
+  auto mask_scores = [&](f32x16_t* sc, int k0) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + 8 * (e >> 2) + 4 * h + (e & 3);
+        const bool vis = key < L && (!p.causal || key <= qlim[cb]) && row_ok[cb];
+        sc[cb][e] = vis ? sc[cb][e] : kNegInf;
+      }
+  };
+
+  f32x16_t s_cur[2], s_nxt[2];
+  float mt_cur[2] = {kNegInf, kNegInf};
   if (ntiles > 0) {
-    gload(0);
-    lstore(0);
-  }
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int k0 = it * TK;
-    const bool more = it + 1 < ntiles;
-    if (more) gload(k0 + TK);
-    if (k0 < kend_w) {
-      const char* kl = smem + (it & 1) * STAGE;
-      const char* vl = kl + K_TILE;
-      // S^T for the two 32-key blocks.
-      f32x16_t s[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16_t a;
+    for (int t = 0; t < 3; ++t)
+      if (t < ntiles) dma_tile(t * TK, t);
+    // Tiles 0 and 1 landed (step 0 reads K of tile 1); tile 2 may stay in
+    // flight (loads finish in order, four DMA instructions per tile and wave).
+    if (ntiles >= 3)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-        for (int e = 0; e < 16; ++e) a[e] = 0.f;
+    for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const i32x4_t kf = *reinterpret_cast<const i32x4_t*>(kl + kb * 32 * K_STRIDE + k_rd + 32 * ks);
-          a = mfma32x32x16(as_bf16x8(kf), qf[ks], a);
-        }
-        s[kb] = a;
-      }
-      // Scale to base-2 units; mask only tiles that cross the diagonal or the end.
-      const bool need_mask = (k0 + TK > kfull_w) || (k0 + TK > L) || (r >= R);
-      float mt = kNegInf;
+      for (int e = 0; e < 16; ++e) s_cur[cb][e] = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float v = s[kb][e] * sl2;
-          if (need_mask) {
-            const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * h + (e & 3);
-            const bool vis = key < L && (!p.causal || key <= qlim) && r < R;
-            v = vis ? v : kNegInf;
-          }
-          s[kb][e] = v;
-          mt = fmaxf(mt, v);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt);
-      float alpha = 1.f;
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      if (m_new != kNegInf) alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pv = fast_exp2(s[kb][e] - m_use);
-          s[kb][e] = pv;
-          ps += pv;
-        }
-      l_part = l_part * alpha + ps;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-
-      // O^T += V^T P^T, four 16-key k-steps.
-#pragma unroll
-      for (int ts = 0; ts < 4; ++ts) {
-        const int kb = ts >> 1, i0 = 2 * (ts & 1);
-        i32x4_t pk;
-        pk[0] = (int)pack_bf16x2(s[kb][4 * i0 + 0], s[kb][4 * i0 + 1]);
-        pk[1] = (int)pack_bf16x2(s[kb][4 * i0 + 2], s[kb][4 * i0 + 3]);
-        pk[2] = (int)pack_bf16x2(s[kb][4 * i0 + 4], s[kb][4 * i0 + 5]);
-        pk[3] = (int)pack_bf16x2(s[kb][4 * i0 + 6], s[kb][4 * i0 + 7]);
-        const bf16x8_t pb = as_bf16x8(pk);
-        const char* vrow = vl + (16 * ts) * V_STRIDE + v_rd;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const i32x2_t lo = ds_read_tr(vrow + 64 * db);
-          const i32x2_t hi = ds_read_tr(vrow + 8 * V_STRIDE + 64 * db);
-          i32x4_t va;
-          va[0] = lo[0];
-          va[1] = lo[1];
-          va[2] = hi[0];
-          va[3] = hi[1];
-          oacc[db] = mfma32x32x16(as_bf16x8(va), pb, oacc[db]);
-        }
-      }
+      for (int ks = 0; ks < 8; ++ks)
+        s_cur[cb] = mfma32x32x16(as_bf16x8(kread(0, ks)), qf[cb][ks], s_cur[cb]);
     }
-    if (more) lstore((it + 1) & 1);
-    __syncthreads();
+    if (n_clean == 0) mask_scores(s_cur, 0);
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      float m = kNegInf;
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) m = fmaxf(m, fmaxf(s_cur[cb][e], s_cur[cb][e + 1]));
+      mt_cur[cb] = fmaxf(m, __shfl_xor(m, 32, 64)) * sl2;
+    }
   }
+
+  // One key tile it, whose scores s_cur are already masked and whose row maxes
+  // are mt_cur.  next: tile it + 1 exists; mask_next: it needs the mask.  Both
+  // are constants at each call site.  Two phases, each a fixed interleave:
+  //   1. the 16 MFMAs of S(it + 1) = K Q^T, each with the exponentials and
+  //      bf16 packing of two scores of tile it; K fragments are read two
+  //      k-steps ahead;
+  //   2. the 16 MFMAs of O += V P(it), each with part of the max of tile it + 1;
+  //      V fragments are read one pair ahead.
+  // Lazy rescale, kept out of the tile loops below so that the loops never do
+  // vector work on the accumulator (which stays in the MFMA accumulator
+  // registers): a row's reference max moves only when the row's max outgrows
+  // it by more than 2^8.
+  auto grow_pending = [&]() {
+    const bool g0 = mt_cur[0] > m_ref[0] + kRescaleThreshold;
+    const bool g1 = mt_cur[1] > m_ref[1] + kRescaleThreshold;
+    return __builtin_amdgcn_ballot_w64(g0 || g1) != 0;
+  };
+  auto rescale = [&]() {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const float m_new = fmaxf(m_ref[cb], mt_cur[cb]);
+      const float alpha = (m_ref[cb] == kNegInf) ? 0.f : fast_exp2(m_ref[cb] - m_new);
+      l_part[cb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[cb][db] *= alpha;
+      m_ref[cb] = m_new;
+    }
+  };
+
+  auto step = [&](const int it, const bool next, const bool mask_next) {
+    const int k0 = it * TK;
+    if (it + 3 < ntiles) dma_tile(k0 + 3 * TK, (it + 3) & 3);
+
+    float m_use[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) m_use[cb] = (m_ref[cb] == kNegInf) ? 0.f : m_ref[cb];
+
+    // Phase 1.
+    uint32_t pk[2][8];
+    const int kst_next = (it + 1) & 3;
+    i32x4_t kf[3];
+    if (next) {
+      kf[0] = kread(kst_next, 0);
+      kf[1] = kread(kst_next, 1);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s_nxt[cb][e] = 0.f;
+    }
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const int ks = g >> 1, cb = g & 1;
+      if (next) {
+        if (cb == 0 && ks + 2 < 8) kf[(ks + 2) % 3] = kread(kst_next, ks + 2);
+        s_nxt[cb] = mfma32x32x16(as_bf16x8(kf[ks % 3]), qf[cb][ks], s_nxt[cb]);
+      }
+      const int pc = g >> 3, e = (2 * g) & 15;
+      const float p0 = fast_exp2(__builtin_fmaf(s_cur[pc][e], sl2, -m_use[pc]));
+      const float p1 = fast_exp2(__builtin_fmaf(s_cur[pc][e + 1], sl2, -m_use[pc]));
+      pk[pc][e >> 1] = pack_bf16x2(p0, p1);
+      // Row sum in fp32 from the unrounded exponentials (exact LSE).
+      l_part[pc] += p0 + p1;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Phase 2.
+    const char* vl = smem + (it & 3) * STAGE + KT;
+    auto vread = [&](int pair, i32x2_t* out) {  // V fragments: 16-key step pair >> 2, d-block pair & 3
+      const int ts = pair >> 2, db = pair & 3;
+      const int key_a = 16 * ts + vkey;
+      const int col = 32 * db + vcol;  // element column, multiple of 4
+      const int ch = col >> 3, within = (col & 7) * 2;
+      out[0] = ds_read_tr(vl + tile_off(key_a, ch) + within);
+      out[1] = ds_read_tr(vl + tile_off(key_a + 8, ch) + within);
+    };
+    i32x2_t vf[2][2];
+    vread(0, vf[0]);
+    if (next && mask_next) mask_scores(s_nxt, k0 + TK);
+    float mx[2] = {kNegInf, kNegInf};
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      const int pair = g >> 1, cb = g & 1;
+      const int ts = pair >> 2, db = pair & 3;
+      if (cb == 0 && pair + 1 < 8) vread(pair + 1, vf[(pair + 1) & 1]);
+      i32x4_t pb;
+      pb[0] = (int)pk[cb][4 * ts + 0];
+      pb[1] = (int)pk[cb][4 * ts + 1];
+      pb[2] = (int)pk[cb][4 * ts + 2];
+      pb[3] = (int)pk[cb][4 * ts + 3];
+      i32x4_t va;
+      va[0] = vf[pair & 1][0][0];
+      va[1] = vf[pair & 1][0][1];
+      va[2] = vf[pair & 1][1][0];
+      va[3] = vf[pair & 1][1][1];
+      oacc[cb][db] = mfma32x32x16(as_bf16x8(va), as_bf16x8(pb), oacc[cb][db]);
+      const int sc = g >> 3;
+      if (next) {
+        const int ne = (2 * g) & 15;
+        mx[sc] = fmaxf(mx[sc], fmaxf(s_nxt[sc][ne], s_nxt[sc][ne + 1]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (next) {
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) mt_cur[cb] = fmaxf(mx[cb], __shfl_xor(mx[cb], 32, 64)) * sl2;
+    }
+
+    // Tile it + 2 must have landed before the next step reads its K; tile
+    // it + 3 may stay in flight.  The barrier also frees stage it & 3.
+    if (it + 3 < ntiles)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (next) {
+      s_cur[0] = s_nxt[0];
+      s_cur[1] = s_nxt[1];
+    }
+  };
+
+  // Steps [it, it_end) with fixed flags.  The inner loop runs until a rescale
+  // is due; the rescale happens between inner loops.
+  auto run = [&](int& it, const int it_end, const bool next, const bool mask_next) {
+    while (it < it_end) {
+      if (grow_pending()) rescale();
+      do {
+        step(it, next, mask_next);
+        ++it;
+      } while (it < it_end && !grow_pending());
+    }
+  };
+  // Every wave runs ntiles steps (one barrier each), whatever its split
+  // between the unmasked and the masked tiles.
+  const int n1 = max(0, min(n_clean, ntiles - 1));
+  int it = 0;
+  run(it, n1 - 1, true, false);
+  run(it, n1, true, n1 < ntiles);
+  run(it, ntiles - 1, true, true);
+  run(it, ntiles, false, false);
 
   // Epilogue: O = U / l (division after the V-matmul), LSE = m + log l.
-  float l_row = l_part + __shfl_xor(l_part, 32, 64);
-  if (r < R) {
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const float l_row = l_part[cb] + __shfl_xor(l_part[cb], 32, 64);
+    if (!row_ok[cb]) continue;
+    const int r = rw0 + 32 * cb + c;
     const int qh = kvh * G + (r % G);
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-    const int64_t obase = (int64_t)b * p.os_b + (int64_t)qi * p.os_t + (int64_t)qh * p.os_h;
+    const int64_t obase = (int64_t)b * p.os_b + (int64_t)qi[cb] * p.os_t + (int64_t)qh * p.os_h;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 32 * db + 8 * i + 4 * h;
-        const float o0 = oacc[db][4 * i + 0] * inv, o1 = oacc[db][4 * i + 1] * inv;
-        const float o2 = oacc[db][4 * i + 2] * inv, o3 = oacc[db][4 * i + 3] * inv;
+        const float o0 = oacc[cb][db][4 * i + 0] * inv, o1 = oacc[cb][db][4 * i + 1] * inv;
+        const float o2 = oacc[cb][db][4 * i + 2] * inv, o3 = oacc[cb][db][4 * i + 3] * inv;
         if (p.o_bf16) {
-          uint2 pk;
-          pk.x = pack_bf16x2(o0, o1);
-          pk.y = pack_bf16x2(o2, o3);
-          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.o) + obase + d) = pk;
+          uint2 pk2;
+          pk2.x = pack_bf16x2(o0, o1);
+          pk2.y = pack_bf16x2(o2, o3);
+          *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(p.o) + obase + d) = pk2;
         } else {
           float4 v = make_float4(o0, o1, o2, o3);
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.o) + obase + d) = v;
         }
       }
     if (h == 0 && p.lse_out)
-      p.lse_out[((int64_t)b * p.Lq + qi) * p.Hq + qh] =
-          l_row > 0.f ? (m_run + fast_log2(l_row)) * kLn2 : kNegInf;
+      p.lse_out[((int64_t)b * p.Lq + qi[cb]) * p.Hq + qh] =
+          l_row > 0.f ? (m_ref[cb] + fast_log2(l_row)) * kLn2 : kNegInf;
   }
 }
 

@@ -42,10 +42,7 @@
 namespace attn {
 namespace {
 
-constexpr int NW = 4;                 // waves per workgroup
-constexpr int NT = NW * 64;
-constexpr int RPW = 64;               // rows per wave (two 32-row column blocks)
-constexpr int ROWS = NW * RPW;        // rows per workgroup
+constexpr int ROWS = 256;             // rows per workgroup
 constexpr int TK = 32;                // keys per tile
 constexpr int RB = 256;               // bytes per K or V row (128 bf16)
 constexpr int KT = TK * RB;           // 8 KiB: one K (or V) tile
@@ -68,8 +65,14 @@ __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 
 // Byte offset of (row, 16-byte chunk c) inside a K or V tile.
 __device__ __forceinline__ int tile_off(int row, int c) { return row * RB + 16 * (c ^ swz(row)); }
 
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// NW waves per workgroup, each owning NCB 32-row MFMA column blocks
+// (NW * NCB * 32 = 256 rows); NW / 4 waves per SIMD.
+template <int NW, int NCB>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 void prefill_d128_kernel(KParams p, int nrt) {
+  constexpr int RPW = 32 * NCB;       // rows per wave
+  constexpr int NDMA = 8 / NW;        // 1 KiB DMA blocks per wave per K (or V) tile
+  static_assert(NW * RPW == ROWS, "a workgroup covers 256 rows");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -98,10 +101,10 @@ void prefill_d128_kernel(KParams p, int nrt) {
   const int c = lane & 31;
   const int h = lane >> 5;
   const int rw0 = r0 + RPW * w;
-  int qi[2], qlim[2];
-  bool row_ok[2];
+  int qi[NCB], qlim[NCB];
+  bool row_ok[NCB];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
     const int r = rw0 + 32 * cb + c;
     qi[cb] = r / G;
     row_ok[cb] = r < R;
@@ -115,11 +118,11 @@ void prefill_d128_kernel(KParams p, int nrt) {
   const int kfull_w = p.causal ? max(0, min(L, rw0 / G + off + 1)) : L;
 
   // Q^T as the B operand (hoisted): lane holds Q[row][16*ks + 8*h .. +7].
-  bf16x8_t qf[2][8];
+  bf16x8_t qf[NCB][8];
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       const int r = rw0 + 32 * cb + c;
       const int qh = kvh * G + (r % G);
       const int64_t qoff = (int64_t)b * p.qs_b + (int64_t)qi[cb] * p.qs_t + (int64_t)qh * p.qs_h;
@@ -132,14 +135,15 @@ void prefill_d128_kernel(KParams p, int nrt) {
     }
     // Wait for Q here, once, rather than at the loop head on every tile.
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[cb][ks]));
   }
 
-  // Tile copy HBM -> LDS without registers: each wave fills rows 4*(2w + u) ..
-  // + 3 (u = 0, 1) of the K tile and of the V tile; lane l writes the 16-byte
-  // slot (row 4*(2w+u) + l/16, position l%16), which holds chunk (l%16) ^ swz(row).
+  // Tile copy HBM -> LDS without registers: each wave fills rows
+  // 4*(NDMA*w + u) .. + 3 (u < NDMA) of the K tile and of the V tile; lane l
+  // writes the 16-byte slot (row 4*(NDMA*w+u) + l/16, position l%16), which
+  // holds chunk (l%16) ^ swz(row).
   // The buffer ranges end at the last key, so rows past it are zero.
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
@@ -147,10 +151,10 @@ void prefill_d128_kernel(KParams p, int nrt) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)L * kst);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)L * vst);
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(smem);
-  uint32_t k_voff[2], v_voff[2];
+  uint32_t k_voff[NDMA], v_voff[NDMA];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int row = 4 * (2 * w + u) + (lane >> 4);
+  for (int u = 0; u < NDMA; ++u) {
+    const int row = 4 * (NDMA * w + u) + (lane >> 4);
     const int chunk = (lane & 15) ^ swz(row);
     k_voff[u] = (uint32_t)row * kst + 16 * chunk;
     v_voff[u] = (uint32_t)row * vst + 16 * chunk;
@@ -163,13 +167,27 @@ void prefill_d128_kernel(KParams p, int nrt) {
     const uint32_t base = smem_lds + (uint32_t)(stage * STAGE);
     const uint32_t ksoff = (uint32_t)k0 * kst, vsoff = (uint32_t)k0 * vst;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint32_t m0k = base + (uint32_t)((2 * w + u) * 1024);
+    for (int u = 0; u < NDMA; ++u) {
+      const uint32_t m0k = base + (uint32_t)((NDMA * w + u) * 1024);
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :: "s"(m0k), "v"(k_voff[u] + ksoff), "s"(krs) : "memory", "m0");
       const uint32_t m0v = m0k + KT;
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :: "s"(m0v), "v"(v_voff[u] + vsoff), "s"(vrs) : "memory", "m0");
+    }
+  };
+
+  // s_waitcnt vmcnt(n * 2 * NDMA): all but the last n tiles' DMA has landed
+  // (loads complete in order; 2 * NDMA instructions per tile and wave).
+  auto wait_tiles_but = [&](int n) {
+    if (n >= 2) {
+      if constexpr (NDMA == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else if (n == 1) {
+      if constexpr (NDMA == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
   };
 
@@ -179,15 +197,19 @@ void prefill_d128_kernel(KParams p, int nrt) {
   const int vkey = 4 * (gq >> 1) + (li >> 2);
   const int vcol = 16 * (gq & 1) + 4 * (li & 3);
 
-  f32x16_t oacc[2][4];
+  f32x16_t oacc[NCB][4];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb)
+  for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int e = 0; e < 16; ++e) oacc[cb][db][e] = 0.f;
-  float m_ref[2] = {kNegInf, kNegInf};   // reference max per row (base-2 units)
-  float l_part[2] = {0.f, 0.f};
+  float m_ref[NCB], l_part[NCB];   // reference max per row (base-2 units), row sum
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    m_ref[cb] = kNegInf;
+    l_part[cb] = 0.f;
+  }
   const float sl2 = p.scale_log2;
 
   const int ntiles = (kend + TK - 1) / TK;
@@ -201,7 +223,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
   // Masked scores are set to -inf.
   auto mask_scores = [&](f32x16_t* sc, int k0) {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -210,21 +232,19 @@ void prefill_d128_kernel(KParams p, int nrt) {
       }
   };
 
-  f32x16_t s_cur[2], s_nxt[2];
-  float mt_cur[2] = {kNegInf, kNegInf};
+  f32x16_t s_cur[NCB], s_nxt[NCB];
+  float mt_cur[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) mt_cur[cb] = kNegInf;
   if (ntiles > 0) {
 #pragma unroll
     for (int t = 0; t < 3; ++t)
       if (t < ntiles) dma_tile(t * TK, t);
-    // Tiles 0 and 1 landed (step 0 reads K of tile 1); tile 2 may stay in
-    // flight (loads finish in order, four DMA instructions per tile and wave).
-    if (ntiles >= 3)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // Tiles 0 and 1 landed (step 0 reads K of tile 1); tile 2 may stay in flight.
+    wait_tiles_but(ntiles >= 3 ? 1 : 0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) s_cur[cb][e] = 0.f;
 #pragma unroll
@@ -233,7 +253,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
     }
     if (n_clean == 0) mask_scores(s_cur, 0);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       float m = kNegInf;
 #pragma unroll
       for (int e = 0; e < 16; e += 2) m = fmaxf(m, fmaxf(s_cur[cb][e], s_cur[cb][e + 1]));
@@ -254,13 +274,14 @@ void prefill_d128_kernel(KParams p, int nrt) {
   // registers): a row's reference max moves only when the row's max outgrows
   // it by more than 2^8.
   auto grow_pending = [&]() {
-    const bool g0 = mt_cur[0] > m_ref[0] + kRescaleThreshold;
-    const bool g1 = mt_cur[1] > m_ref[1] + kRescaleThreshold;
-    return __builtin_amdgcn_ballot_w64(g0 || g1) != 0;
+    bool g = false;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) g = g || (mt_cur[cb] > m_ref[cb] + kRescaleThreshold);
+    return __builtin_amdgcn_ballot_w64(g) != 0;
   };
   auto rescale = [&]() {
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       const float m_new = fmaxf(m_ref[cb], mt_cur[cb]);
       const float alpha = (m_ref[cb] == kNegInf) ? 0.f : fast_exp2(m_ref[cb] - m_new);
       l_part[cb] *= alpha;
@@ -274,30 +295,32 @@ void prefill_d128_kernel(KParams p, int nrt) {
     const int k0 = it * TK;
     if (it + 3 < ntiles) dma_tile(k0 + 3 * TK, (it + 3) & 3);
 
-    float m_use[2];
+    float m_use[NCB];
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) m_use[cb] = (m_ref[cb] == kNegInf) ? 0.f : m_ref[cb];
+    for (int cb = 0; cb < NCB; ++cb) m_use[cb] = (m_ref[cb] == kNegInf) ? 0.f : m_ref[cb];
 
-    // Phase 1.
-    uint32_t pk[2][8];
+    // Phase 1: 8 * NCB MFMAs, 16 * NCB exponentials (16 / 8 per MFMA).
+    constexpr int NG = 8 * NCB;
+    constexpr int EPG = 16 / 8;       // scores per MFMA: 16 * NCB / NG
+    uint32_t pk[NCB][8];
     const int kst_next = (it + 1) & 3;
     i32x4_t kf[3];
     if (next) {
       kf[0] = kread(kst_next, 0);
       kf[1] = kread(kst_next, 1);
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb)
+      for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) s_nxt[cb][e] = 0.f;
     }
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      const int ks = g >> 1, cb = g & 1;
+    for (int g = 0; g < NG; ++g) {
+      const int ks = g / NCB, cb = g % NCB;
       if (next) {
         if (cb == 0 && ks + 2 < 8) kf[(ks + 2) % 3] = kread(kst_next, ks + 2);
         s_nxt[cb] = mfma32x32x16(as_bf16x8(kf[ks % 3]), qf[cb][ks], s_nxt[cb]);
       }
-      const int pc = g >> 3, e = (2 * g) & 15;
+      const int pc = g >> 3, e = (EPG * g) & 15;
       const float p0 = fast_exp2(__builtin_fmaf(s_cur[pc][e], sl2, -m_use[pc]));
       const float p1 = fast_exp2(__builtin_fmaf(s_cur[pc][e + 1], sl2, -m_use[pc]));
       pk[pc][e >> 1] = pack_bf16x2(p0, p1);
@@ -319,10 +342,12 @@ void prefill_d128_kernel(KParams p, int nrt) {
     i32x2_t vf[2][2];
     vread(0, vf[0]);
     if (next && mask_next) mask_scores(s_nxt, k0 + TK);
-    float mx[2] = {kNegInf, kNegInf};
+    float mx[NCB];
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      const int pair = g >> 1, cb = g & 1;
+    for (int cb = 0; cb < NCB; ++cb) mx[cb] = kNegInf;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int pair = g / NCB, cb = g % NCB;
       const int ts = pair >> 2, db = pair & 3;
       if (cb == 0 && pair + 1 < 8) vread(pair + 1, vf[(pair + 1) & 1]);
       i32x4_t pb;
@@ -338,26 +363,24 @@ void prefill_d128_kernel(KParams p, int nrt) {
       oacc[cb][db] = mfma32x32x16(as_bf16x8(va), as_bf16x8(pb), oacc[cb][db]);
       const int sc = g >> 3;
       if (next) {
-        const int ne = (2 * g) & 15;
+        const int ne = (EPG * g) & 15;
         mx[sc] = fmaxf(mx[sc], fmaxf(s_nxt[sc][ne], s_nxt[sc][ne + 1]));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (next) {
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) mt_cur[cb] = fmaxf(mx[cb], __shfl_xor(mx[cb], 32, 64)) * sl2;
+      for (int cb = 0; cb < NCB; ++cb)
+        mt_cur[cb] = fmaxf(mx[cb], __shfl_xor(mx[cb], 32, 64)) * sl2;
     }
 
     // Tile it + 2 must have landed before the next step reads its K; tile
     // it + 3 may stay in flight.  The barrier also frees stage it & 3.
-    if (it + 3 < ntiles)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_tiles_but(it + 3 < ntiles ? 1 : 0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (next) {
-      s_cur[0] = s_nxt[0];
-      s_cur[1] = s_nxt[1];
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) s_cur[cb] = s_nxt[cb];
     }
   };
 
@@ -383,7 +406,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
 
   // Epilogue: O = U / l (division after the V-matmul), LSE = m + log l.
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
+  for (int cb = 0; cb < NCB; ++cb) {
     const float l_row = l_part[cb] + __shfl_xor(l_part[cb], 32, 64);
     if (!row_ok[cb]) continue;
     const int r = rw0 + 32 * cb + c;
@@ -415,19 +438,26 @@ void prefill_d128_kernel(KParams p, int nrt) {
 
 }  // namespace
 
-hipError_t launch_prefill_d128(const KParams& p, hipStream_t s) {
+template <int NW, int NCB>
+hipError_t launch_variant(const KParams& p, int nrt, int64_t nwg, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_d128_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_d128_kernel<NW, NCB>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
+  hipLaunchKernelGGL((prefill_d128_kernel<NW, NCB>), dim3((unsigned)nwg), dim3(NW * 64), LDS_BYTES,
+                     s, p, nrt);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_d128(const KParams& p, hipStream_t s) {
   const int nrt = (p.rows + ROWS - 1) / ROWS;
   const int64_t nwg = (int64_t)p.B * p.Hkv * nrt;
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_d128_kernel, dim3((unsigned)nwg), dim3(NT), LDS_BYTES, s, p, nrt);
-  return hipGetLastError();
+  if (p.waves == 8) return launch_variant<8, 1>(p, nrt, nwg, s);
+  return launch_variant<4, 2>(p, nrt, nwg, s);
 }
 
 }  // namespace attn

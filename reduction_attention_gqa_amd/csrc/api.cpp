@@ -423,7 +423,6 @@ int attn_prefill(const attn_problem* problem, const void* q, const void* k, cons
   kp.chunk = p->kv_len_max;
   kp.s_max = 1;
   kp.split_mode = 0;
-  kp.waves = kPrefillWaves;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (prefill_d128_fits(p, q, k, v, o))
     return hip_status(launch_prefill_d128(kp, s), "prefill_d128 launch");

@@ -60,8 +60,15 @@ __device__ __forceinline__ i32x2_t ds_read_tr(const char* lds) {
   return __builtin_bit_cast(i32x2_t, v);
 }
 
+__device__ __forceinline__ i32x2_t ds_read_tr_at(uint32_t lds_addr) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)lds_addr);
+  return __builtin_bit_cast(i32x2_t, v);
+}
+
 // Chunk swizzle: swap the two 2-bit fields of r mod 16.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// IEEE-754 2019 maximum (v_maximum3_f32): no canonicalisation of its inputs.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 // Byte offset of (row, 16-byte chunk c) inside a K or V tile.
 __device__ __forceinline__ int tile_off(int row, int c) { return row * RB + 16 * (c ^ swz(row)); }
 
@@ -217,8 +224,30 @@ void prefill_d128_kernel(KParams p, int nrt) {
   // ones (the diagonal, the ragged end, rows past R) are masked.
   const int n_clean = (rw0 + RPW <= R) ? min(kfull_w, L) / TK : 0;
 
+  // Per-lane LDS byte offsets inside a tile (loop invariant, kept in
+  // registers, opaque to the compiler so that every read is a base register
+  // plus an immediate stage / key-step offset):
+  //   K fragment of k-step ks: key c, chunk 2*ks + h;
+  //   V fragments of d-block db: keys vkey (j = 0) and vkey + 8 (j = 1) of a
+  //   16-key step, element columns 32*db + vcol .. + 3.
+  // The offsets include the LDS address of the ring.
+  uint32_t koff[8], voff[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    koff[ks] = smem_lds + (uint32_t)tile_off(c, 2 * ks + h);
+    asm volatile("" : "+v"(koff[ks]));
+  }
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = 32 * db + vcol;
+      voff[db][j] = smem_lds + (uint32_t)(KT + tile_off(vkey + 8 * j, col >> 3) + (col & 7) * 2);
+      asm volatile("" : "+v"(voff[db][j]));
+    }
+  typedef __attribute__((address_space(3))) const i32x4_t lds_i32x4_t;
   auto kread = [&](int stage, int ks) {  // K fragment: key c, 16-wide k-step ks
-    return *reinterpret_cast<const i32x4_t*>(smem + stage * STAGE + tile_off(c, 2 * ks + h));
+    return *reinterpret_cast<lds_i32x4_t*>((uintptr_t)(koff[ks] + (uint32_t)(stage * STAGE)));
   };
   // Masked scores are set to -inf.
   auto mask_scores = [&](f32x16_t* sc, int k0) {
@@ -236,6 +265,14 @@ void prefill_d128_kernel(KParams p, int nrt) {
   float mt_cur[NCB];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) mt_cur[cb] = kNegInf;
+  // Row max of a score tile in base-2 units (both lane halves hold the row);
+  // IEEE maximum needs no NaN canonicalisation of the MFMA results.
+  auto tile_max = [&](const f32x16_t& sc) {
+    float m = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 16; e += 2) m = vmax(m, vmax(sc[e], sc[e + 1]));
+    return m;
+  };
   if (ntiles > 0) {
 #pragma unroll
     for (int t = 0; t < 3; ++t)
@@ -254,56 +291,50 @@ void prefill_d128_kernel(KParams p, int nrt) {
     if (n_clean == 0) mask_scores(s_cur, 0);
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      float m = kNegInf;
-#pragma unroll
-      for (int e = 0; e < 16; e += 2) m = fmaxf(m, fmaxf(s_cur[cb][e], s_cur[cb][e + 1]));
-      mt_cur[cb] = fmaxf(m, __shfl_xor(m, 32, 64)) * sl2;
+      const float m = tile_max(s_cur[cb]);
+      mt_cur[cb] = vmax(m, __shfl_xor(m, 32, 64)) * sl2;
     }
   }
 
-  // One key tile it, whose scores s_cur are already masked and whose row maxes
-  // are mt_cur.  next: tile it + 1 exists; mask_next: it needs the mask.  Both
-  // are constants at each call site.  Two phases, each a fixed interleave:
-  //   1. the 16 MFMAs of S(it + 1) = K Q^T, each with the exponentials and
-  //      bf16 packing of two scores of tile it; K fragments are read two
+  // One key tile it (ring stage st = it & 3, a constant at every call site, so
+  // all LDS addresses are a lane base plus an immediate), whose scores s_cur
+  // are already masked and whose row maxes are mt_cur.  next: tile it + 1
+  // exists; mask_next: it needs the mask.  Two phases, each a fixed
+  // interleave pinned with scheduling barriers:
+  //   1. the 8 * NCB MFMAs of S(it + 1) = K Q^T, each with the exponentials
+  //      and bf16 packing of two scores of tile it; K fragments are read two
   //      k-steps ahead;
-  //   2. the 16 MFMAs of O += V P(it), each with part of the max of tile it + 1;
-  //      V fragments are read one pair ahead.
-  // Lazy rescale, kept out of the tile loops below so that the loops never do
-  // vector work on the accumulator (which stays in the MFMA accumulator
-  // registers): a row's reference max moves only when the row's max outgrows
-  // it by more than 2^8.
-  auto grow_pending = [&]() {
-    bool g = false;
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) g = g || (mt_cur[cb] > m_ref[cb] + kRescaleThreshold);
-    return __builtin_amdgcn_ballot_w64(g) != 0;
-  };
-  auto rescale = [&]() {
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const float m_new = fmaxf(m_ref[cb], mt_cur[cb]);
-      const float alpha = (m_ref[cb] == kNegInf) ? 0.f : fast_exp2(m_ref[cb] - m_new);
-      l_part[cb] *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[cb][db] *= alpha;
-      m_ref[cb] = m_new;
-    }
-  };
-
-  auto step = [&](const int it, const bool next, const bool mask_next) {
+  //   2. the 8 * NCB MFMAs of O += V P(it), each with part of the max of tile
+  //      it + 1; V fragments are read one pair ahead.
+  auto step = [&](const int it, const int st, const bool next, const bool mask_next)
+      __attribute__((always_inline)) {
     const int k0 = it * TK;
-    if (it + 3 < ntiles) dma_tile(k0 + 3 * TK, (it + 3) & 3);
+    if (it + 3 < ntiles) dma_tile(k0 + 3 * TK, (st + 3) & 3);
 
+    // Lazy rescale: a row's reference max moves (and its accumulator and row
+    // sum are rescaled) only when the row's max outgrows it by more than 2^8.
+    bool grow = false;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) grow = grow || (mt_cur[cb] > m_ref[cb] + kRescaleThreshold);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const float m_new = fmaxf(m_ref[cb], mt_cur[cb]);
+        const float alpha = (m_ref[cb] == kNegInf) ? 0.f : fast_exp2(m_ref[cb] - m_new);
+        l_part[cb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[cb][db] *= alpha;
+        m_ref[cb] = m_new;
+      }
+    }
     float m_use[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) m_use[cb] = (m_ref[cb] == kNegInf) ? 0.f : m_ref[cb];
 
-    // Phase 1: 8 * NCB MFMAs, 16 * NCB exponentials (16 / 8 per MFMA).
+    // Phase 1: 8 * NCB MFMAs, 16 * NCB exponentials.
     constexpr int NG = 8 * NCB;
-    constexpr int EPG = 16 / 8;       // scores per MFMA: 16 * NCB / NG
     uint32_t pk[NCB][8];
-    const int kst_next = (it + 1) & 3;
+    const int kst_next = (st + 1) & 3;
     i32x4_t kf[3];
     if (next) {
       kf[0] = kread(kst_next, 0);
@@ -320,7 +351,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
         if (cb == 0 && ks + 2 < 8) kf[(ks + 2) % 3] = kread(kst_next, ks + 2);
         s_nxt[cb] = mfma32x32x16(as_bf16x8(kf[ks % 3]), qf[cb][ks], s_nxt[cb]);
       }
-      const int pc = g >> 3, e = (EPG * g) & 15;
+      const int pc = g >> 3, e = (2 * g) & 15;
       const float p0 = fast_exp2(__builtin_fmaf(s_cur[pc][e], sl2, -m_use[pc]));
       const float p1 = fast_exp2(__builtin_fmaf(s_cur[pc][e + 1], sl2, -m_use[pc]));
       pk[pc][e >> 1] = pack_bf16x2(p0, p1);
@@ -330,14 +361,13 @@ void prefill_d128_kernel(KParams p, int nrt) {
     }
 
     // Phase 2.
-    const char* vl = smem + (it & 3) * STAGE + KT;
-    auto vread = [&](int pair, i32x2_t* out) {  // V fragments: 16-key step pair >> 2, d-block pair & 3
+    // V fragments of (16-key step ts = pair >> 2, d-block pair & 3); a 16-key
+    // step moves 16 rows, which the swizzle (a function of row mod 16) leaves alone.
+    auto vread = [&](int pair, i32x2_t* out) {
       const int ts = pair >> 2, db = pair & 3;
-      const int key_a = 16 * ts + vkey;
-      const int col = 32 * db + vcol;  // element column, multiple of 4
-      const int ch = col >> 3, within = (col & 7) * 2;
-      out[0] = ds_read_tr(vl + tile_off(key_a, ch) + within);
-      out[1] = ds_read_tr(vl + tile_off(key_a + 8, ch) + within);
+      const uint32_t add = (uint32_t)(st * STAGE + 16 * ts * RB);
+      out[0] = ds_read_tr_at(voff[db][0] + add);
+      out[1] = ds_read_tr_at(voff[db][1] + add);
     };
     i32x2_t vf[2][2];
     vread(0, vf[0]);
@@ -363,46 +393,53 @@ void prefill_d128_kernel(KParams p, int nrt) {
       oacc[cb][db] = mfma32x32x16(as_bf16x8(va), as_bf16x8(pb), oacc[cb][db]);
       const int sc = g >> 3;
       if (next) {
-        const int ne = (EPG * g) & 15;
-        mx[sc] = fmaxf(mx[sc], fmaxf(s_nxt[sc][ne], s_nxt[sc][ne + 1]));
+        const int ne = (2 * g) & 15;
+        mx[sc] = vmax(mx[sc], vmax(s_nxt[sc][ne], s_nxt[sc][ne + 1]));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (next) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
-        mt_cur[cb] = fmaxf(mx[cb], __shfl_xor(mx[cb], 32, 64)) * sl2;
+      for (int cb = 0; cb < NCB; ++cb) {
+        mt_cur[cb] = vmax(mx[cb], __shfl_xor(mx[cb], 32, 64)) * sl2;
+        s_cur[cb] = s_nxt[cb];
+      }
     }
 
     // Tile it + 2 must have landed before the next step reads its K; tile
-    // it + 3 may stay in flight.  The barrier also frees stage it & 3.
+    // it + 3 may stay in flight.  The barrier also frees stage st.
     wait_tiles_but(it + 3 < ntiles ? 1 : 0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (next) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) s_cur[cb] = s_nxt[cb];
+  };
+  // A step whose ring stage is only known at run time.
+  auto step_any = [&](const int it, const bool next, const bool mask_next)
+      __attribute__((always_inline)) {
+    switch (it & 3) {
+      case 0: step(it, 0, next, mask_next); break;
+      case 1: step(it, 1, next, mask_next); break;
+      case 2: step(it, 2, next, mask_next); break;
+      default: step(it, 3, next, mask_next); break;
     }
   };
 
-  // Steps [it, it_end) with fixed flags.  The inner loop runs until a rescale
-  // is due; the rescale happens between inner loops.
-  auto run = [&](int& it, const int it_end, const bool next, const bool mask_next) {
-    while (it < it_end) {
-      if (grow_pending()) rescale();
-      do {
-        step(it, next, mask_next);
-        ++it;
-      } while (it < it_end && !grow_pending());
-    }
-  };
-  // Every wave runs ntiles steps (one barrier each), whatever its split
-  // between the unmasked and the masked tiles.
+  // Tiles below n_clean need no mask; step it masks tile it + 1 when that
+  // tile needs it.  Every wave runs ntiles steps (one barrier each).  The
+  // unmasked run starts at tile 0 and goes in groups of four (stages 0..3),
+  // then a remainder of at most three with known stages.
   const int n1 = max(0, min(n_clean, ntiles - 1));
+  const int clean_end = max(0, n1 - 1);
   int it = 0;
-  run(it, n1 - 1, true, false);
-  run(it, n1, true, n1 < ntiles);
-  run(it, ntiles - 1, true, true);
-  run(it, ntiles, false, false);
+  for (; it + 4 <= clean_end; it += 4) {
+    step(it, 0, true, false);
+    step(it + 1, 1, true, false);
+    step(it + 2, 2, true, false);
+    step(it + 3, 3, true, false);
+  }
+  if (it < clean_end) step(it++, 0, true, false);
+  if (it < clean_end) step(it++, 1, true, false);
+  if (it < clean_end) step(it++, 2, true, false);
+  for (; it < ntiles - 1; ++it) step_any(it, true, true);
+  if (ntiles > 0) step_any(ntiles - 1, false, false);
 
   // Epilogue: O = U / l (division after the V-matmul), LSE = m + log l.
 #pragma unroll
@@ -456,8 +493,7 @@ hipError_t launch_prefill_d128(const KParams& p, hipStream_t s) {
   const int nrt = (p.rows + ROWS - 1) / ROWS;
   const int64_t nwg = (int64_t)p.B * p.Hkv * nrt;
   if (nwg == 0) return hipSuccess;
-  if (p.waves == 8) return launch_variant<8, 1>(p, nrt, nwg, s);
-  return launch_variant<4, 2>(p, nrt, nwg, s);
+  return launch_variant<8, 1>(p, nrt, nwg, s);
 }
 
 }  // namespace attn

@@ -53,6 +53,7 @@ constexpr int kGqaItemsPerCu = 8;      // planner target: work items per compute
 constexpr int kGqaMinChunk = 256;      // planner floor on keys per split
 constexpr int kGqaBlock = 256;
 constexpr int kGqaMaxRows = 16;
+constexpr int kPrefillStages = 4;     // prefill K/V ring depth (tiles)
 constexpr int kMlaTileN = 32;          // keys per MLA tile
 constexpr int kMlaBlock = 512;         // 8 waves: 4 row groups x 2 halves
 constexpr int kMlaRows = 128;          // query rows per MLA workgroup

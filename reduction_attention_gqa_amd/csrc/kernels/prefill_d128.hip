@@ -1,23 +1,21 @@
 // Fused causal / non-causal GQA prefill for bf16, Dqk = Dv = 128.
 //
-// One workgroup (4 waves) computes one 256-row tile of one (request, KV head)
+// One workgroup (8 waves) computes one 256-row tile of one (request, KV head)
 // group; a row is a (query position, head of the group) pair, so the G query
 // heads that share a KV head share every K/V tile staged in LDS.  This is the
 // inter-threadblock output tiling of Cleave §5.1 / §5.3 ([b_O, d] output tiles,
-// one per workgroup) with GQA packing added.  Inside, the key axis is tiled in
-// 32-key steps (iterative tiling, §5.1 and §5.3); the exp tile feeds both the
-// row sum and the V-matmul in the same step (horizontal fusion, §5.1); the
-// division by the row sum comes after the V-matmul (§2.2, Fig. 2); the Q tile
-// is loaded once, outside the key loop (§6.1).
+// one per workgroup) with GQA packing added.  Inside, the key axis is tiled
+// (iterative tiling, §5.1 and §5.3); the exp tile feeds both the row sum and
+// the V-matmul in the same step (horizontal fusion, §5.1); the division by the
+// row sum comes after the V-matmul (§2.2, Fig. 2); the Q tile is loaded once,
+// outside the key loop (§6.1).
 //
-// Each wave owns 64 rows as two 32-row MFMA column blocks, so every K or V
-// fragment read from LDS feeds two MFMAs.  Per wave and 32-key tile, keys on
-// the MFMA rows:
-//   S^T[32 x 64]  = K[32 x 128] Q^T[128 x 64]     2 x 8 MFMA 32x32x16 bf16
-//   O^T[128 x 64] += V^T[128 x 32] P^T[32 x 64]   2 x 8 MFMA 32x32x16 bf16
-// One wave per SIMD (512 registers each): the matrix cores are kept busy by
-// interleaving, within the wave, the scores of tile i + 1 with the
-// exponentials of tile i, and the V-matmul of tile i with the max of tile
+// Each wave owns 32 rows (one MFMA column block); two waves share a SIMD.
+// Per wave and tile of TK = 32 * KB keys, keys on the MFMA rows:
+//   S^T[TK x 32]  = K[TK x 128] Q^T[128 x 32]     KB x 8 MFMA 32x32x16 bf16
+//   O^T[128 x 32] += V^T[128 x TK] P^T[TK x 32]   KB x 8 MFMA 32x32x16 bf16
+// Within a wave, the scores of tile i + 1 are computed under the
+// exponentials of tile i, and the V-matmul of tile i under the max of tile
 // i + 1 (fixed interleaves pinned with scheduling barriers).
 //
 // The running max is updated lazily: a row's reference max moves (and its
@@ -25,11 +23,13 @@
 // than 2^8; otherwise P = 2^(s - m_ref) <= 256 is used as is.  Row sum and
 // accumulator always share one reference, so O = U / l is unchanged.
 //
-// K/V tiles go HBM -> LDS by buffer loads that write LDS directly, four stages
-// deep (tile i + 3 is in flight while tile i is consumed).  A tile row is 256
-// bytes, and the 16-byte chunk c of row r sits at chunk c ^ swz(r), which keeps
-// both the K operand reads (16 keys, one chunk each) and the transposed V reads
-// (4 keys, 4 chunks each) free of bank conflicts.
+// K/V tiles go HBM -> LDS by buffer loads that write LDS directly, into an
+// NS-stage K ring and an NS-stage V ring (tile i + NS - 1 is in flight while
+// tile i is consumed; four stages measure as fast as eight).  A tile row is 256 bytes, and the 16-byte chunk c of
+// row r sits at chunk c ^ swz(r), which keeps both the K operand reads (16
+// keys, one chunk each) and the transposed V reads (4 keys, 4 chunks each)
+// free of bank conflicts.  Every LDS read is a per-lane base register plus an
+// immediate (stage, key block, key step).
 //
 // Causal tiles beyond a tile's diagonal are never loaded; masking runs only on
 // tiles that straddle the diagonal or the end of the keys.  Workgroups are
@@ -42,27 +42,25 @@
 namespace attn {
 namespace {
 
-constexpr int ROWS = 256;             // rows per workgroup
-constexpr int TK = 32;                // keys per tile
+constexpr int NW = 8;                 // waves per workgroup
+constexpr int NT = NW * 64;
+constexpr int ROWS = NW * 32;         // rows per workgroup
 constexpr int RB = 256;               // bytes per K or V row (128 bf16)
-constexpr int KT = TK * RB;           // 8 KiB: one K (or V) tile
-constexpr int STAGE = 2 * KT;         // K tile then V tile
-constexpr int NSTAGE = 4;
-constexpr int LDS_BYTES = NSTAGE * STAGE;  // 64 KiB
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
+constexpr int lds_bytes(int kb, int ns) { return 2 * ns * 32 * kb * RB; }
+
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) const i32x4_t lds_i32x4_t;
 
 // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element i % 4
 // of the 8 bytes addressed by lanes 4e + i / 4 (e = 0..3) as its element e.
-__device__ __forceinline__ i32x2_t ds_read_tr(const char* lds) {
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds));
-  return __builtin_bit_cast(i32x2_t, v);
-}
-
 __device__ __forceinline__ i32x2_t ds_read_tr_at(uint32_t lds_addr) {
   const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)lds_addr);
   return __builtin_bit_cast(i32x2_t, v);
+}
+__device__ __forceinline__ i32x4_t ds_read16_at(uint32_t lds_addr) {
+  return *reinterpret_cast<lds_i32x4_t*>((uintptr_t)lds_addr);
 }
 
 // Chunk swizzle: swap the two 2-bit fields of r mod 16.
@@ -72,14 +70,16 @@ __device__ __forceinline__ float vmax(float a, float b) { return __builtin_eleme
 // Byte offset of (row, 16-byte chunk c) inside a K or V tile.
 __device__ __forceinline__ int tile_off(int row, int c) { return row * RB + 16 * (c ^ swz(row)); }
 
-// NW waves per workgroup, each owning NCB 32-row MFMA column blocks
-// (NW * NCB * 32 = 256 rows); NW / 4 waves per SIMD.
-template <int NW, int NCB>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
+// KB key blocks of 32 per tile; NS ring stages, tile i + NS - 1 loaded while
+// tile i is consumed.
+template <int KB, int NS>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_d128_kernel(KParams p, int nrt) {
-  constexpr int RPW = 32 * NCB;       // rows per wave
-  constexpr int NDMA = 8 / NW;        // 1 KiB DMA blocks per wave per K (or V) tile
-  static_assert(NW * RPW == ROWS, "a workgroup covers 256 rows");
+  constexpr int TK = 32 * KB;         // keys per tile
+  constexpr int KT = TK * RB;         // bytes of one K (or V) tile
+  constexpr int VRING = NS * KT;      // the V ring follows the K ring
+  constexpr int LOOK = NS - 1;        // DMA lookahead in tiles
+  constexpr int NDMA = KB;            // 1 KiB DMA blocks per wave per K (or V) tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -104,19 +104,14 @@ void prefill_d128_kernel(KParams p, int nrt) {
   const int r0 = rt * ROWS;
   const int off = L - p.Lq;        // causal: row position i sees keys <= i + off
 
-  // This wave's rows: lane (c, h) holds row rw0 + 32*cb + c of column block cb.
+  // This wave's rows: lane (c, h) holds row rw0 + c.
   const int c = lane & 31;
   const int h = lane >> 5;
-  const int rw0 = r0 + RPW * w;
-  int qi[NCB], qlim[NCB];
-  bool row_ok[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const int r = rw0 + 32 * cb + c;
-    qi[cb] = r / G;
-    row_ok[cb] = r < R;
-    qlim[cb] = qi[cb] + off;       // last visible key of this row (causal)
-  }
+  const int rw0 = r0 + 32 * w;
+  const int r = rw0 + c;
+  const int qi = r / G;
+  const bool row_ok = r < R;
+  const int qlim = qi + off;       // last visible key of this row (causal)
   const int wg_rows = max(0, min(ROWS, R - r0));
   int kend = L;                    // keys [0, kend) are visible to some row of the workgroup
   if (p.causal) kend = min(L, (r0 + wg_rows - 1) / G + off + 1);
@@ -124,34 +119,28 @@ void prefill_d128_kernel(KParams p, int nrt) {
   // Keys below kfull_w are visible to every row of this wave.
   const int kfull_w = p.causal ? max(0, min(L, rw0 / G + off + 1)) : L;
 
-  // Q^T as the B operand (hoisted): lane holds Q[row][16*ks + 8*h .. +7].
-  bf16x8_t qf[NCB][8];
+  // Q^T as the B operand (hoisted): lane holds Q[row r][16*ks + 8*h .. +7].
+  bf16x8_t qf[8];
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
+    const int qh = kvh * G + (r % G);
+    const int64_t qoff = (int64_t)b * p.qs_b + (int64_t)qi * p.qs_t + (int64_t)qh * p.qs_h;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const int r = rw0 + 32 * cb + c;
-      const int qh = kvh * G + (r % G);
-      const int64_t qoff = (int64_t)b * p.qs_b + (int64_t)qi[cb] * p.qs_t + (int64_t)qh * p.qs_h;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        i32x4_t v = {0, 0, 0, 0};
-        if (row_ok[cb]) v = *reinterpret_cast<const i32x4_t*>(qp + qoff + 16 * ks + 8 * h);
-        qf[cb][ks] = as_bf16x8(v);
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      i32x4_t v = {0, 0, 0, 0};
+      if (row_ok) v = *reinterpret_cast<const i32x4_t*>(qp + qoff + 16 * ks + 8 * h);
+      qf[ks] = as_bf16x8(v);
     }
     // Wait for Q here, once, rather than at the loop head on every tile.
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[cb][ks]));
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
   // Tile copy HBM -> LDS without registers: each wave fills rows
   // 4*(NDMA*w + u) .. + 3 (u < NDMA) of the K tile and of the V tile; lane l
   // writes the 16-byte slot (row 4*(NDMA*w+u) + l/16, position l%16), which
-  // holds chunk (l%16) ^ swz(row).
-  // The buffer ranges end at the last key, so rows past it are zero.
+  // holds chunk (l%16) ^ swz(row).  The buffer ranges end at the last key, so
+  // rows past it are zero.
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
   const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
   const uint32_t kst = (uint32_t)(p.ks_t * 2), vst = (uint32_t)(p.vs_t * 2);
@@ -171,66 +160,42 @@ void prefill_d128_kernel(KParams p, int nrt) {
   // pair it with conservative waits; its completion is awaited explicitly
   // before each barrier that publishes a tile.
   auto dma_tile = [&](int k0, int stage) {
-    const uint32_t base = smem_lds + (uint32_t)(stage * STAGE);
     const uint32_t ksoff = (uint32_t)k0 * kst, vsoff = (uint32_t)k0 * vst;
 #pragma unroll
     for (int u = 0; u < NDMA; ++u) {
-      const uint32_t m0k = base + (uint32_t)((NDMA * w + u) * 1024);
+      const uint32_t m0k = smem_lds + (uint32_t)(stage * KT + (NDMA * w + u) * 1024);
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :: "s"(m0k), "v"(k_voff[u] + ksoff), "s"(krs) : "memory", "m0");
-      const uint32_t m0v = m0k + KT;
+      const uint32_t m0v = m0k + VRING;
       asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :: "s"(m0v), "v"(v_voff[u] + vsoff), "s"(vrs) : "memory", "m0");
     }
   };
-
-  // s_waitcnt vmcnt(n * 2 * NDMA): all but the last n tiles' DMA has landed
-  // (loads complete in order; 2 * NDMA instructions per tile and wave).
+  // s_waitcnt: all but the newest n tiles' DMA has landed (loads complete in
+  // order; 2 * NDMA = 2 instructions per tile and wave).
+  static_assert(NDMA == 1, "vmcnt values below assume one DMA block per wave and tensor");
   auto wait_tiles_but = [&](int n) {
-    if (n >= 2) {
-      if constexpr (NDMA == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    } else if (n == 1) {
-      if constexpr (NDMA == 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-    } else {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    switch (n) {
+      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+      case 1: asm volatile("s_waitcnt vmcnt(2)" ::: "memory"); break;
+      case 2: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
+      case 3: asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); break;
+      case 4: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
+      case 5: asm volatile("s_waitcnt vmcnt(10)" ::: "memory"); break;
+      default: asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); break;
     }
   };
 
-  // Transposed V read: 16-lane group gq reads keys 4*(gq>>1) + li/4 (+8), element
-  // columns 32*db + 16*(gq&1) + 4*(li&3) .. +3.
+  // Per-lane LDS addresses (loop invariant, kept in registers, opaque to the
+  // compiler so that every read is this base plus an immediate):
+  //   K fragment of k-step ks: key c of a 32-key block, chunk 2*ks + h;
+  //   V fragments of d-block db: 16-lane group gq reads keys vkey (j = 0) and
+  //   vkey + 8 (j = 1) of a 16-key step, element columns 32*db + vcol .. + 3.
+  // Key blocks and 16-key steps move whole multiples of 16 rows, which the
+  // swizzle (a function of row mod 16) leaves alone.
   const int gq = lane >> 4, li = lane & 15;
   const int vkey = 4 * (gq >> 1) + (li >> 2);
   const int vcol = 16 * (gq & 1) + 4 * (li & 3);
-
-  f32x16_t oacc[NCB][4];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) oacc[cb][db][e] = 0.f;
-  float m_ref[NCB], l_part[NCB];   // reference max per row (base-2 units), row sum
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    m_ref[cb] = kNegInf;
-    l_part[cb] = 0.f;
-  }
-  const float sl2 = p.scale_log2;
-
-  const int ntiles = (kend + TK - 1) / TK;
-  // Leading tiles that need no mask for any row of this wave; the remaining
-  // ones (the diagonal, the ragged end, rows past R) are masked.
-  const int n_clean = (rw0 + RPW <= R) ? min(kfull_w, L) / TK : 0;
-
-  // Per-lane LDS byte offsets inside a tile (loop invariant, kept in
-  // registers, opaque to the compiler so that every read is a base register
-  // plus an immediate stage / key-step offset):
-  //   K fragment of k-step ks: key c, chunk 2*ks + h;
-  //   V fragments of d-block db: keys vkey (j = 0) and vkey + 8 (j = 1) of a
-  //   16-key step, element columns 32*db + vcol .. + 3.
-  // The offsets include the LDS address of the ring.
   uint32_t koff[8], voff[4][2];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -242,221 +207,212 @@ void prefill_d128_kernel(KParams p, int nrt) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = 32 * db + vcol;
-      voff[db][j] = smem_lds + (uint32_t)(KT + tile_off(vkey + 8 * j, col >> 3) + (col & 7) * 2);
+      voff[db][j] = smem_lds + (uint32_t)(VRING + tile_off(vkey + 8 * j, col >> 3) + (col & 7) * 2);
       asm volatile("" : "+v"(voff[db][j]));
     }
-  typedef __attribute__((address_space(3))) const i32x4_t lds_i32x4_t;
-  auto kread = [&](int stage, int ks) {  // K fragment: key c, 16-wide k-step ks
-    return *reinterpret_cast<lds_i32x4_t*>((uintptr_t)(koff[ks] + (uint32_t)(stage * STAGE)));
+  auto kread = [&](int stage, int kb, int ks) {
+    return ds_read16_at(koff[ks] + (uint32_t)(stage * KT + kb * 32 * RB));
   };
-  // Masked scores are set to -inf.
+
+  f32x16_t oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  float m_ref = kNegInf;   // reference max of this lane's row (base-2 units)
+  float l_part = 0.f;
+  const float sl2 = p.scale_log2;
+
+  const int ntiles = (kend + TK - 1) / TK;
+  // Leading tiles that need no mask for any row of this wave; the remaining
+  // ones (the diagonal, the ragged end, rows past R) are masked.
+  const int n_clean = (rw0 + 32 <= R) ? min(kfull_w, L) / TK : 0;
+
+  // Masked scores are set to -inf.  Lane element e of key block kb is key
+  // k0 + 32*kb + 8*(e/4) + 4*h + e%4.
   auto mask_scores = [&](f32x16_t* sc, int k0) {
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = k0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        const bool vis = key < L && (!p.causal || key <= qlim[cb]) && row_ok[cb];
-        sc[cb][e] = vis ? sc[cb][e] : kNegInf;
+        const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * h + (e & 3);
+        const bool vis = key < L && (!p.causal || key <= qlim) && row_ok;
+        sc[kb][e] = vis ? sc[kb][e] : kNegInf;
       }
   };
-
-  f32x16_t s_cur[NCB], s_nxt[NCB];
-  float mt_cur[NCB];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) mt_cur[cb] = kNegInf;
   // Row max of a score tile in base-2 units (both lane halves hold the row);
   // IEEE maximum needs no NaN canonicalisation of the MFMA results.
-  auto tile_max = [&](const f32x16_t& sc) {
+  auto tile_max = [&](const f32x16_t* sc) {
     float m = kNegInf;
 #pragma unroll
-    for (int e = 0; e < 16; e += 2) m = vmax(m, vmax(sc[e], sc[e + 1]));
-    return m;
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) m = vmax(m, vmax(sc[kb][e], sc[kb][e + 1]));
+    return vmax(m, __shfl_xor(m, 32, 64)) * sl2;
   };
+
+  f32x16_t s_cur[KB], s_nxt[KB];
+  float mt_cur = kNegInf;
   if (ntiles > 0) {
 #pragma unroll
-    for (int t = 0; t < 3; ++t)
+    for (int t = 0; t < LOOK; ++t)
       if (t < ntiles) dma_tile(t * TK, t);
-    // Tiles 0 and 1 landed (step 0 reads K of tile 1); tile 2 may stay in flight.
-    wait_tiles_but(ntiles >= 3 ? 1 : 0);
+    // Tiles 0 and 1 landed (step 0 reads K of tile 1); later ones may stay in flight.
+    wait_tiles_but(max(0, min(LOOK - 1, ntiles - 1) - 1));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
+    for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s_cur[cb][e] = 0.f;
+      for (int e = 0; e < 16; ++e) s_cur[kb][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks)
-        s_cur[cb] = mfma32x32x16(as_bf16x8(kread(0, ks)), qf[cb][ks], s_cur[cb]);
+        s_cur[kb] = mfma32x32x16(as_bf16x8(kread(0, kb, ks)), qf[ks], s_cur[kb]);
     }
     if (n_clean == 0) mask_scores(s_cur, 0);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      const float m = tile_max(s_cur[cb]);
-      mt_cur[cb] = vmax(m, __shfl_xor(m, 32, 64)) * sl2;
-    }
+    mt_cur = tile_max(s_cur);
   }
 
-  // One key tile it (ring stage st = it & 3, a constant at every call site, so
-  // all LDS addresses are a lane base plus an immediate), whose scores s_cur
-  // are already masked and whose row maxes are mt_cur.  next: tile it + 1
-  // exists; mask_next: it needs the mask.  Two phases, each a fixed
-  // interleave pinned with scheduling barriers:
-  //   1. the 8 * NCB MFMAs of S(it + 1) = K Q^T, each with the exponentials
-  //      and bf16 packing of two scores of tile it; K fragments are read two
-  //      k-steps ahead;
-  //   2. the 8 * NCB MFMAs of O += V P(it), each with part of the max of tile
-  //      it + 1; V fragments are read one pair ahead.
+  // One key tile it (ring stage st = it % NS, a constant at every call site),
+  // whose scores s_cur are already masked and whose row max is mt_cur.  next:
+  // tile it + 1 exists; mask_next: it needs the mask.  Two phases, each a
+  // fixed interleave pinned with scheduling barriers:
+  //   1. the 8 * KB MFMAs of S(it + 1) = K Q^T (key blocks alternate, so
+  //      consecutive MFMAs are independent), each with the exponentials, bf16
+  //      packing and row sum of two scores of tile it; K fragments are read
+  //      two MFMAs ahead;
+  //   2. the 8 * KB MFMAs of O += V P(it), each with part of the max of tile
+  //      it + 1; V fragments are read one MFMA ahead.
   auto step = [&](const int it, const int st, const bool next, const bool mask_next)
       __attribute__((always_inline)) {
     const int k0 = it * TK;
-    if (it + 3 < ntiles) dma_tile(k0 + 3 * TK, (st + 3) & 3);
+    if (it + LOOK < ntiles) dma_tile(k0 + LOOK * TK, (st + LOOK) % NS);
 
-    // Lazy rescale: a row's reference max moves (and its accumulator and row
-    // sum are rescaled) only when the row's max outgrows it by more than 2^8.
-    bool grow = false;
+    // Lazy rescale (rare).
+    if (__builtin_amdgcn_ballot_w64(mt_cur > m_ref + kRescaleThreshold) != 0) {
+      const float m_new = fmaxf(m_ref, mt_cur);
+      const float alpha = (m_ref == kNegInf) ? 0.f : fast_exp2(m_ref - m_new);
+      l_part *= alpha;
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) grow = grow || (mt_cur[cb] > m_ref[cb] + kRescaleThreshold);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const float m_new = fmaxf(m_ref[cb], mt_cur[cb]);
-        const float alpha = (m_ref[cb] == kNegInf) ? 0.f : fast_exp2(m_ref[cb] - m_new);
-        l_part[cb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[cb][db] *= alpha;
-        m_ref[cb] = m_new;
-      }
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      m_ref = m_new;
     }
-    float m_use[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) m_use[cb] = (m_ref[cb] == kNegInf) ? 0.f : m_ref[cb];
+    const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
 
-    // Phase 1: 8 * NCB MFMAs, 16 * NCB exponentials.
-    constexpr int NG = 8 * NCB;
-    uint32_t pk[NCB][8];
-    const int kst_next = (st + 1) & 3;
+    // Phase 1.
+    constexpr int NG = 8 * KB;
+    uint32_t pk[KB][8];
+    const int kst_next = (st + 1) % NS;
     i32x4_t kf[3];
     if (next) {
-      kf[0] = kread(kst_next, 0);
-      kf[1] = kread(kst_next, 1);
+      kf[0] = kread(kst_next, 0 % KB, 0 / KB);
+      kf[1] = kread(kst_next, 1 % KB, 1 / KB);
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s_nxt[cb][e] = 0.f;
+        for (int e = 0; e < 16; ++e) s_nxt[kb][e] = 0.f;
     }
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const int ks = g / NCB, cb = g % NCB;
       if (next) {
-        if (cb == 0 && ks + 2 < 8) kf[(ks + 2) % 3] = kread(kst_next, ks + 2);
-        s_nxt[cb] = mfma32x32x16(as_bf16x8(kf[ks % 3]), qf[cb][ks], s_nxt[cb]);
+        if (g + 2 < NG) kf[(g + 2) % 3] = kread(kst_next, (g + 2) % KB, (g + 2) / KB);
+        s_nxt[g % KB] = mfma32x32x16(as_bf16x8(kf[g % 3]), qf[g / KB], s_nxt[g % KB]);
       }
       const int pc = g >> 3, e = (2 * g) & 15;
-      const float p0 = fast_exp2(__builtin_fmaf(s_cur[pc][e], sl2, -m_use[pc]));
-      const float p1 = fast_exp2(__builtin_fmaf(s_cur[pc][e + 1], sl2, -m_use[pc]));
+      const float p0 = fast_exp2(__builtin_fmaf(s_cur[pc][e], sl2, -m_use));
+      const float p1 = fast_exp2(__builtin_fmaf(s_cur[pc][e + 1], sl2, -m_use));
       pk[pc][e >> 1] = pack_bf16x2(p0, p1);
-      // Row sum in fp32 from the unrounded exponentials (exact LSE).
-      l_part[pc] += p0 + p1;
+      l_part += p0 + p1;  // row sum from the unrounded exponentials (exact LSE)
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    // Phase 2.
-    // V fragments of (16-key step ts = pair >> 2, d-block pair & 3); a 16-key
-    // step moves 16 rows, which the swizzle (a function of row mod 16) leaves alone.
-    auto vread = [&](int pair, i32x2_t* out) {
-      const int ts = pair >> 2, db = pair & 3;
-      const uint32_t add = (uint32_t)(st * STAGE + 16 * ts * RB);
-      out[0] = ds_read_tr_at(voff[db][0] + add);
-      out[1] = ds_read_tr_at(voff[db][1] + add);
+    // Phase 2: MFMA g is 16-key step ts = g / 4 and d-block db = g % 4.
+    auto vread = [&](int g, i32x2_t* out) {
+      const uint32_t add = (uint32_t)(st * KT + 16 * (g >> 2) * RB);
+      out[0] = ds_read_tr_at(voff[g & 3][0] + add);
+      out[1] = ds_read_tr_at(voff[g & 3][1] + add);
     };
     i32x2_t vf[2][2];
     vread(0, vf[0]);
     if (next && mask_next) mask_scores(s_nxt, k0 + TK);
-    float mx[NCB];
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) mx[cb] = kNegInf;
+    float mx = kNegInf;
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      const int pair = g / NCB, cb = g % NCB;
-      const int ts = pair >> 2, db = pair & 3;
-      if (cb == 0 && pair + 1 < 8) vread(pair + 1, vf[(pair + 1) & 1]);
+      const int ts = g >> 2, db = g & 3;
+      if (g + 1 < NG) vread(g + 1, vf[(g + 1) & 1]);
       i32x4_t pb;
-      pb[0] = (int)pk[cb][4 * ts + 0];
-      pb[1] = (int)pk[cb][4 * ts + 1];
-      pb[2] = (int)pk[cb][4 * ts + 2];
-      pb[3] = (int)pk[cb][4 * ts + 3];
+      pb[0] = (int)pk[ts >> 1][4 * (ts & 1) + 0];
+      pb[1] = (int)pk[ts >> 1][4 * (ts & 1) + 1];
+      pb[2] = (int)pk[ts >> 1][4 * (ts & 1) + 2];
+      pb[3] = (int)pk[ts >> 1][4 * (ts & 1) + 3];
       i32x4_t va;
-      va[0] = vf[pair & 1][0][0];
-      va[1] = vf[pair & 1][0][1];
-      va[2] = vf[pair & 1][1][0];
-      va[3] = vf[pair & 1][1][1];
-      oacc[cb][db] = mfma32x32x16(as_bf16x8(va), as_bf16x8(pb), oacc[cb][db]);
-      const int sc = g >> 3;
+      va[0] = vf[g & 1][0][0];
+      va[1] = vf[g & 1][0][1];
+      va[2] = vf[g & 1][1][0];
+      va[3] = vf[g & 1][1][1];
+      oacc[db] = mfma32x32x16(as_bf16x8(va), as_bf16x8(pb), oacc[db]);
       if (next) {
-        const int ne = (2 * g) & 15;
-        mx[sc] = vmax(mx[sc], vmax(s_nxt[sc][ne], s_nxt[sc][ne + 1]));
+        const int mc = g >> 3, ne = (2 * g) & 15;
+        mx = vmax(mx, vmax(s_nxt[mc][ne], s_nxt[mc][ne + 1]));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (next) {
+      mt_cur = vmax(mx, __shfl_xor(mx, 32, 64)) * sl2;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        mt_cur[cb] = vmax(mx[cb], __shfl_xor(mx[cb], 32, 64)) * sl2;
-        s_cur[cb] = s_nxt[cb];
-      }
+      for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_nxt[kb];
     }
 
-    // Tile it + 2 must have landed before the next step reads its K; tile
-    // it + 3 may stay in flight.  The barrier also frees stage st.
-    wait_tiles_but(it + 3 < ntiles ? 1 : 0);
+    // Tile it + 2 must have landed before the next step reads its K; later
+    // tiles may stay in flight.  The barrier also frees stage st.
+    wait_tiles_but(max(0, min(it + LOOK, ntiles - 1) - (it + 2)));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   };
   // A step whose ring stage is only known at run time.
   auto step_any = [&](const int it, const bool next, const bool mask_next)
       __attribute__((always_inline)) {
-    switch (it & 3) {
+    static_assert(NS == 4 || NS == 8, "ring stages");
+    switch (it % NS) {
       case 0: step(it, 0, next, mask_next); break;
       case 1: step(it, 1, next, mask_next); break;
       case 2: step(it, 2, next, mask_next); break;
-      default: step(it, 3, next, mask_next); break;
+      case 3: step(it, 3, next, mask_next); break;
+      case 4: step(it, 4 % NS, next, mask_next); break;
+      case 5: step(it, 5 % NS, next, mask_next); break;
+      case 6: step(it, 6 % NS, next, mask_next); break;
+      default: step(it, 7 % NS, next, mask_next); break;
     }
   };
 
   // Tiles below n_clean need no mask; step it masks tile it + 1 when that
   // tile needs it.  Every wave runs ntiles steps (one barrier each).  The
-  // unmasked run starts at tile 0 and goes in groups of four (stages 0..3),
-  // then a remainder of at most three with known stages.
+  // unmasked run starts at tile 0 and goes in groups of NS (stages 0..NS-1),
+  // then a remainder of at most NS - 1 with known stages.
   const int n1 = max(0, min(n_clean, ntiles - 1));
   const int clean_end = max(0, n1 - 1);
   int it = 0;
-  for (; it + 4 <= clean_end; it += 4) {
-    step(it, 0, true, false);
-    step(it + 1, 1, true, false);
-    step(it + 2, 2, true, false);
-    step(it + 3, 3, true, false);
+  for (; it + NS <= clean_end; it += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) step(it + u, u, true, false);
   }
-  if (it < clean_end) step(it++, 0, true, false);
-  if (it < clean_end) step(it++, 1, true, false);
-  if (it < clean_end) step(it++, 2, true, false);
+#pragma unroll
+  for (int u = 0; u < NS - 1; ++u)
+    if (it < clean_end) step(it++, u, true, false);
   for (; it < ntiles - 1; ++it) step_any(it, true, true);
   if (ntiles > 0) step_any(ntiles - 1, false, false);
 
   // Epilogue: O = U / l (division after the V-matmul), LSE = m + log l.
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    const float l_row = l_part[cb] + __shfl_xor(l_part[cb], 32, 64);
-    if (!row_ok[cb]) continue;
-    const int r = rw0 + 32 * cb + c;
+  const float l_row = l_part + __shfl_xor(l_part, 32, 64);
+  if (row_ok) {
     const int qh = kvh * G + (r % G);
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-    const int64_t obase = (int64_t)b * p.os_b + (int64_t)qi[cb] * p.os_t + (int64_t)qh * p.os_h;
+    const int64_t obase = (int64_t)b * p.os_b + (int64_t)qi * p.os_t + (int64_t)qh * p.os_h;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int d = 32 * db + 8 * i + 4 * h;
-        const float o0 = oacc[cb][db][4 * i + 0] * inv, o1 = oacc[cb][db][4 * i + 1] * inv;
-        const float o2 = oacc[cb][db][4 * i + 2] * inv, o3 = oacc[cb][db][4 * i + 3] * inv;
+        const float o0 = oacc[db][4 * i + 0] * inv, o1 = oacc[db][4 * i + 1] * inv;
+        const float o2 = oacc[db][4 * i + 2] * inv, o3 = oacc[db][4 * i + 3] * inv;
         if (p.o_bf16) {
           uint2 pk2;
           pk2.x = pack_bf16x2(o0, o1);
@@ -468,32 +424,33 @@ void prefill_d128_kernel(KParams p, int nrt) {
         }
       }
     if (h == 0 && p.lse_out)
-      p.lse_out[((int64_t)b * p.Lq + qi[cb]) * p.Hq + qh] =
-          l_row > 0.f ? (m_ref[cb] + fast_log2(l_row)) * kLn2 : kNegInf;
+      p.lse_out[((int64_t)b * p.Lq + qi) * p.Hq + qh] =
+          l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : kNegInf;
   }
 }
 
-}  // namespace
-
-template <int NW, int NCB>
+template <int KB, int NS>
 hipError_t launch_variant(const KParams& p, int nrt, int64_t nwg, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_d128_kernel<NW, NCB>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_d128_kernel<KB, NS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       lds_bytes(KB, NS));
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((prefill_d128_kernel<NW, NCB>), dim3((unsigned)nwg), dim3(NW * 64), LDS_BYTES,
-                     s, p, nrt);
+  hipLaunchKernelGGL((prefill_d128_kernel<KB, NS>), dim3((unsigned)nwg), dim3(NT),
+                     lds_bytes(KB, NS), s, p, nrt);
   return hipGetLastError();
 }
+
+}  // namespace
 
 hipError_t launch_prefill_d128(const KParams& p, hipStream_t s) {
   const int nrt = (p.rows + ROWS - 1) / ROWS;
   const int64_t nwg = (int64_t)p.B * p.Hkv * nrt;
   if (nwg == 0) return hipSuccess;
-  return launch_variant<8, 1>(p, nrt, nwg, s);
+  return launch_variant<1, kPrefillStages>(p, nrt, nwg, s);
 }
 
 }  // namespace attn

@@ -59,6 +59,11 @@ def parse():
     ap.add_argument("--two-launch", action="store_true",
                     help="time decode as split kernel + combine kernel instead of one launch")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain device copy of known size (for PMC byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --copy-calibration --workload W` into profiles/traffic.json")
     return ap.parse_args()
 
 
@@ -122,6 +127,74 @@ def attention_flops(prob):
 def source_sha(relpath):
     with open(os.path.join(ROOT, relpath), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+COPY_CALIBRATION_BYTES = 256 << 20  # bytes read (and written) by the calibration copy
+
+# Kernel-name substring and source file of the dominant kernel of each workload
+# family, for the PMC summary.
+KERNEL_OF = {
+    "gqa_d128": ("decode_gqa_d128_kernel", "reduction_attention_gqa_amd/csrc/kernels/decode_gqa_d128.hip"),
+    "mla": ("decode_mla_kernel", "reduction_attention_gqa_amd/csrc/kernels/decode_mla.hip"),
+    "generic": ("generic", "reduction_attention_gqa_amd/csrc/kernels/generic.hip"),
+    "prefill": ("prefill_d128_kernel", "reduction_attention_gqa_amd/csrc/kernels/prefill_d128.hip"),
+}
+
+
+def copy_calibration(dev):
+    """A plain device copy of COPY_CALIBRATION_BYTES (read) into another buffer
+    (written), twice: the reference for rocprofv3's FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    src = torch.ones(COPY_CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _pmc_per_dispatch(csv_path, counter):
+    """{dispatch id: (kernel name, summed counter value)} from a rocprofv3 csv."""
+    import csv
+    out = {}
+    with open(csv_path) as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] != counter:
+                continue
+            d = int(row["Dispatch_Id"])
+            name, v = out.get(d, (row["Kernel_Name"], 0.0))
+            out[d] = (name, v + float(row["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(fetch_csv, write_csv, workload_name, family, key):
+    """HBM bytes per launch of the dominant kernel, each counter scaled by what it
+    reads for the calibration copy (COPY_CALIBRATION_BYTES read and written)."""
+    sub, src = KERNEL_OF[family]
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        per = _pmc_per_dispatch(path, counter)
+        # The calibration copies are the first two copy dispatches of the run
+        # (bench.py runs them before anything else is copied).
+        copies = [per[d][1] for d in sorted(per) if "copy" in per[d][0].lower()][:2]
+        kern = [v for n, v in per.values() if sub in n]
+        if len(copies) < 2 or not kern:
+            raise SystemExit(f"{path}: no calibration copy or no {sub} dispatch found")
+        copy_kib = sum(copies) / 2
+        factor = COPY_CALIBRATION_BYTES / (copy_kib * 1024.0)
+        kib = sorted(kern)[len(kern) // 2]  # median over the launches
+        res[counter] = dict(kib_per_dispatch=kib, copy_kib=copy_kib, factor=factor,
+                            bytes=kib * 1024.0 * factor, dispatches=len(kern))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[key] = {"workload": workload_name, "kernel": sub, "source": src,
+                 "source_sha": source_sha(src),
+                 "bytes_per_launch": round(res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]),
+                 "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"]}
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1, sort_keys=True)
+        f.write("\n")
+    print(json.dumps(data[key], indent=1))
 
 
 def traffic_for(kernel_src, launches_key):
@@ -330,6 +403,20 @@ def decode_record(prob, r, steps, warmup, extra_src):
 
 def main():
     a = parse()
+    if a.summarize_pmc:
+        from synthetic.inputs import workload as _wl
+        name = a.workload or "llama3_8b_gqa_decode"
+        prob = _wl(name)
+        if prob.lq > 1:
+            family, key = "prefill", f"prefill:{name}"
+        else:
+            family = {128: "gqa_d128", 576: "mla"}.get(prob.dqk, "generic")
+            if prob.dtype != "bf16":
+                family = "generic"
+            fused = family == "gqa_d128" and not a.two_launch
+            key = ("decode:" if fused else "decode_split:") + name
+        summarize_pmc(a.summarize_pmc[0], a.summarize_pmc[1], name, family, key)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": a.gpus}))
@@ -345,6 +432,9 @@ def main():
     name = a.workload or "llama3_8b_gqa_decode"
     if name not in WORKLOADS:
         sys.exit(f"unknown workload {name}; choose from {sorted(WORKLOADS)}")
+    if a.copy_calibration:
+        log("calibration copy")
+        copy_calibration(dev)
     log(f"generating {name}")
     prob = workload(name)
     is_prefill = prob.lq > 1

@@ -123,7 +123,7 @@ int decode_family(const attn_problem* p) {
 int target_wgs_per_cu(int family) {
   switch (family) {
     case ATTN_KERNEL_GQA_D128: return kGqaItemsPerCu;
-    case ATTN_KERNEL_MLA: return 1;  // one 4-wave workgroup fills a CU's register file
+    case ATTN_KERNEL_MLA: return 1;  // one 8-wave workgroup fills a CU (LDS ring)
     default: return 4;
   }
 }

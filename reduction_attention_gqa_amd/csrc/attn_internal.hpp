@@ -55,7 +55,7 @@ constexpr int kGqaBlock = 256;
 constexpr int kGqaMaxRows = 16;
 constexpr int kPrefillStages = 4;     // prefill K/V ring depth (tiles)
 constexpr int kMlaTileN = 32;          // keys per MLA tile
-constexpr int kMlaBlock = 512;         // 8 waves: 4 row groups x 2 halves
+constexpr int kMlaBlock = 512;         // 8 waves of 16 query rows
 constexpr int kMlaRows = 128;          // query rows per MLA workgroup
 
 }  // namespace attn

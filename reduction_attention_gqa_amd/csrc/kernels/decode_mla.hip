@@ -2,28 +2,28 @@
 // V = the first 512 columns of K, up to 128 query rows (heads x queries) per
 // KV head.
 //
-// One workgroup (8 waves) owns one (split, KV head, request) unit, so every
-// latent K row is read from HBM once per split and serves both contractions:
-// the 576-wide QK^T and, through its first 512 columns, the PV.  Waves come in
-// pairs per 32-row group: wave (rg, half) holds Q^T for half of the 576-wide
-// contraction (18 k-steps) and the fp32 accumulator for half of the 512 output
-// columns.  Per 32-key tile:
-//   partial S^T[32 x 32] = K[32 x 288-half] Q^T[288-half x 32]   18 MFMA 32x32x16
-//   the pair adds its two partials through LDS (a + b == b + a bit for bit, so
-//     both waves hold the same scores and take the same softmax decisions)
-//   O^T[256 x 32] += V^T[256-half x 32] P^T[32 x 32]             8 x 2 MFMA 32x32x16
-// Q^T stays in VGPRs for the whole split (loop-invariant, Cleave §6.1).
-// Rescaling the accumulator on every tile would cost more VALU time than the
-// tile's MFMAs, so the running max is updated lazily: a row's reference max
-// moves (and its accumulator and row sum are rescaled) only when the row's max
-// grows by more than 2^8; otherwise P = 2^(s - m_ref) <= 256 is used as is.
-// Row sum and accumulator always share one reference, so O = U / l is
-// unchanged.
+// One workgroup (8 waves, two per SIMD) owns one (split, KV head, request)
+// unit, so every latent K row is read from HBM once per split and serves both
+// contractions: the 576-wide QK^T and, through its first 512 columns, the PV.
+// Wave w owns query rows 16w .. 16w + 15 outright: Q^T for the whole 576-wide
+// contraction stays in registers for the split (loop-invariant, Cleave §6.1)
+// and so does the fp32 accumulator O^T[512 x 16].  No partial result crosses
+// waves, so the only barrier per tile is the one that hands a K tile over.
+// Per 32-key tile and wave (16x16x32 bf16 MFMA, keys on the MFMA rows):
+//   S^T[32 x 16]  = K[32 x 576] Q^T[576 x 16]      2 x 18 MFMA (two chains)
+//   O^T[512 x 16] += V^T[512 x 32] P^T[32 x 16]    32 MFMA (32 accumulators)
+// The two waves of a SIMD overlap one's softmax with the other's MFMAs.
+//
+// The running max is updated lazily: a row's reference max moves (and its
+// accumulator and row sum are rescaled) only when the row's max grows by more
+// than 2^8; otherwise P = 2^(s - m_ref) <= 256 is used as is.  Row sum and
+// accumulator always share one reference, so O = U / l is unchanged.
 //
 // The K tile is copied HBM -> LDS by buffer loads that write LDS directly (no
-// staging registers).  Rows are padded to 73 16-byte chunks, so the A-operand
-// reads of K (8 consecutive keys per pass) hit distinct banks and every LDS
-// offset in the loop is a compile-time immediate.
+// staging registers), four stages deep (three tiles in flight).  Key rows are
+// stored unpadded (72 16-byte chunks) with the chunk index XOR-ed by the low
+// bits of the key, which keeps both the 16-key A-operand reads of K and the
+// transposed 4-key reads of V free of LDS bank conflicts.
 #include "../attn_internal.hpp"
 #include "common.hpp"
 
@@ -34,34 +34,46 @@ constexpr int NW = 8;
 constexpr int NT = NW * 64;
 constexpr int TK = kMlaTileN;          // 32 keys per tile
 constexpr int DQK = 576, DV = 512;
-constexpr int KS_HALF = DQK / 16 / 2;  // 18 k-steps per wave
-constexpr int DB_HALF = DV / 32 / 2;   // 8 output d-blocks per wave
-constexpr int CHUNKS = DQK / 8;        // 72 16-byte chunks of data per key row
-constexpr int SLOTS = CHUNKS + 1;      // + 1 pad chunk
-constexpr int ROW_BYTES = SLOTS * 16;  // 1168
-constexpr int STAGE = TK * ROW_BYTES;  // 37,376
-constexpr int XBUF = NW * 64 * 16 * 4; // partial-score exchange, 32 KiB
-constexpr int NSTAGE = 3;              // tiles it, it + 1, it + 2 resident
-constexpr int LDS_BYTES = NSTAGE * STAGE + XBUF;  // 144,896
-constexpr int NSLOT = TK * SLOTS;      // 2336 16-byte slots per stage
-constexpr int NBLK = (NSLOT + 63) / 64;  // 37 one-KiB DMA blocks
+constexpr int KSTEPS = DQK / 32;       // 18 k-steps of the QK contraction
+constexpr int CBLK = DV / 16;          // 32 output column blocks
+constexpr int CHUNKS = DQK / 8;        // 72 16-byte chunks per key row
+constexpr int ROW_BYTES = CHUNKS * 16; // 1152
+constexpr int HALF = 16 * ROW_BYTES;   // byte offset of key 16 in a stage
+constexpr int STAGE = TK * ROW_BYTES;  // 36,864
+constexpr int NSTAGE = 4;              // tiles it .. it + 3 resident
+constexpr int LDS_BYTES = NSTAGE * STAGE;  // 147,456
+constexpr int NBLK = TK * CHUNKS / 64;     // 36 one-KiB DMA blocks per tile
+constexpr int BLK_ROUNDS = (NBLK + NW - 1) / NW;  // 5: waves 0-3 issue 5, waves 4-7 issue 4
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+static_assert(NBLK * 64 == TK * CHUNKS, "a tile is a whole number of DMA blocks");
+static_assert(NBLK - (BLK_ROUNDS - 1) * NW == 4, "waves 0-3 own the last round");
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) const i32x4_t lds_i32x4_t;
 
-// Byte offset of (key, 16-byte chunk c) in a stage.
-__device__ __forceinline__ int chunk_off(int key, int c) { return key * ROW_BYTES + 16 * c; }
+// Physical 16-byte chunk of logical chunk c of key row `key` (within its row):
+// c XOR (key & 7).  The XOR only touches the low three bits, so a chunk stays
+// inside its aligned group of 8.  Measured on gfx950 with the exact per-lane
+// address lists of both read patterns below, this layout runs the 16-key K
+// fragment reads at the rate of lane-contiguous 16-byte reads and the
+// transposed V reads at the rate of lane-contiguous transposed reads, while an
+// unswizzled 1152-byte row runs both about 3x slower.
+__device__ __forceinline__ int chunk_xor(int key) { return key & 7; }
 
-__device__ __forceinline__ i32x2_t ds_read_tr(const char* lds) {
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(lds));
+__device__ __forceinline__ i32x2_t ds_read_tr_at(uint32_t lds_addr) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(uintptr_t)lds_addr);
   return __builtin_bit_cast(i32x2_t, v);
 }
+__device__ __forceinline__ i32x4_t ds_read16_at(uint32_t lds_addr) {
+  return *reinterpret_cast<lds_i32x4_t*>((uintptr_t)lds_addr);
+}
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
-__global__ __launch_bounds__(NT) void decode_mla_kernel(KParams p) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_mla_kernel(KParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int t = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int j = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
@@ -70,222 +82,246 @@ __global__ __launch_bounds__(NT) void decode_mla_kernel(KParams p) {
   if (lo >= L) return;
   const int hi = min(lo + p.chunk, L);
 
-  const int rg = w >> 1;      // 32-row group
-  const int half = w & 1;     // contraction half for QK, column half for PV
   const int G = p.G;
   const int R = p.rows;
-  const int c = lane & 31;
-  const int h = lane >> 5;
-  const int r = 32 * rg + c;
+  const int li = lane & 15;   // query row within the wave (MFMA column)
+  const int g = lane >> 4;    // 16-lane group
+  const int r = 16 * w + li;
   const int qi = r / G;
   const int qh = kvh * G + r % G;
   const bool row_ok = r < R;
   const int qlim = qi + L - p.Lq;
 
-  // Q^T (this wave's 18 k-steps) as the B operand: Q[row r][16*ks + 8*h .. +7].
-  bf16x8_t qf[KS_HALF];
+  // Q^T as the B operand: lane holds Q[row r][32*ks + 8*g .. +7], ks = 0..17.
+  bf16x8_t qf[KSTEPS];
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + (int64_t)b * p.qs_b +
-                         (int64_t)qi * p.qs_t + (int64_t)qh * p.qs_h + 16 * KS_HALF * half;
+                         (int64_t)qi * p.qs_t + (int64_t)qh * p.qs_h;
 #pragma unroll
-    for (int ks = 0; ks < KS_HALF; ++ks) {
+    for (int ks = 0; ks < KSTEPS; ++ks) {
       i32x4_t v = {0, 0, 0, 0};
-      if (row_ok) v = *reinterpret_cast<const i32x4_t*>(qp + 16 * ks + 8 * h);
+      if (row_ok) v = *reinterpret_cast<const i32x4_t*>(qp + 32 * ks + 8 * g);
       qf[ks] = as_bf16x8(v);
     }
-    // Wait for Q here, once: otherwise the wait lands at the loop head and also
-    // drains the K/V DMA in flight on every tile.
+    // Wait for Q here, once: otherwise the wait lands inside the loop and also
+    // drains the K DMA in flight.
 #pragma unroll
-    for (int ks = 0; ks < KS_HALF; ++ks) asm volatile("" ::"v"(qf[ks]));
+    for (int ks = 0; ks < KSTEPS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
   const uint32_t kst = (uint32_t)(p.ks_t * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)L * kst);
-
-  // Tile copy, HBM -> LDS without registers (buffer_load ... lds): each wave
-  // instruction fills one KiB of the stage, lane l the 16-byte slot 64*blk + l.
-  // Slot P holds chunk P % 73 of key P / 73; pad slots and slots past the stage
-  // are left to inactive lanes.  Waves 0-4 issue 5 instructions per tile, waves
-  // 5-7 issue 4 (37 blocks).
-  // The DMA is issued from inline asm so the compiler does not pair it with
-  // conservative vmcnt waits before unrelated LDS reads; completion is awaited
-  // explicitly (wait_older_tile) before each barrier that publishes a tile.
-  const int w_s = __builtin_amdgcn_readfirstlane(w);  // wave index in an SGPR
+  // The buffer range ends at this split's last key: rows past it read as zero.
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)hi * kst);
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(smem);
-  auto gload_lds = [&](int k0, int stage) {
+
+  // Tile copy, HBM -> LDS without registers (buffer_load ... lds): one wave
+  // instruction fills one KiB of the stage, lane l the 16-byte slot 64*blk + l,
+  // which holds physical chunk P % 72 of key P / 72 (P = the slot).  The whole
+  // byte offset goes in the per-lane offset, which the buffer range check
+  // covers.  The per-lane offsets are recomputed per tile (a few integer
+  // instructions) rather than held in registers across the loop.
+  const int nb = w < NBLK - (BLK_ROUNDS - 1) * NW ? BLK_ROUNDS : BLK_ROUNDS - 1;
+  auto dma_tile = [&](int t, int stage) {
     const uint32_t base = smem_lds + (uint32_t)(stage * STAGE);
-    const uint32_t soff = (uint32_t)k0 * kst;
+    const uint32_t toff = (uint32_t)(lo + t * TK) * kst;
     int ln = lane;
-    asm volatile("" : "+v"(ln));  // recompute the slot offsets per tile (no spills)
+    asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int u = 0; u < (NBLK + NW - 1) / NW; ++u) {
-      const int blk = u * NW + w_s;
-      if (blk < NBLK) {
-        const int P = blk * 64 + ln;
-        const int key = P / SLOTS, cc = P % SLOTS;
-        const uint32_t m0v = base + (uint32_t)(blk * 1024);
-        const uint32_t voff = (uint32_t)key * kst + 16 * cc;
-        if (P < NSLOT && cc < CHUNKS) {
-          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                       :: "s"(m0v), "v"(voff), "s"(krs), "s"(soff) : "memory", "m0");
-        }
+    for (int u = 0; u < BLK_ROUNDS; ++u) {
+      if (u < BLK_ROUNDS - 1 || nb == BLK_ROUNDS) {
+        const int P = 64 * (u * NW + w) + ln;
+        const int key = P / CHUNKS;
+        const int c = (P - key * CHUNKS) ^ chunk_xor(key);
+        const uint32_t m0v = base + (uint32_t)((u * NW + w) * 1024);
+        const uint32_t voff = toff + (uint32_t)key * kst + 16u * (uint32_t)c;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                     :: "s"(m0v), "v"(voff), "s"(krs) : "memory", "m0");
       }
     }
   };
-  // All DMA of the older tile has landed once at most the newer tile's
+  // All DMA of a tile has landed once at most the `later` newer tiles'
   // instructions are outstanding (loads complete in order).
-  auto wait_older_tile = [&]() {
-    if (w < NBLK - 4 * NW)
-      asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  auto wait_tiles_but = [&](int later) {
+    if (later >= 2) {
+      if (nb == 5) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else if (later == 1) {
+      if (nb == 5) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
   };
-  float* xbuf = reinterpret_cast<float*>(smem + NSTAGE * STAGE);   // [NW][16][64] floats
-  float* xmine = xbuf + w * 1024;
-  const float* xpeer = xbuf + (w ^ 1) * 1024;
 
-  f32x16_t oacc[DB_HALF];
+  // Per-lane LDS addresses (opaque to the compiler, so every read is one of
+  // these plus an immediate).
+  //   K fragment (key block kb, k-step ks): key 16*kb + li, logical chunk
+  //   4*ks + g -> physical 4*(ks ^ x2) + (g ^ x01), x = chunk_xor(li) (the
+  //   same for key 16 + li).
+  //   Even ks: 64*ks + 64*x2; odd ks: 64*ks - 64*x2.
+  const int xk = chunk_xor(li);
+  const uint32_t k_lane = smem_lds + (uint32_t)(li * ROW_BYTES + 16 * (g ^ (xk & 3)));
+  uint32_t k_even = k_lane + 64u * (uint32_t)(xk >> 2);
+  uint32_t k_odd = k_lane - 64u * (uint32_t)(xk >> 2);
+  //   V^T fragment (column block cb, key half kh): the 16-lane group g reads
+  //   keys 16*kh + 4*g + (li >> 2), columns 16*cb + 4*(li & 3) .. + 3, i.e.
+  //   logical chunk 2*cb + ((li >> 1) & 1), bytes 8*(li & 1) .. + 7; after the
+  //   transpose lane li holds column 16*cb + li of keys 16*kh + 4*g + 0..3.
+  //   Physical chunk 2*(cb ^ y1) + (((li >> 1) & 1) ^ y0), y = chunk_xor(key):
+  //   one base per cb & 3, plus 128*(cb >> 2).
+  const int vkey = 4 * g + (li >> 2);
+  const int xv = chunk_xor(vkey);
+  const uint32_t v_lane = smem_lds + (uint32_t)(vkey * ROW_BYTES + 16 * (((li >> 1) & 1) ^ (xv & 1)) +
+                                                8 * (li & 1));
+  uint32_t v_base[4];
 #pragma unroll
-  for (int db = 0; db < DB_HALF; ++db)
+  for (int n = 0; n < 4; ++n) v_base[n] = v_lane + 32u * (uint32_t)(n ^ (xv >> 1));
+
+  f32x4_t oacc[CBLK];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
+  for (int cb = 0; cb < CBLK; ++cb) oacc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float m_ref = kNegInf;   // reference max of this lane's row (base-2 units)
-  float l_part = 0.f;
+  float l_part = 0.f;      // this lane's share of the row sum
   const float sl2 = p.scale_log2;
-
-  // Transposed V read: 16-lane group gq reads keys 4*(gq>>1) + li/4 (+8), element
-  // columns 32*db + 16*(gq&1) + 4*(li&3) .. +3 of this wave's 256-column half.
-  const int gq = lane >> 4, li = lane & 15;
-  const int vkey = 4 * (gq >> 1) + (li >> 2);
-  const int vcol = 256 * half + 16 * (gq & 1) + 4 * (li & 3);
-
+  const bool row_causal = p.causal != 0;
   const int ntiles = (hi - lo + TK - 1) / TK;
-  // Barriers are written as s_barrier after an LDS-only wait: a plain
-  // __syncthreads() would also wait for the LDS DMA of the tiles in flight.
-  gload_lds(lo, 0);
-  if (ntiles > 1) {
-    gload_lds(lo + TK, 1);
-    wait_older_tile();
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-  int st_cur = 0, st_pre = 2;  // stage of tile it, stage for tile it + 2
+  // Operand fetches of a tile, in MFMA order: f = 0..35 the K fragments
+  // (f = 2*ks + kb), f = 36..67 the V^T fragments (column block f - 36).  One
+  // rolling window of FD fetches runs across the whole tile and on into the
+  // next tile's K fragments, so V is already in flight during the softmax and
+  // the next scores' K during the V-matmul.
+  constexpr int NF = 2 * KSTEPS + CBLK;  // 68
+  constexpr int FD = 3;                  // fetches in flight
+  auto fetch = [&](int f, uint32_t soff) -> i32x4_t {
+    if (f < 2 * KSTEPS) {
+      const int ks = f >> 1, kb = f & 1;
+      return ds_read16_at((ks & 1 ? k_odd : k_even) + soff + (uint32_t)(kb * HALF + 64 * ks));
+    }
+    const int cb = f - 2 * KSTEPS;
+    const uint32_t a = v_base[cb & 3] + soff + (uint32_t)(128 * (cb >> 2));
+    const i32x2_t v0 = ds_read_tr_at(a);
+    const i32x2_t v1 = ds_read_tr_at(a + HALF);
+    i32x4_t va;
+    va[0] = v0[0];
+    va[1] = v0[1];
+    va[2] = v1[0];
+    va[3] = v1[1];
+    return va;
+  };
+
+  // Prologue: tiles 0..2 in flight, tile 0 landed, its first K fetches issued.
+#pragma unroll
+  for (int t = 0; t < NSTAGE - 1; ++t)
+    if (t < ntiles) dma_tile(t, t);
+  wait_tiles_but(min(ntiles - 1, NSTAGE - 2));
+  asm volatile("s_barrier" ::: "memory");
+  i32x4_t fr[NF + FD];
+#pragma unroll
+  for (int f = 0; f < FD; ++f) fr[f] = fetch(f, 0);
+
   for (int it = 0; it < ntiles; ++it) {
+    const int st = it & (NSTAGE - 1);
+    const uint32_t soff = (uint32_t)(st * STAGE);
+    // The next tile's stage; on the last tile the fetches into it read stale
+    // (in-bounds) LDS and are dropped.
+    const uint32_t soff_next = (uint32_t)(((it + 1) & (NSTAGE - 1)) * STAGE);
+
+    // S^T = K Q^T: two chains (key blocks).
+    f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int f = 0; f < 2 * KSTEPS; ++f) {
+      fr[f + FD] = fetch(f + FD, soff);
+      if (f & 1)
+        s1 = mfma16x16x32(as_bf16x8(fr[f]), qf[f >> 1], s1);
+      else
+        s0 = mfma16x16x32(as_bf16x8(fr[f]), qf[f >> 1], s0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Softmax: lane holds keys k0 + 4*g + e (s0) and k0 + 16 + 4*g + e (s1).
     const int k0 = lo + it * TK;
-    const bool prefetch = it + 2 < ntiles;
-    if (prefetch) gload_lds(k0 + 2 * TK, st_pre);
-    const char* kl = smem + st_cur * STAGE;
-
-    // Partial S^T over this wave's half of the contraction.
-    f32x16_t s;
+    float sc[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KS_HALF; ++ks) {
-      const int chunk = 2 * (KS_HALF * half + ks) + h;
-      const i32x4_t kf = *reinterpret_cast<const i32x4_t*>(kl + chunk_off(c, chunk));
-      s = mfma32x32x16(as_bf16x8(kf), qf[ks], s);
+    for (int e = 0; e < 4; ++e) {
+      sc[e] = s0[e];
+      sc[4 + e] = s1[e];
     }
-    // Exchange partials with the peer wave (column-major [e][lane]: no bank conflicts).
+    const bool need_mask = (k0 + TK > hi) || (row_causal && k0 + TK - 1 > qlim) || !row_ok;
+    if (__builtin_amdgcn_ballot_w64(need_mask) != 0) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) xmine[e * 64 + lane] = s[e];
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s[e] += xpeer[e * 64 + lane];
-
-    const bool need_mask = (k0 + TK > hi) || (p.causal && k0 + TK - 1 > qlim) || !row_ok;
-    float mt = kNegInf;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float v = s[e] * sl2;
-      if (need_mask) {
-        const int key = k0 + 8 * (e >> 2) + 4 * h + (e & 3);
-        const bool vis = key < hi && (!p.causal || key <= qlim) && row_ok;
-        v = vis ? v : kNegInf;
+      for (int e = 0; e < 8; ++e) {
+        const int key = k0 + 16 * (e >> 2) + 4 * g + (e & 3);
+        const bool vis = key < hi && (!row_causal || key <= qlim) && row_ok;
+        sc[e] = vis ? sc[e] : kNegInf;
       }
-      s[e] = v;
-      mt = fmaxf(mt, v);
     }
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    float mx = vmax(vmax(vmax(sc[0], sc[1]), vmax(sc[2], sc[3])),
+                    vmax(vmax(sc[4], sc[5]), vmax(sc[6], sc[7])));
+    mx *= sl2;
     // Lazy rescale: move the reference only when some row's max outgrows it.
-    const bool grow = mt > m_ref + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float m_new = fmaxf(m_ref, mt);
+    if (__builtin_amdgcn_ballot_w64(mx > m_ref + kRescaleThreshold) != 0) {
+      mx = vmax(mx, __shfl_xor(mx, 16, 64));
+      mx = vmax(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = vmax(m_ref, mx);
       // On a row's first update the accumulator and sum are still zero.
       const float alpha = (m_ref == kNegInf) ? 0.f : fast_exp2(m_ref - m_new);
       l_part *= alpha;
 #pragma unroll
-      for (int db = 0; db < DB_HALF; ++db) oacc[db] *= alpha;
+      for (int cb = 0; cb < CBLK; ++cb) oacc[cb] *= alpha;
       m_ref = m_new;
     }
     const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
-    float ps = 0.f;
+    float pv[8];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float pv = fast_exp2(s[e] - m_use);
-      s[e] = pv;
-      ps += pv;
-    }
-    l_part += ps;
+    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(sc[e], sl2, -m_use));
+    l_part += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    // P^T as the B operand: k-slot 8*g + t <-> key 4*g + t (t < 4), 16 + 4*g + t - 4.
+    i32x4_t pk;
+    pk[0] = (int)pack_bf16x2(pv[0], pv[1]);
+    pk[1] = (int)pack_bf16x2(pv[2], pv[3]);
+    pk[2] = (int)pack_bf16x2(pv[4], pv[5]);
+    pk[3] = (int)pack_bf16x2(pv[6], pv[7]);
+    const bf16x8_t pb = as_bf16x8(pk);
 
-    // O^T += V^T P^T over two 16-key steps.
+    // Hand-over: tile it + 1 has landed for every wave (the V-matmul below
+    // starts reading its K), and every wave has finished tile it - 1, whose
+    // stage the DMA of tile it + 3 now refills.  Reads of tile it issued
+    // before the barrier are all consumed before the next one.
+    wait_tiles_but(min(ntiles - it - 2, 1));
+    asm volatile("s_barrier" ::: "memory");
+    if (it + NSTAGE - 1 < ntiles) dma_tile(it + NSTAGE - 1, (it + NSTAGE - 1) & (NSTAGE - 1));
+
+    // O^T += V^T P^T; the window runs on into the next tile's K fragments.
 #pragma unroll
-    for (int ts = 0; ts < 2; ++ts) {
-      const int i0 = 2 * ts;
-      i32x4_t pk;
-      pk[0] = (int)pack_bf16x2(s[4 * i0 + 0], s[4 * i0 + 1]);
-      pk[1] = (int)pack_bf16x2(s[4 * i0 + 2], s[4 * i0 + 3]);
-      pk[2] = (int)pack_bf16x2(s[4 * i0 + 4], s[4 * i0 + 5]);
-      pk[3] = (int)pack_bf16x2(s[4 * i0 + 6], s[4 * i0 + 7]);
-      const bf16x8_t pb = as_bf16x8(pk);
-      const int key_a = 16 * ts + vkey;
-      const int key_b = key_a + 8;
-#pragma unroll
-      for (int db = 0; db < DB_HALF; ++db) {
-        const int col = 32 * db + vcol;   // element column, multiple of 4
-        const int ch = col >> 3, within = (col & 7) * 2;
-        const i32x2_t lo2 = ds_read_tr(kl + chunk_off(key_a, ch) + within);
-        const i32x2_t hi2 = ds_read_tr(kl + chunk_off(key_b, ch) + within);
-        i32x4_t va;
-        va[0] = lo2[0];
-        va[1] = lo2[1];
-        va[2] = hi2[0];
-        va[3] = hi2[1];
-        oacc[db] = mfma32x32x16(as_bf16x8(va), pb, oacc[db]);
-      }
+    for (int f = 2 * KSTEPS; f < NF; ++f) {
+      fr[f + FD] = f + FD < NF ? fetch(f + FD, soff) : fetch(f + FD - NF, soff_next);
+      const int cb = f - 2 * KSTEPS;
+      oacc[cb] = mfma16x16x32(as_bf16x8(fr[f]), pb, oacc[cb]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    // Tile it + 1 must have landed; tile it + 2 may stay in flight.
-    if (prefetch)
-      wait_older_tile();
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    st_cur = st_cur == NSTAGE - 1 ? 0 : st_cur + 1;
-    st_pre = st_pre == NSTAGE - 1 ? 0 : st_pre + 1;
+#pragma unroll
+    for (int f = 0; f < FD; ++f) fr[f] = fr[NF + f];
   }
 
-  // Split epilogue: O_j = U / l (fp32), LSE_j = (m_ref + log2 l) ln 2.
-  const float l_row = l_part + __shfl_xor(l_part, 32, 64);
-  if (row_ok) {
+  // Split epilogue: O_j = U / l (fp32), LSE_j = (m_ref + log2 l) ln 2.  Lane
+  // holds columns 16*cb + 4*g .. + 3 of row r.  The row's indices are
+  // recomputed here rather than kept live across the loop.
+  float l_row = l_part + __shfl_xor(l_part, 16, 64);
+  l_row += __shfl_xor(l_row, 32, 64);
+  int e_lane = threadIdx.x;
+  asm volatile("" : "+v"(e_lane));
+  const int e_r = 16 * w + (e_lane & 15), e_g = (e_lane >> 4) & 3;
+  if (e_r < R) {
+    const int e_qi = e_r / G, e_qh = kvh * G + e_r % G;
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-    const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + ((int64_t)b * p.Lq + qi) * p.Hq + qh;
-    float* dst = p.ws_o + slot * DV + 256 * half;
+    const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + ((int64_t)b * p.Lq + e_qi) * p.Hq + e_qh;
+    float* dst = p.ws_o + slot * DV + 4 * e_g;
 #pragma unroll
-    for (int db = 0; db < DB_HALF; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4_t v;
-        v[0] = oacc[db][4 * i + 0] * inv;
-        v[1] = oacc[db][4 * i + 1] * inv;
-        v[2] = oacc[db][4 * i + 2] * inv;
-        v[3] = oacc[db][4 * i + 3] * inv;
-        *reinterpret_cast<f32x4_t*>(dst + 32 * db + 8 * i + 4 * h) = v;
-      }
-    if (h == 0 && half == 0)
-      p.ws_lse[slot] = l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : kNegInf;
+    for (int cb = 0; cb < CBLK; ++cb)
+      *reinterpret_cast<f32x4_t*>(dst + 16 * cb) = oacc[cb] * inv;
+    if (e_g == 0) p.ws_lse[slot] = l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : kNegInf;
   }
 }
 

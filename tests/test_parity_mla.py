@@ -37,3 +37,16 @@ def test_mla_full_size_sampled_rows():
     o, lse = attention_rows(p.q, p.k, v_rows(p), False, p.scale, rows)
     assert_close("mla full sampled", np.stack([out[r] for r in rows]), o, BF16_MAX, BF16_MEAN)
     assert_lse_close("mla full sampled", np.array([lse_g[r] for r in rows]), lse)
+
+
+@pytest.mark.parametrize("s", [0, 2])
+def test_mla_partial_row_groups_causal_two_queries(s):
+    # 40 heads x 2 query rows = 80 rows: the last 16-row group is half empty;
+    # causal bottom-right mask, a one-key request and ragged tails.
+    p = make_problem(dtype="bf16", batch=3, lq=2, hq=40, hkv=1, dqk=576, dv=512,
+                     kv_len=[1, 77, 645], lcap=704, seed=42, mla=True, causal=True)
+    d = DeviceProblem(p)
+    plan = d.decode(s_request=s)
+    o, lse = attention(p.q, p.k, v_rows(p), True, p.scale)
+    assert_close(f"mla causal lq=2 s={s} kernel={plan.kernel}", d.out(), o, BF16_MAX, BF16_MEAN)
+    assert_lse_close(f"mla causal lq=2 s={s}", d.lse_out(), lse)

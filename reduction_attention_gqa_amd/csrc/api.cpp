@@ -235,23 +235,19 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
 
   // GQA D=128: when there are at least as many (request, KV head) units as
   // compute units and no request is much longer than the mean, one split per
-  // request (no partials, no merge) with 8-wave workgroups; otherwise 4-wave
-  // workgroups and the key axis split to about kGqaItemsPerCu items per CU.
-  int waves = 4;
+  // request (no partials, no merge); otherwise the key axis is split to about
+  // kGqaItemsPerCu items per CU.
+  bool one_split = false;
   if (family == ATTN_KERNEL_GQA_D128 && p->batch > 0) {
     const bool balanced = lmax * 4 * p->batch <= keys_total * 5;
-    const bool one_split = s_request == 1 ||
+    one_split = s_request == 1 ||
         (s_request <= 0 && (int64_t)p->batch * p->kv_heads >= cus && balanced);
-    if (one_split) {
-      waves = 8;
-      tile_n = kGqaTileN * 2;
-    }
   }
 
   int64_t s_max = 1, chunk = tile_n;
   if (lmax > 0) {
     const int64_t max_tiles = ceil_div(lmax, tile_n);
-    if (waves == 8) {
+    if (one_split) {
       chunk = max_tiles * tile_n;
     } else if (s_request > 0) {
       s_max = std::min<int64_t>(s_request, max_tiles);
@@ -295,7 +291,7 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
     out->grid[0] = (uint32_t)(ceil_div(n_items, 8) * 8);  // workgroup x runs on XCD x % 8
     out->grid[1] = 1;
     out->grid[2] = 1;
-    out->block = 64 * waves;
+    out->block = kGqaBlock;
   } else {
     out->grid[0] = (uint32_t)s_max;
     out->grid[1] = (uint32_t)p->kv_heads;
@@ -338,7 +334,6 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan, const 
 
   const dim3 unit_grid(plan->s_max, p->kv_heads, p->batch);
   kp.n_items = plan->n_items;
-  kp.waves = plan->block == 512 ? 8 : 4;
   if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_fits(p, q, k, v))
     return hip_status(launch_decode_gqa_d128(kp, s), "decode_gqa_d128 launch");
   if (plan->kernel == ATTN_KERNEL_MLA && mla_fits(p, q, k, v))
@@ -376,7 +371,6 @@ int attn_decode(const attn_problem* problem, const attn_plan* plan, const void* 
     kp.chunk = plan->chunk;
     kp.s_max = plan->s_max;
     kp.n_items = plan->n_items;
-    kp.waves = plan->block == 512 ? 8 : 4;
     kp.split_mode = plan->s_max == 1 ? 0 : 2;
     return hip_status(launch_decode_gqa_d128(kp, s), "decode_gqa_d128 launch");
   }

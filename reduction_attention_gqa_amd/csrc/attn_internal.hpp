@@ -33,7 +33,6 @@ struct KParams {
   int32_t rows;         // G * Lq rows per (request, KV head)
   int32_t row_tile;     // rows per workgroup (generic kernel)
   int32_t split_mode;   // 0: write o (+ lse_out); 1: write ws_o/ws_lse; 2: 1 + in-kernel merge
-  int32_t waves;        // waves per workgroup of the GQA decode kernel (4 or 8)
   float scale_log2;     // tau * log2(e): scores are kept in base-2 units
 };
 

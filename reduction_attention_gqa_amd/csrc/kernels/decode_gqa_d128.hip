@@ -7,11 +7,13 @@
 // head into the MFMA column dimension, so every K/V byte is read from HBM once.
 //
 // Work items are numbered with the split fastest, then the KV head, then the
-// request; XCD x (workgroups x, x + 8, ...) takes one contiguous range of
-// them, so each XCD streams a compact region of the K/V cache (all heads of
-// the same tokens together).  The item of a workgroup is found on the device
-// from the per-request key counts, so one compiled kernel serves any mix of
-// lengths.
+// request.  With several splits per request, XCD x (workgroups x, x + 8, ...)
+// takes one contiguous range of them, so each XCD streams a compact region of
+// the K/V cache; with one split per request, workgroup i takes item i, which
+// spreads the KV heads of a request over the XCDs (measured faster for that
+// case, the other way round for many splits).  The item of a workgroup is
+// found on the device from the per-request key counts, so one compiled kernel
+// serves any mix of lengths.
 //
 // Within the workgroup the four waves take interleaved 32-key blocks of the
 // split and each keeps its own running max / sum / output (a second, on-chip
@@ -71,6 +73,18 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // Every wave computes the same answer.
 __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, int& kvh, int& j,
                                           int& sb, int& L) {
+  // One split per request: workgroup i is unit i (request i / Hkv, KV head
+  // i % Hkv), every request has exactly one item, and only this request's
+  // length is needed (a scalar load).
+  if (p.s_max == 1) {
+    if ((int64_t)blockIdx.x >= (int64_t)p.B * p.Hkv) return false;
+    b = blockIdx.x / p.Hkv;
+    kvh = blockIdx.x - b * p.Hkv;
+    j = 0;
+    sb = 1;
+    L = kv_len_of(p.kv_lens, b, p.Lcap);
+    return true;
+  }
   const int64_t N = p.n_items;
   const int x = blockIdx.x & 7;
   const int64_t k = blockIdx.x >> 3;
@@ -169,12 +183,15 @@ __device__ __forceinline__ void store_o8(const KParams& p, int64_t off, const f3
   }
 }
 
-// NW waves per workgroup (4 or 8); a workgroup round covers KB * NW keys.
-template <int NW>
+// Four waves per workgroup; a workgroup round covers KB * NW keys.  NB
+// register blocks per wave are in flight (four measured slower than two, also
+// with one workgroup per CU).
+constexpr int NW = 4;
+constexpr int NB = 2;
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_gqa_d128_kernel(KParams p) {
   constexpr int STEP = KB * NW;
-  __shared__ __attribute__((aligned(16))) char lds_raw[NW * VTILE];  // 36 or 72 KiB
+  __shared__ __attribute__((aligned(16))) char lds_raw[NW * VTILE];  // 36 KiB
   __shared__ float m_w[NW][16];
   __shared__ float l_w[NW][16];
 
@@ -183,6 +200,14 @@ void decode_gqa_d128_kernel(KParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int b, kvh, j, sb, L;
   if (!find_item(p, lane, b, kvh, j, sb, L)) return;
+  // The item is the same in every lane; saying so keeps the buffer resources
+  // below in scalar registers (otherwise every load is wrapped in a loop over
+  // the distinct descriptor values of the wave).
+  b = __builtin_amdgcn_readfirstlane(b);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  j = __builtin_amdgcn_readfirstlane(j);
+  sb = __builtin_amdgcn_readfirstlane(sb);
+  L = __builtin_amdgcn_readfirstlane(L);
   const int lo = j * p.chunk;
   const int hi = min(lo + p.chunk, L);
 
@@ -318,20 +343,22 @@ void decode_gqa_d128_kernel(KParams p) {
     }
   };
 
-  // Ping-pong over two register blocks: while one block is processed, the
-  // next one is in flight.  Wave w takes blocks lo + 32*w + 128*i.
-  Block A, Bk;
+  // Rotation over NB register blocks: while one block is processed, the next
+  // NB - 1 are in flight.  Wave w takes blocks lo + 32*w + 128*i.  Loads past
+  // the split return zero without touching memory.
+  Block X[NB];
   int kb = lo + KB * w;
-  load_block(A, kb);
+#pragma unroll
+  for (int i = 0; i < NB - 1; ++i) load_block(X[i], kb + i * STEP);
   // The scheduling barriers keep each block's loads issued before the wait for
   // the block being processed.
-  for (; kb < hi; kb += 2 * STEP) {
-    load_block(Bk, kb + STEP);
-    __builtin_amdgcn_sched_barrier(0);
-    process_block(A, kb);
-    load_block(A, kb + 2 * STEP);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kb + STEP < hi) process_block(Bk, kb + STEP);
+  for (; kb < hi; kb += NB * STEP) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      load_block(X[(i + NB - 1) % NB], kb + (i + NB - 1) * STEP);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i == 0 || kb + i * STEP < hi) process_block(X[i], kb + i * STEP);
+    }
   }
 
   // Merge the four waves' partial states.
@@ -424,23 +451,49 @@ void decode_gqa_d128_kernel(KParams p) {
     const int h = kvh * p.G + orow % p.G;
     const int64_t nrows = (int64_t)p.B * p.Lq * p.Hq;
     const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
-    float M = kNegInf;
-    for (int jj = 0; jj < sb; ++jj) M = fmaxf(M, load_dev(p.ws_lse + jj * nrows + row));
+    // One pass over the splits in split order, MB at a time: the loads of a
+    // batch are independent (one memory round trip per batch, not two per
+    // split); the running max and weight sum are rescaled per batch.
+    constexpr int MB = 4;
+    float M = kNegInf;  // natural-log units
     f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
-    if (M != kNegInf) {
-      const float m2 = M * kLog2e;
-      for (int jj = 0; jj < sb; ++jj) {
-        const int64_t slot = jj * nrows + row;
-        const float wgt = fast_exp2(load_dev(p.ws_lse + slot) * kLog2e - m2);
+    for (int j0 = 0; j0 < sb; j0 += MB) {
+      float lse[MB];
+      f32x4_t x0[MB], x1[MB];
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        const int64_t slot = (int64_t)min(j0 + u, sb - 1) * nrows + row;
+        lse[u] = load_dev(p.ws_lse + slot);
         const float* src = p.ws_o + slot * D + oc;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          a0[e] += wgt * load_dev(src + e);
-          a1[e] += wgt * load_dev(src + 4 + e);
+          x0[u][e] = load_dev(src + e);
+          x1[u][e] = load_dev(src + 4 + e);
         }
-        wsum += wgt;
       }
+      float mb = M;
+#pragma unroll
+      for (int u = 0; u < MB; ++u)
+        if (j0 + u < sb) mb = fmaxf(mb, lse[u]);
+      if (mb == kNegInf) continue;
+      const float m2 = mb * kLog2e;
+      const float sc = (M == kNegInf) ? 0.f : fast_exp2(M * kLog2e - m2);
+      a0 *= sc;
+      a1 *= sc;
+      wsum *= sc;
+#pragma unroll
+      for (int u = 0; u < MB; ++u) {
+        if (j0 + u < sb) {
+          const float wgt = fast_exp2(lse[u] * kLog2e - m2);
+          a0 += wgt * x0[u];
+          a1 += wgt * x1[u];
+          wsum += wgt;
+        }
+      }
+      M = mb;
+    }
+    if (M != kNegInf) {
       const float inv = 1.f / wsum;
       a0 *= inv;
       a1 *= inv;
@@ -458,10 +511,7 @@ void decode_gqa_d128_kernel(KParams p) {
 hipError_t launch_decode_gqa_d128(const KParams& p, hipStream_t s) {
   const int64_t nwg = (p.n_items + 7) / 8 * 8;
   if (nwg == 0) return hipSuccess;
-  if (p.waves == 8)
-    hipLaunchKernelGGL(decode_gqa_d128_kernel<8>, dim3((unsigned)nwg), dim3(512), 0, s, p);
-  else
-    hipLaunchKernelGGL(decode_gqa_d128_kernel<4>, dim3((unsigned)nwg), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(decode_gqa_d128_kernel, dim3((unsigned)nwg), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -233,9 +233,9 @@ def test_plan_llama_decode_uses_gqa_kernel_and_fills_the_gpu(lib):
     _check_plan_invariants(p, plan, [4096] * 32)
     assert plan.n_items >= 256  # at least one workgroup per compute unit
     # 32 x 8 = 256 (request, KV head) units fill 256 CUs and the lengths are
-    # equal: one split per request, the key axis split across the 8 waves of
+    # equal: one split per request, the key axis split across the 4 waves of
     # each workgroup instead (no partials, no merge).
-    assert plan.s_max == 1 and plan.block == 512 and plan.tile_n == 256
+    assert plan.s_max == 1 and plan.block == 256 and plan.tile_n == 128
     # With more compute units than units the key axis is split across workgroups.
     st, plan2 = plan_status(lib, p, num_cus=1024)
     assert st == 0 and plan2.s_max > 1 and plan2.block == 256

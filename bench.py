@@ -5,7 +5,8 @@ Default run (N = 1):
   * value: split-K decode throughput in algorithmic HBM GB/s on the
     Llama-3-8B-shaped GQA decode (B=32, 32/8 heads, D=128, 4096 keys, bf16);
     one step = plan + one attn_decode call over the whole batch (for this
-    kernel family a single launch whose last split per (request, KV head)
+    kernel family a single launch: one split per (request, KV head) writes O
+    directly; with several splits the last split of each (request, KV head)
     merges the partials); the two-launch form (split kernel + combine kernel)
     is timed beside it as an ablation.
   * prefill: causal GQA prefill (B=4, L=4096, 32/8 heads, D=128, bf16) in
@@ -14,7 +15,10 @@ Default run (N = 1):
     launch stream), the split-off (s = 1) ablation, and the fp64 oracle timed
     on the host cores over a bounded sample of the same workload.
 Inputs are synthetic (seeded i.i.d. N(0,1), rounded to bf16) and resident in
-HBM before timing.  Several copies of the inputs are rotated so that a step
+HBM before timing.  The decode K/V cache is stored head-major, [B, Hkv, L, D]
+(each (request, KV head) one contiguous stream; the library takes any
+strides), and the token-major [B, L, Hkv, D] cache is timed beside it as an
+ablation (--kv-layout token makes it the measured one).  Several copies of the inputs are rotated so that a step
 never finds its K/V in the 256 MB Infinity Cache from the previous step.
 
 Algorithmic work: bytes = unique Q, K and V reads + O write (the split
@@ -56,6 +60,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--kv-layout", choices=("token", "head"), default="head",
+                    help="decode K/V cache storage: token-major [B, L, Hkv, D] or head-major "
+                         "[B, Hkv, L, D] (the kernels take either through strides)")
     ap.add_argument("--two-launch", action="store_true",
                     help="time decode as split kernel + combine kernel instead of one launch")
     ap.add_argument("--json-out", default=None)
@@ -69,15 +76,24 @@ def parse():
 
 # ----------------------------------------------------------------------- inputs
 
-def device_copies(prob, n_copies, dev):
+def kv_buffer(prob, d, dt, dev, layout):
+    """A zero K or V cache seen as [B, Lcap, Hkv, d]: token-major storage
+    [B, Lcap, Hkv, d], or head-major storage [B, Hkv, Lcap, d] (a permuted view;
+    the library takes the strides)."""
+    import torch
+    if layout == "head":
+        return torch.zeros((prob.batch, prob.hkv, prob.lcap, d), dtype=dt, device=dev).permute(0, 2, 1, 3)
+    return torch.zeros((prob.batch, prob.lcap, prob.hkv, d), dtype=dt, device=dev)
+
+
+def device_copies(prob, n_copies, dev, layout="token"):
     """n_copies independent device copies of one synthetic problem (zero padding)."""
     import numpy as np
     import torch
     dt = torch.bfloat16 if prob.dtype == "bf16" else torch.float32
     q = torch.from_numpy(prob.q).to(dev).to(dt)
-    k = torch.zeros((prob.batch, prob.lcap, prob.hkv, prob.dqk), dtype=dt, device=dev)
-    v = None if prob.v_aliases_k else torch.zeros((prob.batch, prob.lcap, prob.hkv, prob.dv),
-                                                   dtype=dt, device=dev)
+    k = kv_buffer(prob, prob.dqk, dt, dev, layout)
+    v = None if prob.v_aliases_k else kv_buffer(prob, prob.dv, dt, dev, layout)
     for b in range(prob.batch):
         n = int(prob.lens[b])
         if n:
@@ -215,14 +231,14 @@ def traffic_for(kernel_src, launches_key):
 
 # ----------------------------------------------------------------------- timing
 
-def time_decode(prob, steps, warmup, s_request, dev, fused):
+def time_decode(prob, steps, warmup, s_request, dev, fused, layout="token"):
     """Time `steps` decode steps.  fused: one attn_decode call per step (for the
     GQA family a single launch that merges its own splits); otherwise the split
     launch and the combine launch, timed separately."""
     import torch
     import reduction_attention_gqa_amd as ra
     qb, kvb, ob = decode_bytes(prob)
-    copies, lens = device_copies(prob, n_copies_for(qb + kvb + ob), dev)
+    copies, lens = device_copies(prob, n_copies_for(qb + kvb + ob), dev, layout)
     dt = copies[0][0].dtype
     o = torch.empty((prob.batch, prob.lq, prob.hq, prob.dv), dtype=dt, device=dev)
     lens_host = [int(x) for x in prob.lens]
@@ -393,8 +409,10 @@ def decode_record(prob, r, steps, warmup, extra_src):
         roofline={"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                   "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                   "traffic": traffic,
-                  "kernel": ("decode kernel, single launch with in-kernel merge" if r["fused"]
-                             else "decode split kernel"),
+                  "kernel": (("decode kernel, single launch, one split per (request, KV head)"
+                              if plan.s_max == 1 else
+                              "decode kernel, single launch with in-kernel merge")
+                             if r["fused"] else "decode split kernel"),
                   "algorithmic_bytes_per_launch": kern_bytes,
                   "launch_ms": split},
         combine=None if r["combine_ms"] is None else stats(r["combine_ms"]),
@@ -446,7 +464,7 @@ def main():
         # The GQA family runs as one fused launch; the others as split + combine.
         fused = prob.dtype == "bf16" and prob.dqk == 128 and prob.dv == 128 and not a.two_launch
         log(f"timing decode ({'single launch' if fused else 'split + combine'})")
-        r = time_decode(prob, a.steps, a.warmup, a.s, dev, fused)
+        r = time_decode(prob, a.steps, a.warmup, a.s, dev, fused, a.kv_layout)
         src = ("reduction_attention_gqa_amd/csrc/kernels/"
                + {0: "generic.hip", 1: "decode_gqa_d128.hip", 2: "decode_mla.hip"}[r["plan"].kernel])
         rec = decode_record(prob, r, a.steps, a.warmup, src)
@@ -456,7 +474,8 @@ def main():
         out["config"] = {"workload": name, "batch": prob.batch, "q_heads": prob.hq,
                          "kv_heads": prob.hkv, "head_dim_qk": prob.dqk, "head_dim_v": prob.dv,
                          "kv_len_total": int(prob.lens.sum()), "kv_len_max": int(prob.lens.max()),
-                         "q_len": prob.lq, "split_s": rec["plan"]["s_max"],
+                         "q_len": prob.lq, "kv_layout": a.kv_layout,
+                         "split_s": rec["plan"]["s_max"],
                          "chunk": rec["plan"]["chunk"],
                          "kernel": ra.KERNEL_NAMES[rec["plan"]["kernel"]]}
         out["roofline"] = rec["roofline"]
@@ -468,7 +487,7 @@ def main():
             n_abl = max(10, a.steps // 5)
             if fused:
                 log("timing the two-launch ablation (split kernel + combine kernel)")
-                r2 = time_decode(prob, n_abl, 3, 0, dev, False)
+                r2 = time_decode(prob, n_abl, 3, 0, dev, False, a.kv_layout)
                 rec2 = decode_record(prob, r2, n_abl, 3, src)
                 out["two_launch"] = {"value": rec2["value"], "unit": "GB/s",
                                      "ms_per_step": rec2["ms_per_step"],
@@ -476,8 +495,17 @@ def main():
                                      "combine_launch_ms": rec2["combine"]["mean_ms"],
                                      "speedup_of_single_launch":
                                          round(rec["value"] / rec2["value"], 3)}
+            if a.kv_layout == "head":
+                log("timing the token-major cache ablation")
+                r3 = time_decode(prob, n_abl, 3, 0, dev, fused, "token")
+                rec3 = decode_record(prob, r3, n_abl, 3, src)
+                out["token_major"] = {"value": rec3["value"], "unit": "GB/s",
+                                      "ms_per_step": rec3["ms_per_step"],
+                                      "launch_ms": rec3["roofline"]["launch_ms"]["mean_ms"],
+                                      "speedup_of_head_major":
+                                          round(rec["value"] / rec3["value"], 3)}
             log("timing split-off ablation (s = 1)")
-            r1 = time_decode(prob, n_abl, 3, 1, dev, fused)
+            r1 = time_decode(prob, n_abl, 3, 1, dev, fused, a.kv_layout)
             rec1 = decode_record(prob, r1, n_abl, 3, src)
             out["split_off"] = {"value": rec1["value"], "unit": "GB/s",
                                 "ms_per_step": rec1["ms_per_step"],

@@ -151,13 +151,15 @@ def _sample_rows(p, n, seed):
     return sorted(rows)
 
 
+@pytest.mark.parametrize("layout", ["head", "token"])
 @pytest.mark.parametrize("fused", [False, True])
 @pytest.mark.parametrize("name", ["llama3_8b_gqa_decode", "ragged_decode_qwen3_32b"])
-def test_full_size_decode_sampled_rows(name, fused):
+def test_full_size_decode_sampled_rows(name, fused, layout):
     # The full workload in the launch configuration the benchmark times
-    # (planner-chosen s, attn_decode); the oracle checks sampled outputs one by one.
+    # (planner-chosen s, attn_decode, head-major cache; token-major as well);
+    # the oracle checks sampled outputs one by one.
     p = workload(name)
-    d = DeviceProblem(p)
+    d = DeviceProblem(p, layout=layout)
     plan = d.decode(fused=fused)
     print(f"[plan] {name}: kernel={plan.kernel} s_max={plan.s_max} chunk={plan.chunk}", flush=True)
     out, lse_g = d.out(), d.lse_out()

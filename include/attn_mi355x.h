@@ -23,6 +23,33 @@
  *   sees no key gets O = 0 and LSE = -inf.
  * - MLA (one latent KV head whose first Dv columns are V): pass v = k with
  *   v_stride = k_stride and head_dim_v < head_dim_qk.
+ * - Variable-length and paged layouts (the paged and ragged attention
+ *   operators of the Cleave paper's dynamic-operator benchmark, §7.1 and
+ *   §7.4).  Three optional DEVICE index arrays change how rows are found;
+ *   each is NULL for the plain layout above:
+ *     kv_indptr  packed keys: request b owns rows kv_indptr[b] ..
+ *                kv_indptr[b+1] - 1 of K [T, Hkv, Dqk] and V [T, Hkv, Dv]; key
+ *                t is at (kv_indptr[b] + t) * k_stride[1] + head * k_stride[2]
+ *                (k_stride[0] unused) and L_b = kv_indptr[b+1] - kv_indptr[b].
+ *     page_table paged keys: K and V are pools of num_pages pages of
+ *                page_size rows; request b's key t lives on page
+ *                page_table[b * pages_per_req + t / page_size] at row
+ *                t % page_size: offset page * k_stride[0] +
+ *                (t % page_size) * k_stride[1] + head * k_stride[2].  Page ids
+ *                are clamped to [0, num_pages) before use, so a bad id reads
+ *                the wrong page but never outside the pool.  L_b comes from
+ *                kv_lens (or is Lcap), as in the plain layout.
+ *     q_indptr   packed (ragged) queries, attn_prefill only: request b owns
+ *                rows q_indptr[b] .. q_indptr[b+1] - 1 of Q [T, Hq, Dqk] and
+ *                O [T, Hq, Dv] (q_stride[0] and o_stride[0] unused), so it has
+ *                Lq_b = q_indptr[b+1] - q_indptr[b] query rows, with Lq an
+ *                upper bound on every Lq_b; lse_out is then [T, Hq].  Causal
+ *                masking uses Lq_b: row i sees key j iff j <= i + L_b - Lq_b.
+ *                O and LSE rows of the packed tensor that no request owns are
+ *                not written.
+ *   Lengths taken from an indptr are clamped to [0, Lq] / [0, Lcap] on the
+ *   device; an indptr must be non-decreasing.  kv_indptr excludes kv_lens and
+ *   page_table.
  * - Pointers named q, k, v, o, ws_*, lse_out and problem->kv_lens are DEVICE
  *   pointers.  Pointers to attn_problem / attn_plan and kv_lens_host are host
  *   pointers.  The caller owns every buffer; the library allocates no device
@@ -46,7 +73,7 @@
 extern "C" {
 #endif
 
-#define ATTN_MI355X_VERSION 2
+#define ATTN_MI355X_VERSION 3
 
 typedef enum attn_dtype {
   ATTN_F32 = 0,   /* IEEE binary32 */
@@ -82,6 +109,14 @@ typedef struct attn_problem {
   int64_t k_stride[3];
   int64_t v_stride[3];
   int64_t o_stride[3];
+  /* Variable-length and paged layouts (see above); NULL / 0 when unused. */
+  const int32_t* q_indptr;    /* DEVICE int32 [B + 1] or NULL */
+  const int32_t* kv_indptr;   /* DEVICE int32 [B + 1] or NULL */
+  const int32_t* page_table;  /* DEVICE int32 [B * pages_per_req] or NULL */
+  int32_t page_size;          /* rows per page >= 1 (0 without page_table) */
+  int32_t pages_per_req;      /* page_table row length >= ceil(Lcap / page_size) */
+  int32_t num_pages;          /* pages in the K and V pools >= 1 */
+  int32_t reserved1;          /* must be 0 */
 } attn_problem;
 
 /* Kernel families the decode planner can pick. */

@@ -38,6 +38,10 @@ class AttnProblem(ctypes.Structure):
         ("kv_lens", ctypes.c_void_p),
         ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("q_indptr", ctypes.c_void_p), ("kv_indptr", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p), ("page_size", ctypes.c_int32),
+        ("pages_per_req", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("reserved1", ctypes.c_int32),
     ]
 
 
@@ -117,35 +121,89 @@ def _dtype_code(t) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
+def _index_tensor(name, t):
+    import torch
+    if t.dtype != torch.int32 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous int32 tensor")
+    return _ptr(t)
+
+
 def make_problem(q, k, v, o, *, kv_lens=None, kv_len_max: Optional[int] = None,
-                 causal: bool = False, scale: float = 0.0) -> AttnProblem:
-    """Describe tensors q [B, Lq, Hq, Dqk], k [B, Lcap, Hkv, Dqk], v [B, Lcap, Hkv, Dv]
-    and o [B, Lq, Hq, Dv] (any strides with a contiguous last dim; v may be a
-    view of k).  ``kv_lens`` is a device int32 tensor [B] or None."""
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        if t.dim() != 4:
-            raise ValueError(f"{name} must be 4-D")
+                 causal: bool = False, scale: float = 0.0, q_indptr=None,
+                 q_len_max: Optional[int] = None, kv_indptr=None,
+                 page_table=None) -> AttnProblem:
+    """Describe the tensors of one attention call (each with a contiguous last dim).
+
+    Plain layout: q [B, Lq, Hq, Dqk], k [B, Lcap, Hkv, Dqk], v [B, Lcap, Hkv, Dv],
+    o [B, Lq, Hq, Dv], any strides; v may be a view of k.  ``kv_lens`` is a
+    device int32 tensor [B] or None.
+
+    Packed queries (``q_indptr`` int32 [B + 1], prefill only): q [T, Hq, Dqk] and
+    o [T, Hq, Dv]; ``q_len_max`` bounds every request's row count.
+    Packed keys (``kv_indptr`` int32 [B + 1]): k [T, Hkv, Dqk], v [T, Hkv, Dv];
+    ``kv_len_max`` bounds every request's key count.
+    Paged keys (``page_table`` int32 [B, pages_per_req]): k and v are page pools
+    [num_pages, page_size, Hkv, D] (any strides, e.g. a permuted head-major
+    pool); ``kv_len_max`` defaults to pages_per_req * page_size and key counts
+    come from ``kv_lens``.
+    """
+    if q_indptr is not None:
+        qdims, batch = 3, int(q_indptr.numel()) - 1
+    else:
+        qdims, batch = 4, int(q.shape[0])
+    kdims = 3 if kv_indptr is not None else 4
+    for name, t, nd in (("q", q, qdims), ("o", o, qdims), ("k", k, kdims), ("v", v, kdims)):
+        if t.dim() != nd:
+            raise ValueError(f"{name} must be {nd}-D for this layout")
         if t.shape[-1] > 1 and t.stride(-1) != 1:
             raise ValueError(f"{name}: the head dimension must be contiguous")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
+    if kv_indptr is not None and (kv_lens is not None or page_table is not None):
+        raise ValueError("kv_indptr excludes kv_lens and page_table")
     p = AttnProblem()
     p.dtype = _dtype_code(q)
     p.o_dtype = _dtype_code(o)
-    p.batch, p.q_len, p.q_heads, p.head_dim_qk = (int(x) for x in q.shape)
-    p.kv_heads = int(k.shape[2])
-    p.head_dim_v = int(v.shape[3])
-    p.kv_len_max = int(k.shape[1]) if kv_len_max is None else int(kv_len_max)
+    p.batch = batch
+    p.q_heads, p.head_dim_qk = int(q.shape[-2]), int(q.shape[-1])
+    p.kv_heads = int(k.shape[-2])
+    p.head_dim_v = int(v.shape[-1])
+    if q_indptr is not None:
+        if q_len_max is None:
+            raise ValueError("packed queries need q_len_max")
+        p.q_len = int(q_len_max)
+        p.q_indptr = _index_tensor("q_indptr", q_indptr)
+        p.q_stride[0], p.q_stride[1], p.q_stride[2] = 0, q.stride(0), q.stride(1)
+        p.o_stride[0], p.o_stride[1], p.o_stride[2] = 0, o.stride(0), o.stride(1)
+    else:
+        p.q_len = int(q.shape[1])
+        p.q_stride[0], p.q_stride[1], p.q_stride[2] = q.stride(0), q.stride(1), q.stride(2)
+        p.o_stride[0], p.o_stride[1], p.o_stride[2] = o.stride(0), o.stride(1), o.stride(2)
+    if kv_indptr is not None:
+        if kv_len_max is None:
+            raise ValueError("packed keys need kv_len_max")
+        p.kv_len_max = int(kv_len_max)
+        p.kv_indptr = _index_tensor("kv_indptr", kv_indptr)
+        p.k_stride[0], p.k_stride[1], p.k_stride[2] = 0, k.stride(0), k.stride(1)
+        p.v_stride[0], p.v_stride[1], p.v_stride[2] = 0, v.stride(0), v.stride(1)
+    else:
+        for dst, t in ((p.k_stride, k), (p.v_stride, v)):
+            dst[0], dst[1], dst[2] = t.stride(0), t.stride(1), t.stride(2)
+        if page_table is not None:
+            if page_table.dim() != 2 or int(page_table.shape[0]) != batch:
+                raise ValueError("page_table must be [B, pages_per_req]")
+            if k.shape[:2] != v.shape[:2]:
+                raise ValueError("k and v pools must have the same pages")
+            p.page_table = _index_tensor("page_table", page_table)
+            p.num_pages, p.page_size = int(k.shape[0]), int(k.shape[1])
+            p.pages_per_req = int(page_table.shape[1])
+            p.kv_len_max = (p.pages_per_req * p.page_size if kv_len_max is None
+                            else int(kv_len_max))
+        else:
+            p.kv_len_max = int(k.shape[1]) if kv_len_max is None else int(kv_len_max)
     p.causal = 1 if causal else 0
     p.scale = float(scale)
-    p.reserved0 = 0
-    p.kv_lens = _ptr(kv_lens) if kv_lens is not None else None
-    if kv_lens is not None:
-        import torch
-        if kv_lens.dtype != torch.int32 or not kv_lens.is_contiguous():
-            raise TypeError("kv_lens must be a contiguous int32 tensor")
-    for dst, t in ((p.q_stride, q), (p.k_stride, k), (p.v_stride, v), (p.o_stride, o)):
-        dst[0], dst[1], dst[2] = t.stride(0), t.stride(1), t.stride(2)
+    p.kv_lens = _index_tensor("kv_lens", kv_lens) if kv_lens is not None else None
     return p
 
 

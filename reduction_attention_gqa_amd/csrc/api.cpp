@@ -67,13 +67,43 @@ int check_problem(const attn_problem* p) {
       return fail(ATTN_ERR_ARG, "strides must be >= 0");
   if (p->head_dim_qk > 768 || p->head_dim_v > 512)
     return fail(ATTN_ERR_UNSUPPORTED, "head_dim_qk > 768 or head_dim_v > 512");
+  if (p->reserved1 != 0) return fail(ATTN_ERR_ARG, "reserved1 must be 0");
+  if (p->kv_indptr && (p->kv_lens || p->page_table))
+    return fail(ATTN_ERR_ARG, "kv_indptr excludes kv_lens and page_table");
+  if (p->page_table) {
+    if (p->page_size < 1) return fail(ATTN_ERR_ARG, "page_size < 1");
+    if (p->num_pages < 1) return fail(ATTN_ERR_ARG, "num_pages < 1");
+    if ((int64_t)p->pages_per_req * p->page_size < p->kv_len_max)
+      return fail(ATTN_ERR_ARG, "pages_per_req * page_size (%lld) < kv_len_max (%d)",
+                  (long long)p->pages_per_req * p->page_size, p->kv_len_max);
+  } else if (p->page_size != 0 || p->pages_per_req != 0 || p->num_pages != 0) {
+    return fail(ATTN_ERR_ARG, "page_size, pages_per_req and num_pages must be 0 without page_table");
+  }
   return ATTN_OK;
+}
+
+// Decode entry points take one query tensor of uniform Lq rows per request.
+int check_decode_layout(const attn_problem* p) {
+  if (p->q_indptr)
+    return fail(ATTN_ERR_UNSUPPORTED, "packed queries (q_indptr) are a prefill layout");
+  return ATTN_OK;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2_of(int x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return s;
 }
 
 uint64_t problem_key(const attn_problem* p) {
   // The output dtype is not part of the key: the split partials are fp32 either way.
+  // The layout kind (packed, paged and the page size) selects kernels and
+  // bounds the split size, so it is part of the key; the arrays are not.
   const int32_t f[] = {p->dtype, p->batch, p->q_heads, p->kv_heads, p->head_dim_qk,
-                       p->head_dim_v, p->q_len, p->kv_len_max, p->causal};
+                       p->head_dim_v, p->q_len, p->kv_len_max, p->causal,
+                       p->q_indptr != nullptr, p->kv_indptr != nullptr,
+                       p->page_table ? p->page_size : 0};
   uint64_t h = 1469598103934665603ull;
   for (int32_t x : f) {
     for (int s = 0; s < 32; s += 8) {
@@ -92,6 +122,13 @@ KParams base_params(const attn_problem* p) {
   KParams k;
   std::memset(&k, 0, sizeof(k));
   k.kv_lens = p->kv_lens;
+  k.q_indptr = p->q_indptr;
+  k.kv_indptr = p->kv_indptr;
+  k.page_table = p->page_table;
+  k.page_size = p->page_table ? p->page_size : 1;
+  k.ppr = p->pages_per_req;
+  k.num_pages = p->num_pages;
+  k.page_shift = is_pow2(k.page_size) ? log2_of(k.page_size) : -1;
   k.qs_b = p->q_stride[0]; k.qs_t = p->q_stride[1]; k.qs_h = p->q_stride[2];
   k.ks_b = p->k_stride[0]; k.ks_t = p->k_stride[1]; k.ks_h = p->k_stride[2];
   k.vs_b = p->v_stride[0]; k.vs_t = p->v_stride[1]; k.vs_h = p->v_stride[2];
@@ -110,13 +147,22 @@ KParams base_params(const attn_problem* p) {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
 // Shape-level kernel choice for decode (pointers are checked at launch).
+// Paged K/V runs on the GQA MFMA kernel when the page size is a power of two,
+// and on the generic kernel otherwise; the MLA kernel takes the plain layout only.
 int decode_family(const attn_problem* p) {
   const int rows = (p->q_heads / p->kv_heads) * p->q_len;
-  if (p->dtype == ATTN_BF16 && p->head_dim_qk == 128 && p->head_dim_v == 128 && rows <= kGqaMaxRows)
+  if (p->dtype == ATTN_BF16 && p->head_dim_qk == 128 && p->head_dim_v == 128 &&
+      rows <= kGqaMaxRows && (!p->page_table || is_pow2(p->page_size)))
     return ATTN_KERNEL_GQA_D128;
-  if (p->dtype == ATTN_BF16 && p->head_dim_qk == 576 && p->head_dim_v == 512 && rows <= kMlaRows)
+  if (p->dtype == ATTN_BF16 && p->head_dim_qk == 576 && p->head_dim_v == 512 && rows <= kMlaRows &&
+      !p->page_table && !p->kv_indptr)
     return ATTN_KERNEL_MLA;
   return ATTN_KERNEL_GENERIC;
+}
+
+// Longest split the paged GQA kernel accepts: its page ids fit in LDS.
+int64_t gqa_paged_max_chunk(const attn_problem* p) {
+  return (int64_t)(kGqaPageIds - 1) * p->page_size / kGqaTileN * kGqaTileN;
 }
 
 // Workgroups per compute unit the planner aims for, by kernel family.
@@ -142,6 +188,8 @@ bool gqa_d128_fits(const attn_problem* p, const void* q, const void* k, const vo
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return false;
   for (int a = 0; a < 3; ++a)
     if ((p->q_stride[a] | p->k_stride[a] | p->v_stride[a]) & 7) return false;
+  // Paged rows are addressed with 64-bit pointers, not buffer offsets.
+  if (p->page_table) return true;
   // Buffer offsets reach up to 64 rows past the last key (clamped block starts).
   const int64_t kbytes = ((int64_t)p->kv_len_max + 64) * p->k_stride[1] * 2 + 256;
   const int64_t vbytes = ((int64_t)p->kv_len_max + 64) * p->v_stride[1] * 2 + 256;
@@ -151,7 +199,7 @@ bool gqa_d128_fits(const attn_problem* p, const void* q, const void* k, const vo
 // Can the MLA kernel run?  V must be the first Dv columns of K (same pointer
 // and strides), with 16-byte rows and 32-bit buffer offsets.
 bool mla_fits(const attn_problem* p, const void* q, const void* k, const void* v) {
-  if (v != k) return false;
+  if (v != k || p->page_table || p->kv_indptr) return false;
   for (int a = 0; a < 3; ++a)
     if (p->v_stride[a] != p->k_stride[a]) return false;
   return gqa_d128_fits(p, q, k, v);
@@ -161,6 +209,7 @@ bool mla_fits(const attn_problem* p, const void* q, const void* k, const void* v
 bool prefill_d128_fits(const attn_problem* p, const void* q, const void* k, const void* v,
                        const void* o) {
   if (p->dtype != ATTN_BF16 || p->head_dim_qk != 128 || p->head_dim_v != 128) return false;
+  if (p->q_indptr || p->kv_indptr || p->page_table) return false;
   if (!gqa_d128_fits(p, q, k, v)) return false;
   const int oal = p->o_dtype == ATTN_BF16 ? 8 : 16;
   if ((reinterpret_cast<uintptr_t>(o) & (oal - 1)) != 0) return false;
@@ -168,6 +217,15 @@ bool prefill_d128_fits(const attn_problem* p, const void* q, const void* k, cons
     if (p->o_stride[a] & 3) return false;
   const int64_t rows = (int64_t)(p->q_heads / p->kv_heads) * p->q_len;
   return rows < (1ll << 30);
+}
+
+// The GQA kernel for a plan: pointers and strides fit, and a paged split's
+// page ids fit in the kernel's LDS table.
+bool gqa_d128_usable(const attn_problem* p, const attn_plan* plan, const void* q, const void* k,
+                     const void* v) {
+  if (p->page_table && (!is_pow2(p->page_size) || plan->chunk > gqa_paged_max_chunk(p)))
+    return false;
+  return gqa_d128_fits(p, q, k, v);
 }
 
 int check_ptrs(const void* a, const char* na, const void* b, const char* nb, const void* c,
@@ -211,6 +269,7 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
   if (!out) return fail(ATTN_ERR_ARG, "plan output is NULL");
   std::memset(out, 0, sizeof(*out));
   if (int st = check_problem(problem)) return st;
+  if (int st = check_decode_layout(problem)) return st;
   const attn_problem* p = problem;
   int cus = num_cus;
   if (cus <= 0 && device_cu_count(&cus) != 0)
@@ -262,6 +321,9 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
       chunk_tiles = std::min<int64_t>(chunk_tiles, max_tiles);
       chunk = chunk_tiles * tile_n;
     }
+    // The paged GQA kernel stages one split's page ids in LDS.
+    if (family == ATTN_KERNEL_GQA_D128 && p->page_table)
+      chunk = std::min<int64_t>(chunk, gqa_paged_max_chunk(p));
     s_max = ceil_div(lmax, chunk);
   }
   if (s_max > 65535) return fail(ATTN_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)s_max);
@@ -312,6 +374,7 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan, const 
                       size_t ws_lse_bytes, void* stream) {
   g_err[0] = 0;
   if (int st = check_problem(problem)) return st;
+  if (int st = check_decode_layout(problem)) return st;
   const attn_problem* p = problem;
   if (!plan) return fail(ATTN_ERR_ARG, "plan is NULL");
   if (plan->problem_key != problem_key(p))
@@ -334,7 +397,7 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan, const 
 
   const dim3 unit_grid(plan->s_max, p->kv_heads, p->batch);
   kp.n_items = plan->n_items;
-  if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_fits(p, q, k, v))
+  if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_usable(p, plan, q, k, v))
     return hip_status(launch_decode_gqa_d128(kp, s), "decode_gqa_d128 launch");
   if (plan->kernel == ATTN_KERNEL_MLA && mla_fits(p, q, k, v))
     return hip_status(launch_decode_mla(kp, unit_grid, s), "decode_mla launch");
@@ -348,6 +411,7 @@ int attn_decode(const attn_problem* problem, const attn_plan* plan, const void* 
                 int32_t* ws_cnt, size_t ws_cnt_bytes, void* o, float* lse_out, void* stream) {
   g_err[0] = 0;
   if (int st = check_problem(problem)) return st;
+  if (int st = check_decode_layout(problem)) return st;
   const attn_problem* p = problem;
   if (!plan) return fail(ATTN_ERR_ARG, "plan is NULL");
   if (plan->problem_key != problem_key(p))
@@ -363,7 +427,7 @@ int attn_decode(const attn_problem* problem, const attn_plan* plan, const void* 
                 (unsigned long long)plan->ws_o_bytes, (unsigned long long)plan->ws_lse_bytes,
                 (unsigned long long)plan->ws_cnt_bytes);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_fits(p, q, k, v)) {
+  if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_usable(p, plan, q, k, v)) {
     KParams kp = base_params(p);
     kp.q = q; kp.k = k; kp.v = v; kp.o = o;
     kp.ws_o = ws_o; kp.ws_lse = ws_lse; kp.lse_out = lse_out;
@@ -385,6 +449,7 @@ int attn_combine(const attn_problem* problem, const attn_plan* plan, const float
                  const float* ws_lse, void* o, float* lse_out, void* stream) {
   g_err[0] = 0;
   if (int st = check_problem(problem)) return st;
+  if (int st = check_decode_layout(problem)) return st;
   const attn_problem* p = problem;
   if (!plan) return fail(ATTN_ERR_ARG, "plan is NULL");
   if (plan->problem_key != problem_key(p))

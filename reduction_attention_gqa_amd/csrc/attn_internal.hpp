@@ -19,6 +19,14 @@ struct KParams {
   float* lse_out;       // optional [B, Lq, Hq]
   int32_t* counters;    // split arrivals per (request, KV head), zero between calls (mode 2)
   const int32_t* kv_lens;  // device, may be null
+  // Variable-length and paged layouts (device, each may be null).
+  const int32_t* q_indptr;    // [B + 1] packed query rows (prefill)
+  const int32_t* kv_indptr;   // [B + 1] packed keys
+  const int32_t* page_table;  // [B, ppr] page ids; ks_b / vs_b are then page strides
+  int32_t page_size;          // rows per page
+  int32_t ppr;                // page-table row length
+  int32_t num_pages;          // page ids are clamped to [0, num_pages)
+  int32_t page_shift;         // log2(page_size) when it is a power of two, else -1
   int64_t n_items;      // (request, KV head, split) work items of the 1-D decode grid
   int64_t qs_b, qs_t, qs_h;
   int64_t ks_b, ks_t, ks_h;
@@ -56,5 +64,6 @@ constexpr int kPrefillStages = 4;     // prefill K/V ring depth (tiles)
 constexpr int kMlaTileN = 32;          // keys per MLA tile
 constexpr int kMlaBlock = 512;         // 8 waves of 16 query rows
 constexpr int kMlaRows = 128;          // query rows per MLA workgroup
+constexpr int kGqaPageIds = 8448;      // page ids one paged GQA work item stages in LDS
 
 }  // namespace attn

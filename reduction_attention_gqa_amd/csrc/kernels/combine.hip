@@ -8,6 +8,7 @@
 // One wave per row; lanes own 4 consecutive output columns (16-byte loads).
 #include "../attn_internal.hpp"
 #include "common.hpp"
+#include "layout.hpp"
 
 namespace attn {
 namespace {
@@ -22,7 +23,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void combine_kernel(KParams p) 
   const int h = (int)(row % p.Hq);
   const int i = (int)((row / p.Hq) % p.Lq);
   const int b = (int)(row / ((int64_t)p.Hq * p.Lq));
-  const int L = kv_len_of(p.kv_lens, b, p.Lcap);
+  const int L = kv_len_b(p, b);
   int sb = L == 0 ? 0 : (L + p.chunk - 1) / p.chunk;
   sb = min(sb, p.s_max);
 

@@ -35,6 +35,7 @@
 //      O directly.
 #include "../attn_internal.hpp"
 #include "common.hpp"
+#include "layout.hpp"
 
 namespace attn {
 namespace {
@@ -82,7 +83,7 @@ __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, in
     kvh = blockIdx.x - b * p.Hkv;
     j = 0;
     sb = 1;
-    L = kv_len_of(p.kv_lens, b, p.Lcap);
+    L = kv_len_b(p, b);
     return true;
   }
   const int64_t N = p.n_items;
@@ -95,7 +96,7 @@ __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, in
   // still owns one item, which writes O = 0 and LSE = -inf), and at most the
   // plan's s_max (the workspace has s_max slots; keys past s_max * chunk are
   // outside the plan).
-  if (p.kv_lens == nullptr) {
+  if (p.kv_lens == nullptr && p.kv_indptr == nullptr) {
     sb = max(1, min((p.Lcap + p.chunk - 1) / p.chunk, p.s_max));
     const int64_t per = (int64_t)p.Hkv * sb;
     if (per == 0 || item >= per * p.B) return false;
@@ -112,7 +113,7 @@ __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, in
     const int bb = c + lane;
     int n = 0;
     if (bb < p.B)
-      n = p.Hkv * max(1, min((kv_len_of(p.kv_lens, bb, p.Lcap) + p.chunk - 1) / p.chunk, p.s_max));
+      n = p.Hkv * max(1, min((kv_len_b(p, bb) + p.chunk - 1) / p.chunk, p.s_max));
     const int incl = wave_incl_scan(n, lane);
     const int total = __shfl(incl, 63, 64);
     if (item < base + total) {
@@ -125,7 +126,7 @@ __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, in
       const int local = rel - excl;
       kvh = local / sb;
       j = local - kvh * sb;
-      L = kv_len_of(p.kv_lens, b, p.Lcap);
+      L = kv_len_b(p, b);
       return true;
     }
     base += total;
@@ -186,14 +187,21 @@ __device__ __forceinline__ void store_o8(const KParams& p, int64_t off, const f3
 // Four waves per workgroup; a workgroup round covers KB * NW keys.  NB
 // register blocks per wave are in flight (four measured slower than two, also
 // with one workgroup per CU).
+//
+// PAGED: K and V rows are found through the page table (page size a power of
+// two).  The item's page ids are staged in LDS once; each lane then forms the
+// 64-bit address of every row it loads, so pages of any size, down to one
+// row, are read with the same 16-byte-per-lane loads as the strided layout.
 constexpr int NW = 4;
 constexpr int NB = 2;
+template <bool PAGED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_gqa_d128_kernel(KParams p) {
   constexpr int STEP = KB * NW;
   __shared__ __attribute__((aligned(16))) char lds_raw[NW * VTILE];  // 36 KiB
   __shared__ float m_w[NW][16];
   __shared__ float l_w[NW][16];
+  __shared__ int page_ids[PAGED ? kGqaPageIds : 1];
 
   const int lane = threadIdx.x & 63;
   // Wave index, made visibly wave-uniform so the key loop below is a scalar loop.
@@ -233,12 +241,40 @@ void decode_gqa_d128_kernel(KParams p) {
   // The buffer ranges end at this split's last key: loads past it return zero
   // without touching memory, so every load below is unconditional (which lets
   // the compiler wait only for the block about to be used).
-  const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
-  const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)kvh * p.ks_h;
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)kvh * p.vs_h;
+  if constexpr (!PAGED) {
+    kp += kv_base_off(p, b, p.ks_b, p.ks_t);
+    vp += kv_base_off(p, b, p.vs_b, p.vs_t);
+  }
   const uint32_t kst = (uint32_t)(p.ks_t * 2);  // bytes between consecutive keys
   const uint32_t vst = (uint32_t)(p.vs_t * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)hi * kst);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)hi * vst);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, PAGED ? 0u : (uint32_t)hi * kst);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, PAGED ? 0u : (uint32_t)hi * vst);
+
+  // Paged: the ids of the pages holding keys [lo, hi), clamped into the pool.
+  const int psh = PAGED ? p.page_shift : 0;
+  const int pmask = (1 << psh) - 1;
+  const int pg0 = lo >> psh;
+  if constexpr (PAGED) {
+    const int n_ids = hi > lo ? min(((hi - 1) >> psh) - pg0 + 1, kGqaPageIds) : 0;
+    const int32_t* row = p.page_table + (int64_t)b * p.ppr + pg0;
+    for (int e = threadIdx.x; e < n_ids; e += NW * 64) {
+      const int pg = row[e];
+      page_ids[e] = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+    }
+    __syncthreads();
+  }
+  const int64_t kpage = p.ks_b * 2;  // bytes between pages (paged layout)
+  const int64_t vpage = p.vs_b * 2;
+  // Address of key `key` in a pool; keys past the split read the split's last
+  // key instead (its scores are masked and its probabilities are zero).
+  auto paged_row = [&](const uint16_t* pool, int64_t page_bytes, uint32_t st, int key) {
+    const int kc = min(key, hi - 1);
+    const int pg = page_ids[(kc >> psh) - pg0];
+    return reinterpret_cast<const char*>(pool) + (int64_t)pg * page_bytes +
+           (int64_t)(kc & pmask) * st;
+  };
 
   // Per-lane load offsets inside a block (bytes), independent of the block start.
   //   K: sub-block sb, d-block db -> key 16*sb + r, d = 32*db + 8*h4
@@ -259,6 +295,20 @@ void decode_gqa_d128_kernel(KParams p) {
   const int qlim = qi + L - p.Lq;  // causal: keys <= qlim are visible
 
   auto load_block = [&](Block& x, int kb0) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const char* kr = paged_row(kp, kpage, kst, kb0 + 16 * sb + r) + 16 * h4;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+          x.k[sb * 4 + db] = *reinterpret_cast<const i32x4_t*>(kr + 64 * db);
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        x.v[c] = *reinterpret_cast<const i32x4_t*>(paged_row(vp, vpage, vst, kb0 + 4 * c + h4) +
+                                                    16 * r);
+      return;
+    }
     const uint32_t kbc = (uint32_t)min(kb0, hi);
     const uint32_t kbase = kbc * kst;
     const uint32_t vbase = kbc * vst;
@@ -346,18 +396,21 @@ void decode_gqa_d128_kernel(KParams p) {
   // Rotation over NB register blocks: while one block is processed, the next
   // NB - 1 are in flight.  Wave w takes blocks lo + 32*w + 128*i.  Loads past
   // the split return zero without touching memory.
+  // A paged item with no keys loads nothing (there is no row to clamp to).
   Block X[NB];
   int kb = lo + KB * w;
+  if (!PAGED || hi > lo) {
 #pragma unroll
-  for (int i = 0; i < NB - 1; ++i) load_block(X[i], kb + i * STEP);
-  // The scheduling barriers keep each block's loads issued before the wait for
-  // the block being processed.
-  for (; kb < hi; kb += NB * STEP) {
+    for (int i = 0; i < NB - 1; ++i) load_block(X[i], kb + i * STEP);
+    // The scheduling barriers keep each block's loads issued before the wait for
+    // the block being processed.
+    for (; kb < hi; kb += NB * STEP) {
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      load_block(X[(i + NB - 1) % NB], kb + (i + NB - 1) * STEP);
-      __builtin_amdgcn_sched_barrier(0);
-      if (i == 0 || kb + i * STEP < hi) process_block(X[i], kb + i * STEP);
+      for (int i = 0; i < NB; ++i) {
+        load_block(X[(i + NB - 1) % NB], kb + (i + NB - 1) * STEP);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i == 0 || kb + i * STEP < hi) process_block(X[i], kb + i * STEP);
+      }
     }
   }
 
@@ -511,7 +564,10 @@ void decode_gqa_d128_kernel(KParams p) {
 hipError_t launch_decode_gqa_d128(const KParams& p, hipStream_t s) {
   const int64_t nwg = (p.n_items + 7) / 8 * 8;
   if (nwg == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_gqa_d128_kernel, dim3((unsigned)nwg), dim3(NW * 64), 0, s, p);
+  if (p.page_table)
+    hipLaunchKernelGGL(decode_gqa_d128_kernel<true>, dim3((unsigned)nwg), dim3(NW * 64), 0, s, p);
+  else
+    hipLaunchKernelGGL(decode_gqa_d128_kernel<false>, dim3((unsigned)nwg), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

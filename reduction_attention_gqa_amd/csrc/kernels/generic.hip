@@ -11,6 +11,7 @@
 // tile: Cleave §5.1, Listing 1 walk-through; the division comes last: §2.2).
 #include "../attn_internal.hpp"
 #include "common.hpp"
+#include "layout.hpp"
 
 namespace attn {
 namespace {
@@ -43,7 +44,8 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
   const int rt = blockIdx.y;
   const int b = blockIdx.z / p.Hkv;
   const int kvh = blockIdx.z % p.Hkv;
-  const int L = kv_len_of(p.kv_lens, b, p.Lcap);
+  const int L = kv_len_b(p, b);
+  const int Lqb = q_len_b(p, b);  // query rows of this request (packed queries: ragged)
 
   int lo = 0, hi = L;
   if (p.split_mode) {
@@ -52,13 +54,14 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
     hi = min(lo + p.chunk, L);
   }
   const int r0 = rt * RT;
-  const int nrows = min(RT, p.rows - r0);
+  const int nrows = min(RT, p.G * Lqb - r0);
+  if (nrows <= 0) return;  // row tile past this request's queries
 
   // Causal: rows of this tile see keys j <= i + L - Lq; the tile needs keys
   // up to the largest such bound.
   if (p.causal) {
     const int i_last = (r0 + nrows - 1) / p.G;
-    hi = min(hi, i_last + L - p.Lq + 1);
+    hi = min(hi, i_last + L - Lqb + 1);
   }
 
   // Q tile (hoisted out of the key loop: Cleave §6.1, loop-invariant input).
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
     float val = 0.f;
     if (r < nrows) {
       const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
-      val = ld_elem<BF16>(p.q, (int64_t)b * p.qs_b + (int64_t)i * p.qs_t + (int64_t)h * p.qs_h + d);
+      val = ld_elem<BF16>(p.q, q_row_off(p, b, i) + (int64_t)h * p.qs_h + d);
     }
     q_s[e] = val;
   }
@@ -81,8 +84,8 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
   for (int c = 0; c < MAXC; ++c) acc[c] = 0.f;
   const int npairs = RT * p.Dv;
 
-  const int64_t kbase = (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
-  const int64_t vbase = (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
+  const int64_t khead = (int64_t)kvh * p.ks_h;
+  const int64_t vhead = (int64_t)kvh * p.vs_h;
   __syncthreads();
 
   for (int k0 = lo; k0 < hi; k0 += TN) {
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
       const int rb = (t / TN) * 4;
       float dot[4] = {0.f, 0.f, 0.f, 0.f};
       if (jj < nk) {
-        const int64_t krow = kbase + (int64_t)(k0 + jj) * p.ks_t;
+        const int64_t krow = kv_row_off(p, b, k0 + jj, p.ks_b, p.ks_t) + khead;
         for (int d = 0; d < p.Dqk; ++d) {
           const float kv = ld_elem<BF16>(p.k, krow + d);
 #pragma unroll
@@ -107,7 +110,7 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
         bool vis = (jj < nk) && (r < nrows);
         if (vis && p.causal) {
           const int i = (r0 + r) / p.G;
-          vis = key <= i + L - p.Lq;
+          vis = key <= i + L - Lqb;
         }
         s_s[r * TN + jj] = vis ? dot[u] * p.scale_log2 : kNegInf;
       }
@@ -158,7 +161,8 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
         const int r = e / p.Dv, d = e % p.Dv;
         float a = acc[c] * a_s[r];
         for (int jj = 0; jj < nk; ++jj)
-          a = fmaf(s_s[r * TN + jj], ld_elem<BF16>(p.v, vbase + (int64_t)(k0 + jj) * p.vs_t + d), a);
+          a = fmaf(s_s[r * TN + jj],
+                   ld_elem<BF16>(p.v, kv_row_off(p, b, k0 + jj, p.vs_b, p.vs_t) + vhead + d), a);
         acc[c] = a;
       }
     }
@@ -176,18 +180,18 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
         const float l = l_s[r];
         const float o = l > 0.f ? acc[c] / l : 0.f;
         const float lse = l > 0.f ? (m_s[r] + fast_log2(l)) * kLn2 : kNegInf;
-        const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
         if (p.split_mode) {
+          const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
           const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + row;
           p.ws_o[slot * p.Dv + d] = o;
           if (d == 0) p.ws_lse[slot] = lse;
         } else {
-          const int64_t oi = (int64_t)b * p.os_b + (int64_t)i * p.os_t + (int64_t)h * p.os_h + d;
+          const int64_t oi = o_row_off(p, b, i) + (int64_t)h * p.os_h + d;
           if (p.o_bf16)
             reinterpret_cast<uint16_t*>(p.o)[oi] = (uint16_t)f32_to_bf16_bits(o);
           else
             reinterpret_cast<float*>(p.o)[oi] = o;
-          if (d == 0 && p.lse_out) p.lse_out[row] = lse;
+          if (d == 0 && p.lse_out) p.lse_out[lse_row(p, b, i) * p.Hq + h] = lse;
         }
       }
     }

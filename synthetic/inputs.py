@@ -33,6 +33,11 @@ Recipe (stated once, used by tests, smoke and bench):
 * Padding rows past a request's length are filled with ``pad`` (NaN for
   parity runs, so any read past the valid rows poisons the output; zero for
   timing runs).
+* Paged K/V caches (``page_layout``): request b's rows fill ceil(L_b / page
+  size) pages in order; the pages of all requests, plus a few spare pages,
+  are numbered by one ``default_rng(seed).permutation`` of the pool, so
+  neighbouring pages of a request sit at unrelated places in the pool.
+  Page-table entries a request does not use hold -7 (never read).
 """
 from __future__ import annotations
 
@@ -43,7 +48,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Problem", "WORKLOADS", "workload", "make_problem", "to_bf16_exact",
-           "padded", "log_uniform_lengths"]
+           "padded", "log_uniform_lengths", "page_layout"]
 
 
 @dataclasses.dataclass
@@ -174,3 +179,24 @@ def padded(rows: list, lcap: int, pad: float = float("nan")) -> np.ndarray:
     for i, r in enumerate(rows):
         out[i, : r.shape[0]] = r
     return out
+
+
+def page_layout(lens, page_size: int, seed: int, lcap: Optional[int] = None,
+                spare_pages: int = 3):
+    """A shuffled page table for per-request key counts ``lens``.
+
+    Returns (table int32 [B, pages_per_req], num_pages).  pages_per_req covers
+    ``lcap`` (default: the longest request).
+    """
+    rng = np.random.default_rng(seed)
+    need = [-(-int(n) // page_size) for n in lens]
+    cap = max(lens) if lcap is None and len(lens) else (lcap or 0)
+    ppr = max([1, -(-int(cap) // page_size)] + need)
+    total = sum(need) + spare_pages
+    perm = rng.permutation(total).astype(np.int32)
+    table = np.full((len(lens), ppr), -7, dtype=np.int32)
+    pos = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[pos:pos + n]
+        pos += n
+    return table, total

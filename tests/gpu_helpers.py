@@ -96,6 +96,120 @@ class DeviceProblem:
         return self.lse.cpu().numpy().astype(np.float64)
 
 
+def _to_dev(a, dt):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dt)
+
+
+class PagedDeviceProblem(DeviceProblem):
+    """A synthetic Problem whose K/V live in a shuffled page pool.
+
+    layout "token": pools [num_pages, ps, Hkv, D]; "head": [num_pages, Hkv, ps, D]
+    exposed as a [num_pages, ps, Hkv, D] view.  Pool rows no request owns hold
+    ``pad``.  Q, O and LSE are as in DeviceProblem.
+    """
+
+    def __init__(self, prob, page_size, layout="token", seed=0, pad=float("nan"),
+                 o_dtype=None):
+        from synthetic.inputs import page_layout
+        self.prob = prob
+        dt = torch_dtype(prob.dtype)
+        b, lq, hq, dqk = prob.q.shape
+        self.lcap = prob.lcap
+        self.page_size = page_size
+        table, self.num_pages = page_layout(prob.lens, page_size, seed, lcap=prob.lcap)
+        self.table_host = table
+        self.table = torch.from_numpy(table).to(DEV)
+        self.q = _to_dev(prob.q, dt)
+        self.k = self._pool(prob.k, prob.hkv, dqk, dt, layout, pad)
+        if prob.v_aliases_k:
+            self.v = self.k[..., : prob.dv]
+        else:
+            self.v = self._pool(prob.v, prob.hkv, prob.dv, dt, layout, pad)
+        self.lens = torch.tensor(prob.lens, dtype=torch.int32, device=DEV)
+        od = dt if o_dtype is None else torch_dtype(o_dtype)
+        self.o_dtype = od
+        self.o = torch.full((b, lq, hq, prob.dv), float("nan"), dtype=od, device=DEV)
+        self.lse = torch.full((b, lq, hq), float("nan"), dtype=torch.float32, device=DEV)
+
+    def _pool(self, rows, hkv, d, dt, layout, pad):
+        ps = self.page_size
+        host = np.full((self.num_pages, ps, hkv, d), pad, dtype=np.float32)
+        for b, r in enumerate(rows):
+            n = r.shape[0]
+            npg = -(-n // ps)
+            if npg == 0:
+                continue
+            blk = np.full((npg * ps, hkv, d), pad, dtype=np.float32)
+            blk[:n] = r
+            host[self.table_host[b, :npg]] = blk.reshape(npg, ps, hkv, d)
+        if layout == "token":
+            return _to_dev(host, dt)
+        if layout == "head":
+            return _to_dev(host.transpose(0, 2, 1, 3), dt).permute(0, 2, 1, 3)
+        raise ValueError(layout)
+
+    def problem(self):
+        p = self.prob
+        return ra.make_problem(self.q, self.k, self.v, self.o, kv_lens=self.lens,
+                               kv_len_max=self.lcap, causal=p.causal, scale=p.scale,
+                               page_table=self.table)
+
+
+class PackedDeviceProblem(DeviceProblem):
+    """A synthetic Problem with packed keys (kv_indptr) and, when ``q_lens`` is
+    given, packed ragged queries (q_indptr): request b keeps its first
+    q_lens[b] query rows.  ``spare`` extra rows after the last request in the
+    packed K/V, O and LSE tensors hold ``pad`` / NaN."""
+
+    def __init__(self, prob, q_lens=None, pad=float("nan"), spare=5, o_dtype=None):
+        self.prob = prob
+        dt = torch_dtype(prob.dtype)
+        b, lq, hq, dqk = prob.q.shape
+        self.lcap = prob.lcap
+        lens = [int(n) for n in prob.lens]
+        self.kv_indptr = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32,
+                                      device=DEV)
+        tk = sum(lens)
+        kh = np.full((tk + spare, prob.hkv, dqk), pad, dtype=np.float32)
+        if tk:
+            kh[:tk] = np.concatenate(prob.k)
+        self.k = _to_dev(kh, dt)
+        if prob.v_aliases_k:
+            self.v = self.k[..., : prob.dv]
+        else:
+            vh = np.full((tk + spare, prob.hkv, prob.dv), pad, dtype=np.float32)
+            if tk:
+                vh[:tk] = np.concatenate(prob.v)
+            self.v = _to_dev(vh, dt)
+        od = dt if o_dtype is None else torch_dtype(o_dtype)
+        self.o_dtype = od
+        self.q_lens = q_lens
+        if q_lens is None:
+            self.q_indptr = None
+            self.q = _to_dev(prob.q, dt)
+            self.o = torch.full((b, lq, hq, prob.dv), float("nan"), dtype=od, device=DEV)
+            self.lse = torch.full((b, lq, hq), float("nan"), dtype=torch.float32, device=DEV)
+        else:
+            assert len(q_lens) == b and max(q_lens) <= lq
+            self.q_indptr = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]),
+                                         dtype=torch.int32, device=DEV)
+            tq = int(sum(q_lens))
+            qh = np.full((tq + spare, hq, dqk), pad, dtype=np.float32)
+            rows = [prob.q[i, :n] for i, n in enumerate(q_lens)]
+            if tq:
+                qh[:tq] = np.concatenate(rows)
+            self.q = _to_dev(qh, dt)
+            self.tq = tq
+            self.o = torch.full((tq + spare, hq, prob.dv), float("nan"), dtype=od, device=DEV)
+            self.lse = torch.full((tq + spare, hq), float("nan"), dtype=torch.float32, device=DEV)
+
+    def problem(self):
+        p = self.prob
+        return ra.make_problem(self.q, self.k, self.v, self.o, kv_len_max=self.lcap,
+                               causal=p.causal, scale=p.scale, kv_indptr=self.kv_indptr,
+                               q_indptr=self.q_indptr, q_len_max=p.lq)
+
+
 def v_rows(prob):
     return [prob.v_rows(b) for b in range(prob.batch)]
 

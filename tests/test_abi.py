@@ -57,12 +57,27 @@ def test_status_strings(lib):
     assert lib.attn_status_str(99) == b"unknown status"
 
 
-def test_struct_layout_matches_c():
-    # attn_problem: 12 int32/float fields, a pointer, 12 int64 strides.
-    assert ctypes.sizeof(_lib.AttnProblem) == 12 * 4 + 8 + 12 * 8
-    assert _lib.AttnProblem.kv_lens.offset == 48
-    assert ctypes.sizeof(_lib.AttnPlan) == 6 * 4 + 3 * 4 + 4 + 5 * 8
-    assert _lib.AttnPlan.problem_key.offset == 40 + 4 * 8
+def _c_layout(tmp_path, struct, fields):
+    """sizeof and offsetof of a header struct, from a C program compiled against the header."""
+    lines = [f'printf("size %zu\\n", sizeof({struct}));']
+    lines += [f'printf("{f} %zu\\n", offsetof({struct}, {f}));' for f in fields]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"attn_mi355x.h\"\n"
+                   "int main(void) {\n" + "\n".join(lines) + "\nreturn 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout
+    return {k: int(v) for k, v in (line.split() for line in out.splitlines())}
+
+
+@pytest.mark.parametrize("py,c", [(_lib.AttnProblem, "attn_problem"), (_lib.AttnPlan, "attn_plan")])
+def test_struct_layout_matches_c(tmp_path, py, c):
+    names = [f[0] for f in py._fields_]
+    got = _c_layout(tmp_path, c, names)
+    assert got["size"] == ctypes.sizeof(py)
+    for n in names:
+        assert got[n] == getattr(py, n).offset, n
 
 
 def problem(**kw):
@@ -277,3 +292,98 @@ def test_plan_generic_for_other_shapes(lib):
     st, plan = plan_status(lib, p)
     assert st == 0 and ra.KERNEL_NAMES[plan.kernel] == "generic"
     _check_plan_invariants(p, plan, [4096] * 32)
+
+
+# ------------------------------------------------ packed and paged layouts
+
+def paged(ps=16, lmax=4096, **kw):
+    """A problem whose K/V are pools of pages [num_pages, ps, Hkv, D] (fake pointers)."""
+    p = problem(kv_len_max=lmax, **kw)
+    hkv, dqk, dv = p.kv_heads, p.head_dim_qk, p.head_dim_v
+    p.page_table = 0x2000
+    p.page_size = ps
+    p.pages_per_req = -(-lmax // ps)
+    p.num_pages = p.batch * p.pages_per_req
+    for dst, d in ((p.k_stride, dqk), (p.v_stride, dv)):
+        dst[0], dst[1], dst[2] = ps * hkv * d, hkv * d, d
+    return p
+
+
+@pytest.mark.parametrize("edit", [
+    dict(reserved1=1),
+    dict(page_size=0),
+    dict(num_pages=0),
+    dict(pages_per_req=1),                       # 16 rows < kv_len_max
+    dict(page_table=None),                       # page fields without a table
+    dict(kv_indptr=0x3000),                      # kv_indptr with a page table
+])
+def test_invalid_layout_is_rejected(lib, edit):
+    p = paged()
+    for k, v in edit.items():
+        setattr(p, k, v)
+    assert plan_status(lib, p)[0] == ra.ATTN_ERR_ARG
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.attn_prefill(ctypes.byref(p), fake, fake, fake, fake, None, None) == ra.ATTN_ERR_ARG
+
+
+def test_kv_indptr_excludes_kv_lens(lib):
+    p = problem()
+    p.kv_indptr = 0x3000
+    p.kv_lens = 0x4000
+    assert plan_status(lib, p)[0] == ra.ATTN_ERR_ARG
+    p.kv_lens = None
+    assert plan_status(lib, p)[0] == 0
+
+
+def test_packed_queries_are_prefill_only(lib):
+    p = problem(q_len=4)
+    p.q_indptr = 0x3000
+    st, _ = plan_status(lib, p)
+    assert st == ra.ATTN_ERR_UNSUPPORTED
+    fake = ctypes.c_void_p(0x1000)
+    plan = _lib.AttnPlan()
+    assert lib.attn_decode_split(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, fake,
+                                 1 << 30, fake, 1 << 30, None) == ra.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_combine(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, None,
+                            None) == ra.ATTN_ERR_UNSUPPORTED
+    assert lib.attn_decode(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, fake, 1 << 30,
+                           fake, 1 << 30, fake, 1 << 30, fake, None, None) == ra.ATTN_ERR_UNSUPPORTED
+
+
+def test_paged_plan_is_not_valid_for_the_plain_problem(lib):
+    st, plan = plan_status(lib, paged())
+    assert st == 0
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.attn_decode_split(ctypes.byref(problem()), ctypes.byref(plan), fake, fake, fake,
+                                 fake, 1 << 30, fake, 1 << 30, None) == ra.ATTN_ERR_ARG
+
+
+@pytest.mark.parametrize("ps,kernel", [(1, 1), (16, 1), (64, 1), (256, 1), (24, 0), (48, 0)])
+def test_paged_gqa_family_and_split_bound(lib, ps, kernel):
+    # Power-of-two pages run on the GQA MFMA kernel, whose split must keep its
+    # page ids (at most 8448 per split) in LDS; other page sizes run generic.
+    lmax = 32768
+    p = paged(ps=ps, lmax=lmax, batch=4)
+    lens = [lmax, 100, 9000, 0]
+    st, plan = plan_status(lib, p, 0, lens)
+    assert st == 0
+    assert plan.kernel == kernel
+    if kernel == 1:
+        assert (plan.chunk + ps - 1) // ps + 1 <= 8448
+    _check_plan_invariants(p, plan, lens)
+    st, plan = plan_status(lib, p, 1, lens)          # one split requested
+    assert st == 0
+    if kernel == 1:
+        assert (plan.chunk + ps - 1) // ps + 1 <= 8448
+        assert plan.s_max == math.ceil(lmax / plan.chunk)
+
+
+def test_mla_with_paged_or_packed_keys_runs_generic(lib):
+    for edit in ("page", "indptr"):
+        p = problem(q_heads=16, kv_heads=1, head_dim_qk=576, head_dim_v=512)
+        if edit == "page":
+            p = paged(ps=64, q_heads=16, kv_heads=1, head_dim_qk=576, head_dim_v=512)
+        else:
+            p.kv_indptr = 0x3000
+        st, plan = plan_status(lib, p)
+        assert st == 0 and plan.kernel == 0

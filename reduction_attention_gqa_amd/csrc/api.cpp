@@ -209,7 +209,11 @@ bool mla_fits(const attn_problem* p, const void* q, const void* k, const void* v
 bool prefill_d128_fits(const attn_problem* p, const void* q, const void* k, const void* v,
                        const void* o) {
   if (p->dtype != ATTN_BF16 || p->head_dim_qk != 128 || p->head_dim_v != 128) return false;
-  if (p->q_indptr || p->kv_indptr || p->page_table) return false;
+  // Paged: a power-of-two page size, and the page ids of the longest request
+  // fit in the workgroup's LDS table.
+  if (p->page_table && (!is_pow2(p->page_size) ||
+                        ceil_div(p->kv_len_max, p->page_size) > kPrefillPageIds))
+    return false;
   if (!gqa_d128_fits(p, q, k, v)) return false;
   const int oal = p->o_dtype == ATTN_BF16 ? 8 : 16;
   if ((reinterpret_cast<uintptr_t>(o) & (oal - 1)) != 0) return false;

@@ -58,4 +58,14 @@ __device__ __forceinline__ int64_t kv_base_off(const KParams& p, int b, int64_t 
   return (int64_t)b * s0;
 }
 
+// Wave-uniform copies of a value every lane computed the same way (for a
+// request index that is the same in every lane): they keep buffer
+// descriptors and loop bounds in scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uniform(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 }  // namespace attn

@@ -38,6 +38,7 @@
 // XCD's L2.
 #include "../attn_internal.hpp"
 #include "common.hpp"
+#include "layout.hpp"
 
 namespace attn {
 namespace {
@@ -71,8 +72,10 @@ __device__ __forceinline__ float vmax(float a, float b) { return __builtin_eleme
 __device__ __forceinline__ int tile_off(int row, int c) { return row * RB + 16 * (c ^ swz(row)); }
 
 // KB key blocks of 32 per tile; NS ring stages, tile i + NS - 1 loaded while
-// tile i is consumed.
-template <int KB, int NS>
+// tile i is consumed.  PAGED: K/V rows come from a page pool (power-of-two
+// page size); the request's page ids are staged in LDS after the rings and
+// each lane copies its row with a 64-bit-addressed global load into LDS.
+template <int KB, int NS, bool PAGED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_d128_kernel(KParams p, int nrt) {
   constexpr int TK = 32 * KB;         // keys per tile
@@ -98,11 +101,13 @@ void prefill_d128_kernel(KParams p, int nrt) {
   }
   const int b = group / p.Hkv;
   const int kvh = group % p.Hkv;
-  const int L = kv_len_of(p.kv_lens, b, p.Lcap);
+  const int L = uniform(kv_len_b(p, b));
+  const int Lqb = uniform(q_len_b(p, b));  // query rows of this request (packed queries: ragged)
   const int G = p.G;
-  const int R = p.rows;            // Lq * G
+  const int R = Lqb * G;           // rows of this request
   const int r0 = rt * ROWS;
-  const int off = L - p.Lq;        // causal: row position i sees keys <= i + off
+  if (r0 >= R) return;             // a row tile past this request's queries
+  const int off = L - Lqb;         // causal: row position i sees keys <= i + off
 
   // This wave's rows: lane (c, h) holds row rw0 + c.
   const int c = lane & 31;
@@ -124,7 +129,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
   {
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q);
     const int qh = kvh * G + (r % G);
-    const int64_t qoff = (int64_t)b * p.qs_b + (int64_t)qi * p.qs_t + (int64_t)qh * p.qs_h;
+    const int64_t qoff = q_row_off(p, b, qi) + (int64_t)qh * p.qs_h;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       i32x4_t v = {0, 0, 0, 0};
@@ -141,11 +146,38 @@ void prefill_d128_kernel(KParams p, int nrt) {
   // writes the 16-byte slot (row 4*(NDMA*w+u) + l/16, position l%16), which
   // holds chunk (l%16) ^ swz(row).  The buffer ranges end at the last key, so
   // rows past it are zero.
-  const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
-  const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)b * p.vs_b + (int64_t)kvh * p.vs_h;
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)kvh * p.ks_h;
+  const uint16_t* vp = reinterpret_cast<const uint16_t*>(p.v) + (int64_t)kvh * p.vs_h;
+  if constexpr (!PAGED) {
+    kp += uniform(kv_base_off(p, b, p.ks_b, p.ks_t));
+    vp += uniform(kv_base_off(p, b, p.vs_b, p.vs_t));
+  }
   const uint32_t kst = (uint32_t)(p.ks_t * 2), vst = (uint32_t)(p.vs_t * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)L * kst);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, (uint32_t)L * vst);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, PAGED ? 0u : (uint32_t)L * kst);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, PAGED ? 0u : (uint32_t)L * vst);
+
+  // Paged: keys [0, kload) are the ones any tile copy reads; tile rows past
+  // kload re-read key kload - 1 (masked, zero probability).  The ids of their
+  // pages go to LDS after the K/V rings, clamped into the pool.
+  const int ntiles = (kend + TK - 1) / TK;
+  const int kload = min(L, ntiles * TK);
+  const int psh = PAGED ? p.page_shift : 0;
+  const int pmask = (1 << psh) - 1;
+  int* page_ids = reinterpret_cast<int*>(smem + 2 * NS * KT);
+  if constexpr (PAGED) {
+    const int n_ids = kload > 0 ? min(((kload - 1) >> psh) + 1, kPrefillPageIds) : 0;
+    const int32_t* trow = p.page_table + (int64_t)b * p.ppr;
+    for (int e = threadIdx.x; e < n_ids; e += NT) {
+      const int pg = trow[e];
+      page_ids[e] = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+    }
+    __syncthreads();
+  }
+  const int dma_row = 4 * w + (lane >> 4);  // this lane's row of a tile copy (NDMA == 1)
+  const int dma_chunk = (lane & 15) ^ swz(dma_row);
+  const int64_t kpage = p.ks_b * 2, vpage = p.vs_b * 2;  // bytes between pages
+  auto page_of_tile = [&](int k0) { return page_ids[min(k0 + dma_row, kload - 1) >> psh]; };
+  int pg_next = (PAGED && ntiles > 0) ? page_of_tile(0) : 0;
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(smem);
   uint32_t k_voff[NDMA], v_voff[NDMA];
 #pragma unroll
@@ -160,6 +192,23 @@ void prefill_d128_kernel(KParams p, int nrt) {
   // pair it with conservative waits; its completion is awaited explicitly
   // before each barrier that publishes a tile.
   auto dma_tile = [&](int k0, int stage) {
+    if constexpr (PAGED) {
+      // Tiles are copied in order; the page of this one was read from LDS
+      // when the previous copy was issued.
+      const int key = min(k0 + dma_row, kload - 1);
+      const int64_t in_page = (int64_t)(key & pmask);
+      const char* ka = reinterpret_cast<const char*>(kp) + (int64_t)pg_next * kpage +
+                       in_page * kst + 16 * dma_chunk;
+      const char* va = reinterpret_cast<const char*>(vp) + (int64_t)pg_next * vpage +
+                       in_page * vst + 16 * dma_chunk;
+      const uint32_t m0k = __builtin_amdgcn_readfirstlane(smem_lds + (uint32_t)(stage * KT + w * 1024));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(m0k), "v"(ka) : "memory", "m0");
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :: "s"(m0k + VRING), "v"(va) : "memory", "m0");
+      pg_next = page_of_tile(k0 + TK);
+      return;
+    }
     const uint32_t ksoff = (uint32_t)k0 * kst, vsoff = (uint32_t)k0 * vst;
 #pragma unroll
     for (int u = 0; u < NDMA; ++u) {
@@ -223,7 +272,6 @@ void prefill_d128_kernel(KParams p, int nrt) {
   float l_part = 0.f;
   const float sl2 = p.scale_log2;
 
-  const int ntiles = (kend + TK - 1) / TK;
   // Leading tiles that need no mask for any row of this wave; the remaining
   // ones (the diagonal, the ragged end, rows past R) are masked.
   const int n_clean = (rw0 + 32 <= R) ? min(kfull_w, L) / TK : 0;
@@ -405,7 +453,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
   if (row_ok) {
     const int qh = kvh * G + (r % G);
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-    const int64_t obase = (int64_t)b * p.os_b + (int64_t)qi * p.os_t + (int64_t)qh * p.os_h;
+    const int64_t obase = o_row_off(p, b, qi) + (int64_t)qh * p.os_h;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -424,23 +472,24 @@ void prefill_d128_kernel(KParams p, int nrt) {
         }
       }
     if (h == 0 && p.lse_out)
-      p.lse_out[((int64_t)b * p.Lq + qi) * p.Hq + qh] =
+      p.lse_out[lse_row(p, b, qi) * p.Hq + qh] =
           l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : kNegInf;
   }
 }
 
-template <int KB, int NS>
+template <int KB, int NS, bool PAGED>
 hipError_t launch_variant(const KParams& p, int nrt, int64_t nwg, hipStream_t s) {
+  constexpr int lds = lds_bytes(KB, NS) + (PAGED ? 4 * kPrefillPageIds : 0);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_d128_kernel<KB, NS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       lds_bytes(KB, NS));
+    hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&prefill_d128_kernel<KB, NS, PAGED>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((prefill_d128_kernel<KB, NS>), dim3((unsigned)nwg), dim3(NT),
-                     lds_bytes(KB, NS), s, p, nrt);
+  hipLaunchKernelGGL((prefill_d128_kernel<KB, NS, PAGED>), dim3((unsigned)nwg), dim3(NT), lds, s,
+                     p, nrt);
   return hipGetLastError();
 }
 
@@ -450,7 +499,8 @@ hipError_t launch_prefill_d128(const KParams& p, hipStream_t s) {
   const int nrt = (p.rows + ROWS - 1) / ROWS;
   const int64_t nwg = (int64_t)p.B * p.Hkv * nrt;
   if (nwg == 0) return hipSuccess;
-  return launch_variant<1, kPrefillStages>(p, nrt, nwg, s);
+  if (p.page_table) return launch_variant<1, kPrefillStages, true>(p, nrt, nwg, s);
+  return launch_variant<1, kPrefillStages, false>(p, nrt, nwg, s);
 }
 
 }  // namespace attn

@@ -100,6 +100,30 @@ def _to_dev(a, dt):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(dt)
 
 
+def _place_queries(obj, prob, q_lens, dt, od, pad, spare):
+    """Q, O and LSE on the device: [B, Lq, ...] when q_lens is None, else packed
+    [T + spare, ...] with q_indptr (request b keeps its first q_lens[b] rows)."""
+    b, lq, hq, dqk = prob.q.shape
+    obj.q_lens = q_lens
+    if q_lens is None:
+        obj.q_indptr = None
+        obj.q = _to_dev(prob.q, dt)
+        obj.o = torch.full((b, lq, hq, prob.dv), float("nan"), dtype=od, device=DEV)
+        obj.lse = torch.full((b, lq, hq), float("nan"), dtype=torch.float32, device=DEV)
+        return
+    assert len(q_lens) == b and max(q_lens) <= lq
+    obj.q_indptr = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]), dtype=torch.int32,
+                                device=DEV)
+    tq = int(sum(q_lens))
+    qh = np.full((tq + spare, hq, dqk), pad, dtype=np.float32)
+    if tq:
+        qh[:tq] = np.concatenate([prob.q[i, :n] for i, n in enumerate(q_lens)])
+    obj.q = _to_dev(qh, dt)
+    obj.tq = tq
+    obj.o = torch.full((tq + spare, hq, prob.dv), float("nan"), dtype=od, device=DEV)
+    obj.lse = torch.full((tq + spare, hq), float("nan"), dtype=torch.float32, device=DEV)
+
+
 class PagedDeviceProblem(DeviceProblem):
     """A synthetic Problem whose K/V live in a shuffled page pool.
 
@@ -109,7 +133,7 @@ class PagedDeviceProblem(DeviceProblem):
     """
 
     def __init__(self, prob, page_size, layout="token", seed=0, pad=float("nan"),
-                 o_dtype=None):
+                 o_dtype=None, q_lens=None, spare=5):
         from synthetic.inputs import page_layout
         self.prob = prob
         dt = torch_dtype(prob.dtype)
@@ -119,7 +143,6 @@ class PagedDeviceProblem(DeviceProblem):
         table, self.num_pages = page_layout(prob.lens, page_size, seed, lcap=prob.lcap)
         self.table_host = table
         self.table = torch.from_numpy(table).to(DEV)
-        self.q = _to_dev(prob.q, dt)
         self.k = self._pool(prob.k, prob.hkv, dqk, dt, layout, pad)
         if prob.v_aliases_k:
             self.v = self.k[..., : prob.dv]
@@ -128,8 +151,7 @@ class PagedDeviceProblem(DeviceProblem):
         self.lens = torch.tensor(prob.lens, dtype=torch.int32, device=DEV)
         od = dt if o_dtype is None else torch_dtype(o_dtype)
         self.o_dtype = od
-        self.o = torch.full((b, lq, hq, prob.dv), float("nan"), dtype=od, device=DEV)
-        self.lse = torch.full((b, lq, hq), float("nan"), dtype=torch.float32, device=DEV)
+        _place_queries(self, prob, q_lens, dt, od, pad, spare)
 
     def _pool(self, rows, hkv, d, dt, layout, pad):
         ps = self.page_size
@@ -152,7 +174,7 @@ class PagedDeviceProblem(DeviceProblem):
         p = self.prob
         return ra.make_problem(self.q, self.k, self.v, self.o, kv_lens=self.lens,
                                kv_len_max=self.lcap, causal=p.causal, scale=p.scale,
-                               page_table=self.table)
+                               page_table=self.table, q_indptr=self.q_indptr, q_len_max=p.lq)
 
 
 class PackedDeviceProblem(DeviceProblem):
@@ -183,25 +205,7 @@ class PackedDeviceProblem(DeviceProblem):
             self.v = _to_dev(vh, dt)
         od = dt if o_dtype is None else torch_dtype(o_dtype)
         self.o_dtype = od
-        self.q_lens = q_lens
-        if q_lens is None:
-            self.q_indptr = None
-            self.q = _to_dev(prob.q, dt)
-            self.o = torch.full((b, lq, hq, prob.dv), float("nan"), dtype=od, device=DEV)
-            self.lse = torch.full((b, lq, hq), float("nan"), dtype=torch.float32, device=DEV)
-        else:
-            assert len(q_lens) == b and max(q_lens) <= lq
-            self.q_indptr = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]),
-                                         dtype=torch.int32, device=DEV)
-            tq = int(sum(q_lens))
-            qh = np.full((tq + spare, hq, dqk), pad, dtype=np.float32)
-            rows = [prob.q[i, :n] for i, n in enumerate(q_lens)]
-            if tq:
-                qh[:tq] = np.concatenate(rows)
-            self.q = _to_dev(qh, dt)
-            self.tq = tq
-            self.o = torch.full((tq + spare, hq, prob.dv), float("nan"), dtype=od, device=DEV)
-            self.lse = torch.full((tq + spare, hq), float("nan"), dtype=torch.float32, device=DEV)
+        _place_queries(self, prob, q_lens, dt, od, pad, spare)
 
     def problem(self):
         p = self.prob

@@ -167,7 +167,7 @@ def test_ragged_prefill_packed(dtype, dqk, causal):
     assert_lse_close(name, got_lse[:tq], lse, 1e-3 if dtype == "bf16" else 1e-5)
 
 
-@pytest.mark.parametrize("ps", [16, 128])
+@pytest.mark.parametrize("ps", [1, 2, 16, 128, 24])
 def test_paged_prefill(ps):
     # Prefill over a paged cache (a prefix already cached): 96 new rows per
     # request, bottom-right causal against up to 700 keys.
@@ -178,3 +178,24 @@ def test_paged_prefill(ps):
     o, lse = _oracle(p)
     assert_close(f"paged prefill ps={ps}", d.out(), o, BF16_MAX, BF16_MEAN)
     assert_lse_close(f"paged prefill ps={ps}", d.lse_out(), lse)
+
+
+@pytest.mark.parametrize("kv", ["packed", "paged16", "paged1"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_prefill_several_row_tiles(causal, kv):
+    # Packed queries over G = 4: 100 and 257 query rows span two and five
+    # 256-row tiles; one request has no query and one a single query row.
+    q_lens = [100, 0, 257, 1]
+    p = make_problem(dtype="bf16", batch=4, lq=257, kv_len=[300, 10, 257, 1000], lcap=1024,
+                     seed=20, causal=causal, **LLAMA)
+    if kv == "packed":
+        d = PackedDeviceProblem(p, q_lens=q_lens)
+    else:
+        d = PagedDeviceProblem(p, int(kv[5:]), q_lens=q_lens, seed=21)
+    d.prefill()
+    o, lse = _oracle_ragged(p, q_lens)
+    out, got_lse, tq = d.out(), d.lse_out(), d.tq
+    assert np.isnan(out[tq:]).all() and np.isnan(got_lse[tq:]).all()
+    name = f"ragged prefill {kv} causal={causal}"
+    assert_close(name, out[:tq], o, BF16_MAX, BF16_MEAN)
+    assert_lse_close(name, got_lse[:tq], lse)

@@ -18,8 +18,11 @@ Inputs are synthetic (seeded i.i.d. N(0,1), rounded to bf16) and resident in
 HBM before timing.  The decode K/V cache is stored head-major, [B, Hkv, L, D]
 (each (request, KV head) one contiguous stream; the library takes any
 strides), and the token-major [B, L, Hkv, D] cache is timed beside it as an
-ablation (--kv-layout token makes it the measured one).  Several copies of the inputs are rotated so that a step
-never finds its K/V in the 256 MB Infinity Cache from the previous step.
+ablation (--kv-layout token makes it the measured one).  A paged cache (16-row
+pages scattered over a pool by a seeded shuffle, read through a page table) is
+timed as a further ablation; --paged PS makes a paged cache the measured one.
+Several copies of the inputs are rotated so that a step never finds its K/V in
+the 256 MB Infinity Cache from the previous step.
 
 Algorithmic work: bytes = unique Q, K and V reads + O write (the split
 workspace is not counted); flops = 2 (Dqk + Dv) per visible (query, key) pair.
@@ -60,6 +63,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ablation", action="store_true")
+    ap.add_argument("--paged", type=int, default=0, metavar="PS",
+                    help="decode from a paged K/V cache with PS rows per page (0 = contiguous)")
     ap.add_argument("--kv-layout", choices=("token", "head"), default="head",
                     help="decode K/V cache storage: token-major [B, L, Hkv, D] or head-major "
                          "[B, Hkv, L, D] (the kernels take either through strides)")
@@ -86,27 +91,53 @@ def kv_buffer(prob, d, dt, dev, layout):
     return torch.zeros((prob.batch, prob.lcap, prob.hkv, d), dtype=dt, device=dev)
 
 
-def device_copies(prob, n_copies, dev, layout="token"):
-    """n_copies independent device copies of one synthetic problem (zero padding)."""
+def pool_buffer(num_pages, page_size, hkv, d, dt, dev, layout):
+    """A zero page pool seen as [num_pages, page_size, Hkv, d]: token-major pages,
+    or head-major pages [num_pages, Hkv, page_size, d] (a permuted view)."""
+    import torch
+    if layout == "head":
+        return torch.zeros((num_pages, hkv, page_size, d), dtype=dt, device=dev).permute(0, 2, 1, 3)
+    return torch.zeros((num_pages, page_size, hkv, d), dtype=dt, device=dev)
+
+
+def device_copies(prob, n_copies, dev, layout="token", page_size=0):
+    """n_copies independent device copies of one synthetic problem (zero padding).
+    page_size > 0: K/V live in a page pool whose pages are shuffled by a seeded
+    permutation (synthetic.inputs.page_layout); the page table is returned too."""
     import numpy as np
     import torch
     dt = torch.bfloat16 if prob.dtype == "bf16" else torch.float32
     q = torch.from_numpy(prob.q).to(dev).to(dt)
-    k = kv_buffer(prob, prob.dqk, dt, dev, layout)
-    v = None if prob.v_aliases_k else kv_buffer(prob, prob.dv, dt, dev, layout)
+    table = None
+    if page_size:
+        from synthetic.inputs import page_layout
+        table_h, n_pages = page_layout(prob.lens, page_size, seed=1, lcap=prob.lcap)
+        table = torch.from_numpy(table_h).to(dev)
+        k = pool_buffer(n_pages, page_size, prob.hkv, prob.dqk, dt, dev, layout)
+        v = None if prob.v_aliases_k else pool_buffer(n_pages, page_size, prob.hkv, prob.dv, dt,
+                                                      dev, layout)
+    else:
+        k = kv_buffer(prob, prob.dqk, dt, dev, layout)
+        v = None if prob.v_aliases_k else kv_buffer(prob, prob.dv, dt, dev, layout)
     for b in range(prob.batch):
         n = int(prob.lens[b])
-        if n:
-            k[b, :n] = torch.from_numpy(np.ascontiguousarray(prob.k[b])).to(dev).to(dt)
-            if v is not None:
-                v[b, :n] = torch.from_numpy(np.ascontiguousarray(prob.v[b])).to(dev).to(dt)
+        if not n:
+            continue
+        if page_size:
+            t = torch.arange(n, device=dev)
+            rows = (torch.from_numpy(table_h[b]).to(dev).long()[t // page_size], t % page_size)
+        else:
+            rows = (b, slice(0, n))
+        k[rows] = torch.from_numpy(np.ascontiguousarray(prob.k[b])).to(dev).to(dt)
+        if v is not None:
+            v[rows] = torch.from_numpy(np.ascontiguousarray(prob.v[b])).to(dev).to(dt)
     copies = []
     for c in range(n_copies):
         qc, kc = (q, k) if c == 0 else (q.clone(), k.clone())
         vc = kc[..., : prob.dv] if v is None else (v if c == 0 else v.clone())
         copies.append((qc, kc, vc))
     lens = torch.tensor(prob.lens, dtype=torch.int32, device=dev)
-    return copies, lens
+    return copies, lens, table
 
 
 def n_copies_for(step_bytes):
@@ -231,19 +262,21 @@ def traffic_for(kernel_src, launches_key):
 
 # ----------------------------------------------------------------------- timing
 
-def time_decode(prob, steps, warmup, s_request, dev, fused, layout="token"):
+def time_decode(prob, steps, warmup, s_request, dev, fused, layout="token", page_size=0):
     """Time `steps` decode steps.  fused: one attn_decode call per step (for the
     GQA family a single launch that merges its own splits); otherwise the split
-    launch and the combine launch, timed separately."""
+    launch and the combine launch, timed separately.  page_size > 0: a paged
+    K/V cache."""
     import torch
     import reduction_attention_gqa_amd as ra
     qb, kvb, ob = decode_bytes(prob)
-    copies, lens = device_copies(prob, n_copies_for(qb + kvb + ob), dev, layout)
+    copies, lens, table = device_copies(prob, n_copies_for(qb + kvb + ob), dev, layout,
+                                        page_size)
     dt = copies[0][0].dtype
     o = torch.empty((prob.batch, prob.lq, prob.hq, prob.dv), dtype=dt, device=dev)
     lens_host = [int(x) for x in prob.lens]
     probs = [ra.make_problem(q, k, v, o, kv_lens=lens, kv_len_max=prob.lcap, causal=prob.causal,
-                             scale=prob.scale) for q, k, v in copies]
+                             scale=prob.scale, page_table=table) for q, k, v in copies]
     plan = ra.attn_decode_plan(probs[0], s_request, lens_host)
     ws_o, ws_lse, ws_cnt = ra.workspace(plan, dev)
     stream = torch.cuda.current_stream()
@@ -291,7 +324,7 @@ def time_prefill(prob, steps, warmup, dev):
     import torch
     import reduction_attention_gqa_amd as ra
     qb, kvb, ob = decode_bytes(prob)
-    copies, lens = device_copies(prob, n_copies_for(qb + kvb + ob), dev)
+    copies, lens, _ = device_copies(prob, n_copies_for(qb + kvb + ob), dev)
     dt = copies[0][0].dtype
     o = torch.empty((prob.batch, prob.lq, prob.hq, prob.dv), dtype=dt, device=dev)
     probs = [ra.make_problem(q, k, v, o, kv_lens=lens, kv_len_max=prob.lcap, causal=prob.causal,
@@ -464,7 +497,7 @@ def main():
         # The GQA family runs as one fused launch; the others as split + combine.
         fused = prob.dtype == "bf16" and prob.dqk == 128 and prob.dv == 128 and not a.two_launch
         log(f"timing decode ({'single launch' if fused else 'split + combine'})")
-        r = time_decode(prob, a.steps, a.warmup, a.s, dev, fused, a.kv_layout)
+        r = time_decode(prob, a.steps, a.warmup, a.s, dev, fused, a.kv_layout, a.paged)
         src = ("reduction_attention_gqa_amd/csrc/kernels/"
                + {0: "generic.hip", 1: "decode_gqa_d128.hip", 2: "decode_mla.hip"}[r["plan"].kernel])
         rec = decode_record(prob, r, a.steps, a.warmup, src)
@@ -475,6 +508,7 @@ def main():
                          "kv_heads": prob.hkv, "head_dim_qk": prob.dqk, "head_dim_v": prob.dv,
                          "kv_len_total": int(prob.lens.sum()), "kv_len_max": int(prob.lens.max()),
                          "q_len": prob.lq, "kv_layout": a.kv_layout,
+                         "page_size": a.paged or None,
                          "split_s": rec["plan"]["s_max"],
                          "chunk": rec["plan"]["chunk"],
                          "kernel": ra.KERNEL_NAMES[rec["plan"]["kernel"]]}
@@ -483,8 +517,17 @@ def main():
                                 "combine_launch_ms": rec["combine"],
                                 "algorithmic_bytes_per_step": rec["algorithmic_bytes_per_step"],
                                 "wall_s_timed": round(r["wall_s"], 4)}
-        if not a.no_ablation and a.s == 0:
+        if not a.no_ablation and a.s == 0 and not a.paged:
             n_abl = max(10, a.steps // 5)
+            log("timing the paged-cache ablation (16-row pages, shuffled pool)")
+            rp = time_decode(prob, n_abl, 3, 0, dev, fused, a.kv_layout, 16)
+            recp = decode_record(prob, rp, n_abl, 3, src)
+            out["paged"] = {"page_size": 16, "value": recp["value"], "unit": "GB/s",
+                            "ms_per_step": recp["ms_per_step"],
+                            "launch_ms": recp["roofline"]["launch_ms"]["mean_ms"],
+                            "frac": recp["roofline"]["frac"],
+                            "split_s": recp["plan"]["s_max"],
+                            "ratio_to_contiguous": round(recp["value"] / rec["value"], 3)}
             if fused:
                 log("timing the two-launch ablation (split kernel + combine kernel)")
                 r2 = time_decode(prob, n_abl, 3, 0, dev, False, a.kv_layout)

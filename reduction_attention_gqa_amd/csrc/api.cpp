@@ -147,21 +147,22 @@ KParams base_params(const attn_problem* p) {
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; }
 
 // Shape-level kernel choice for decode (pointers are checked at launch).
-// Paged K/V runs on the GQA MFMA kernel when the page size is a power of two,
-// and on the generic kernel otherwise; the MLA kernel takes the plain layout only.
+// Paged K/V runs on the MFMA kernels when the page size is a power of two,
+// and on the generic kernel otherwise.
 int decode_family(const attn_problem* p) {
   const int rows = (p->q_heads / p->kv_heads) * p->q_len;
   if (p->dtype == ATTN_BF16 && p->head_dim_qk == 128 && p->head_dim_v == 128 &&
       rows <= kGqaMaxRows && (!p->page_table || is_pow2(p->page_size)))
     return ATTN_KERNEL_GQA_D128;
   if (p->dtype == ATTN_BF16 && p->head_dim_qk == 576 && p->head_dim_v == 512 && rows <= kMlaRows &&
-      !p->page_table && !p->kv_indptr)
+      (!p->page_table || is_pow2(p->page_size)))
     return ATTN_KERNEL_MLA;
   return ATTN_KERNEL_GENERIC;
 }
 
-// Longest split the paged GQA kernel accepts: its page ids fit in LDS.
-int64_t gqa_paged_max_chunk(const attn_problem* p) {
+// Longest split a paged MFMA decode kernel accepts: its page ids fit in LDS.
+int64_t paged_max_chunk(const attn_problem* p, int family) {
+  if (family == ATTN_KERNEL_MLA) return (int64_t)(kMlaPageIds - 1) * p->page_size / kMlaTileN * kMlaTileN;
   return (int64_t)(kGqaPageIds - 1) * p->page_size / kGqaTileN * kGqaTileN;
 }
 
@@ -199,7 +200,7 @@ bool gqa_d128_fits(const attn_problem* p, const void* q, const void* k, const vo
 // Can the MLA kernel run?  V must be the first Dv columns of K (same pointer
 // and strides), with 16-byte rows and 32-bit buffer offsets.
 bool mla_fits(const attn_problem* p, const void* q, const void* k, const void* v) {
-  if (v != k || p->page_table || p->kv_indptr) return false;
+  if (v != k) return false;
   for (int a = 0; a < 3; ++a)
     if (p->v_stride[a] != p->k_stride[a]) return false;
   return gqa_d128_fits(p, q, k, v);
@@ -227,9 +228,18 @@ bool prefill_d128_fits(const attn_problem* p, const void* q, const void* k, cons
 // page ids fit in the kernel's LDS table.
 bool gqa_d128_usable(const attn_problem* p, const attn_plan* plan, const void* q, const void* k,
                      const void* v) {
-  if (p->page_table && (!is_pow2(p->page_size) || plan->chunk > gqa_paged_max_chunk(p)))
+  if (p->page_table &&
+      (!is_pow2(p->page_size) || plan->chunk > paged_max_chunk(p, ATTN_KERNEL_GQA_D128)))
     return false;
   return gqa_d128_fits(p, q, k, v);
+}
+
+bool mla_usable(const attn_problem* p, const attn_plan* plan, const void* q, const void* k,
+                const void* v) {
+  if (p->page_table &&
+      (!is_pow2(p->page_size) || plan->chunk > paged_max_chunk(p, ATTN_KERNEL_MLA)))
+    return false;
+  return mla_fits(p, q, k, v);
 }
 
 int check_ptrs(const void* a, const char* na, const void* b, const char* nb, const void* c,
@@ -325,9 +335,9 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
       chunk_tiles = std::min<int64_t>(chunk_tiles, max_tiles);
       chunk = chunk_tiles * tile_n;
     }
-    // The paged GQA kernel stages one split's page ids in LDS.
-    if (family == ATTN_KERNEL_GQA_D128 && p->page_table)
-      chunk = std::min<int64_t>(chunk, gqa_paged_max_chunk(p));
+    // The paged MFMA kernels stage one split's page ids in LDS.
+    if (family != ATTN_KERNEL_GENERIC && p->page_table)
+      chunk = std::min<int64_t>(chunk, paged_max_chunk(p, family));
     s_max = ceil_div(lmax, chunk);
   }
   if (s_max > 65535) return fail(ATTN_ERR_UNSUPPORTED, "too many splits (%lld)", (long long)s_max);
@@ -403,7 +413,7 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan, const 
   kp.n_items = plan->n_items;
   if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_usable(p, plan, q, k, v))
     return hip_status(launch_decode_gqa_d128(kp, s), "decode_gqa_d128 launch");
-  if (plan->kernel == ATTN_KERNEL_MLA && mla_fits(p, q, k, v))
+  if (plan->kernel == ATTN_KERNEL_MLA && mla_usable(p, plan, q, k, v))
     return hip_status(launch_decode_mla(kp, unit_grid, s), "decode_mla launch");
   const int row_tiles = (int)ceil_div(kp.rows, kGenericRowTile);
   const dim3 grid(plan->s_max, row_tiles, (unsigned)((int64_t)p->batch * p->kv_heads));

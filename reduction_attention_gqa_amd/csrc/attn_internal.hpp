@@ -66,5 +66,6 @@ constexpr int kMlaBlock = 512;         // 8 waves of 16 query rows
 constexpr int kMlaRows = 128;          // query rows per MLA workgroup
 constexpr int kGqaPageIds = 8448;      // page ids one paged GQA work item stages in LDS
 constexpr int kPrefillPageIds = 4096;  // page ids one paged prefill workgroup stages in LDS
+constexpr int kMlaPageIds = 4096;      // page ids one paged MLA split stages in LDS
 
 }  // namespace attn

@@ -26,6 +26,7 @@
 // transposed 4-key reads of V free of LDS bank conflicts.
 #include "../attn_internal.hpp"
 #include "common.hpp"
+#include "layout.hpp"
 
 namespace attn {
 namespace {
@@ -69,6 +70,10 @@ __device__ __forceinline__ i32x4_t ds_read16_at(uint32_t lds_addr) {
 }
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// PAGED: K rows come from a page pool (power-of-two page size).  The split's
+// page ids are staged in LDS after the stages, and each lane copies its
+// 16-byte slot with a 64-bit-addressed global load into LDS (same slot layout).
+template <bool PAGED>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void decode_mla_kernel(KParams p) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -77,7 +82,7 @@ void decode_mla_kernel(KParams p) {
   const int j = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
-  const int L = kv_len_of(p.kv_lens, b, p.Lcap);
+  const int L = uniform(kv_len_b(p, b));
   const int lo = j * p.chunk;
   if (lo >= L) return;
   const int hi = min(lo + p.chunk, L);
@@ -109,11 +114,29 @@ void decode_mla_kernel(KParams p) {
     for (int ks = 0; ks < KSTEPS; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
-  const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)b * p.ks_b + (int64_t)kvh * p.ks_h;
+  const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)kvh * p.ks_h;
+  if constexpr (!PAGED) kp += uniform(kv_base_off(p, b, p.ks_b, p.ks_t));
   const uint32_t kst = (uint32_t)(p.ks_t * 2);
   // The buffer range ends at this split's last key: rows past it read as zero.
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (uint32_t)hi * kst);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, PAGED ? 0u : (uint32_t)hi * kst);
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(smem);
+
+  // Paged: the ids of the pages holding keys [lo, hi) (lo < hi here), clamped
+  // into the pool.  Slots past the split re-read key hi - 1 (masked).
+  const int psh = PAGED ? p.page_shift : 0;
+  const int pmask = (1 << psh) - 1;
+  const int pg0 = lo >> psh;
+  const int64_t kpage = p.ks_b * 2;  // bytes between pages
+  int* page_ids = reinterpret_cast<int*>(smem + LDS_BYTES);
+  if constexpr (PAGED) {
+    const int n_ids = min(((hi - 1) >> psh) - pg0 + 1, kMlaPageIds);
+    const int32_t* trow = p.page_table + (int64_t)b * p.ppr + pg0;
+    for (int e = threadIdx.x; e < n_ids; e += NT) {
+      const int pg = trow[e];
+      page_ids[e] = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+    }
+    __syncthreads();
+  }
 
   // Tile copy, HBM -> LDS without registers (buffer_load ... lds): one wave
   // instruction fills one KiB of the stage, lane l the 16-byte slot 64*blk + l,
@@ -127,6 +150,25 @@ void decode_mla_kernel(KParams p) {
     const uint32_t toff = (uint32_t)(lo + t * TK) * kst;
     int ln = lane;
     asm volatile("" : "+v"(ln));
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int u = 0; u < BLK_ROUNDS; ++u) {
+        if (u < BLK_ROUNDS - 1 || nb == BLK_ROUNDS) {
+          const int P = 64 * (u * NW + w) + ln;
+          const int key = P / CHUNKS;
+          const int c = (P - key * CHUNKS) ^ chunk_xor(key);
+          const int ka = min(lo + t * TK + key, hi - 1);
+          const int pg = page_ids[(ka >> psh) - pg0];
+          const char* src = reinterpret_cast<const char*>(kp) + (int64_t)pg * kpage +
+                            (int64_t)(ka & pmask) * kst + 16 * c;
+          const uint32_t m0v =
+              __builtin_amdgcn_readfirstlane(base + (uint32_t)((u * NW + w) * 1024));
+          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                       :: "s"(m0v), "v"(src) : "memory", "m0");
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < BLK_ROUNDS; ++u) {
       if (u < BLK_ROUNDS - 1 || nb == BLK_ROUNDS) {
@@ -325,18 +367,25 @@ void decode_mla_kernel(KParams p) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_decode_mla(const KParams& p, dim3 grid, hipStream_t s) {
+template <bool PAGED>
+hipError_t launch_mla_variant(const KParams& p, dim3 grid, hipStream_t s) {
+  constexpr int lds = LDS_BYTES + (PAGED ? 4 * kMlaPageIds : 0);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mla_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mla_kernel<PAGED>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(decode_mla_kernel, grid, dim3(NT), LDS_BYTES, s, p);
+  hipLaunchKernelGGL(decode_mla_kernel<PAGED>, grid, dim3(NT), lds, s, p);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mla(const KParams& p, dim3 grid, hipStream_t s) {
+  if (p.page_table) return launch_mla_variant<true>(p, grid, s);
+  return launch_mla_variant<false>(p, grid, s);
 }
 
 }  // namespace attn

@@ -378,12 +378,20 @@ def test_paged_gqa_family_and_split_bound(lib, ps, kernel):
         assert plan.s_max == math.ceil(lmax / plan.chunk)
 
 
-def test_mla_with_paged_or_packed_keys_runs_generic(lib):
-    for edit in ("page", "indptr"):
-        p = problem(q_heads=16, kv_heads=1, head_dim_qk=576, head_dim_v=512)
-        if edit == "page":
-            p = paged(ps=64, q_heads=16, kv_heads=1, head_dim_qk=576, head_dim_v=512)
-        else:
-            p.kv_indptr = 0x3000
-        st, plan = plan_status(lib, p)
-        assert st == 0 and plan.kernel == 0
+@pytest.mark.parametrize("layout,kernel", [("page1", 2), ("page64", 2), ("page48", 0),
+                                           ("indptr", 2)])
+def test_mla_layout_family_and_split_bound(lib, layout, kernel):
+    # Power-of-two pages and packed keys run on the MLA kernel, whose split
+    # must keep its page ids (at most 4096) in LDS; other page sizes run generic.
+    mla = dict(q_heads=16, kv_heads=1, head_dim_qk=576, head_dim_v=512)
+    if layout.startswith("page"):
+        ps = int(layout[4:])
+        p = paged(ps=ps, lmax=20000, **mla)
+    else:
+        p = problem(kv_len_max=20000, **mla)
+        p.kv_indptr = 0x3000
+    for s_request in (0, 1):
+        st, plan = plan_status(lib, p, s_request)
+        assert st == 0 and plan.kernel == kernel
+        if kernel == 2 and layout.startswith("page"):
+            assert (plan.chunk + ps - 1) // ps + 1 <= 4096

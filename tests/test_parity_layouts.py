@@ -117,15 +117,43 @@ def test_paged_causal_query_rows(fused):
     assert_lse_close(f"paged causal fused={fused}", d.lse_out(), lse)
 
 
-def test_paged_mla_decode():
-    # MLA (one latent KV head, V = first 512 columns of K) over 64-key pages.
-    p = make_problem(dtype="bf16", batch=2, lq=1, hq=16, hkv=1, dqk=576, dv=512,
-                     kv_len=[300, 77], seed=16, mla=True)
-    d = PagedDeviceProblem(p, 64, seed=9)
-    d.decode()
+@pytest.mark.parametrize("ps,s", [(1, 0), (1, 3), (64, 0), (48, 0)])
+def test_paged_mla_decode(ps, s):
+    # MLA (one latent KV head, V = first 512 columns of K); power-of-two pages
+    # run on the MLA kernel, 48-key pages on the generic one.
+    p = make_problem(dtype="bf16", batch=3, lq=1, hq=16, hkv=1, dqk=576, dv=512,
+                     kv_len=[300, 77, 1031], lcap=1040, seed=16, mla=True)
+    d = PagedDeviceProblem(p, ps, seed=9, layout="head" if ps == 1 else "token")
+    plan = d.decode(s_request=s)
+    assert plan.kernel == (0 if ps == 48 else 2)
     o, lse = _oracle(p)
-    assert_close("paged mla", d.out(), o, BF16_MAX, BF16_MEAN)
-    assert_lse_close("paged mla", d.lse_out(), lse)
+    name = f"paged mla ps={ps} s={s} (s_max {plan.s_max})"
+    assert_close(name, d.out(), o, BF16_MAX, BF16_MEAN)
+    assert_lse_close(name, d.lse_out(), lse)
+
+
+def test_paged_mla_one_key_pages_split_at_the_page_id_bound():
+    # One key per page: an MLA split holds at most 4064 keys.
+    p = make_problem(dtype="bf16", batch=1, lq=2, hq=16, hkv=1, dqk=576, dv=512,
+                     kv_len=[5000], seed=22, mla=True, causal=True)
+    d = PagedDeviceProblem(p, 1, seed=23)
+    plan = d.decode(s_request=1)
+    assert plan.kernel == 2 and plan.s_max == 2
+    o, lse = _oracle(p)
+    assert_close("paged mla ps=1 long", d.out(), o, BF16_MAX, BF16_MEAN)
+    assert_lse_close("paged mla ps=1 long", d.lse_out(), lse)
+
+
+@pytest.mark.parametrize("s", [0, 2])
+def test_packed_key_mla_decode(s):
+    p = make_problem(dtype="bf16", batch=3, lq=1, hq=16, hkv=1, dqk=576, dv=512,
+                     kv_len=[300, 0, 1031], lcap=1040, seed=24, mla=True)
+    d = PackedDeviceProblem(p)
+    plan = d.decode(s_request=s)
+    assert plan.kernel == 2
+    o, lse = _oracle(p)
+    assert_close(f"packed mla s={s}", d.out(), o, BF16_MAX, BF16_MEAN)
+    assert_lse_close(f"packed mla s={s}", d.lse_out(), lse)
 
 
 # ------------------------------------------------------ packed-key decode

@@ -424,7 +424,7 @@ def oracle_prefill_baseline(prob, groups=24):
 
 # ------------------------------------------------------------------------ main
 
-def decode_record(prob, r, steps, warmup, extra_src):
+def decode_record(prob, r, steps, warmup, extra_src, key_suffix=""):
     qb, kvb, ob = r["bytes"]
     total = qb + kvb + ob
     ms_step = r["wall_s"] * 1e3 / steps
@@ -434,7 +434,8 @@ def decode_record(prob, r, steps, warmup, extra_src):
     kern_bytes = total if r["fused"] else qb + kvb
     achieved = kern_bytes / (split["mean_ms"] * 1e-3) / 1e9
     plan = r["plan"]
-    traffic = traffic_for(extra_src, ("decode:" if r["fused"] else "decode_split:") + prob.name)
+    traffic = traffic_for(extra_src, ("decode:" if r["fused"] else "decode_split:") + prob.name
+                          + key_suffix)
     return dict(
         value=round(total / (ms_step * 1e-3) / 1e9, 2), ms_per_step=round(ms_step, 5),
         plan=dict(kernel=plan.kernel, s_max=plan.s_max, chunk=plan.chunk, n_items=plan.n_items,
@@ -466,6 +467,8 @@ def main():
                 family = "generic"
             fused = family == "gqa_d128" and not a.two_launch
             key = ("decode:" if fused else "decode_split:") + name
+            if a.paged:
+                key += f":paged{a.paged}"
         summarize_pmc(a.summarize_pmc[0], a.summarize_pmc[1], name, family, key)
         return
     if a.gpus != 1:
@@ -500,7 +503,8 @@ def main():
         r = time_decode(prob, a.steps, a.warmup, a.s, dev, fused, a.kv_layout, a.paged)
         src = ("reduction_attention_gqa_amd/csrc/kernels/"
                + {0: "generic.hip", 1: "decode_gqa_d128.hip", 2: "decode_mla.hip"}[r["plan"].kernel])
-        rec = decode_record(prob, r, a.steps, a.warmup, src)
+        rec = decode_record(prob, r, a.steps, a.warmup, src,
+                            f":paged{a.paged}" if a.paged else "")
         out["unit"] = "GB/s"
         out["value"] = rec["value"]
         out["ms_per_step"] = rec["ms_per_step"]

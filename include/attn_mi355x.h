@@ -164,6 +164,10 @@ typedef struct attn_plan {
  *              clamped to [0, Lcap]), or NULL for "all Lcap".
  * num_cus      compute units to plan for; <= 0 queries the current device.
  * out          receives the plan.
+ * With a page table, the MFMA kernels stage one split's page ids on chip, so
+ * the planner bounds a split to 8447 (GQA) or 4095 (MLA) pages, adding
+ * splits where needed.  Decode takes no packed queries: a problem with
+ * q_indptr gives ATTN_ERR_UNSUPPORTED here and in every decode call.
  * Returns ATTN_OK, ATTN_ERR_ARG, ATTN_ERR_UNSUPPORTED or ATTN_ERR_HIP (only
  * when num_cus <= 0 and the device query fails).  Enqueues nothing.
  */

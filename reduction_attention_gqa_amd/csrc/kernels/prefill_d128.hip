@@ -68,6 +68,15 @@ __device__ __forceinline__ i32x4_t ds_read16_at(uint32_t lds_addr) {
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 // IEEE-754 2019 maximum (v_maximum3_f32): no canonicalisation of its inputs.
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// Combine lane l with lane l ^ 32 (the two lanes of a row) with gfx950's
+// v_permlane32_swap: a VALU exchange instead of an LDS-unit permute.  With both
+// operands equal, the two results are the lower and the upper lane's value.
+__device__ __forceinline__ f32x2_t row_halves(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return f32x2_t{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float row_max(float v) { const f32x2_t h = row_halves(v); return vmax(h[0], h[1]); }
+__device__ __forceinline__ float row_sum(float v) { const f32x2_t h = row_halves(v); return h[0] + h[1]; }
 // Byte offset of (row, 16-byte chunk c) inside a K or V tile.
 __device__ __forceinline__ int tile_off(int row, int c) { return row * RB + 16 * (c ^ swz(row)); }
 
@@ -296,7 +305,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; e += 2) m = vmax(m, vmax(sc[kb][e], sc[kb][e + 1]));
-    return vmax(m, __shfl_xor(m, 32, 64)) * sl2;
+    return row_max(m) * sl2;
   };
 
   f32x16_t s_cur[KB], s_nxt[KB];
@@ -405,7 +414,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
       __builtin_amdgcn_sched_barrier(0);
     }
     if (next) {
-      mt_cur = vmax(mx, __shfl_xor(mx, 32, 64)) * sl2;
+      mt_cur = row_max(mx) * sl2;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_nxt[kb];
     }
@@ -449,7 +458,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
   if (ntiles > 0) step_any(ntiles - 1, false, false);
 
   // Epilogue: O = U / l (division after the V-matmul), LSE = m + log l.
-  const float l_row = l_part + __shfl_xor(l_part, 32, 64);
+  const float l_row = row_sum(l_part);
   if (row_ok) {
     const int qh = kvh * G + (r % G);
     const float inv = l_row > 0.f ? 1.f / l_row : 0.f;

@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the fused-attention hot path.  TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle for the fused hot paths (attention; RMSNorm + MatMul).  TEST
+INFRASTRUCTURE ONLY.
 
 Imported only by ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py``.  The product library never imports,
@@ -7,7 +8,11 @@ the product library.
 """
 from .attention import (attention, attention_rows, attention_split, combine,
                         split_partials, visible_mask)
-from .brute import brute_attention
+from .brute import brute_attention, brute_rmsnorm_matmul
+from .rmsnorm_matmul import (RMS_EPS, rmsnorm, rmsnorm_matmul, rmsnorm_matmul_combine,
+                             rmsnorm_matmul_partials, rmsnorm_matmul_split)
 
 __all__ = ["attention", "attention_rows", "attention_split", "combine",
-           "split_partials", "visible_mask", "brute_attention"]
+           "split_partials", "visible_mask", "brute_attention", "brute_rmsnorm_matmul",
+           "RMS_EPS", "rmsnorm", "rmsnorm_matmul", "rmsnorm_matmul_combine",
+           "rmsnorm_matmul_partials", "rmsnorm_matmul_split"]

@@ -53,3 +53,16 @@ def brute_attention(q, k, v, causal, scale, dv):
         out_o.append(o_b)
         out_l.append(l_b)
     return out_o, out_l
+
+
+def brute_rmsnorm_matmul(x, g, w, eps):
+    """RMSNorm then Matmul with explicit loops (Cleave §1, Fig. 1), for tiny
+    shapes: x [M][K], g [K], w [N][K] as nested lists.  Returns Y [M][N]."""
+    out = []
+    for row in x:
+        k = len(row)
+        mean_sq = math.fsum(v * v for v in row) / k
+        inv = 1.0 / math.sqrt(mean_sq + eps)
+        normed = [row[c] * inv * g[c] for c in range(k)]
+        out.append([math.fsum(normed[c] * wrow[c] for c in range(k)) for wrow in w])
+    return out

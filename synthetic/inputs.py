@@ -38,6 +38,13 @@ Recipe (stated once, used by tests, smoke and bench):
   are numbered by one ``default_rng(seed).permutation`` of the pool, so
   neighbouring pages of a request sit at unrelated places in the pool.
   Page-table entries a request does not use hold -7 (never read).
+* RMSNorm + MatMul (``make_rms_problem``): draw X [M, K] ~ N(0, 1), then the
+  gain g [K] = 1 + 0.1 N(0, 1), then W [N, K] ~ N(0, 1) / sqrt(K) (the usual
+  initialisation scale, so Y stays of order one), each fp32 and rounded to
+  bf16 like the attention inputs.  Workloads:
+  ``llama3_8b_rmsnorm_matmul_decode`` M=32 tokens, K=4096 (hidden size),
+  N=14336 (MLP projection width), eps 1e-5; ``tiny_rmsnorm_matmul`` M=5,
+  K=256, N=200.
 """
 from __future__ import annotations
 
@@ -48,7 +55,8 @@ from typing import Optional
 import numpy as np
 
 __all__ = ["Problem", "WORKLOADS", "workload", "make_problem", "to_bf16_exact",
-           "padded", "log_uniform_lengths", "page_layout"]
+           "padded", "log_uniform_lengths", "page_layout", "RmsProblem", "RMS_WORKLOADS",
+           "make_rms_problem", "rms_workload"]
 
 
 @dataclasses.dataclass
@@ -200,3 +208,51 @@ def page_layout(lens, page_size: int, seed: int, lcap: Optional[int] = None,
         table[b, :n] = perm[pos:pos + n]
         pos += n
     return table, total
+
+
+@dataclasses.dataclass
+class RmsProblem:
+    """RMSNorm(X) W^T as plain host arrays: x [M, K], g [K], w [N, K]."""
+    name: str
+    dtype: str
+    x: np.ndarray
+    g: np.ndarray
+    w: np.ndarray
+    eps: float
+    s: Optional[int] = None
+
+    @property
+    def m(self) -> int:
+        return int(self.x.shape[0])
+
+    @property
+    def k(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def n(self) -> int:
+        return int(self.w.shape[0])
+
+
+RMS_WORKLOADS = {
+    "tiny_rmsnorm_matmul": dict(m=5, k=256, n=200),
+    "llama3_8b_rmsnorm_matmul_decode": dict(m=32, k=4096, n=14336),
+}
+
+
+def make_rms_problem(*, name: str = "custom", dtype: str = "bf16", m: int, k: int, n: int,
+                     seed: int = 0, eps: float = 1e-5, s: Optional[int] = None) -> RmsProblem:
+    """Draw X, then g, then W (see the recipe above)."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
+    rng = np.random.default_rng(seed)
+    rnd = (lambda a: to_bf16_exact(a)) if dtype == "bf16" else (lambda a: a)
+    x = rnd(rng.standard_normal((m, k), dtype=np.float32))
+    g = rnd((1.0 + 0.1 * rng.standard_normal(k, dtype=np.float32)).astype(np.float32))
+    w = rnd((rng.standard_normal((n, k), dtype=np.float32) / np.float32(math.sqrt(k))).astype(np.float32))
+    return RmsProblem(name=name, dtype=dtype, x=x, g=g, w=w, eps=float(eps), s=s)
+
+
+def rms_workload(name: str, seed: int = 0) -> RmsProblem:
+    w = RMS_WORKLOADS[name]
+    return make_rms_problem(name=name, seed=seed, m=w["m"], k=w["k"], n=w["n"])

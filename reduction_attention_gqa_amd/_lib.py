@@ -25,7 +25,8 @@ ATTN_ERR_HIP = 4
 KERNEL_NAMES = {0: "generic", 1: "gqa_d128", 2: "mla"}
 
 EXPORTED = ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_decode", "attn_prefill",
-            "attn_status_str", "attn_last_error", "attn_version")
+            "attn_status_str", "attn_last_error", "attn_version", "rmsnorm_matmul_plan",
+            "rmsnorm_matmul")
 
 
 class AttnProblem(ctypes.Structure):
@@ -56,6 +57,23 @@ class AttnPlan(ctypes.Structure):
     ]
 
 
+class RmsProblem(ctypes.Structure):
+    """rmsnorm_matmul_problem (include/rmsnorm_matmul.h)."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32), ("m", ctypes.c_int32),
+        ("k", ctypes.c_int32), ("n", ctypes.c_int32), ("eps", ctypes.c_float),
+        ("x_stride", ctypes.c_int64), ("w_stride", ctypes.c_int64), ("y_stride", ctypes.c_int64),
+    ]
+
+
+class RmsConfig(ctypes.Structure):
+    """rmsnorm_matmul_config (include/rmsnorm_matmul.h)."""
+    _fields_ = [
+        ("s", ctypes.c_int32), ("k_chunk", ctypes.c_int32), ("grid", ctypes.c_uint32 * 3),
+        ("block", ctypes.c_uint32), ("ws_bytes", ctypes.c_uint64), ("problem_key", ctypes.c_uint64),
+    ]
+
+
 class AttnError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"[{status}] {msg}")
@@ -82,8 +100,11 @@ def load() -> ctypes.CDLL:
     lib.attn_decode.argtypes = [P, PL, V, V, V, V, ctypes.c_size_t, V, ctypes.c_size_t, V,
                                 ctypes.c_size_t, V, V, V]
     lib.attn_prefill.argtypes = [P, V, V, V, V, V, V]
+    RP, RC = ctypes.POINTER(RmsProblem), ctypes.POINTER(RmsConfig)
+    lib.rmsnorm_matmul_plan.argtypes = [RP, ctypes.c_int32, ctypes.c_int32, RC]
+    lib.rmsnorm_matmul.argtypes = [RP, RC, V, V, V, V, V, ctypes.c_size_t, V]
     for f in ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_decode",
-              "attn_prefill"):
+              "attn_prefill", "rmsnorm_matmul_plan", "rmsnorm_matmul"):
         getattr(lib, f).restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -287,3 +308,50 @@ def prefill(q, k, v, o, *, kv_lens=None, causal=False, scale=0.0, lse_out=None, 
 
 def default_scale(dqk: int) -> float:
     return 1.0 / math.sqrt(dqk)
+
+
+# ------------------------------------------------------ RMSNorm + MatMul
+
+def make_rms_problem(x, g, w, y, *, eps: float = 1e-5) -> RmsProblem:
+    """Describe X [m, k], g [k], W [n, k] and Y [m, n] (row strides taken from
+    the tensors; the last dimension must be contiguous)."""
+    if x.dim() != 2 or w.dim() != 2 or y.dim() != 2 or g.dim() != 1:
+        raise ValueError("x, w, y must be 2-D and g 1-D")
+    for name, t in (("x", x), ("w", w), ("y", y), ("g", g)):
+        if t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError(f"{name}: the last dimension must be contiguous")
+    if g.dtype != x.dtype or w.dtype != x.dtype:
+        raise TypeError("x, g and w must share one dtype")
+    p = RmsProblem()
+    p.dtype = _dtype_code(x)
+    p.y_dtype = _dtype_code(y)
+    p.m, p.k = int(x.shape[0]), int(x.shape[1])
+    p.n = int(w.shape[0])
+    if int(w.shape[1]) != p.k or int(g.shape[0]) != p.k or tuple(y.shape) != (p.m, p.n):
+        raise ValueError("shapes: x [m, k], g [k], w [n, k], y [m, n]")
+    p.eps = float(eps)
+    p.x_stride, p.w_stride, p.y_stride = x.stride(0), w.stride(0), y.stride(0)
+    return p
+
+
+def rmsnorm_matmul_plan(problem: RmsProblem, s_request: int = 0, num_cus: int = 0) -> RmsConfig:
+    lib = load()
+    cfg = RmsConfig()
+    _check(lib.rmsnorm_matmul_plan(ctypes.byref(problem), int(s_request), int(num_cus),
+                                   ctypes.byref(cfg)))
+    return cfg
+
+
+def rms_workspace(plan: RmsConfig, device):
+    """The fp32 workspace a plan asks for (torch owns the memory), or None."""
+    import torch
+    if plan.ws_bytes == 0:
+        return None
+    return torch.empty(plan.ws_bytes // 4, dtype=torch.float32, device=device)
+
+
+def rmsnorm_matmul(problem: RmsProblem, plan: RmsConfig, x, g, w, y, ws=None, stream=None) -> None:
+    lib = load()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.rmsnorm_matmul(ctypes.byref(problem), ctypes.byref(plan), _ptr(x), _ptr(g), _ptr(w),
+                              _ptr(y), _ptr(ws), nbytes, _stream(stream)))

@@ -25,6 +25,7 @@ SOURCES = [
     "kernels/decode_gqa_d128.hip",
     "kernels/prefill_d128.hip",
     "kernels/decode_mla.hip",
+    "kernels/rmsnorm_matmul.hip",
 ]
 
 # Packed-fp32 VALU forms are switched off for all device code.

@@ -12,6 +12,7 @@
 
 #include "attn_internal.hpp"
 #include "attn_mi355x.h"
+#include "rmsnorm_matmul.h"
 
 namespace attn {
 namespace {
@@ -503,6 +504,124 @@ int attn_prefill(const attn_problem* problem, const void* q, const void* k, cons
   if (row_tiles > 65535) return fail(ATTN_ERR_UNSUPPORTED, "too many query rows per KV head");
   const dim3 grid(1, row_tiles, (unsigned)((int64_t)p->batch * p->kv_heads));
   return hip_status(launch_generic(kp, grid, dim3(kGenericBlock), s), "generic prefill launch");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------ RMSNorm + MatMul
+
+namespace attn {
+namespace {
+
+constexpr int kRmsTileN = 64;   // weight rows per split-kernel workgroup
+constexpr int kRmsTileM = 32;   // tokens per split-kernel workgroup
+constexpr int kRmsBlock = 256;
+
+int check_rms(const rmsnorm_matmul_problem* p) {
+  if (!p) return fail(ATTN_ERR_ARG, "problem is NULL");
+  if ((p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) ||
+      (p->y_dtype != ATTN_F32 && p->y_dtype != ATTN_BF16))
+    return fail(ATTN_ERR_ARG, "dtype/y_dtype must be ATTN_F32 or ATTN_BF16");
+  if (p->m < 0 || p->n < 0) return fail(ATTN_ERR_ARG, "m and n must be >= 0");
+  if (p->k < 1) return fail(ATTN_ERR_ARG, "k must be >= 1");
+  if (!std::isfinite(p->eps) || p->eps < 0.f) return fail(ATTN_ERR_ARG, "eps must be finite and >= 0");
+  if (p->x_stride < p->k || p->w_stride < p->k || p->y_stride < p->n)
+    return fail(ATTN_ERR_ARG, "row strides must cover the rows");
+  if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "only bf16 X, g and W are supported");
+  if (p->k % 8 != 0) return fail(ATTN_ERR_UNSUPPORTED, "k must be a multiple of 8");
+  if ((p->x_stride | p->w_stride) & 7)
+    return fail(ATTN_ERR_UNSUPPORTED, "row strides of X and W must be multiples of 8 elements");
+  // 32-bit buffer offsets: a workgroup's 64 weight rows and 32 tokens.
+  if ((int64_t)kRmsTileN * p->w_stride * 2 >= (1ll << 31) ||
+      (int64_t)kRmsTileM * p->x_stride * 2 >= (1ll << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "row strides too large");
+  return ATTN_OK;
+}
+
+uint64_t rms_key(const rmsnorm_matmul_problem* p) {
+  const int32_t f[] = {0x524d53, p->dtype, p->m, p->k, p->n};
+  uint64_t h = 1469598103934665603ull;
+  for (int32_t x : f)
+    for (int s = 0; s < 32; s += 8) {
+      h ^= (uint64_t)((x >> s) & 0xff);
+      h *= 1099511628211ull;
+    }
+  return h | 1ull;
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" {
+
+int rmsnorm_matmul_plan(const rmsnorm_matmul_problem* problem, int32_t s_request, int32_t num_cus,
+                        rmsnorm_matmul_config* out) {
+  g_err[0] = 0;
+  if (!out) return fail(ATTN_ERR_ARG, "plan output is NULL");
+  std::memset(out, 0, sizeof(*out));
+  if (int st = check_rms(problem)) return st;
+  const rmsnorm_matmul_problem* p = problem;
+  int cus = num_cus;
+  if (cus <= 0 && device_cu_count(&cus) != 0)
+    return fail(ATTN_ERR_HIP, "cannot query the compute-unit count of the current device");
+  const int64_t steps = ceil_div(p->k, 32);   // 32-column k-steps
+  const int64_t tiles = ceil_div(p->n, kRmsTileN) * ceil_div(p->m, kRmsTileM);
+  int64_t s = 1;
+  if (s_request > 0) {
+    s = std::min<int64_t>(s_request, steps);
+  } else if (tiles > 0) {
+    // About three workgroups per compute unit, at least four k-steps per part.
+    s = ceil_div((int64_t)cus * 3, tiles);
+    s = std::max<int64_t>(1, std::min<int64_t>(s, steps / 4));
+  }
+  const int64_t chunk_steps = ceil_div(steps, s);
+  s = ceil_div(steps, chunk_steps);
+  if (s > 65535 || ceil_div(p->m, kRmsTileM) > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "too many parts or token tiles for the grid");
+  out->s = (int32_t)s;
+  out->k_chunk = (int32_t)(chunk_steps * 32);
+  out->grid[0] = (uint32_t)ceil_div(p->n, kRmsTileN);
+  out->grid[1] = (uint32_t)s;
+  out->grid[2] = (uint32_t)ceil_div(p->m, kRmsTileM);
+  out->block = kRmsBlock;
+  out->ws_bytes = s > 1 ? (uint64_t)s * p->m * ((uint64_t)p->n + 1) * sizeof(float) : 0;
+  out->problem_key = rms_key(p);
+  return ATTN_OK;
+}
+
+int rmsnorm_matmul(const rmsnorm_matmul_problem* problem, const rmsnorm_matmul_config* plan,
+                   const void* x, const void* g, const void* w, void* y, float* ws,
+                   size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  if (int st = check_rms(problem)) return st;
+  const rmsnorm_matmul_problem* p = problem;
+  if (!plan) return fail(ATTN_ERR_ARG, "plan is NULL");
+  if (plan->problem_key != rms_key(p)) return fail(ATTN_ERR_ARG, "plan was made for a different problem");
+  if (plan->s < 1 || plan->k_chunk < 32 || plan->k_chunk % 32 ||
+      (int64_t)plan->s * plan->k_chunk < p->k || (int64_t)(plan->s - 1) * plan->k_chunk >= p->k)
+    return fail(ATTN_ERR_ARG, "corrupt plan");
+  if (p->m == 0 || p->n == 0) return ATTN_OK;
+  if (!x || !g || !w || !y) return fail(ATTN_ERR_ARG, "x, g, w and y must not be NULL");
+  if (!aligned16(x) || !aligned16(g) || !aligned16(w))
+    return fail(ATTN_ERR_UNSUPPORTED, "x, g and w must be 16-byte aligned");
+  const uint64_t need = plan->s > 1 ? (uint64_t)plan->s * p->m * ((uint64_t)p->n + 1) * sizeof(float) : 0;
+  if (need && (!ws || ws_bytes < need))
+    return fail(ATTN_ERR_WORKSPACE, "workspace too small: need %llu bytes", (unsigned long long)need);
+  if (need && (reinterpret_cast<uintptr_t>(ws) & 15))
+    return fail(ATTN_ERR_ARG, "workspace must be 16-byte aligned");
+  RmsParams k;
+  std::memset(&k, 0, sizeof(k));
+  k.x = x; k.g = g; k.w = w; k.y = y;
+  k.ws_u = plan->s > 1 ? ws : nullptr;
+  k.ws_ssq = plan->s > 1 ? ws + (int64_t)plan->s * p->m * p->n : nullptr;
+  k.x_row = p->x_stride; k.w_row = p->w_stride; k.y_row = p->y_stride;
+  k.M = p->m; k.K = p->k; k.N = p->n;
+  k.s = plan->s;
+  k.k_chunk = plan->k_chunk;
+  k.y_bf16 = p->y_dtype == ATTN_BF16;
+  k.eps = p->eps;
+  return hip_status(launch_rmsnorm_matmul(k, reinterpret_cast<hipStream_t>(stream)),
+                    "rmsnorm_matmul launch");
 }
 
 }  // extern "C"

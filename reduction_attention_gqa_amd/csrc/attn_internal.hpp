@@ -44,6 +44,24 @@ struct KParams {
   float scale_log2;     // tau * log2(e): scores are kept in base-2 units
 };
 
+// RMSNorm followed by a MatMul: X [M, K], g [K], W [N, K], Y [M, N] (bf16
+// inputs); row strides in elements.
+struct RmsParams {
+  const void* x;
+  const void* g;
+  const void* w;
+  void* y;
+  float* ws_u;          // split partials [s, M, N] (s > 1)
+  float* ws_ssq;        // split sums of squares [s, M] (s > 1)
+  int64_t x_row, w_row, y_row;
+  int32_t M, K, N;
+  int32_t s;            // K splits
+  int32_t k_chunk;      // columns per split, a multiple of 32
+  int32_t y_bf16;
+  float eps;
+};
+hipError_t launch_rmsnorm_matmul(const RmsParams& p, hipStream_t s);
+
 // Launchers (one per kernel family).  Each returns a hipError_t.
 hipError_t launch_generic(const KParams& p, dim3 grid, dim3 block, hipStream_t s);
 hipError_t launch_combine(const KParams& p, hipStream_t s);

@@ -1,0 +1,211 @@
+// RMSNorm followed by a MatMul, Y = RMSNorm(X) W^T, in the rewritten form of
+// the Cleave paper (§1, Fig. 1): RMSNorm's row scale is moved after the
+// Matmul, so the Matmul runs on the raw input and the rows' sums of squares
+// are accumulated from the same X tiles in the same loop (the two reductions
+// fused horizontally); the scale 1 / sqrt(mean(x^2) + eps) is applied to the
+// finished dot products and the normalised input never exists.  With few
+// output tiles (decode: a few tokens) the K axis is split (Cleave §2.2
+// "Split-K"): each split writes its partial dot products and sums of squares,
+// and a combine kernel adds them up and applies the row scale.
+//
+// Layout: X [M, K], g [K], W [N, K] (linear-layer weights), Y [M, N], row
+// strides in elements, bf16 inputs.  A workgroup is four waves; wave w owns
+// the 16 weight rows n0 + 16w .. + 15 of the workgroup's 64 and up to 32
+// tokens (two MFMA column groups), over the split's K range:
+//   U^T[16 x 16] += W[16 x 32] (X * g)^T[32 x 16]     16x16x32 bf16 MFMA
+// W streams from HBM straight into the A operand (16 bytes per lane, four
+// k-steps in flight); X and g come through the caches (a few KB, shared by all
+// workgroups).  x * g is exact in fp32 (two 8-bit significands); it enters the
+// MFMA as a bf16 pair hi + lo, so the gain costs no precision.
+#include "../attn_internal.hpp"
+#include "common.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int NW = 4;      // waves per workgroup
+constexpr int NBUF = 4;    // k-steps in flight per wave
+constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every range: loads read zero
+
+struct Frag {
+  i32x4_t w;
+  i32x4_t x[2];
+  i32x4_t g;
+};
+
+// Y[m, n .. n + 3] (columns past N are skipped), bf16 (round to nearest
+// even) or fp32; one vector store when the address allows.
+__device__ __forceinline__ void store_row4(const RmsParams& p, int m, int n, const f32x4_t& v) {
+  if (p.y_bf16) {
+    uint16_t* yp = reinterpret_cast<uint16_t*>(p.y) + (int64_t)m * p.y_row + n;
+    if (n + 3 < p.N && (reinterpret_cast<uintptr_t>(yp) & 7) == 0) {
+      uint2 pk;
+      pk.x = pack_bf16x2(v[0], v[1]);
+      pk.y = pack_bf16x2(v[2], v[3]);
+      *reinterpret_cast<uint2*>(yp) = pk;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n + i < p.N) yp[i] = (uint16_t)f32_to_bf16_bits(v[i]);
+    }
+  } else {
+    float* yp = reinterpret_cast<float*>(p.y) + (int64_t)m * p.y_row + n;
+    if (n + 3 < p.N && (reinterpret_cast<uintptr_t>(yp) & 15) == 0) {
+      *reinterpret_cast<f32x4_t*>(yp) = v;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n + i < p.N) yp[i] = v[i];
+    }
+  }
+}
+
+__global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams p) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15;   // MFMA row (weight row) / column (token) index
+  const int kg = lane >> 4;  // 8-column group of a 32-column k-step
+  const int n_wg = blockIdx.x * (NW * 16);
+  const int j = blockIdx.y;
+  const int m0 = blockIdx.z * 32;
+  const int lo = j * p.k_chunk;
+  const int hi = min(lo + p.k_chunk, p.K);
+
+  // Buffer ranges end at the last valid weight row / token, so rows past N or
+  // M read as zero.  Offsets stay 32-bit: a workgroup's 64 rows, 32 tokens.
+  const int wrows = min(NW * 16, p.N - n_wg);
+  const int xrows = min(32, p.M - m0);
+  const uint16_t* wp = reinterpret_cast<const uint16_t*>(p.w) + (int64_t)n_wg * p.w_row;
+  const uint16_t* xp = reinterpret_cast<const uint16_t*>(p.x) + (int64_t)m0 * p.x_row;
+  const uint32_t wst = (uint32_t)(p.w_row * 2), xst = (uint32_t)(p.x_row * 2);
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wp, (uint32_t)wrows * wst);
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xp, (uint32_t)xrows * xst);
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc(p.g, (uint32_t)p.K * 2);
+  const uint32_t w_lane = (uint32_t)(16 * w + r) * wst + 16u * kg;
+  const uint32_t x_lane0 = (uint32_t)r * xst + 16u * kg;
+  const uint32_t x_lane1 = (uint32_t)(16 + r) * xst + 16u * kg;
+
+  // k-step at column k: this lane's 8 columns k + 8 kg .. + 7; columns past
+  // the split or past K read as zero without a memory access.
+  auto load = [&](Frag& f, int k) {
+    const uint32_t oob = (k < hi && k + 8 * kg < p.K) ? 0u : kOob;
+    const uint32_t kb = (uint32_t)k * 2;
+    f.w = buf_load16(wrs, (w_lane + kb) | oob);
+    f.x[0] = buf_load16(xrs, (x_lane0 + kb) | oob);
+    f.x[1] = buf_load16(xrs, (x_lane1 + kb) | oob);
+    f.g = buf_load16(grs, (16u * kg + kb) | oob);
+  };
+
+  f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float ssq[2] = {0.f, 0.f};
+
+  auto compute = [&](const Frag& f) {
+    float gv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      gv[2 * e] = bf16_lo((uint32_t)f.g[e]);
+      gv[2 * e + 1] = bf16_hi((uint32_t)f.g[e]);
+    }
+    const bf16x8_t wa = as_bf16x8(f.w);
+#pragma unroll
+    for (int mg = 0; mg < 2; ++mg) {
+      i32x4_t h, l;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = bf16_lo((uint32_t)f.x[mg][e]), x1 = bf16_hi((uint32_t)f.x[mg][e]);
+        ssq[mg] = __builtin_fmaf(x0, x0, ssq[mg]);
+        ssq[mg] = __builtin_fmaf(x1, x1, ssq[mg]);
+        const float p0 = x0 * gv[2 * e], p1 = x1 * gv[2 * e + 1];  // exact
+        const uint32_t hp = pack_bf16x2(p0, p1);
+        h[e] = (int)hp;
+        l[e] = (int)pack_bf16x2(p0 - bf16_lo(hp), p1 - bf16_hi(hp));  // exact residuals
+      }
+      acc[mg] = mfma16x16x32(wa, as_bf16x8(h), acc[mg]);
+      acc[mg] = mfma16x16x32(wa, as_bf16x8(l), acc[mg]);
+    }
+  };
+
+  Frag f[NBUF];
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) load(f[i], lo + 32 * i);
+  for (int k0 = lo; k0 < hi; k0 += 32 * NBUF) {
+#pragma unroll
+    for (int i = 0; i < NBUF; ++i) {
+      load(f[(i + NBUF - 1) % NBUF], k0 + 32 * (i + NBUF - 1));
+      __builtin_amdgcn_sched_barrier(0);
+      if (k0 + 32 * i < hi) compute(f[i]);
+    }
+  }
+
+  // Sums of squares of token r over the split: add the four column groups.
+#pragma unroll
+  for (int mg = 0; mg < 2; ++mg) {
+    ssq[mg] += __shfl_xor(ssq[mg], 16, 64);
+    ssq[mg] += __shfl_xor(ssq[mg], 32, 64);
+  }
+
+  // Lane holds U^T[weight row 4 kg + i][token r] of each column group.
+  const int n_lane = n_wg + 16 * w + 4 * kg;
+#pragma unroll
+  for (int mg = 0; mg < 2; ++mg) {
+    const int m = m0 + 16 * mg + r;
+    if (m >= p.M) continue;
+    if (p.s == 1) {
+      // The whole K range is here: apply the row scale after the Matmul.
+      const float scale = 1.0f / sqrtf(ssq[mg] / (float)p.K + p.eps);
+      store_row4(p, m, n_lane, acc[mg] * scale);
+    } else {
+      float* dst = p.ws_u + ((int64_t)j * p.M + m) * p.N + n_lane;
+      if (n_lane + 3 < p.N && (p.N & 3) == 0) {
+        *reinterpret_cast<f32x4_t*>(dst) = acc[mg];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n_lane + i < p.N) dst[i] = acc[mg][i];
+      }
+      if (blockIdx.x == 0 && w == 0 && kg == 0) p.ws_ssq[(int64_t)j * p.M + m] = ssq[mg];
+    }
+  }
+}
+
+// Combine: Y[m, n] = (sum_j U_j[m, n]) / sqrt(sum_j SSQ_j[m] / K + eps).
+// Thread t handles four consecutive n of one row.
+__global__ __launch_bounds__(256) void rmsnorm_matmul_combine_kernel(RmsParams p) {
+  const int64_t quads = (int64_t)(p.N + 3) / 4;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= quads * p.M) return;
+  const int m = (int)(t / quads);
+  const int n = (int)(t - (int64_t)m * quads) * 4;
+  float ssq = 0.f;
+  for (int j = 0; j < p.s; ++j) ssq += p.ws_ssq[(int64_t)j * p.M + m];
+  const float scale = 1.0f / sqrtf(ssq / (float)p.K + p.eps);
+  f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < p.s; ++j) {
+    const float* src = p.ws_u + ((int64_t)j * p.M + m) * p.N + n;
+    if (n + 3 < p.N && (p.N & 3) == 0) {
+      u += *reinterpret_cast<const f32x4_t*>(src);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n + i < p.N) u[i] += src[i];
+    }
+  }
+  store_row4(p, m, n, u * scale);
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm_matmul(const RmsParams& p, hipStream_t s) {
+  if (p.M == 0 || p.N == 0) return hipSuccess;
+  const dim3 grid((unsigned)((p.N + NW * 16 - 1) / (NW * 16)), (unsigned)p.s,
+                  (unsigned)((p.M + 31) / 32));
+  hipLaunchKernelGGL(rmsnorm_matmul_split_kernel, grid, dim3(NW * 64), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.s == 1) return e;
+  const int64_t threads = (int64_t)p.M * ((p.N + 3) / 4);
+  hipLaunchKernelGGL(rmsnorm_matmul_combine_kernel, dim3((unsigned)((threads + 255) / 256)),
+                     dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace attn

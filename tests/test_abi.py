@@ -27,10 +27,15 @@ def lib():
     return ra.load()
 
 
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
+
+
 def _declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(attn_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?((?:attn|rmsnorm)_\w+)\s*\(", text,
+                                 flags=re.M)))
 
 
 def test_header_declares_the_entry_points():
@@ -63,6 +68,7 @@ def _c_layout(tmp_path, struct, fields):
     lines += [f'printf("{f} %zu\\n", offsetof({struct}, {f}));' for f in fields]
     src = tmp_path / "layout.c"
     src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"attn_mi355x.h\"\n"
+                   "#include \"rmsnorm_matmul.h\"\n"
                    "int main(void) {\n" + "\n".join(lines) + "\nreturn 0;\n}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
@@ -71,7 +77,9 @@ def _c_layout(tmp_path, struct, fields):
     return {k: int(v) for k, v in (line.split() for line in out.splitlines())}
 
 
-@pytest.mark.parametrize("py,c", [(_lib.AttnProblem, "attn_problem"), (_lib.AttnPlan, "attn_plan")])
+@pytest.mark.parametrize("py,c", [(_lib.AttnProblem, "attn_problem"), (_lib.AttnPlan, "attn_plan"),
+                                  (_lib.RmsProblem, "rmsnorm_matmul_problem"),
+                                  (_lib.RmsConfig, "rmsnorm_matmul_config")])
 def test_struct_layout_matches_c(tmp_path, py, c):
     names = [f[0] for f in py._fields_]
     got = _c_layout(tmp_path, c, names)
@@ -395,3 +403,87 @@ def test_mla_layout_family_and_split_bound(lib, layout, kernel):
         assert st == 0 and plan.kernel == kernel
         if kernel == 2 and layout.startswith("page"):
             assert (plan.chunk + ps - 1) // ps + 1 <= 4096
+
+
+# ------------------------------------------------------ RMSNorm + MatMul
+
+def rms_problem(**kw):
+    f = dict(dtype=ra.ATTN_BF16, y_dtype=ra.ATTN_BF16, m=32, k=4096, n=14336, eps=1e-5)
+    f.update(kw)
+    p = _lib.RmsProblem()
+    for k, v in f.items():
+        setattr(p, k, v)
+    p.x_stride = kw.get("x_stride", p.k)
+    p.w_stride = kw.get("w_stride", p.k)
+    p.y_stride = kw.get("y_stride", p.n)
+    return p
+
+
+def rms_plan(lib, p, s_request=0, num_cus=256):
+    cfg = _lib.RmsConfig()
+    st = lib.rmsnorm_matmul_plan(ctypes.byref(p) if p is not None else None, s_request, num_cus,
+                                 ctypes.byref(cfg))
+    return st, cfg
+
+
+@pytest.mark.parametrize("edit,code", [
+    (dict(m=-1), ra.ATTN_ERR_ARG),
+    (dict(k=0), ra.ATTN_ERR_ARG),
+    (dict(eps=float("nan")), ra.ATTN_ERR_ARG),
+    (dict(eps=-1.0), ra.ATTN_ERR_ARG),
+    (dict(dtype=5), ra.ATTN_ERR_ARG),
+    (dict(x_stride=100), ra.ATTN_ERR_ARG),          # shorter than a row
+    (dict(dtype=ra.ATTN_F32), ra.ATTN_ERR_UNSUPPORTED),
+    (dict(k=4100, x_stride=4100, w_stride=4100), ra.ATTN_ERR_UNSUPPORTED),  # k % 8
+    (dict(w_stride=4100), ra.ATTN_ERR_UNSUPPORTED),  # stride % 8
+])
+def test_rms_invalid_problem(lib, edit, code):
+    p = rms_problem(**edit)
+    st, _ = rms_plan(lib, p)
+    assert st == code and lib.attn_last_error()
+    fake = ctypes.c_void_p(0x1000)
+    cfg = _lib.RmsConfig()
+    assert lib.rmsnorm_matmul(ctypes.byref(p), ctypes.byref(cfg), fake, fake, fake, fake, fake,
+                              1 << 30, None) == code
+
+
+@pytest.mark.parametrize("m,k,n,s_req", [(32, 4096, 14336, 0), (32, 4096, 4096, 0), (1, 4096, 6144, 0),
+                                         (300, 4096, 4096, 0), (5, 256, 200, 0), (5, 264, 70, 0),
+                                         (32, 4096, 14336, 3), (32, 4096, 14336, 1000)])
+def test_rms_plan_invariants(lib, m, k, n, s_req):
+    st, cfg = rms_plan(lib, rms_problem(m=m, k=k, n=n, x_stride=k, w_stride=k, y_stride=n), s_req)
+    assert st == 0
+    steps = -(-k // 32)
+    assert cfg.k_chunk % 32 == 0 and cfg.s >= 1
+    assert cfg.s * cfg.k_chunk >= k and (cfg.s - 1) * cfg.k_chunk < k   # no empty part
+    assert cfg.s <= steps
+    if s_req > 0:
+        assert cfg.s <= s_req
+    assert tuple(cfg.grid) == (-(-n // 64), cfg.s, -(-m // 32)) and cfg.block == 256
+    assert cfg.ws_bytes == (cfg.s * m * (n + 1) * 4 if cfg.s > 1 else 0)
+
+
+def test_rms_workspace_and_plan_checks(lib):
+    p = rms_problem()
+    st, cfg = rms_plan(lib, p, 4)
+    assert st == 0 and cfg.s == 4
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.rmsnorm_matmul(ctypes.byref(p), ctypes.byref(cfg), fake, fake, fake, fake, fake,
+                              cfg.ws_bytes - 4, None) == ra.ATTN_ERR_WORKSPACE
+    assert lib.rmsnorm_matmul(ctypes.byref(p), ctypes.byref(cfg), fake, fake, fake, fake, None,
+                              0, None) == ra.ATTN_ERR_WORKSPACE
+    other = rms_problem(n=4096, y_stride=4096)
+    assert lib.rmsnorm_matmul(ctypes.byref(other), ctypes.byref(cfg), fake, fake, fake, fake, fake,
+                              1 << 40, None) == ra.ATTN_ERR_ARG
+    bad = _lib.RmsConfig.from_buffer_copy(cfg)
+    bad.k_chunk = 100                                     # not a multiple of 32
+    assert lib.rmsnorm_matmul(ctypes.byref(p), ctypes.byref(bad), fake, fake, fake, fake, fake,
+                              1 << 40, None) == ra.ATTN_ERR_ARG
+    unaligned = ctypes.c_void_p(0x1008)
+    assert lib.rmsnorm_matmul(ctypes.byref(p), ctypes.byref(cfg), unaligned, fake, fake, fake, fake,
+                              1 << 40, None) == ra.ATTN_ERR_UNSUPPORTED
+    empty = rms_problem(m=0)
+    st, cfg0 = rms_plan(lib, empty)
+    assert st == 0
+    assert lib.rmsnorm_matmul(ctypes.byref(empty), ctypes.byref(cfg0), None, None, None, None, None,
+                              0, None) == 0

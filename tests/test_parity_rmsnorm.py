@@ -1,0 +1,102 @@
+"""GPU parity of RMSNorm followed by a MatMul against the fp64 oracle, through
+the C ABI.
+
+The kernel computes the rewritten graph (Cleave §1, Fig. 1: the Matmul on the
+raw input with the rows' sums of squares beside it, the row scale applied
+last), split over K (Cleave §2.2 "Split-K") when the plan says so; the oracle
+is the definition (normalise, then multiply).  Tolerance as for the attention
+path with bf16 inputs and fp32 accumulation: max abs 1e-2, mean abs 1e-3 on the
+fp32 output, and the bf16 output must be the round-to-nearest-even of the fp32
+one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import BF16_MAX, BF16_MEAN, DEV, assert_close
+import reduction_attention_gqa_amd as ra
+from oracle import rmsnorm_matmul
+from synthetic.inputs import make_rms_problem, rms_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a, stride=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(torch.bfloat16)
+    if stride is None or stride == a.shape[-1]:
+        return t
+    wide = torch.full((a.shape[0], stride), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wide[:, : a.shape[1]] = t
+    return wide[:, : a.shape[1]]
+
+
+def _run(p, s_request=0, y_dtype=torch.float32, x_stride=None, w_stride=None):
+    x, w = _dev(p.x, x_stride), _dev(p.w, w_stride)
+    g = _dev(p.g[None, :])[0]
+    y = torch.full((p.m, p.n), float("nan"), dtype=y_dtype, device=DEV)
+    prob = ra.make_rms_problem(x, g, w, y, eps=p.eps)
+    plan = ra.rmsnorm_matmul_plan(prob, s_request)
+    ws = ra.rms_workspace(plan, DEV)
+    ra.rmsnorm_matmul(prob, plan, x, g, w, y, ws)
+    torch.cuda.synchronize()
+    return y, plan
+
+
+def _check(name, p, **kw):
+    want = rmsnorm_matmul(p.x, p.g, p.w, p.eps)
+    y32, plan = _run(p, **kw)
+    assert_close(f"{name} (s={plan.s})", y32.cpu().numpy().astype(np.float64), want, BF16_MAX,
+                 BF16_MEAN)
+    y16, _ = _run(p, y_dtype=torch.bfloat16, **kw)
+    assert torch.equal(y16, y32.to(torch.bfloat16)), f"{name}: bf16 Y != RNE(fp32 Y)"
+    return plan
+
+
+@pytest.mark.parametrize("s", [0, 1, 2, 3, 8])
+def test_tiny_split_counts(s):
+    # n = 200 ends inside a 64-row tile; several splits over k = 256.
+    p = rms_workload("tiny_rmsnorm_matmul")
+    plan = _check(f"tiny s={s}", p, s_request=s)
+    if s:
+        assert plan.s == s
+
+
+@pytest.mark.parametrize("s", [1, 4])
+def test_ragged_tails(s):
+    # m = 33 spans two 32-token tiles; k = 264 ends mid k-step; n = 70.
+    p = make_rms_problem(m=33, k=264, n=70, seed=31)
+    _check(f"tails s={s}", p, s_request=s)
+
+
+def test_strided_rows():
+    # X and W rows padded (NaN beyond k): only the first k columns may be read.
+    p = make_rms_problem(m=7, k=512, n=130, seed=32)
+    _check("strided", p, s_request=3, x_stride=520, w_stride=640)
+
+
+def test_zero_and_tiny_rows():
+    # A zero row gives Y = 0 (0 / sqrt(eps)); a tiny row is damped by eps.
+    p = make_rms_problem(m=4, k=128, n=64, seed=33)
+    p.x[1] = 0.0
+    p.x[2] = (p.x[2] * np.float32(1e-3)).astype(np.float32)
+    import synthetic.inputs as si
+    p.x[2] = si.to_bf16_exact(p.x[2])
+    y, _ = _run(p, s_request=2)
+    assert torch.all(y[1] == 0)
+    _check("zero/tiny rows", p, s_request=2)
+
+
+def test_full_size_decode():
+    # The Llama-3 8B decode shape (32 tokens, K = 4096, N = 14336) with the
+    # planner's split; every output checked.
+    p = rms_workload("llama3_8b_rmsnorm_matmul_decode")
+    plan = _check("llama3_8b decode", p)
+    assert plan.s >= 1
+
+
+def test_one_part_equals_many_parts():
+    # The split and unsplit paths agree to fp32 rounding (different summation order).
+    p = make_rms_problem(m=16, k=1024, n=256, seed=34)
+    y1, _ = _run(p, s_request=1)
+    y8, _ = _run(p, s_request=8)
+    np.testing.assert_allclose(y1.cpu().numpy(), y8.cpu().numpy(), rtol=0, atol=2e-5)

@@ -11,6 +11,10 @@ Default run (N = 1):
     is timed beside it as an ablation.
   * prefill: causal GQA prefill (B=4, L=4096, 32/8 heads, D=128, bf16) in
     algorithmic TFLOP/s; one step = one fused prefill launch.
+  * rmsnorm_matmul: RMSNorm followed by a MatMul on the Llama-3 8B decode
+    shape (32 tokens, K=4096, N=14336, bf16) in algorithmic HBM GB/s (W, X, g
+    read once, Y written once); one step = one call (split launch, plus the
+    combine launch when K is split).
   * roofline of the dominant kernel of each (per-launch HIP-event times on the
     launch stream), the split-off (s = 1) ablation, and the fp64 oracle timed
     on the host cores over a bounded sample of the same workload.
@@ -28,7 +32,7 @@ Algorithmic work: bytes = unique Q, K and V reads + O write (the split
 workspace is not counted); flops = 2 (Dqk + Dv) per visible (query, key) pair.
 
 --workload NAME benches one of the other named workloads instead (its own
-JSON line, decode or prefill by shape).
+JSON line, decode or prefill by shape, or llama3_8b_rmsnorm_matmul_decode).
 """
 from __future__ import annotations
 
@@ -185,6 +189,8 @@ KERNEL_OF = {
     "mla": ("decode_mla_kernel", "reduction_attention_gqa_amd/csrc/kernels/decode_mla.hip"),
     "generic": ("generic", "reduction_attention_gqa_amd/csrc/kernels/generic.hip"),
     "prefill": ("prefill_d128_kernel", "reduction_attention_gqa_amd/csrc/kernels/prefill_d128.hip"),
+    "rms": ("rmsnorm_matmul_split_kernel",
+            "reduction_attention_gqa_amd/csrc/kernels/rmsnorm_matmul.hip"),
 }
 
 
@@ -356,6 +362,95 @@ def time_prefill(prob, steps, warmup, dev):
     return dict(wall_s=wall, kernel_ms=k_ms, bytes=(qb, kvb, ob))
 
 
+def rms_bytes(prob):
+    """Algorithmic bytes of RMSNorm + MatMul: W, X and g read once, Y written once (bf16)."""
+    return (prob.n * prob.k + prob.m * prob.k + prob.k) * 2, prob.m * prob.n * 2
+
+
+def time_rms(prob, steps, warmup, dev, s_request=0):
+    """Time `steps` RMSNorm + MatMul calls (the split launch and, with s > 1, the
+    combine launch), rotating copies of W so no step finds it in the Infinity Cache."""
+    import torch
+    import reduction_attention_gqa_amd as ra
+    rd, wr = rms_bytes(prob)
+    n_copies = n_copies_for(rd + wr)
+    bf = torch.bfloat16
+    x = torch.from_numpy(prob.x).to(dev).to(bf)
+    g = torch.from_numpy(prob.g).to(dev).to(bf)
+    w0 = torch.from_numpy(prob.w).to(dev).to(bf)
+    ws_copies = [w0] + [w0.clone() for _ in range(n_copies - 1)]
+    y = torch.empty((prob.m, prob.n), dtype=bf, device=dev)
+    prob_c = ra.make_rms_problem(x, g, w0, y, eps=prob.eps)
+    plan = ra.rmsnorm_matmul_plan(prob_c, s_request)
+    ws = ra.rms_workspace(plan, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        w = ws_copies[i % n_copies]
+        if ev is not None:
+            ev[0].record(stream)
+        ra.rmsnorm_matmul(prob_c, ra.rmsnorm_matmul_plan(prob_c, s_request), x, g, w, y, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    call_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    del ws_copies
+    return dict(plan=plan, wall_s=wall, call_ms=call_ms, bytes=(rd, wr))
+
+
+def rms_record(prob, r, steps):
+    rd, wr = r["bytes"]
+    total = rd + wr
+    ms_step = r["wall_s"] * 1e3 / steps
+    call = stats(r["call_ms"])
+    achieved = total / (call["mean_ms"] * 1e-3) / 1e9
+    plan = r["plan"]
+    return {
+        "value": round(total / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "ms_per_step": round(ms_step, 5),
+        "config": {"workload": prob.name, "m": prob.m, "k": prob.k, "n": prob.n, "eps": prob.eps,
+                   "split_s": plan.s, "k_chunk": plan.k_chunk},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/"
+                                            "rmsnorm_matmul.hip", f"rms:{prob.name}"),
+                     "kernel": ("RMSNorm+MatMul kernel, one launch" if plan.s == 1 else
+                                "RMSNorm+MatMul split kernel + combine kernel (timed together)"),
+                     "algorithmic_bytes_per_launch": total, "launch_ms": call}}
+
+
+def oracle_rms_baseline(prob):
+    """The fp64 oracle on the whole RMSNorm + MatMul workload (one call)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import rmsnorm_matmul
+    cores = cpu_cores()
+    rd, wr = rms_bytes(prob)
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            rmsnorm_matmul(prob.x, prob.g, prob.w, prob.eps)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > 5.0 or reps >= 20:
+                break
+    return {"value": round((rd + wr) * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"the whole workload, {reps} call(s) in {el:.1f} s, numpy fp64"}
+
+
 def stats(ms):
     n = len(ms)
     return dict(mean_ms=sum(ms) / n, median_ms=ms[n // 2], min_ms=ms[0], p10_ms=ms[n // 10],
@@ -456,10 +551,12 @@ def decode_record(prob, r, steps, warmup, extra_src, key_suffix=""):
 def main():
     a = parse()
     if a.summarize_pmc:
-        from synthetic.inputs import workload as _wl
+        from synthetic.inputs import RMS_WORKLOADS as RMS_WORKLOADS_NAMES, workload as _wl
         name = a.workload or "llama3_8b_gqa_decode"
-        prob = _wl(name)
-        if prob.lq > 1:
+        prob = None if name in RMS_WORKLOADS_NAMES else _wl(name)
+        if name in RMS_WORKLOADS_NAMES:
+            family, key = "rms", f"rms:{name}"
+        elif prob.lq > 1:
             family, key = "prefill", f"prefill:{name}"
         else:
             family = {128: "gqa_d128", 576: "mla"}.get(prob.dqk, "generic")
@@ -481,11 +578,28 @@ def main():
         sys.exit(1)
     import reduction_attention_gqa_amd as ra
     ra.load()
-    from synthetic.inputs import WORKLOADS, workload
+    from synthetic.inputs import RMS_WORKLOADS, WORKLOADS, rms_workload, workload
     dev = "cuda:0"
     name = a.workload or "llama3_8b_gqa_decode"
+    if name in RMS_WORKLOADS:
+        if a.copy_calibration:
+            log("calibration copy")
+            copy_calibration(dev)
+        log(f"timing {name}")
+        rprob = rms_workload(name)
+        rec = rms_record(rprob, time_rms(rprob, a.steps, a.warmup, dev, a.s), a.steps)
+        out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+               "data": "synthetic (seeded; X ~ N(0,1), g ~ 1 + 0.1 N(0,1), W ~ N(0,1)/sqrt(K), "
+                       "bf16-rounded; no model weights needed)"}
+        out.update(rec)
+        if not a.no_cpu:
+            log("timing the fp64 oracle on the host")
+            out["cpu_baseline"] = oracle_rms_baseline(rprob)
+        print(json.dumps(out), flush=True)
+        return
     if name not in WORKLOADS:
-        sys.exit(f"unknown workload {name}; choose from {sorted(WORKLOADS)}")
+        sys.exit(f"unknown workload {name}; choose from {sorted(WORKLOADS) + sorted(RMS_WORKLOADS)}")
     if a.copy_calibration:
         log("calibration copy")
         copy_calibration(dev)
@@ -597,6 +711,11 @@ def main():
                 out["cpu_baseline"] = pre["cpu_baseline"]
         else:
             out["prefill"] = pre
+    if a.workload is None and not a.no_prefill:
+        rname = "llama3_8b_rmsnorm_matmul_decode"
+        log(f"timing {rname}")
+        rprob = rms_workload(rname)
+        out["rmsnorm_matmul"] = rms_record(rprob, time_rms(rprob, a.steps, a.warmup, dev), a.steps)
     line = json.dumps(out)
     print(line, flush=True)
     if a.json_out:

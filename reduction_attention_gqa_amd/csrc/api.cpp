@@ -513,7 +513,7 @@ int attn_prefill(const attn_problem* problem, const void* q, const void* k, cons
 namespace attn {
 namespace {
 
-constexpr int kRmsTileN = 64;   // weight rows per split-kernel workgroup
+constexpr int kRmsTileN = 256;  // weight rows per split-kernel workgroup
 constexpr int kRmsTileM = 32;   // tokens per split-kernel workgroup
 constexpr int kRmsBlock = 256;
 
@@ -570,8 +570,9 @@ int rmsnorm_matmul_plan(const rmsnorm_matmul_problem* problem, int32_t s_request
   if (s_request > 0) {
     s = std::min<int64_t>(s_request, steps);
   } else if (tiles > 0) {
-    // About three workgroups per compute unit, at least four k-steps per part.
-    s = ceil_div((int64_t)cus * 3, tiles);
+    // The most parts whose workgroups still run in one round (one per compute
+    // unit; each keeps ~48 KB of W in flight), at least four k-steps per part.
+    s = (int64_t)cus / tiles;
     s = std::max<int64_t>(1, std::min<int64_t>(s, steps / 4));
   }
   const int64_t chunk_steps = ceil_div(steps, s);

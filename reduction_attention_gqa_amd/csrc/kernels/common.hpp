@@ -81,6 +81,20 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(const i32x4_t& v) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
+// Device-coherent (sc1) stores and loads for single-launch merges.  They do
+// not stay dirty in one XCD's L2 and do not hit stale lines there, so a
+// partial published by one workgroup and read by another after an arrival
+// counter needs no whole-L2 write-back or invalidate (which a device-scope
+// release/acquire fence would issue for ordinary stores and loads).
+__device__ __forceinline__ void store_dev(float* ptr, float v) {
+  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* ptr) {
+  return __hip_atomic_load(const_cast<float*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): every memory operation this wave issued has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Key count of request b, clamped to [0, cap].
 __device__ __forceinline__ int kv_len_of(const int32_t* lens, int b, int cap) {
   if (lens == nullptr) return cap;

@@ -134,19 +134,6 @@ __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, in
   return false;
 }
 
-// Device-coherent (sc1) stores and loads of the single-launch merge.  They do
-// not stay dirty in one XCD's L2 and do not hit stale lines there, so a
-// partial published by one workgroup and read by another after the arrival
-// counter needs no whole-L2 write-back or invalidate (which a device-scope
-// release/acquire fence would issue for ordinary stores and loads).
-__device__ __forceinline__ void store_dev(float* ptr, float v) {
-  __hip_atomic_store(ptr, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_dev(const float* ptr) {
-  return __hip_atomic_load(const_cast<float*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// s_waitcnt vmcnt(0): every memory operation this wave issued has completed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Eight consecutive output values of one row to O (bf16 or f32), 16-byte
 // stores when the address allows.

@@ -10,12 +10,13 @@
 //
 // Layout: X [M, K], g [K], W [N, K] (linear-layer weights), Y [M, N], row
 // strides in elements, bf16 inputs.  A workgroup is four waves; wave w owns
-// the 16 weight rows n0 + 16w .. + 15 of the workgroup's 64 and up to 32
+// 64 weight rows (four MFMA row blocks) of the workgroup's 256 and up to 32
 // tokens (two MFMA column groups), over the split's K range:
 //   U^T[16 x 16] += W[16 x 32] (X * g)^T[32 x 16]     16x16x32 bf16 MFMA
-// W streams from HBM straight into the A operand (16 bytes per lane, four
-// k-steps in flight); X and g come through the caches (a few KB, shared by all
-// workgroups).  x * g is exact in fp32 (two 8-bit significands); it enters the
+// W streams from HBM straight into the A operand (16 bytes per lane and row
+// block, four k-steps in flight); X and g come through the caches (a few KB,
+// shared by all workgroups) and each fragment serves the wave's four row
+// blocks.  x * g is exact in fp32 (two 8-bit significands); it enters the
 // MFMA as a bf16 pair hi + lo, so the gain costs no precision.
 #include "../attn_internal.hpp"
 #include "common.hpp"
@@ -24,13 +25,22 @@ namespace attn {
 namespace {
 
 constexpr int NW = 4;      // waves per workgroup
+constexpr int NRB = 4;     // 16-row weight blocks per wave
+constexpr int ROWS = NW * NRB * 16;  // weight rows per workgroup
 constexpr int NBUF = 4;    // k-steps in flight per wave
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every range: loads read zero
 
-struct Frag {
-  i32x4_t w;
-  i32x4_t x[2];
-  i32x4_t g;
+// One super-step: SS consecutive 32-column k-steps.  Its W loads for one
+// weight row cover SS * 64 contiguous bytes and are issued back to back, so
+// the memory sees whole row segments rather than 64-byte pieces spread over
+// time.
+constexpr int SS = 4;
+struct WBuf {
+  i32x4_t w[SS][NRB];
+};
+struct XBuf {
+  i32x4_t x[SS][2];
+  i32x4_t g[SS];
 };
 
 // Y[m, n .. n + 3] (columns past N are skipped), bf16 (round to nearest
@@ -65,15 +75,15 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;   // MFMA row (weight row) / column (token) index
   const int kg = lane >> 4;  // 8-column group of a 32-column k-step
-  const int n_wg = blockIdx.x * (NW * 16);
+  const int n_wg = blockIdx.x * ROWS;
   const int j = blockIdx.y;
   const int m0 = blockIdx.z * 32;
   const int lo = j * p.k_chunk;
   const int hi = min(lo + p.k_chunk, p.K);
 
   // Buffer ranges end at the last valid weight row / token, so rows past N or
-  // M read as zero.  Offsets stay 32-bit: a workgroup's 64 rows, 32 tokens.
-  const int wrows = min(NW * 16, p.N - n_wg);
+  // M read as zero.  Offsets stay 32-bit: a workgroup's 256 rows, 32 tokens.
+  const int wrows = min(ROWS, p.N - n_wg);
   const int xrows = min(32, p.M - m0);
   const uint16_t* wp = reinterpret_cast<const uint16_t*>(p.w) + (int64_t)n_wg * p.w_row;
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(p.x) + (int64_t)m0 * p.x_row;
@@ -81,38 +91,53 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wp, (uint32_t)wrows * wst);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xp, (uint32_t)xrows * xst);
   const __amdgpu_buffer_rsrc_t grs = make_rsrc(p.g, (uint32_t)p.K * 2);
-  const uint32_t w_lane = (uint32_t)(16 * w + r) * wst + 16u * kg;
+  const uint32_t w_lane = (uint32_t)(NRB * 16 * w + r) * wst + 16u * kg;
   const uint32_t x_lane0 = (uint32_t)r * xst + 16u * kg;
   const uint32_t x_lane1 = (uint32_t)(16 + r) * xst + 16u * kg;
 
   // k-step at column k: this lane's 8 columns k + 8 kg .. + 7; columns past
   // the split or past K read as zero without a memory access.
-  auto load = [&](Frag& f, int k) {
-    const uint32_t oob = (k < hi && k + 8 * kg < p.K) ? 0u : kOob;
-    const uint32_t kb = (uint32_t)k * 2;
-    f.w = buf_load16(wrs, (w_lane + kb) | oob);
-    f.x[0] = buf_load16(xrs, (x_lane0 + kb) | oob);
-    f.x[1] = buf_load16(xrs, (x_lane1 + kb) | oob);
-    f.g = buf_load16(grs, (16u * kg + kb) | oob);
+  // Columns past the split or past K read as zero without a memory access.
+  auto oob_of = [&](int k) -> uint32_t { return (k < hi && k + 8 * kg < p.K) ? 0u : kOob; };
+  auto load_w = [&](WBuf& b, int k0) {
+#pragma unroll
+    for (int blk = 0; blk < NRB; ++blk)
+#pragma unroll
+      for (int t = 0; t < SS; ++t) {
+        const int k = k0 + 32 * t;
+        b.w[t][blk] = buf_load16(
+            wrs, (w_lane + (uint32_t)(16 * blk) * wst + (uint32_t)k * 2) | oob_of(k));
+      }
+  };
+  auto load_x = [&](XBuf& b, int k0) {
+#pragma unroll
+    for (int t = 0; t < SS; ++t) {
+      const int k = k0 + 32 * t;
+      const uint32_t oob = oob_of(k), kb = (uint32_t)k * 2;
+      b.g[t] = buf_load16(grs, (16u * kg + kb) | oob);
+      b.x[t][0] = buf_load16(xrs, (x_lane0 + kb) | oob);
+      b.x[t][1] = buf_load16(xrs, (x_lane1 + kb) | oob);
+    }
   };
 
-  f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  f32x4_t acc[NRB][2];
+#pragma unroll
+  for (int b = 0; b < NRB; ++b) acc[b][0] = acc[b][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float ssq[2] = {0.f, 0.f};
 
-  auto compute = [&](const Frag& f) {
+  auto compute = [&](const i32x4_t* wf, const i32x4_t* xf, const i32x4_t& gf) {
     float gv[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      gv[2 * e] = bf16_lo((uint32_t)f.g[e]);
-      gv[2 * e + 1] = bf16_hi((uint32_t)f.g[e]);
+      gv[2 * e] = bf16_lo((uint32_t)gf[e]);
+      gv[2 * e + 1] = bf16_hi((uint32_t)gf[e]);
     }
-    const bf16x8_t wa = as_bf16x8(f.w);
 #pragma unroll
     for (int mg = 0; mg < 2; ++mg) {
       i32x4_t h, l;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x0 = bf16_lo((uint32_t)f.x[mg][e]), x1 = bf16_hi((uint32_t)f.x[mg][e]);
+        const float x0 = bf16_lo((uint32_t)xf[mg][e]), x1 = bf16_hi((uint32_t)xf[mg][e]);
         ssq[mg] = __builtin_fmaf(x0, x0, ssq[mg]);
         ssq[mg] = __builtin_fmaf(x1, x1, ssq[mg]);
         const float p0 = x0 * gv[2 * e], p1 = x1 * gv[2 * e + 1];  // exact
@@ -120,20 +145,36 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
         h[e] = (int)hp;
         l[e] = (int)pack_bf16x2(p0 - bf16_lo(hp), p1 - bf16_hi(hp));  // exact residuals
       }
-      acc[mg] = mfma16x16x32(wa, as_bf16x8(h), acc[mg]);
-      acc[mg] = mfma16x16x32(wa, as_bf16x8(l), acc[mg]);
+#pragma unroll
+      for (int b = 0; b < NRB; ++b) {
+        acc[b][mg] = mfma16x16x32(as_bf16x8(wf[b]), as_bf16x8(h), acc[b][mg]);
+        acc[b][mg] = mfma16x16x32(as_bf16x8(wf[b]), as_bf16x8(l), acc[b][mg]);
+      }
     }
   };
 
-  Frag f[NBUF];
+  // Double-buffered super-steps.  Loads complete in order, so each super-step
+  // issues its own X and g first and then the next super-step's W; the wait
+  // before computing then leaves that W in flight.  Scheduling barriers keep
+  // the issue order.
+  constexpr int STEP = 32 * SS;
+  WBuf wb[2];
+  XBuf xb;
+  load_w(wb[0], lo);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int k0 = lo; k0 < hi; k0 += 2 * STEP) {
 #pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i) load(f[i], lo + 32 * i);
-  for (int k0 = lo; k0 < hi; k0 += 32 * NBUF) {
-#pragma unroll
-    for (int i = 0; i < NBUF; ++i) {
-      load(f[(i + NBUF - 1) % NBUF], k0 + 32 * (i + NBUF - 1));
+    for (int u = 0; u < 2; ++u) {
+      const int kc = k0 + u * STEP;
+      if (u == 1 && kc >= hi) break;
+      load_x(xb, kc);
       __builtin_amdgcn_sched_barrier(0);
-      if (k0 + 32 * i < hi) compute(f[i]);
+      load_w(wb[u ^ 1], kc + STEP);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int t = 0; t < SS; ++t)
+        if (kc + 32 * t < hi) compute(wb[u].w[t], xb.x[t], xb.g[t]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -144,27 +185,30 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
     ssq[mg] += __shfl_xor(ssq[mg], 32, 64);
   }
 
-  // Lane holds U^T[weight row 4 kg + i][token r] of each column group.
-  const int n_lane = n_wg + 16 * w + 4 * kg;
+  // Lane holds U^T[weight row 16 b + 4 kg + i][token r] of each column group.
 #pragma unroll
   for (int mg = 0; mg < 2; ++mg) {
     const int m = m0 + 16 * mg + r;
     if (m >= p.M) continue;
-    if (p.s == 1) {
-      // The whole K range is here: apply the row scale after the Matmul.
-      const float scale = 1.0f / sqrtf(ssq[mg] / (float)p.K + p.eps);
-      store_row4(p, m, n_lane, acc[mg] * scale);
-    } else {
+    // With the whole K range here, apply the row scale after the Matmul.
+    const float scale = p.s == 1 ? 1.0f / sqrtf(ssq[mg] / (float)p.K + p.eps) : 1.0f;
+#pragma unroll
+    for (int b = 0; b < NRB; ++b) {
+      const int n_lane = n_wg + NRB * 16 * w + 16 * b + 4 * kg;
+      if (p.s == 1) {
+        store_row4(p, m, n_lane, acc[b][mg] * scale);
+        continue;
+      }
       float* dst = p.ws_u + ((int64_t)j * p.M + m) * p.N + n_lane;
       if (n_lane + 3 < p.N && (p.N & 3) == 0) {
-        *reinterpret_cast<f32x4_t*>(dst) = acc[mg];
+        *reinterpret_cast<f32x4_t*>(dst) = acc[b][mg];
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (n_lane + i < p.N) dst[i] = acc[mg][i];
+          if (n_lane + i < p.N) dst[i] = acc[b][mg][i];
       }
-      if (blockIdx.x == 0 && w == 0 && kg == 0) p.ws_ssq[(int64_t)j * p.M + m] = ssq[mg];
     }
+    if (p.s > 1 && blockIdx.x == 0 && w == 0 && kg == 0) p.ws_ssq[(int64_t)j * p.M + m] = ssq[mg];
   }
 }
 
@@ -197,7 +241,7 @@ __global__ __launch_bounds__(256) void rmsnorm_matmul_combine_kernel(RmsParams p
 
 hipError_t launch_rmsnorm_matmul(const RmsParams& p, hipStream_t s) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  const dim3 grid((unsigned)((p.N + NW * 16 - 1) / (NW * 16)), (unsigned)p.s,
+  const dim3 grid((unsigned)((p.N + ROWS - 1) / ROWS), (unsigned)p.s,
                   (unsigned)((p.M + 31) / 32));
   hipLaunchKernelGGL(rmsnorm_matmul_split_kernel, grid, dim3(NW * 64), 0, s, p);
   hipError_t e = hipGetLastError();

@@ -459,7 +459,7 @@ def test_rms_plan_invariants(lib, m, k, n, s_req):
     assert cfg.s <= steps
     if s_req > 0:
         assert cfg.s <= s_req
-    assert tuple(cfg.grid) == (-(-n // 64), cfg.s, -(-m // 32)) and cfg.block == 256
+    assert tuple(cfg.grid) == (-(-n // 256), cfg.s, -(-m // 32)) and cfg.block == 256
     assert cfg.ws_bytes == (cfg.s * m * (n + 1) * 4 if cfg.s > 1 else 0)
 
 

@@ -100,3 +100,21 @@ def test_one_part_equals_many_parts():
     y1, _ = _run(p, s_request=1)
     y8, _ = _run(p, s_request=8)
     np.testing.assert_allclose(y1.cpu().numpy(), y8.cpu().numpy(), rtol=0, atol=2e-5)
+
+
+def test_workspace_reused_across_calls():
+    # One workspace serves call after call; each result matches the oracle.
+    p = make_rms_problem(m=9, k=768, n=300, seed=35)
+    want = rmsnorm_matmul(p.x, p.g, p.w, p.eps)
+    x, w = _dev(p.x), _dev(p.w)
+    g = _dev(p.g[None, :])[0]
+    y = torch.empty((p.m, p.n), dtype=torch.float32, device=DEV)
+    prob = ra.make_rms_problem(x, g, w, y, eps=p.eps)
+    plan = ra.rmsnorm_matmul_plan(prob, 3)
+    ws = ra.rms_workspace(plan, DEV)
+    for call in range(3):
+        y.fill_(float("nan"))
+        ra.rmsnorm_matmul(prob, plan, x, g, w, y, ws)
+        torch.cuda.synchronize()
+        assert_close(f"reuse call {call}", y.cpu().numpy().astype(np.float64), want, BF16_MAX,
+                     BF16_MEAN)

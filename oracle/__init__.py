@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the fused hot paths (attention; RMSNorm + MatMul).  TEST
+"""fp64 CPU oracle for the fused hot paths (attention; RMSNorm + MatMul; SwiGLU).  TEST
 INFRASTRUCTURE ONLY.
 
 Imported only by ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -8,11 +8,13 @@ the product library.
 """
 from .attention import (attention, attention_rows, attention_split, combine,
                         split_partials, visible_mask)
-from .brute import brute_attention, brute_rmsnorm_matmul
+from .brute import brute_attention, brute_rmsnorm_matmul, brute_swiglu
 from .rmsnorm_matmul import (RMS_EPS, rmsnorm, rmsnorm_matmul, rmsnorm_matmul_combine,
                              rmsnorm_matmul_partials, rmsnorm_matmul_split)
+from .swiglu import silu, swiglu, swiglu_combine, swiglu_partials, swiglu_split
 
 __all__ = ["attention", "attention_rows", "attention_split", "combine",
            "split_partials", "visible_mask", "brute_attention", "brute_rmsnorm_matmul",
            "RMS_EPS", "rmsnorm", "rmsnorm_matmul", "rmsnorm_matmul_combine",
-           "rmsnorm_matmul_partials", "rmsnorm_matmul_split"]
+           "rmsnorm_matmul_partials", "rmsnorm_matmul_split", "brute_swiglu", "silu", "swiglu",
+           "swiglu_combine", "swiglu_partials", "swiglu_split"]

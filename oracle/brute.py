@@ -66,3 +66,17 @@ def brute_rmsnorm_matmul(x, g, w, eps):
         normed = [row[c] * inv * g[c] for c in range(k)]
         out.append([math.fsum(normed[c] * wrow[c] for c in range(k)) for wrow in w])
     return out
+
+
+def brute_swiglu(x, w_gate, w_up):
+    """silu(x . w_gate_n) * (x . w_up_n) with explicit loops, for tiny shapes:
+    x [M][K], w_gate and w_up [N][K] as nested lists.  Returns H [M][N]."""
+    out = []
+    for row in x:
+        hrow = []
+        for wg, wu in zip(w_gate, w_up):
+            gsum = math.fsum(a * b for a, b in zip(row, wg))
+            usum = math.fsum(a * b for a, b in zip(row, wu))
+            hrow.append(gsum / (1.0 + math.exp(-gsum)) * usum)
+        out.append(hrow)
+    return out

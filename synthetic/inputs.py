@@ -45,6 +45,10 @@ Recipe (stated once, used by tests, smoke and bench):
   ``llama3_8b_rmsnorm_matmul_decode`` M=32 tokens, K=4096 (hidden size),
   N=14336 (MLP projection width), eps 1e-5; ``tiny_rmsnorm_matmul`` M=5,
   K=256, N=200.
+* SwiGLU (``make_swiglu_problem``): draw X [M, K] ~ N(0, 1), then W_gate and
+  W_up [N, K] ~ N(0, 1) / sqrt(K), bf16-rounded.  Workloads:
+  ``llama3_8b_swiglu_decode`` M=32, K=4096, N=14336 (Llama-3 8B's MLP);
+  ``tiny_swiglu`` M=5, K=256, N=200.
 """
 from __future__ import annotations
 
@@ -56,7 +60,8 @@ import numpy as np
 
 __all__ = ["Problem", "WORKLOADS", "workload", "make_problem", "to_bf16_exact",
            "padded", "log_uniform_lengths", "page_layout", "RmsProblem", "RMS_WORKLOADS",
-           "make_rms_problem", "rms_workload"]
+           "make_rms_problem", "rms_workload", "SwigluProblem", "SWIGLU_WORKLOADS",
+           "make_swiglu_problem", "swiglu_workload"]
 
 
 @dataclasses.dataclass
@@ -256,3 +261,48 @@ def make_rms_problem(*, name: str = "custom", dtype: str = "bf16", m: int, k: in
 def rms_workload(name: str, seed: int = 0) -> RmsProblem:
     w = RMS_WORKLOADS[name]
     return make_rms_problem(name=name, seed=seed, m=w["m"], k=w["k"], n=w["n"])
+
+
+@dataclasses.dataclass
+class SwigluProblem:
+    """silu(X W_gate^T) * (X W_up^T) as host arrays: x [M, K], w_gate, w_up [N, K]."""
+    name: str
+    dtype: str
+    x: np.ndarray
+    w_gate: np.ndarray
+    w_up: np.ndarray
+    s: Optional[int] = None
+
+    @property
+    def m(self) -> int:
+        return int(self.x.shape[0])
+
+    @property
+    def k(self) -> int:
+        return int(self.x.shape[1])
+
+    @property
+    def n(self) -> int:
+        return int(self.w_gate.shape[0])
+
+
+SWIGLU_WORKLOADS = {
+    "tiny_swiglu": dict(m=5, k=256, n=200),
+    "llama3_8b_swiglu_decode": dict(m=32, k=4096, n=14336),
+}
+
+
+def make_swiglu_problem(*, name: str = "custom", m: int, k: int, n: int, seed: int = 0,
+                        s: Optional[int] = None) -> SwigluProblem:
+    """Draw X, then W_gate, then W_up (see the recipe above), bf16-rounded."""
+    rng = np.random.default_rng(seed)
+    sc = np.float32(1.0 / math.sqrt(k))
+    x = to_bf16_exact(rng.standard_normal((m, k), dtype=np.float32))
+    wg = to_bf16_exact((rng.standard_normal((n, k), dtype=np.float32) * sc).astype(np.float32))
+    wu = to_bf16_exact((rng.standard_normal((n, k), dtype=np.float32) * sc).astype(np.float32))
+    return SwigluProblem(name=name, dtype="bf16", x=x, w_gate=wg, w_up=wu, s=s)
+
+
+def swiglu_workload(name: str, seed: int = 0) -> SwigluProblem:
+    w = SWIGLU_WORKLOADS[name]
+    return make_swiglu_problem(name=name, seed=seed, m=w["m"], k=w["k"], n=w["n"])

@@ -15,6 +15,9 @@ Default run (N = 1):
     shape (32 tokens, K=4096, N=14336, bf16) in algorithmic HBM GB/s (W, X, g
     read once, Y written once); one step = one call (split launch, plus the
     combine launch when K is split).
+  * swiglu: SwiGLU on Llama-3 8B's MLP at 32 tokens (K=4096, N=14336, bf16)
+    in algorithmic HBM GB/s (both weight matrices and X read once, H written
+    once); one step = one call.
   * roofline of the dominant kernel of each (per-launch HIP-event times on the
     launch stream), the split-off (s = 1) ablation, and the fp64 oracle timed
     on the host cores over a bounded sample of the same workload.
@@ -191,6 +194,7 @@ KERNEL_OF = {
     "prefill": ("prefill_d128_kernel", "reduction_attention_gqa_amd/csrc/kernels/prefill_d128.hip"),
     "rms": ("rmsnorm_matmul_split_kernel",
             "reduction_attention_gqa_amd/csrc/kernels/rmsnorm_matmul.hip"),
+    "swiglu": ("swiglu_split_kernel", "reduction_attention_gqa_amd/csrc/kernels/swiglu.hip"),
 }
 
 
@@ -451,6 +455,95 @@ def oracle_rms_baseline(prob):
             "sample": f"the whole workload, {reps} call(s) in {el:.1f} s, numpy fp64"}
 
 
+def swiglu_bytes(prob):
+    """Algorithmic bytes of SwiGLU: both weight matrices and X read once, H written once."""
+    return (2 * prob.n * prob.k + prob.m * prob.k) * 2, prob.m * prob.n * 2
+
+
+def time_swiglu(prob, steps, warmup, dev, s_request=0):
+    """Time `steps` SwiGLU calls, rotating copies of the weights past the
+    Infinity Cache."""
+    import torch
+    import reduction_attention_gqa_amd as ra
+    rd, wr = swiglu_bytes(prob)
+    n_copies = n_copies_for(rd + wr)
+    bf = torch.bfloat16
+    x = torch.from_numpy(prob.x).to(dev).to(bf)
+    g0 = torch.from_numpy(prob.w_gate).to(dev).to(bf)
+    u0 = torch.from_numpy(prob.w_up).to(dev).to(bf)
+    weights = [(g0, u0)] + [(g0.clone(), u0.clone()) for _ in range(n_copies - 1)]
+    y = torch.empty((prob.m, prob.n), dtype=bf, device=dev)
+    pr = ra.make_swiglu_problem(x, g0, u0, y)
+    cfg = ra.swiglu_plan(pr, s_request)
+    ws = ra.swiglu_workspace(cfg, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        wg, wu = weights[i % n_copies]
+        if ev is not None:
+            ev[0].record(stream)
+        ra.swiglu(pr, ra.swiglu_plan(pr, s_request), x, wg, wu, y, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    call_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
+    del weights
+    return dict(plan=cfg, wall_s=wall, call_ms=call_ms, bytes=(rd, wr))
+
+
+def swiglu_record(prob, r, steps):
+    rd, wr = r["bytes"]
+    total = rd + wr
+    ms_step = r["wall_s"] * 1e3 / steps
+    call = stats(r["call_ms"])
+    achieved = total / (call["mean_ms"] * 1e-3) / 1e9
+    cfg = r["plan"]
+    return {
+        "value": round(total / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "ms_per_step": round(ms_step, 5),
+        "config": {"workload": prob.name, "m": prob.m, "k": prob.k, "n": prob.n,
+                   "split_s": cfg.s, "k_chunk": cfg.k_chunk},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/swiglu.hip",
+                                            f"swiglu:{prob.name}"),
+                     "kernel": ("SwiGLU kernel, one launch" if cfg.s == 1 else
+                                "SwiGLU split kernel + combine kernel (timed together)"),
+                     "algorithmic_bytes_per_launch": total, "launch_ms": call}}
+
+
+def oracle_swiglu_baseline(prob):
+    """The fp64 oracle on the whole SwiGLU workload."""
+    from threadpoolctl import threadpool_limits
+    from oracle import swiglu
+    cores = cpu_cores()
+    rd, wr = swiglu_bytes(prob)
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            swiglu(prob.x, prob.w_gate, prob.w_up)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el > 5.0 or reps >= 20:
+                break
+    return {"value": round((rd + wr) * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"the whole workload, {reps} call(s) in {el:.1f} s, numpy fp64"}
+
+
 def stats(ms):
     n = len(ms)
     return dict(mean_ms=sum(ms) / n, median_ms=ms[n // 2], min_ms=ms[0], p10_ms=ms[n // 10],
@@ -552,9 +645,12 @@ def main():
     a = parse()
     if a.summarize_pmc:
         from synthetic.inputs import RMS_WORKLOADS as RMS_WORKLOADS_NAMES, workload as _wl
+        from synthetic.inputs import SWIGLU_WORKLOADS as SW_NAMES
         name = a.workload or "llama3_8b_gqa_decode"
-        prob = None if name in RMS_WORKLOADS_NAMES else _wl(name)
-        if name in RMS_WORKLOADS_NAMES:
+        prob = None if (name in RMS_WORKLOADS_NAMES or name in SW_NAMES) else _wl(name)
+        if name in SW_NAMES:
+            family, key = "swiglu", f"swiglu:{name}"
+        elif name in RMS_WORKLOADS_NAMES:
             family, key = "rms", f"rms:{name}"
         elif prob.lq > 1:
             family, key = "prefill", f"prefill:{name}"
@@ -578,9 +674,27 @@ def main():
         sys.exit(1)
     import reduction_attention_gqa_amd as ra
     ra.load()
-    from synthetic.inputs import RMS_WORKLOADS, WORKLOADS, rms_workload, workload
+    from synthetic.inputs import (RMS_WORKLOADS, SWIGLU_WORKLOADS, WORKLOADS, rms_workload,
+                                  swiglu_workload, workload)
     dev = "cuda:0"
     name = a.workload or "llama3_8b_gqa_decode"
+    if name in SWIGLU_WORKLOADS:
+        if a.copy_calibration:
+            log("calibration copy")
+            copy_calibration(dev)
+        log(f"timing {name}")
+        sprob = swiglu_workload(name)
+        rec = swiglu_record(sprob, time_swiglu(sprob, a.steps, a.warmup, dev, a.s), a.steps)
+        out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+               "data": "synthetic (seeded; X ~ N(0,1), W_gate, W_up ~ N(0,1)/sqrt(K), "
+                       "bf16-rounded; no model weights needed)"}
+        out.update(rec)
+        if not a.no_cpu:
+            log("timing the fp64 oracle on the host")
+            out["cpu_baseline"] = oracle_swiglu_baseline(sprob)
+        print(json.dumps(out), flush=True)
+        return
     if name in RMS_WORKLOADS:
         if a.copy_calibration:
             log("calibration copy")
@@ -599,7 +713,8 @@ def main():
         print(json.dumps(out), flush=True)
         return
     if name not in WORKLOADS:
-        sys.exit(f"unknown workload {name}; choose from {sorted(WORKLOADS) + sorted(RMS_WORKLOADS)}")
+        sys.exit(f"unknown workload {name}; choose from "
+                 f"{sorted(WORKLOADS) + sorted(RMS_WORKLOADS) + sorted(SWIGLU_WORKLOADS)}")
     if a.copy_calibration:
         log("calibration copy")
         copy_calibration(dev)
@@ -716,6 +831,10 @@ def main():
         log(f"timing {rname}")
         rprob = rms_workload(rname)
         out["rmsnorm_matmul"] = rms_record(rprob, time_rms(rprob, a.steps, a.warmup, dev), a.steps)
+        sname = "llama3_8b_swiglu_decode"
+        log(f"timing {sname}")
+        sprob = swiglu_workload(sname)
+        out["swiglu"] = swiglu_record(sprob, time_swiglu(sprob, a.steps, a.warmup, dev), a.steps)
     line = json.dumps(out)
     print(line, flush=True)
     if a.json_out:

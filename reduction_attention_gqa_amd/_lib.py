@@ -26,7 +26,7 @@ KERNEL_NAMES = {0: "generic", 1: "gqa_d128", 2: "mla"}
 
 EXPORTED = ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_decode", "attn_prefill",
             "attn_status_str", "attn_last_error", "attn_version", "rmsnorm_matmul_plan",
-            "rmsnorm_matmul")
+            "rmsnorm_matmul", "swiglu_plan", "swiglu")
 
 
 class AttnProblem(ctypes.Structure):
@@ -74,6 +74,24 @@ class RmsConfig(ctypes.Structure):
     ]
 
 
+class SwigluProblem(ctypes.Structure):
+    """swiglu_problem (include/swiglu.h)."""
+    _fields_ = [
+        ("dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32), ("m", ctypes.c_int32),
+        ("k", ctypes.c_int32), ("n", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("x_stride", ctypes.c_int64), ("wg_stride", ctypes.c_int64),
+        ("wu_stride", ctypes.c_int64), ("y_stride", ctypes.c_int64),
+    ]
+
+
+class SwigluConfig(ctypes.Structure):
+    """swiglu_config (include/swiglu.h)."""
+    _fields_ = [
+        ("s", ctypes.c_int32), ("k_chunk", ctypes.c_int32), ("grid", ctypes.c_uint32 * 3),
+        ("block", ctypes.c_uint32), ("ws_bytes", ctypes.c_uint64), ("problem_key", ctypes.c_uint64),
+    ]
+
+
 class AttnError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"[{status}] {msg}")
@@ -103,8 +121,11 @@ def load() -> ctypes.CDLL:
     RP, RC = ctypes.POINTER(RmsProblem), ctypes.POINTER(RmsConfig)
     lib.rmsnorm_matmul_plan.argtypes = [RP, ctypes.c_int32, ctypes.c_int32, RC]
     lib.rmsnorm_matmul.argtypes = [RP, RC, V, V, V, V, V, ctypes.c_size_t, V]
+    SP, SC = ctypes.POINTER(SwigluProblem), ctypes.POINTER(SwigluConfig)
+    lib.swiglu_plan.argtypes = [SP, ctypes.c_int32, ctypes.c_int32, SC]
+    lib.swiglu.argtypes = [SP, SC, V, V, V, V, V, ctypes.c_size_t, V]
     for f in ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_decode",
-              "attn_prefill", "rmsnorm_matmul_plan", "rmsnorm_matmul"):
+              "attn_prefill", "rmsnorm_matmul_plan", "rmsnorm_matmul", "swiglu_plan", "swiglu"):
         getattr(lib, f).restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -355,3 +376,51 @@ def rmsnorm_matmul(problem: RmsProblem, plan: RmsConfig, x, g, w, y, ws=None, st
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib.rmsnorm_matmul(ctypes.byref(problem), ctypes.byref(plan), _ptr(x), _ptr(g), _ptr(w),
                               _ptr(y), _ptr(ws), nbytes, _stream(stream)))
+
+
+# ----------------------------------------------------------------- SwiGLU
+
+def make_swiglu_problem(x, w_gate, w_up, y) -> SwigluProblem:
+    """Describe X [m, k], W_gate and W_up [n, k] and H [m, n] (row strides taken
+    from the tensors; the last dimension must be contiguous)."""
+    for name, t in (("x", x), ("w_gate", w_gate), ("w_up", w_up), ("y", y)):
+        if t.dim() != 2:
+            raise ValueError(f"{name} must be 2-D")
+        if t.shape[-1] > 1 and t.stride(-1) != 1:
+            raise ValueError(f"{name}: the last dimension must be contiguous")
+    if w_gate.dtype != x.dtype or w_up.dtype != x.dtype:
+        raise TypeError("x and the weights must share one dtype")
+    p = SwigluProblem()
+    p.dtype = _dtype_code(x)
+    p.y_dtype = _dtype_code(y)
+    p.m, p.k = int(x.shape[0]), int(x.shape[1])
+    p.n = int(w_gate.shape[0])
+    if (tuple(w_gate.shape) != (p.n, p.k) or tuple(w_up.shape) != (p.n, p.k)
+            or tuple(y.shape) != (p.m, p.n)):
+        raise ValueError("shapes: x [m, k], w_gate and w_up [n, k], y [m, n]")
+    p.x_stride, p.wg_stride, p.wu_stride, p.y_stride = (x.stride(0), w_gate.stride(0),
+                                                        w_up.stride(0), y.stride(0))
+    return p
+
+
+def swiglu_plan(problem: SwigluProblem, s_request: int = 0, num_cus: int = 0) -> SwigluConfig:
+    lib = load()
+    cfg = SwigluConfig()
+    _check(lib.swiglu_plan(ctypes.byref(problem), int(s_request), int(num_cus), ctypes.byref(cfg)))
+    return cfg
+
+
+def swiglu_workspace(config: SwigluConfig, device):
+    """The fp32 workspace a config asks for (torch owns the memory), or None."""
+    import torch
+    if config.ws_bytes == 0:
+        return None
+    return torch.empty(config.ws_bytes // 4, dtype=torch.float32, device=device)
+
+
+def swiglu(problem: SwigluProblem, config: SwigluConfig, x, w_gate, w_up, y, ws=None,
+           stream=None) -> None:
+    lib = load()
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib.swiglu(ctypes.byref(problem), ctypes.byref(config), _ptr(x), _ptr(w_gate),
+                      _ptr(w_up), _ptr(y), _ptr(ws), nbytes, _stream(stream)))

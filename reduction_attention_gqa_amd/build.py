@@ -26,6 +26,7 @@ SOURCES = [
     "kernels/prefill_d128.hip",
     "kernels/decode_mla.hip",
     "kernels/rmsnorm_matmul.hip",
+    "kernels/swiglu.hip",
 ]
 
 # Packed-fp32 VALU forms are switched off for all device code.

@@ -13,6 +13,7 @@
 #include "attn_internal.hpp"
 #include "attn_mi355x.h"
 #include "rmsnorm_matmul.h"
+#include "swiglu.h"
 
 namespace attn {
 namespace {
@@ -623,6 +624,121 @@ int rmsnorm_matmul(const rmsnorm_matmul_problem* problem, const rmsnorm_matmul_c
   k.eps = p->eps;
   return hip_status(launch_rmsnorm_matmul(k, reinterpret_cast<hipStream_t>(stream)),
                     "rmsnorm_matmul launch");
+}
+
+}  // extern "C"
+
+// ----------------------------------------------------------------- SwiGLU
+
+namespace attn {
+namespace {
+
+constexpr int kSwTileN = 128;  // output columns per split-kernel workgroup
+constexpr int kSwTileM = 32;   // tokens per split-kernel workgroup
+
+int check_swiglu(const swiglu_problem* p) {
+  if (!p) return fail(ATTN_ERR_ARG, "problem is NULL");
+  if (p->reserved0 != 0) return fail(ATTN_ERR_ARG, "reserved0 must be 0");
+  if ((p->dtype != ATTN_F32 && p->dtype != ATTN_BF16) ||
+      (p->y_dtype != ATTN_F32 && p->y_dtype != ATTN_BF16))
+    return fail(ATTN_ERR_ARG, "dtype/y_dtype must be ATTN_F32 or ATTN_BF16");
+  if (p->m < 0 || p->n < 0) return fail(ATTN_ERR_ARG, "m and n must be >= 0");
+  if (p->k < 1) return fail(ATTN_ERR_ARG, "k must be >= 1");
+  if (p->x_stride < p->k || p->wg_stride < p->k || p->wu_stride < p->k || p->y_stride < p->n)
+    return fail(ATTN_ERR_ARG, "row strides must cover the rows");
+  if (p->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "only bf16 X and weights are supported");
+  if (p->k % 8 != 0) return fail(ATTN_ERR_UNSUPPORTED, "k must be a multiple of 8");
+  if ((p->x_stride | p->wg_stride | p->wu_stride) & 7)
+    return fail(ATTN_ERR_UNSUPPORTED, "row strides of X and the weights must be multiples of 8 elements");
+  if ((int64_t)kSwTileN * std::max(p->wg_stride, p->wu_stride) * 2 >= (1ll << 31) ||
+      (int64_t)kSwTileM * p->x_stride * 2 >= (1ll << 31))
+    return fail(ATTN_ERR_UNSUPPORTED, "row strides too large");
+  return ATTN_OK;
+}
+
+uint64_t swiglu_key(const swiglu_problem* p) {
+  const int32_t f[] = {0x535747, p->dtype, p->m, p->k, p->n};
+  uint64_t h = 1469598103934665603ull;
+  for (int32_t x : f)
+    for (int s = 0; s < 32; s += 8) {
+      h ^= (uint64_t)((x >> s) & 0xff);
+      h *= 1099511628211ull;
+    }
+  return h | 1ull;
+}
+
+}  // namespace
+}  // namespace attn
+
+extern "C" {
+
+int swiglu_plan(const swiglu_problem* problem, int32_t s_request, int32_t num_cus,
+                swiglu_config* out) {
+  g_err[0] = 0;
+  if (!out) return fail(ATTN_ERR_ARG, "config output is NULL");
+  std::memset(out, 0, sizeof(*out));
+  if (int st = check_swiglu(problem)) return st;
+  const swiglu_problem* p = problem;
+  int cus = num_cus;
+  if (cus <= 0 && device_cu_count(&cus) != 0)
+    return fail(ATTN_ERR_HIP, "cannot query the compute-unit count of the current device");
+  const int64_t steps = ceil_div(p->k, 32);
+  const int64_t tiles = ceil_div(p->n, kSwTileN) * ceil_div(p->m, kSwTileM);
+  int64_t s = 1;
+  if (s_request > 0) {
+    s = std::min<int64_t>(s_request, steps);
+  } else if (tiles > 0) {
+    s = (int64_t)cus / tiles;
+    s = std::max<int64_t>(1, std::min<int64_t>(s, steps / 4));
+  }
+  const int64_t chunk_steps = ceil_div(steps, s);
+  s = ceil_div(steps, chunk_steps);
+  if (s > 65535 || ceil_div(p->m, kSwTileM) > 65535)
+    return fail(ATTN_ERR_UNSUPPORTED, "too many parts or token tiles for the grid");
+  out->s = (int32_t)s;
+  out->k_chunk = (int32_t)(chunk_steps * 32);
+  out->grid[0] = (uint32_t)ceil_div(p->n, kSwTileN);
+  out->grid[1] = (uint32_t)s;
+  out->grid[2] = (uint32_t)ceil_div(p->m, kSwTileM);
+  out->block = 256;
+  out->ws_bytes = s > 1 ? 2ull * (uint64_t)s * p->m * p->n * sizeof(float) : 0;
+  out->problem_key = swiglu_key(p);
+  return ATTN_OK;
+}
+
+int swiglu(const swiglu_problem* problem, const swiglu_config* config, const void* x,
+           const void* w_gate, const void* w_up, void* y, float* ws, size_t ws_bytes,
+           void* stream) {
+  g_err[0] = 0;
+  if (int st = check_swiglu(problem)) return st;
+  const swiglu_problem* p = problem;
+  if (!config) return fail(ATTN_ERR_ARG, "config is NULL");
+  if (config->problem_key != swiglu_key(p)) return fail(ATTN_ERR_ARG, "config was made for a different problem");
+  if (config->s < 1 || config->k_chunk < 32 || config->k_chunk % 32 ||
+      (int64_t)config->s * config->k_chunk < p->k || (int64_t)(config->s - 1) * config->k_chunk >= p->k)
+    return fail(ATTN_ERR_ARG, "corrupt config");
+  if (p->m == 0 || p->n == 0) return ATTN_OK;
+  if (!x || !w_gate || !w_up || !y) return fail(ATTN_ERR_ARG, "x, w_gate, w_up and y must not be NULL");
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up))
+    return fail(ATTN_ERR_UNSUPPORTED, "x, w_gate and w_up must be 16-byte aligned");
+  const uint64_t need = config->s > 1 ? 2ull * (uint64_t)config->s * p->m * p->n * sizeof(float) : 0;
+  if (need && (!ws || ws_bytes < need))
+    return fail(ATTN_ERR_WORKSPACE, "workspace too small: need %llu bytes", (unsigned long long)need);
+  if (need && (reinterpret_cast<uintptr_t>(ws) & 15))
+    return fail(ATTN_ERR_ARG, "workspace must be 16-byte aligned");
+  SwigluParams k;
+  std::memset(&k, 0, sizeof(k));
+  k.x = x; k.wg = w_gate; k.wu = w_up; k.y = y;
+  if (config->s > 1) {
+    k.ws_g = ws;
+    k.ws_u = ws + (int64_t)config->s * p->m * p->n;
+  }
+  k.x_row = p->x_stride; k.wg_row = p->wg_stride; k.wu_row = p->wu_stride; k.y_row = p->y_stride;
+  k.M = p->m; k.K = p->k; k.N = p->n;
+  k.s = config->s;
+  k.k_chunk = config->k_chunk;
+  k.y_bf16 = p->y_dtype == ATTN_BF16;
+  return hip_status(launch_swiglu(k, reinterpret_cast<hipStream_t>(stream)), "swiglu launch");
 }
 
 }  // extern "C"

@@ -62,6 +62,23 @@ struct RmsParams {
 };
 hipError_t launch_rmsnorm_matmul(const RmsParams& p, hipStream_t s);
 
+// SwiGLU: X [M, K], W_gate and W_up [N, K], H [M, N] (bf16 inputs); row
+// strides in elements.
+struct SwigluParams {
+  const void* x;
+  const void* wg;
+  const void* wu;
+  void* y;
+  float* ws_g;          // gate partials [s, M, N] (s > 1)
+  float* ws_u;          // up partials [s, M, N] (s > 1)
+  int64_t x_row, wg_row, wu_row, y_row;
+  int32_t M, K, N;
+  int32_t s;            // K splits
+  int32_t k_chunk;      // columns per split, a multiple of 32
+  int32_t y_bf16;
+};
+hipError_t launch_swiglu(const SwigluParams& p, hipStream_t s);
+
 // Launchers (one per kernel family).  Each returns a hipError_t.
 hipError_t launch_generic(const KParams& p, dim3 grid, dim3 block, hipStream_t s);
 hipError_t launch_combine(const KParams& p, hipStream_t s);

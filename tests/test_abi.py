@@ -34,7 +34,7 @@ HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.j
 def _declared_functions():
     text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?((?:attn|rmsnorm)_\w+)\s*\(", text,
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?((?:attn|rmsnorm|swiglu)\w*)\s*\(", text,
                                  flags=re.M)))
 
 
@@ -68,7 +68,7 @@ def _c_layout(tmp_path, struct, fields):
     lines += [f'printf("{f} %zu\\n", offsetof({struct}, {f}));' for f in fields]
     src = tmp_path / "layout.c"
     src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"attn_mi355x.h\"\n"
-                   "#include \"rmsnorm_matmul.h\"\n"
+                   "#include \"rmsnorm_matmul.h\"\n#include \"swiglu.h\"\n"
                    "int main(void) {\n" + "\n".join(lines) + "\nreturn 0;\n}\n")
     exe = tmp_path / "layout"
     subprocess.run(["gcc", "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
@@ -79,7 +79,9 @@ def _c_layout(tmp_path, struct, fields):
 
 @pytest.mark.parametrize("py,c", [(_lib.AttnProblem, "attn_problem"), (_lib.AttnPlan, "attn_plan"),
                                   (_lib.RmsProblem, "rmsnorm_matmul_problem"),
-                                  (_lib.RmsConfig, "rmsnorm_matmul_config")])
+                                  (_lib.RmsConfig, "rmsnorm_matmul_config"),
+                                  (_lib.SwigluProblem, "swiglu_problem"),
+                                  (_lib.SwigluConfig, "swiglu_config")])
 def test_struct_layout_matches_c(tmp_path, py, c):
     names = [f[0] for f in py._fields_]
     got = _c_layout(tmp_path, c, names)
@@ -487,3 +489,68 @@ def test_rms_workspace_and_plan_checks(lib):
     assert st == 0
     assert lib.rmsnorm_matmul(ctypes.byref(empty), ctypes.byref(cfg0), None, None, None, None, None,
                               0, None) == 0
+
+
+# ----------------------------------------------------------------- SwiGLU
+
+def sw_problem(**kw):
+    f = dict(dtype=ra.ATTN_BF16, y_dtype=ra.ATTN_BF16, m=32, k=4096, n=14336)
+    f.update({k: v for k, v in kw.items() if k in f or k == "reserved0"})
+    p = _lib.SwigluProblem()
+    for k, v in f.items():
+        setattr(p, k, v)
+    p.x_stride = kw.get("x_stride", p.k)
+    p.wg_stride = kw.get("wg_stride", p.k)
+    p.wu_stride = kw.get("wu_stride", p.k)
+    p.y_stride = kw.get("y_stride", p.n)
+    return p
+
+
+def sw_plan(lib, p, s_request=0, num_cus=256):
+    cfg = _lib.SwigluConfig()
+    return lib.swiglu_plan(ctypes.byref(p), s_request, num_cus, ctypes.byref(cfg)), cfg
+
+
+@pytest.mark.parametrize("edit,code", [
+    (dict(m=-1), ra.ATTN_ERR_ARG),
+    (dict(k=0), ra.ATTN_ERR_ARG),
+    (dict(reserved0=3), ra.ATTN_ERR_ARG),
+    (dict(wu_stride=10), ra.ATTN_ERR_ARG),
+    (dict(dtype=ra.ATTN_F32), ra.ATTN_ERR_UNSUPPORTED),
+    (dict(k=4100, x_stride=4104, wg_stride=4104, wu_stride=4104), ra.ATTN_ERR_UNSUPPORTED),
+    (dict(wg_stride=4100), ra.ATTN_ERR_UNSUPPORTED),
+])
+def test_swiglu_invalid_problem(lib, edit, code):
+    p = sw_problem(**edit)
+    st, _ = sw_plan(lib, p)
+    assert st == code and lib.attn_last_error()
+    fake = ctypes.c_void_p(0x1000)
+    cfg = _lib.SwigluConfig()
+    assert lib.swiglu(ctypes.byref(p), ctypes.byref(cfg), fake, fake, fake, fake, fake, 1 << 30,
+                      None) == code
+
+
+@pytest.mark.parametrize("m,k,n,s_req", [(32, 4096, 14336, 0), (1, 4096, 14336, 0),
+                                         (5, 256, 200, 0), (33, 264, 70, 3), (32, 4096, 14336, 999)])
+def test_swiglu_plan_invariants(lib, m, k, n, s_req):
+    st, cfg = sw_plan(lib, sw_problem(m=m, k=k, n=n), s_req)
+    assert st == 0
+    assert cfg.k_chunk % 32 == 0 and cfg.s * cfg.k_chunk >= k and (cfg.s - 1) * cfg.k_chunk < k
+    assert tuple(cfg.grid) == (-(-n // 128), cfg.s, -(-m // 32)) and cfg.block == 256
+    assert cfg.ws_bytes == (2 * cfg.s * m * n * 4 if cfg.s > 1 else 0)
+    if s_req == 0:
+        assert cfg.grid[0] * cfg.grid[1] * cfg.grid[2] <= max(256, cfg.grid[0] * cfg.grid[2])
+
+
+def test_swiglu_workspace_and_config_checks(lib):
+    p = sw_problem()
+    st, cfg = sw_plan(lib, p, 2)
+    assert st == 0 and cfg.s == 2
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.swiglu(ctypes.byref(p), ctypes.byref(cfg), fake, fake, fake, fake, fake,
+                      cfg.ws_bytes - 4, None) == ra.ATTN_ERR_WORKSPACE
+    other = sw_problem(n=4096)
+    assert lib.swiglu(ctypes.byref(other), ctypes.byref(cfg), fake, fake, fake, fake, fake,
+                      1 << 40, None) == ra.ATTN_ERR_ARG
+    assert lib.swiglu(ctypes.byref(p), ctypes.byref(cfg), fake, ctypes.c_void_p(0x1004), fake, fake,
+                      fake, 1 << 40, None) == ra.ATTN_ERR_UNSUPPORTED

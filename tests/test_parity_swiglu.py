@@ -1,0 +1,77 @@
+"""GPU parity of SwiGLU against the fp64 oracle, through the C ABI.
+
+The kernel streams both weight matrices in one loop over K (horizontal
+fusion, Cleave §7.3), split over K when the plan says so (Cleave §2.2
+"Split-K", parts added before the gate).  Tolerance as for the other bf16
+paths: max abs 1e-2, mean abs 1e-3 on the fp32 output; the bf16 output must be
+the round-to-nearest-even of the fp32 one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import BF16_MAX, BF16_MEAN, DEV, assert_close
+import reduction_attention_gqa_amd as ra
+from oracle import swiglu
+from synthetic.inputs import make_swiglu_problem, swiglu_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a, stride=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(torch.bfloat16)
+    if stride is None or stride == a.shape[-1]:
+        return t
+    wide = torch.full((a.shape[0], stride), float("nan"), dtype=torch.bfloat16, device=DEV)
+    wide[:, : a.shape[1]] = t
+    return wide[:, : a.shape[1]]
+
+
+def _run(p, s_request=0, y_dtype=torch.float32, strides=(None, None, None)):
+    x, wg, wu = _dev(p.x, strides[0]), _dev(p.w_gate, strides[1]), _dev(p.w_up, strides[2])
+    y = torch.full((p.m, p.n), float("nan"), dtype=y_dtype, device=DEV)
+    prob = ra.make_swiglu_problem(x, wg, wu, y)
+    cfg = ra.swiglu_plan(prob, s_request)
+    ra.swiglu(prob, cfg, x, wg, wu, y, ra.swiglu_workspace(cfg, DEV))
+    torch.cuda.synchronize()
+    return y, cfg
+
+
+def _check(name, p, **kw):
+    want = swiglu(p.x, p.w_gate, p.w_up)
+    y32, cfg = _run(p, **kw)
+    assert_close(f"{name} (s={cfg.s})", y32.cpu().numpy().astype(np.float64), want, BF16_MAX,
+                 BF16_MEAN)
+    y16, _ = _run(p, y_dtype=torch.bfloat16, **kw)
+    assert torch.equal(y16, y32.to(torch.bfloat16)), f"{name}: bf16 H != RNE(fp32 H)"
+    return cfg
+
+
+@pytest.mark.parametrize("s", [0, 1, 2, 3, 8])
+def test_tiny_split_counts(s):
+    cfg = _check(f"tiny s={s}", swiglu_workload("tiny_swiglu"), s_request=s)
+    if s:
+        assert cfg.s == s
+
+
+@pytest.mark.parametrize("s", [1, 4])
+def test_ragged_tails(s):
+    # m = 33 spans two token tiles; k = 264 ends mid k-step; n = 70 mid tile.
+    _check(f"tails s={s}", make_swiglu_problem(m=33, k=264, n=70, seed=41), s_request=s)
+
+
+def test_strided_rows():
+    _check("strided", make_swiglu_problem(m=7, k=512, n=130, seed=42), s_request=3,
+           strides=(520, 640, 576))
+
+
+def test_full_size_decode():
+    # Llama-3 8B's MLP at 32 tokens: K = 4096, N = 14336; every output checked.
+    _check("llama3_8b decode", swiglu_workload("llama3_8b_swiglu_decode"))
+
+
+def test_one_part_equals_many_parts():
+    p = make_swiglu_problem(m=16, k=1024, n=256, seed=43)
+    y1, _ = _run(p, s_request=1)
+    y8, _ = _run(p, s_request=8)
+    np.testing.assert_allclose(y1.cpu().numpy(), y8.cpu().numpy(), rtol=0, atol=5e-5)

@@ -80,3 +80,32 @@ def brute_swiglu(x, w_gate, w_up):
             hrow.append(gsum / (1.0 + math.exp(-gsum)) * usum)
         out.append(hrow)
     return out
+
+
+def brute_matmul_matmul(q, k, v, causal, scale, dv):
+    """MatMul+MatMul (Cleave §7.3 subgraph list) with explicit loops and exact sums.
+
+    q: [B][Lq][Hq][D]; k[b]: [L_b][Hkv][D]; v[b]: [L_b][Hkv][Dv].  For each
+    output (b, i, h, c): sum over visible keys j of t_j * V[b][j][h // G][c],
+    where t_j = scale * sum_d Q[b][i][h][d] K[b][j][h // G][d].  A row with no
+    visible key gives 0.  Returns O [B][Lq][Hq][Dv] as nested lists.
+    """
+    out = []
+    for b in range(len(q)):
+        lq = len(q[b])
+        n = len(k[b])
+        o_b = []
+        for i in range(lq):
+            hq = len(q[b][i])
+            hkv = len(k[b][0]) if n else 1
+            g = hq // hkv
+            o_i = []
+            for h in range(hq):
+                kvh = h // g
+                keys = [j for j in range(n) if (not causal) or j <= i + n - lq]
+                t = {j: scale * math.fsum(q[b][i][h][d] * k[b][j][kvh][d]
+                                          for d in range(len(q[b][i][h]))) for j in keys}
+                o_i.append([math.fsum(t[j] * v[b][j][kvh][c] for j in keys) for c in range(dv)])
+            o_b.append(o_i)
+        out.append(o_b)
+    return out

@@ -103,7 +103,7 @@ def matmul_matmul_rows(q, k, v, causal, scale, rows):
     return out
 
 
-def error_bounds(q, k, v, causal, scale=None):
+def error_bounds(q, k, v, causal, scale=None, rounds_intermediate: bool = True):
     """What a kernel may differ from the exact O by, per output element.
 
     The kernel forms each intermediate entry in fp32 from exact bf16 products
@@ -116,15 +116,17 @@ def error_bounds(q, k, v, causal, scale=None):
     of the first product errs relative to A, not to |T|, when terms cancel).
     Treating the bf16 roundings as independent, each at most u |T_ij| in size,
     the typical error has root-mean-square at most
-        rms = u / sqrt(3) * sqrt(sum_j T_ij^2 V_jc^2)
-    plus the fp32 terms, which are 2^16 times smaller.
+        rms = (u / sqrt(3) + n e) * sqrt(sum_j T_ij^2 V_jc^2)
+    (the n e term covers fp32 accumulation, 2^16 times smaller than u).
+    With ``rounds_intermediate=False`` (every tau Q K^T entry exactly
+    representable in bf16, e.g. small integers) the bf16 term u drops out.
     Returns (worst, rms), both [B, Lq, Hq, dv].
     """
     q = np.asarray(q, dtype=np.float64)
     bsz, lq, hq, dqk, hkv, g = _heads(q, k)
     if scale is None:
         scale = 1.0 / math.sqrt(dqk)
-    u, e = BF16_UNIT_ROUNDOFF, F32_UNIT_ROUNDOFF
+    u, e = (BF16_UNIT_ROUNDOFF if rounds_intermediate else 0.0), F32_UNIT_ROUNDOFF
     dv = v[0].shape[2]
     worst = np.zeros((bsz, lq, hq, dv))
     rms = np.zeros((bsz, lq, hq, dv))
@@ -141,5 +143,5 @@ def error_bounds(q, k, v, causal, scale=None):
             va = np.abs(vb)
             worst[b, :, h, :] = ((u + n * e * (1 + u) ** 2) * np.matmul(np.abs(t), va)
                                  + (dqk + 1) * e * (1 + u) * (1 + n * e) * np.matmul(a_abs, va))
-            rms[b, :, h, :] = u / math.sqrt(3.0) * np.sqrt(np.matmul(t * t, vb * vb))
+            rms[b, :, h, :] = (u / math.sqrt(3.0) + n * e) * np.sqrt(np.matmul(t * t, vb * vb))
     return worst, rms

@@ -11,6 +11,9 @@ Default run (N = 1):
     is timed beside it as an ablation.
   * prefill: causal GQA prefill (B=4, L=4096, 32/8 heads, D=128, bf16) in
     algorithmic TFLOP/s; one step = one fused prefill launch.
+  * matmul_matmul: MatMul+MatMul, O = (tau Q K^T) V per head with no softmax
+    (B=4, 4096 queries and keys, 32/8 heads, D=128, bf16) in algorithmic
+    TFLOP/s; one step = one launch.
   * rmsnorm_matmul: RMSNorm followed by a MatMul on the Llama-3 8B decode
     shape (32 tokens, K=4096, N=14336, bf16) in algorithmic HBM GB/s (W, X, g
     read once, Y written once); one step = one call (split launch, plus the
@@ -35,7 +38,8 @@ Algorithmic work: bytes = unique Q, K and V reads + O write (the split
 workspace is not counted); flops = 2 (Dqk + Dv) per visible (query, key) pair.
 
 --workload NAME benches one of the other named workloads instead (its own
-JSON line, decode or prefill by shape, or llama3_8b_rmsnorm_matmul_decode).
+JSON line, decode or prefill by shape, llama3_8b_rmsnorm_matmul_decode,
+llama3_8b_swiglu_decode or llama3_8b_matmul_matmul_prefill).
 """
 from __future__ import annotations
 
@@ -330,7 +334,8 @@ def time_decode(prob, steps, warmup, s_request, dev, fused, layout="token", page
                 bytes=(qb, kvb, ob), fused=fused)
 
 
-def time_prefill(prob, steps, warmup, dev):
+def time_prefill(prob, steps, warmup, dev, mm=False):
+    """Time `steps` fused prefill launches (mm: MatMul+MatMul launches instead)."""
     import torch
     import reduction_attention_gqa_amd as ra
     qb, kvb, ob = decode_bytes(prob)
@@ -345,7 +350,10 @@ def time_prefill(prob, steps, warmup, dev):
         q, k, v = copies[i % len(copies)]
         if ev is not None:
             ev[0].record(stream)
-        ra.attn_prefill(probs[i % len(copies)], q, k, v, o, None, stream)
+        if mm:
+            ra.attn_matmul_matmul(probs[i % len(copies)], q, k, v, o, stream)
+        else:
+            ra.attn_prefill(probs[i % len(copies)], q, k, v, o, None, stream)
         if ev is not None:
             ev[1].record(stream)
 
@@ -610,6 +618,51 @@ def oracle_prefill_baseline(prob, groups=24):
                       f"({g} heads x {prob.lq} queries each), {el:.1f} s, numpy fp64"}
 
 
+def oracle_mm_baseline(prob, heads=128):
+    """The fp64 MatMul+MatMul oracle on `heads` (request, query head) pairs."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import matmul_matmul
+    cores = cpu_cores()
+    g = prob.hq // prob.hkv
+    with threadpool_limits(limits=cores):
+        t0 = time.perf_counter()
+        for idx in range(heads):
+            b, h = idx % prob.batch, (idx // prob.batch) % prob.hq
+            q = np.ascontiguousarray(prob.q[b:b + 1, :, h:h + 1, :])
+            k = [prob.k[b][:, h // g:h // g + 1, :]]
+            v = [prob.v_rows(b)[:, h // g:h // g + 1, :]]
+            matmul_matmul(q, k, v, prob.causal, prob.scale)
+        el = time.perf_counter() - t0
+    n = int(prob.lens[0])
+    pairs = (n * (n + 1) // 2 if prob.causal else n * n) * heads
+    flops = 2 * (prob.dqk + prob.dv) * pairs
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{heads} of {prob.batch * prob.hq} (request, query head) pairs "
+                      f"({prob.lq} queries x {n} keys each), {el:.1f} s, numpy fp64"}
+
+
+def mm_record(prob, r, steps):
+    """JSON record of a MatMul+MatMul timing (same kernel source as prefill)."""
+    flops = attention_flops(prob)
+    ks = stats(r["kernel_ms"])
+    ms_step = r["wall_s"] * 1e3 / steps
+    achieved = flops / (ks["mean_ms"] * 1e-3) / 1e12
+    return {"value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "ms_per_step": round(ms_step, 5),
+            "config": {"workload": prob.name, "batch": prob.batch, "q_len": prob.lq,
+                       "kv_len": int(prob.lens.max()), "q_heads": prob.hq,
+                       "kv_heads": prob.hkv, "head_dim": prob.dqk, "causal": bool(prob.causal)},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/"
+                                                "prefill_d128.hip", f"mm:{prob.name}"),
+                         "kernel": "MatMul+MatMul kernel (prefill kernel without the softmax)",
+                         "algorithmic_flops_per_launch": flops, "launch_ms": ks}}
+
+
 # ------------------------------------------------------------------------ main
 
 def decode_record(prob, r, steps, warmup, extra_src, key_suffix=""):
@@ -645,10 +698,13 @@ def main():
     a = parse()
     if a.summarize_pmc:
         from synthetic.inputs import RMS_WORKLOADS as RMS_WORKLOADS_NAMES, workload as _wl
-        from synthetic.inputs import SWIGLU_WORKLOADS as SW_NAMES
+        from synthetic.inputs import SWIGLU_WORKLOADS as SW_NAMES, MM_WORKLOADS as MM_NAMES
         name = a.workload or "llama3_8b_gqa_decode"
-        prob = None if (name in RMS_WORKLOADS_NAMES or name in SW_NAMES) else _wl(name)
-        if name in SW_NAMES:
+        prob = None if (name in RMS_WORKLOADS_NAMES or name in SW_NAMES or
+                        name in MM_NAMES) else _wl(name)
+        if name in MM_NAMES:
+            family, key = "prefill", f"mm:{name}"
+        elif name in SW_NAMES:
             family, key = "swiglu", f"swiglu:{name}"
         elif name in RMS_WORKLOADS_NAMES:
             family, key = "rms", f"rms:{name}"
@@ -674,10 +730,26 @@ def main():
         sys.exit(1)
     import reduction_attention_gqa_amd as ra
     ra.load()
-    from synthetic.inputs import (RMS_WORKLOADS, SWIGLU_WORKLOADS, WORKLOADS, rms_workload,
-                                  swiglu_workload, workload)
+    from synthetic.inputs import (MM_WORKLOADS, RMS_WORKLOADS, SWIGLU_WORKLOADS, WORKLOADS,
+                                  mm_workload, rms_workload, swiglu_workload, workload)
     dev = "cuda:0"
     name = a.workload or "llama3_8b_gqa_decode"
+    if name in MM_WORKLOADS:
+        if a.copy_calibration:
+            log("calibration copy")
+            copy_calibration(dev)
+        log(f"timing {name}")
+        mprob = mm_workload(name)
+        rec = mm_record(mprob, time_prefill(mprob, a.steps, a.warmup, dev, mm=True), a.steps)
+        out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+               "data": "synthetic (seeded i.i.d. N(0,1), bf16-rounded; no model weights needed)"}
+        out.update(rec)
+        if not a.no_cpu:
+            log("timing the fp64 oracle on the host")
+            out["cpu_baseline"] = oracle_mm_baseline(mprob)
+        print(json.dumps(out), flush=True)
+        return
     if name in SWIGLU_WORKLOADS:
         if a.copy_calibration:
             log("calibration copy")
@@ -714,7 +786,8 @@ def main():
         return
     if name not in WORKLOADS:
         sys.exit(f"unknown workload {name}; choose from "
-                 f"{sorted(WORKLOADS) + sorted(RMS_WORKLOADS) + sorted(SWIGLU_WORKLOADS)}")
+                 f"{sorted(WORKLOADS) + sorted(RMS_WORKLOADS) + sorted(SWIGLU_WORKLOADS)}"
+                 f" + {sorted(MM_WORKLOADS)}")
     if a.copy_calibration:
         log("calibration copy")
         copy_calibration(dev)
@@ -827,6 +900,14 @@ def main():
         else:
             out["prefill"] = pre
     if a.workload is None and not a.no_prefill:
+        mname = "llama3_8b_matmul_matmul_prefill"
+        log(f"timing {mname}")
+        mprob = mm_workload(mname)
+        out["matmul_matmul"] = mm_record(mprob, time_prefill(mprob, a.steps, a.warmup, dev,
+                                                             mm=True), a.steps)
+        if not a.no_cpu:
+            log("timing the fp64 oracle on MatMul+MatMul heads")
+            out["matmul_matmul"]["cpu_baseline"] = oracle_mm_baseline(mprob)
         rname = "llama3_8b_rmsnorm_matmul_decode"
         log(f"timing {rname}")
         rprob = rms_workload(rname)

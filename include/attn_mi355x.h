@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define ATTN_MI355X_VERSION 3
+#define ATTN_MI355X_VERSION 4
 
 typedef enum attn_dtype {
   ATTN_F32 = 0,   /* IEEE binary32 */
@@ -243,6 +243,24 @@ int attn_combine(const attn_problem* problem, const attn_plan* plan,
  */
 int attn_prefill(const attn_problem* problem, const void* q, const void* k,
                  const void* v, void* o, float* lse_out, void* stream);
+
+/* MatMul+MatMul: O[b, i, h, :] = sum over visible keys j of
+ *   (tau * sum_d Q[b, i, h, d] K[b, j, h / G, d]) * V[b, j, h / G, :]
+ * i.e. O = (tau Q K^T) V per (request, query head) with no softmax between the
+ * two products (Cleave §7.3, Table 1: one of the two "consecutive reduction"
+ * subgraphs, where iterative tiling and memory planning matter).  The
+ * [Lq, L_b] intermediate exists one key tile at a time, in registers (§5.1 /
+ * §5.3 iterative tiling), rounded to bf16 as the second product's operand.
+ * Same problem description, layouts (strides, kv_lens, packed and paged K/V,
+ * packed ragged queries) and causal rule as attn_prefill; a key that is not
+ * visible contributes nothing, and a row with no visible key gives O = 0.
+ * tau = problem->scale, or 1/sqrt(head_dim_qk) when scale <= 0.
+ * Supported: bf16 Q/K/V with head_dim_qk = head_dim_v = 128 on the MFMA path
+ * (the layouts attn_prefill's MFMA kernel accepts); anything else returns
+ * ATTN_ERR_UNSUPPORTED before any launch.  o in problem->o_dtype.
+ */
+int attn_matmul_matmul(const attn_problem* problem, const void* q, const void* k,
+                       const void* v, void* o, void* stream);
 
 /* Static description of a status code; never NULL. */
 const char* attn_status_str(int status);

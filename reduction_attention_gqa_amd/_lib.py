@@ -25,7 +25,7 @@ ATTN_ERR_HIP = 4
 KERNEL_NAMES = {0: "generic", 1: "gqa_d128", 2: "mla"}
 
 EXPORTED = ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_decode", "attn_prefill",
-            "attn_status_str", "attn_last_error", "attn_version", "rmsnorm_matmul_plan",
+            "attn_matmul_matmul", "attn_status_str", "attn_last_error", "attn_version", "rmsnorm_matmul_plan",
             "rmsnorm_matmul", "swiglu_plan", "swiglu")
 
 
@@ -118,6 +118,7 @@ def load() -> ctypes.CDLL:
     lib.attn_decode.argtypes = [P, PL, V, V, V, V, ctypes.c_size_t, V, ctypes.c_size_t, V,
                                 ctypes.c_size_t, V, V, V]
     lib.attn_prefill.argtypes = [P, V, V, V, V, V, V]
+    lib.attn_matmul_matmul.argtypes = [P, V, V, V, V, V]
     RP, RC = ctypes.POINTER(RmsProblem), ctypes.POINTER(RmsConfig)
     lib.rmsnorm_matmul_plan.argtypes = [RP, ctypes.c_int32, ctypes.c_int32, RC]
     lib.rmsnorm_matmul.argtypes = [RP, RC, V, V, V, V, V, ctypes.c_size_t, V]
@@ -125,7 +126,8 @@ def load() -> ctypes.CDLL:
     lib.swiglu_plan.argtypes = [SP, ctypes.c_int32, ctypes.c_int32, SC]
     lib.swiglu.argtypes = [SP, SC, V, V, V, V, V, ctypes.c_size_t, V]
     for f in ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_decode",
-              "attn_prefill", "rmsnorm_matmul_plan", "rmsnorm_matmul", "swiglu_plan", "swiglu"):
+              "attn_prefill", "attn_matmul_matmul", "rmsnorm_matmul_plan", "rmsnorm_matmul",
+              "swiglu_plan", "swiglu"):
         getattr(lib, f).restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
     lib.attn_status_str.restype = ctypes.c_char_p
@@ -293,6 +295,12 @@ def attn_prefill(problem: AttnProblem, q, k, v, o, lse_out=None, stream=None) ->
                             _ptr(lse_out), _stream(stream)))
 
 
+def attn_matmul_matmul(problem: AttnProblem, q, k, v, o, stream=None) -> None:
+    lib = load()
+    _check(lib.attn_matmul_matmul(ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _stream(stream)))
+
+
 def workspace(plan: AttnPlan, device):
     """Allocate the workspace a plan asks for (torch owns the memory):
     (ws_o, ws_lse, ws_cnt); the arrival counters start at zero, as attn_decode
@@ -325,6 +333,12 @@ def decode(q, k, v, o, *, kv_lens=None, kv_lens_host=None, causal=False, scale=0
 def prefill(q, k, v, o, *, kv_lens=None, causal=False, scale=0.0, lse_out=None, stream=None):
     prob = make_problem(q, k, v, o, kv_lens=kv_lens, causal=causal, scale=scale)
     attn_prefill(prob, q, k, v, o, lse_out, stream)
+
+
+def matmul_matmul(q, k, v, o, *, kv_lens=None, causal=False, scale=0.0, stream=None):
+    """O = (tau Q K^T) V per (request, query head), no softmax between the products."""
+    prob = make_problem(q, k, v, o, kv_lens=kv_lens, causal=causal, scale=scale)
+    attn_matmul_matmul(prob, q, k, v, o, stream)
 
 
 def default_scale(dqk: int) -> float:

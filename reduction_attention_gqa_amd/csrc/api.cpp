@@ -507,6 +507,28 @@ int attn_prefill(const attn_problem* problem, const void* q, const void* k, cons
   return hip_status(launch_generic(kp, grid, dim3(kGenericBlock), s), "generic prefill launch");
 }
 
+int attn_matmul_matmul(const attn_problem* problem, const void* q, const void* k, const void* v,
+                       void* o, void* stream) {
+  g_err[0] = 0;
+  if (int st = check_problem(problem)) return st;
+  const attn_problem* p = problem;
+  if (p->batch == 0) return ATTN_OK;
+  if (int st = check_ptrs(q, "q", k, "k", v, "v")) return st;
+  if (!o) return fail(ATTN_ERR_ARG, "o is NULL");
+  if (!prefill_d128_fits(p, q, k, v, o))
+    return fail(ATTN_ERR_UNSUPPORTED,
+                "MatMul+MatMul needs bf16 Q/K/V with head_dim 128 and the MFMA prefill layouts");
+  KParams kp = base_params(p);
+  kp.q = q; kp.k = k; kp.v = v; kp.o = o;
+  kp.chunk = p->kv_len_max;
+  kp.s_max = 1;
+  kp.split_mode = 0;
+  kp.no_softmax = 1;
+  kp.scale_log2 = scale_of(p);  // the kernel multiplies the fp32 scores by tau itself
+  return hip_status(launch_prefill_d128(kp, reinterpret_cast<hipStream_t>(stream)),
+                    "matmul_matmul launch");
+}
+
 }  // extern "C"
 
 // ------------------------------------------------------ RMSNorm + MatMul

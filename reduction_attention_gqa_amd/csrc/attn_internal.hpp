@@ -41,7 +41,8 @@ struct KParams {
   int32_t rows;         // G * Lq rows per (request, KV head)
   int32_t row_tile;     // rows per workgroup (generic kernel)
   int32_t split_mode;   // 0: write o (+ lse_out); 1: write ws_o/ws_lse; 2: 1 + in-kernel merge
-  float scale_log2;     // tau * log2(e): scores are kept in base-2 units
+  float scale_log2;     // tau * log2(e): scores are kept in base-2 units (tau itself when no_softmax)
+  int32_t no_softmax;   // prefill only: 1 = MatMul+MatMul, O = (tau Q K^T) V
 };
 
 // RMSNorm followed by a MatMul: X [M, K], g [K], W [N, K], Y [M, N] (bf16

@@ -31,6 +31,12 @@
 // free of bank conflicts.  Every LDS read is a per-lane base register plus an
 // immediate (stage, key block, key step).
 //
+// SOFTMAX = false gives MatMul+MatMul (Cleave §7.3 subgraph list, the two
+// consecutive reductions without the softmax between them): the scores times
+// tau (KParams::scale_log2 then carries tau itself) are the intermediate, a
+// hidden key contributes 0, and O = U; the intermediate still lives one key
+// tile at a time in registers (iterative tiling, §5.1 / §5.3).
+//
 // Causal tiles beyond a tile's diagonal are never loaded; masking runs only on
 // tiles that straddle the diagonal or the end of the keys.  Workgroups are
 // issued heaviest first, and (when the group count allows) each XCD works
@@ -84,7 +90,7 @@ __device__ __forceinline__ int tile_off(int row, int c) { return row * RB + 16 *
 // tile i is consumed.  PAGED: K/V rows come from a page pool (power-of-two
 // page size); the request's page ids are staged in LDS after the rings and
 // each lane copies its row with a 64-bit-addressed global load into LDS.
-template <int KB, int NS, bool PAGED>
+template <int KB, int NS, bool PAGED, bool SOFTMAX>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_d128_kernel(KParams p, int nrt) {
   constexpr int TK = 32 * KB;         // keys per tile
@@ -285,7 +291,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
   // ones (the diagonal, the ragged end, rows past R) are masked.
   const int n_clean = (rw0 + 32 <= R) ? min(kfull_w, L) / TK : 0;
 
-  // Masked scores are set to -inf.  Lane element e of key block kb is key
+  // Masked scores are set to -inf (0 without the softmax).  Lane element e of key block kb is key
   // k0 + 32*kb + 8*(e/4) + 4*h + e%4.
   auto mask_scores = [&](f32x16_t* sc, int k0) {
 #pragma unroll
@@ -294,7 +300,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + 32 * kb + 8 * (e >> 2) + 4 * h + (e & 3);
         const bool vis = key < L && (!p.causal || key <= qlim) && row_ok;
-        sc[kb][e] = vis ? sc[kb][e] : kNegInf;
+        sc[kb][e] = vis ? sc[kb][e] : (SOFTMAX ? kNegInf : 0.f);
       }
   };
   // Row max of a score tile in base-2 units (both lane halves hold the row);
@@ -326,7 +332,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
         s_cur[kb] = mfma32x32x16(as_bf16x8(kread(0, kb, ks)), qf[ks], s_cur[kb]);
     }
     if (n_clean == 0) mask_scores(s_cur, 0);
-    mt_cur = tile_max(s_cur);
+    if constexpr (SOFTMAX) mt_cur = tile_max(s_cur);
   }
 
   // One key tile it (ring stage st = it % NS, a constant at every call site),
@@ -345,7 +351,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
     if (it + LOOK < ntiles) dma_tile(k0 + LOOK * TK, (st + LOOK) % NS);
 
     // Lazy rescale (rare).
-    if (__builtin_amdgcn_ballot_w64(mt_cur > m_ref + kRescaleThreshold) != 0) {
+    if (SOFTMAX && __builtin_amdgcn_ballot_w64(mt_cur > m_ref + kRescaleThreshold) != 0) {
       const float m_new = fmaxf(m_ref, mt_cur);
       const float alpha = (m_ref == kNegInf) ? 0.f : fast_exp2(m_ref - m_new);
       l_part *= alpha;
@@ -375,10 +381,14 @@ void prefill_d128_kernel(KParams p, int nrt) {
         s_nxt[g % KB] = mfma32x32x16(as_bf16x8(kf[g % 3]), qf[g / KB], s_nxt[g % KB]);
       }
       const int pc = g >> 3, e = (2 * g) & 15;
-      const float p0 = fast_exp2(__builtin_fmaf(s_cur[pc][e], sl2, -m_use));
-      const float p1 = fast_exp2(__builtin_fmaf(s_cur[pc][e + 1], sl2, -m_use));
-      pk[pc][e >> 1] = pack_bf16x2(p0, p1);
-      l_part += p0 + p1;  // row sum from the unrounded exponentials (exact LSE)
+      if constexpr (SOFTMAX) {
+        const float p0 = fast_exp2(__builtin_fmaf(s_cur[pc][e], sl2, -m_use));
+        const float p1 = fast_exp2(__builtin_fmaf(s_cur[pc][e + 1], sl2, -m_use));
+        pk[pc][e >> 1] = pack_bf16x2(p0, p1);
+        l_part += p0 + p1;  // row sum from the unrounded exponentials (exact LSE)
+      } else {
+        pk[pc][e >> 1] = pack_bf16x2(s_cur[pc][e] * sl2, s_cur[pc][e + 1] * sl2);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -407,14 +417,14 @@ void prefill_d128_kernel(KParams p, int nrt) {
       va[2] = vf[g & 1][1][0];
       va[3] = vf[g & 1][1][1];
       oacc[db] = mfma32x32x16(as_bf16x8(va), as_bf16x8(pb), oacc[db]);
-      if (next) {
+      if (SOFTMAX && next) {
         const int mc = g >> 3, ne = (2 * g) & 15;
         mx = vmax(mx, vmax(s_nxt[mc][ne], s_nxt[mc][ne + 1]));
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (next) {
-      mt_cur = row_max(mx) * sl2;
+      if constexpr (SOFTMAX) mt_cur = row_max(mx) * sl2;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_nxt[kb];
     }
@@ -457,11 +467,12 @@ void prefill_d128_kernel(KParams p, int nrt) {
   for (; it < ntiles - 1; ++it) step_any(it, true, true);
   if (ntiles > 0) step_any(ntiles - 1, false, false);
 
-  // Epilogue: O = U / l (division after the V-matmul), LSE = m + log l.
+  // Epilogue: O = U / l (division after the V-matmul), LSE = m + log l;
+  // without the softmax O = U.
   const float l_row = row_sum(l_part);
   if (row_ok) {
     const int qh = kvh * G + (r % G);
-    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+    const float inv = !SOFTMAX ? 1.f : (l_row > 0.f ? 1.f / l_row : 0.f);
     const int64_t obase = o_row_off(p, b, qi) + (int64_t)qh * p.os_h;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -480,24 +491,24 @@ void prefill_d128_kernel(KParams p, int nrt) {
           *reinterpret_cast<float4*>(reinterpret_cast<float*>(p.o) + obase + d) = v;
         }
       }
-    if (h == 0 && p.lse_out)
+    if (SOFTMAX && h == 0 && p.lse_out)
       p.lse_out[lse_row(p, b, qi) * p.Hq + qh] =
           l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : kNegInf;
   }
 }
 
-template <int KB, int NS, bool PAGED>
+template <int KB, int NS, bool PAGED, bool SOFTMAX>
 hipError_t launch_variant(const KParams& p, int nrt, int64_t nwg, hipStream_t s) {
   constexpr int lds = lds_bytes(KB, NS) + (PAGED ? 4 * kPrefillPageIds : 0);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_d128_kernel<KB, NS, PAGED>),
+        reinterpret_cast<const void*>(&prefill_d128_kernel<KB, NS, PAGED, SOFTMAX>),
         hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((prefill_d128_kernel<KB, NS, PAGED>), dim3((unsigned)nwg), dim3(NT), lds, s,
+  hipLaunchKernelGGL((prefill_d128_kernel<KB, NS, PAGED, SOFTMAX>), dim3((unsigned)nwg), dim3(NT), lds, s,
                      p, nrt);
   return hipGetLastError();
 }
@@ -508,8 +519,12 @@ hipError_t launch_prefill_d128(const KParams& p, hipStream_t s) {
   const int nrt = (p.rows + ROWS - 1) / ROWS;
   const int64_t nwg = (int64_t)p.B * p.Hkv * nrt;
   if (nwg == 0) return hipSuccess;
-  if (p.page_table) return launch_variant<1, kPrefillStages, true>(p, nrt, nwg, s);
-  return launch_variant<1, kPrefillStages, false>(p, nrt, nwg, s);
+  if (p.no_softmax) {
+    if (p.page_table) return launch_variant<1, kPrefillStages, true, false>(p, nrt, nwg, s);
+    return launch_variant<1, kPrefillStages, false, false>(p, nrt, nwg, s);
+  }
+  if (p.page_table) return launch_variant<1, kPrefillStages, true, true>(p, nrt, nwg, s);
+  return launch_variant<1, kPrefillStages, false, true>(p, nrt, nwg, s);
 }
 
 }  // namespace attn

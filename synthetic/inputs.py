@@ -17,6 +17,9 @@ Workloads (named by what they are, with their sizes):
 * ``mla_decode``            bf16, B=64, 128 query heads over one latent KV head,
   Dqk=576 (512 latent + 64 rotary), Dv=512 (V is the first 512 columns of K),
   8192 keys.
+* ``llama3_8b_matmul_matmul_prefill`` (``mm_workload``) bf16, B=4, 4096 queries
+  and keys, 32/8 heads, D=128, no mask: MatMul+MatMul, O = (tau Q K^T) V per
+  head, at Llama-3 8B's attention shapes.
 
 Recipe (stated once, used by tests, smoke and bench):
 
@@ -138,11 +141,14 @@ def log_uniform_lengths(rng: np.random.Generator, n: int, lo: int, hi: int) -> n
 def make_problem(*, name: str = "custom", dtype: str = "bf16", batch: int, lq: int,
                  hq: int, hkv: int, dqk: int, dv: int, kv_len, seed: int = 0,
                  causal: bool = False, mla: bool = False, lcap: Optional[int] = None,
-                 scale: Optional[float] = None, s: Optional[int] = None) -> Problem:
+                 scale: Optional[float] = None, s: Optional[int] = None,
+                 qk_ternary: bool = False) -> Problem:
     """Draw one problem.
 
     ``kv_len`` is an int (every request has that many keys), a (lo, hi) tuple
     (log-uniform per request), or an explicit sequence of per-request lengths.
+    ``qk_ternary``: Q and K entries drawn uniformly from {-1, 0, 1} instead
+    (same draw order), so every Q K^T entry is a small integer.
     """
     if dtype not in ("f32", "bf16"):
         raise ValueError(f"dtype must be 'f32' or 'bf16', got {dtype!r}")
@@ -161,8 +167,12 @@ def make_problem(*, name: str = "custom", dtype: str = "bf16", batch: int, lq: i
         raise ValueError("a request length exceeds the capacity")
     rnd = (lambda a: to_bf16_exact(a)) if dtype == "bf16" else (lambda a: a)
 
-    q = rnd(rng.standard_normal((batch, lq, hq, dqk), dtype=np.float32))
-    k = [rnd(rng.standard_normal((int(n), hkv, dqk), dtype=np.float32)) for n in lens]
+    if qk_ternary:
+        draw = lambda shape: rng.integers(-1, 2, size=shape).astype(np.float32)  # noqa: E731
+    else:
+        draw = lambda shape: rnd(rng.standard_normal(shape, dtype=np.float32))  # noqa: E731
+    q = draw((batch, lq, hq, dqk))
+    k = [draw((int(n), hkv, dqk)) for n in lens]
     if mla:
         if dv > dqk:
             raise ValueError("MLA needs dv <= dqk (V is a slice of K)")
@@ -182,6 +192,20 @@ def workload(name: str, seed: int = 0) -> Problem:
                         lq=w["lq"], hq=w["hq"], hkv=w["hkv"], dqk=w["dqk"], dv=w["dv"],
                         kv_len=w["kv_len"], causal=w.get("causal", False),
                         mla=w.get("mla", False), lcap=w.get("lcap"), s=w.get("s"))
+
+
+MM_WORKLOADS = {
+    "llama3_8b_matmul_matmul_prefill": dict(dtype="bf16", batch=4, lq=4096, hq=32, hkv=8,
+                                            dqk=128, dv=128, kv_len=4096, causal=False),
+}
+
+
+def mm_workload(name: str, seed: int = 0) -> Problem:
+    """The named MatMul+MatMul workload (same Problem layout and recipe as attention)."""
+    w = dict(MM_WORKLOADS[name])
+    return make_problem(name=name, seed=seed, dtype=w["dtype"], batch=w["batch"], lq=w["lq"],
+                        hq=w["hq"], hkv=w["hkv"], dqk=w["dqk"], dv=w["dv"], kv_len=w["kv_len"],
+                        causal=w["causal"])
 
 
 def padded(rows: list, lcap: int, pad: float = float("nan")) -> np.ndarray:

@@ -142,6 +142,32 @@ def test_invalid_problem_is_rejected_everywhere(lib, field, value, code):
                             None) == code
     assert lib.attn_decode(ctypes.byref(p), ctypes.byref(plan), fake, fake, fake, fake, 1 << 30,
                            fake, 1 << 30, fake, 1 << 30, fake, None, None) == code
+    assert lib.attn_matmul_matmul(ctypes.byref(p), fake, fake, fake, fake, None) == code
+
+
+@pytest.mark.parametrize("field,value", [("dtype", ra.ATTN_F32), ("head_dim_qk", 64),
+                                         ("head_dim_v", 64)])
+def test_matmul_matmul_unsupported_shapes_fail_before_launch(lib, field, value):
+    # Valid problems the MFMA path does not cover: rejected before any device
+    # access (the pointers are never dereferenced).
+    kw = {field: value}
+    if field == "dtype":
+        kw["o_dtype"] = ra.ATTN_F32
+    p = problem(q_len=64, kv_len_max=64, **kw)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.attn_matmul_matmul(ctypes.byref(p), fake, fake, fake, fake, None) == \
+        ra.ATTN_ERR_UNSUPPORTED
+    assert b"MatMul+MatMul" in lib.attn_last_error()
+
+
+def test_matmul_matmul_arguments(lib):
+    fake = ctypes.c_void_p(0x1000)
+    p = problem(q_len=64, kv_len_max=64)
+    assert lib.attn_matmul_matmul(None, fake, fake, fake, fake, None) == ra.ATTN_ERR_ARG
+    assert lib.attn_matmul_matmul(ctypes.byref(p), None, fake, fake, fake, None) == ra.ATTN_ERR_ARG
+    assert lib.attn_matmul_matmul(ctypes.byref(p), fake, fake, fake, None, None) == ra.ATTN_ERR_ARG
+    p0 = problem(batch=0, q_len=64, kv_len_max=64)
+    assert lib.attn_matmul_matmul(ctypes.byref(p0), None, None, None, None, None) == ra.ATTN_OK
 
 
 def test_negative_stride_and_nonfinite_scale(lib):

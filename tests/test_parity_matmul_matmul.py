@@ -114,3 +114,32 @@ def test_full_size_sampled_rows():
     report("mm full sampled", got, want)
     assert np.all(err <= worst)
     assert err.mean() <= rms.mean()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_packed_keys_and_ragged_queries(causal):
+    # Packed keys (kv_indptr) and packed ragged queries (q_indptr): request b
+    # keeps its first q_lens[b] query rows, bottom-right causal alignment with
+    # its own row count; the spare O rows after the last request stay unwritten.
+    from gpu_helpers import PackedDeviceProblem
+    p = make_problem(dtype="bf16", batch=3, lq=300, hq=8, hkv=2, dqk=128, dv=128,
+                     kv_len=[260, 40, 300], seed=57, causal=causal, scale=1.0, qk_ternary=True)
+    q_lens = [300, 17, 0]
+    d = PackedDeviceProblem(p, q_lens=q_lens, o_dtype="f32")
+    ra.attn_matmul_matmul(d.problem(), d.q, d.k, d.v, d.o)
+    torch.cuda.synchronize()
+    out = d.o.float().cpu().numpy().astype(np.float64)
+    assert np.all(np.isnan(out[d.tq:])), "rows past the last request were written"
+    got = out[:d.tq]
+    want, worst = [], []
+    vr = v_rows(p)
+    for b, n in enumerate(q_lens):
+        if n == 0:
+            continue
+        qb = p.q[b:b + 1, :n]
+        want.append(matmul_matmul(qb, [p.k[b]], [vr[b]], causal, p.scale)[0])
+        worst.append(error_bounds(qb, [p.k[b]], [vr[b]], causal, p.scale,
+                                  rounds_intermediate=False)[0][0])
+    want, worst = np.concatenate(want), np.concatenate(worst)
+    report(f"mm packed causal={causal}", got, want)
+    assert np.all(np.abs(got - want) <= worst)

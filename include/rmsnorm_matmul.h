@@ -52,7 +52,7 @@ typedef struct rmsnorm_matmul_problem {
 typedef struct rmsnorm_matmul_config {
   int32_t s;            /* K parts, >= 1 */
   int32_t k_chunk;      /* columns per part, a multiple of 32 */
-  uint32_t grid[3];     /* split-kernel grid: 256-column tiles of n, s, 32-row tiles of m */
+  uint32_t grid[3];     /* split-kernel grid: 64-column tiles of n, s, 32-row tiles of m */
   uint32_t block;       /* split-kernel threads per workgroup */
   uint64_t ws_bytes;    /* fp32 workspace: (s*m*n + s*m) * 4 bytes when s > 1, else 0 */
   uint64_t problem_key; /* fingerprint of the planned problem */
@@ -62,9 +62,10 @@ typedef struct rmsnorm_matmul_config {
  * rmsnorm_matmul_plan - choose s (Cleave §2.2 "Split-K"; §7.3 decode setting).
  *
  * s_request  <= 0: the planner picks the largest s whose workgroups (one
- *            per 256 x 32 output tile and part) fit on num_cus compute units
- *            at once, with at least 128 columns of K per part.  > 0: s = min(s_request, k / 32), rounded
- *            to whole 32-column steps.
+ *            per 64 x 32 output tile and part; the four waves of a workgroup
+ *            split the part's columns among themselves) fit on num_cus compute
+ *            units at once, with at least 512 columns of K per part.  > 0:
+ *            s = min(s_request, k / 32), rounded to whole 32-column steps.
  * num_cus    compute units to plan for; <= 0 queries the current device.
  * Returns ATTN_OK, ATTN_ERR_ARG, ATTN_ERR_UNSUPPORTED or ATTN_ERR_HIP (device
  * query failed).  Enqueues nothing.

@@ -52,7 +52,7 @@ typedef struct swiglu_problem {
 typedef struct swiglu_config {
   int32_t s;            /* K parts, >= 1 */
   int32_t k_chunk;      /* columns per part, a multiple of 32 */
-  uint32_t grid[3];     /* split-kernel grid: 128-column tiles of n, s, 32-row tiles of m */
+  uint32_t grid[3];     /* split-kernel grid: 64-column tiles of n, s, 32-row tiles of m */
   uint32_t block;       /* split-kernel threads per workgroup */
   uint64_t ws_bytes;    /* fp32 workspace: 2 * s * m * n * 4 bytes when s > 1, else 0 */
   uint64_t problem_key; /* fingerprint of the planned problem */
@@ -60,9 +60,10 @@ typedef struct swiglu_config {
 
 /*
  * swiglu_plan - choose s (Cleave §2.2 "Split-K").
- * s_request  <= 0: the largest s whose workgroups (one per 128 x 32 output
- *            tile and part) fit on num_cus compute units at once, with at
- *            least 128 columns of K per part.  > 0: s = min(s_request, k / 32).
+ * s_request  <= 0: the largest s whose workgroups (one per 64 x 32 output
+ *            tile and part; two waves split each part's columns) fit on
+ *            num_cus compute units at once, with at least 256 columns of K per
+ *            part.  > 0: s = min(s_request, k / 32).
  * num_cus    compute units to plan for; <= 0 queries the current device.
  * Returns ATTN_OK, ATTN_ERR_ARG, ATTN_ERR_UNSUPPORTED or ATTN_ERR_HIP.
  */

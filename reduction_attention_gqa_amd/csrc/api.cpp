@@ -536,7 +536,7 @@ int attn_matmul_matmul(const attn_problem* problem, const void* q, const void* k
 namespace attn {
 namespace {
 
-constexpr int kRmsTileN = 256;  // weight rows per split-kernel workgroup
+constexpr int kRmsTileN = 64;   // weight rows per split-kernel workgroup
 constexpr int kRmsTileM = 32;   // tokens per split-kernel workgroup
 constexpr int kRmsBlock = 256;
 
@@ -594,9 +594,10 @@ int rmsnorm_matmul_plan(const rmsnorm_matmul_problem* problem, int32_t s_request
     s = std::min<int64_t>(s_request, steps);
   } else if (tiles > 0) {
     // The most parts whose workgroups still run in one round (one per compute
-    // unit; each keeps ~48 KB of W in flight), at least four k-steps per part.
+    // unit; each of its four waves keeps a 16 KiB super-step of W in flight),
+    // at least four k-steps per wave (a part is split over the four waves).
     s = (int64_t)cus / tiles;
-    s = std::max<int64_t>(1, std::min<int64_t>(s, steps / 4));
+    s = std::max<int64_t>(1, std::min<int64_t>(s, steps / 16));
   }
   const int64_t chunk_steps = ceil_div(steps, s);
   s = ceil_div(steps, chunk_steps);
@@ -655,7 +656,7 @@ int rmsnorm_matmul(const rmsnorm_matmul_problem* problem, const rmsnorm_matmul_c
 namespace attn {
 namespace {
 
-constexpr int kSwTileN = 128;  // output columns per split-kernel workgroup
+constexpr int kSwTileN = 64;   // output columns per split-kernel workgroup
 constexpr int kSwTileM = 32;   // tokens per split-kernel workgroup
 
 int check_swiglu(const swiglu_problem* p) {
@@ -711,7 +712,7 @@ int swiglu_plan(const swiglu_problem* problem, int32_t s_request, int32_t num_cu
     s = std::min<int64_t>(s_request, steps);
   } else if (tiles > 0) {
     s = (int64_t)cus / tiles;
-    s = std::max<int64_t>(1, std::min<int64_t>(s, steps / 4));
+    s = std::max<int64_t>(1, std::min<int64_t>(s, steps / 8));  // >= 4 k-steps per wave
   }
   const int64_t chunk_steps = ceil_div(steps, s);
   s = ceil_div(steps, chunk_steps);

@@ -9,15 +9,20 @@
 // and a combine kernel adds them up and applies the row scale.
 //
 // Layout: X [M, K], g [K], W [N, K] (linear-layer weights), Y [M, N], row
-// strides in elements, bf16 inputs.  A workgroup is four waves; wave w owns
-// 64 weight rows (four MFMA row blocks) of the workgroup's 256 and up to 32
-// tokens (two MFMA column groups), over the split's K range:
+// strides in elements, bf16 inputs.  A workgroup is four waves that share the
+// workgroup's 64 weight rows (four MFMA row blocks) and up to 32 tokens (two
+// MFMA column groups) and split the part's K range four ways, wave w taking
+// the w-th quarter (a second, on-chip level of the same split-K):
 //   U^T[16 x 16] += W[16 x 32] (X * g)^T[32 x 16]     16x16x32 bf16 MFMA
 // W streams from HBM straight into the A operand (16 bytes per lane and row
 // block, four k-steps in flight); X and g come through the caches (a few KB,
 // shared by all workgroups) and each fragment serves the wave's four row
 // blocks.  x * g is exact in fp32 (two 8-bit significands); it enters the
-// MFMA as a bf16 pair hi + lo, so the gain costs no precision.
+// MFMA as a bf16 pair hi + lo, so the gain costs no precision.  The four
+// waves' partial dot products and sums of squares are added through LDS, and
+// wave w finishes row block w: with the whole K range in one part (s = 1) it
+// applies the row scale and writes Y, so one launch does everything;
+// otherwise it writes the part's sums for the combine kernel.
 #include "../attn_internal.hpp"
 #include "common.hpp"
 
@@ -26,7 +31,8 @@ namespace {
 
 constexpr int NW = 4;      // waves per workgroup
 constexpr int NRB = 4;     // 16-row weight blocks per wave
-constexpr int ROWS = NW * NRB * 16;  // weight rows per workgroup
+constexpr int ROWS = NRB * 16;  // weight rows per workgroup (shared by its waves)
+static_assert(NRB == NW, "wave w finishes row block w");
 constexpr int NBUF = 4;    // k-steps in flight per wave
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every range: loads read zero
 
@@ -78,8 +84,12 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
   const int n_wg = blockIdx.x * ROWS;
   const int j = blockIdx.y;
   const int m0 = blockIdx.z * 32;
-  const int lo = j * p.k_chunk;
-  const int hi = min(lo + p.k_chunk, p.K);
+  // This wave's quarter of the part's columns (a multiple of 32 wide).
+  const int lo_j = j * p.k_chunk;
+  const int hi_j = min(lo_j + p.k_chunk, p.K);
+  const int kcw = (p.k_chunk + 32 * NW - 1) / (32 * NW) * 32;
+  const int lo = min(lo_j + w * kcw, hi_j);
+  const int hi = min(lo + kcw, hi_j);
 
   // Buffer ranges end at the last valid weight row / token, so rows past N or
   // M read as zero.  Offsets stay 32-bit: a workgroup's 256 rows, 32 tokens.
@@ -91,7 +101,7 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wp, (uint32_t)wrows * wst);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xp, (uint32_t)xrows * xst);
   const __amdgpu_buffer_rsrc_t grs = make_rsrc(p.g, (uint32_t)p.K * 2);
-  const uint32_t w_lane = (uint32_t)(NRB * 16 * w + r) * wst + 16u * kg;
+  const uint32_t w_lane = (uint32_t)r * wst + 16u * kg;
   const uint32_t x_lane0 = (uint32_t)r * xst + 16u * kg;
   const uint32_t x_lane1 = (uint32_t)(16 + r) * xst + 16u * kg;
 
@@ -178,37 +188,59 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
     }
   }
 
-  // Sums of squares of token r over the split: add the four column groups.
+  // Sums of squares of token r over this wave's columns: add the four column groups.
 #pragma unroll
   for (int mg = 0; mg < 2; ++mg) {
     ssq[mg] += __shfl_xor(ssq[mg], 16, 64);
     ssq[mg] += __shfl_xor(ssq[mg], 32, 64);
   }
 
-  // Lane holds U^T[weight row 16 b + 4 kg + i][token r] of each column group.
+  // Add the four waves' parts: wave w keeps row block w.  Lane holds
+  // U^T[weight row 16 b + 4 kg + i][token r] of each column group.
+  __shared__ f32x4_t red[NW][NRB * 2][64];  // 32 KiB
+  __shared__ float red_ssq[NW][2][16];
+#pragma unroll
+  for (int b = 0; b < NRB; ++b)
+#pragma unroll
+    for (int mg = 0; mg < 2; ++mg) red[w][2 * b + mg][lane] = acc[b][mg];
+  if (kg == 0) {
+    red_ssq[w][0][r] = ssq[0];
+    red_ssq[w][1][r] = ssq[1];
+  }
+  __syncthreads();
+  f32x4_t tot[2];
+  float ssq_tot[2];
+#pragma unroll
+  for (int mg = 0; mg < 2; ++mg) {
+    tot[mg] = red[0][2 * w + mg][lane];
+    ssq_tot[mg] = red_ssq[0][mg][r];
+#pragma unroll
+    for (int u = 1; u < NW; ++u) {
+      tot[mg] += red[u][2 * w + mg][lane];
+      ssq_tot[mg] += red_ssq[u][mg][r];
+    }
+  }
+
+  const int n_lane = n_wg + 16 * w + 4 * kg;
 #pragma unroll
   for (int mg = 0; mg < 2; ++mg) {
     const int m = m0 + 16 * mg + r;
     if (m >= p.M) continue;
-    // With the whole K range here, apply the row scale after the Matmul.
-    const float scale = p.s == 1 ? 1.0f / sqrtf(ssq[mg] / (float)p.K + p.eps) : 1.0f;
-#pragma unroll
-    for (int b = 0; b < NRB; ++b) {
-      const int n_lane = n_wg + NRB * 16 * w + 16 * b + 4 * kg;
-      if (p.s == 1) {
-        store_row4(p, m, n_lane, acc[b][mg] * scale);
-        continue;
-      }
-      float* dst = p.ws_u + ((int64_t)j * p.M + m) * p.N + n_lane;
-      if (n_lane + 3 < p.N && (p.N & 3) == 0) {
-        *reinterpret_cast<f32x4_t*>(dst) = acc[b][mg];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (n_lane + i < p.N) dst[i] = acc[b][mg][i];
-      }
+    if (p.s == 1) {
+      // The whole K range is here: apply the row scale after the Matmul.
+      const float scale = 1.0f / sqrtf(ssq_tot[mg] / (float)p.K + p.eps);
+      store_row4(p, m, n_lane, tot[mg] * scale);
+      continue;
     }
-    if (p.s > 1 && blockIdx.x == 0 && w == 0 && kg == 0) p.ws_ssq[(int64_t)j * p.M + m] = ssq[mg];
+    float* dst = p.ws_u + ((int64_t)j * p.M + m) * p.N + n_lane;
+    if (n_lane + 3 < p.N && (p.N & 3) == 0) {
+      *reinterpret_cast<f32x4_t*>(dst) = tot[mg];
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (n_lane + i < p.N) dst[i] = tot[mg][i];
+    }
+    if (blockIdx.x == 0 && w == 0 && kg == 0) p.ws_ssq[(int64_t)j * p.M + m] = ssq_tot[mg];
   }
 }
 

@@ -7,13 +7,19 @@
 // before silu is applied.
 //
 // Layout: X [M, K], W_gate and W_up [N, K] (linear-layer weights), H [M, N],
-// row strides in elements, bf16 inputs.  A workgroup is four waves; wave w
-// owns 32 output columns (two 16-row blocks of each weight matrix, the same
-// rows in both) and up to 32 tokens on the MFMA columns:
+// row strides in elements, bf16 inputs.  A workgroup is four waves and owns
+// 64 output columns and up to 32 tokens on the MFMA columns; waves 2c and
+// 2c + 1 share columns 32c .. 32c + 31 (two 16-row blocks of each weight
+// matrix, the same rows in both) and take the two halves of the part's K
+// range (a second, on-chip level of the same split-K):
 //   G^T[16 x 16] += W_gate[16 x 32] X^T[32 x 16],  U^T likewise   16x16x32 MFMA
 // The weights move a super-step (four 32-column k-steps, 256 contiguous
 // bytes per row) ahead of use, double-buffered; X (a few KB, through the
 // caches) is issued first so in-order completion never holds it behind W.
+// The two halves are added through LDS and each wave of the pair finishes
+// one row block: with the whole K range in one part (s = 1) it applies the
+// gate and writes H, so one launch does everything; otherwise it writes the
+// part's sums for the combine kernel.
 #include "../attn_internal.hpp"
 #include "common.hpp"
 
@@ -22,7 +28,8 @@ namespace {
 
 constexpr int NW = 4;       // waves per workgroup
 constexpr int NRB = 2;      // 16-row blocks per wave and weight matrix
-constexpr int COLS = NW * NRB * 16;  // output columns per workgroup
+constexpr int COLS = NW / 2 * NRB * 16;  // output columns per workgroup (64)
+static_assert(NW == 4 && NRB == 2, "a wave pair covers one column group; each wave finishes one block");
 constexpr int SS = 4;       // k-steps per super-step
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every range: loads read zero
 
@@ -83,11 +90,15 @@ __global__ __launch_bounds__(NW * 64) void swiglu_split_kernel(SwigluParams p) {
   const int n_wg = blockIdx.x * COLS;
   const int j = blockIdx.y;
   const int m0 = blockIdx.z * 32;
-  const int lo = j * p.k_chunk;
-  const int hi = min(lo + p.k_chunk, p.K);
+  // This wave's half of the part's columns (a multiple of 32 wide).
+  const int lo_j = j * p.k_chunk;
+  const int hi_j = min(lo_j + p.k_chunk, p.K);
+  const int kch = (p.k_chunk + 63) / 64 * 32;
+  const int lo = min(lo_j + (w & 1) * kch, hi_j);
+  const int hi = min(lo + kch, hi_j);
 
   // Buffer ranges end at the last valid weight row / token, so rows past N or
-  // M read as zero.  Offsets stay 32-bit: a workgroup's 128 rows, 32 tokens.
+  // M read as zero.  Offsets stay 32-bit: a workgroup's 64 rows, 32 tokens.
   const int wrows = min(COLS, p.N - n_wg);
   const int xrows = min(32, p.M - m0);
   const uint16_t* gp = reinterpret_cast<const uint16_t*>(p.wg) + (int64_t)n_wg * p.wg_row;
@@ -98,7 +109,7 @@ __global__ __launch_bounds__(NW * 64) void swiglu_split_kernel(SwigluParams p) {
   const __amdgpu_buffer_rsrc_t grs = make_rsrc(gp, (uint32_t)wrows * gst);
   const __amdgpu_buffer_rsrc_t urs = make_rsrc(up, (uint32_t)wrows * ust);
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xp, (uint32_t)xrows * xst);
-  const int row0 = NRB * 16 * w + r;  // this lane's first weight row in the workgroup
+  const int row0 = NRB * 16 * (w >> 1) + r;  // this lane's first weight row in the workgroup
   const uint32_t x_lane0 = (uint32_t)r * xst + 16u * kg;
   const uint32_t x_lane1 = (uint32_t)(16 + r) * xst + 16u * kg;
 
@@ -164,24 +175,34 @@ __global__ __launch_bounds__(NW * 64) void swiglu_split_kernel(SwigluParams p) {
     }
   }
 
-  // Lane holds G^T / U^T[weight row 16 b + 4 kg + i][token r] of each group.
+  // Add the pair's halves: lane holds G^T / U^T[weight row 16 b + 4 kg + i]
+  // [token r] of each token group; wave w keeps row block w & 1 of its pair.
+  __shared__ f32x4_t red[NW][2][NRB][2][64];  // [wave][gate, up][block][token group][lane]: 32 KiB
+#pragma unroll
+  for (int b = 0; b < NRB; ++b)
+#pragma unroll
+    for (int mg = 0; mg < 2; ++mg) {
+      red[w][0][b][mg][lane] = acc_g[b][mg];
+      red[w][1][b][mg][lane] = acc_u[b][mg];
+    }
+  __syncthreads();
+  const int blk = w & 1, w0 = w & ~1;
+  const int n_lane = n_wg + NRB * 16 * (w >> 1) + 16 * blk + 4 * kg;
 #pragma unroll
   for (int mg = 0; mg < 2; ++mg) {
     const int m = m0 + 16 * mg + r;
     if (m >= p.M) continue;
+    const f32x4_t g = red[w0][0][blk][mg][lane] + red[w0 + 1][0][blk][mg][lane];
+    const f32x4_t u = red[w0][1][blk][mg][lane] + red[w0 + 1][1][blk][mg][lane];
+    if (p.s == 1) {
+      f32x4_t h;
 #pragma unroll
-    for (int b = 0; b < NRB; ++b) {
-      const int n_lane = n_wg + NRB * 16 * w + 16 * b + 4 * kg;
-      if (p.s == 1) {
-        f32x4_t h;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = silu(acc_g[b][mg][i]) * acc_u[b][mg][i];
-        store_h4(p, m, n_lane, h);
-      } else {
-        const int64_t part = (int64_t)j * p.M * p.N;
-        store_part4(p.ws_g + part, p, m, n_lane, acc_g[b][mg]);
-        store_part4(p.ws_u + part, p, m, n_lane, acc_u[b][mg]);
-      }
+      for (int i = 0; i < 4; ++i) h[i] = silu(g[i]) * u[i];
+      store_h4(p, m, n_lane, h);
+    } else {
+      const int64_t part = (int64_t)j * p.M * p.N;
+      store_part4(p.ws_g + part, p, m, n_lane, g);
+      store_part4(p.ws_u + part, p, m, n_lane, u);
     }
   }
 }

@@ -912,10 +912,14 @@ def main():
         log(f"timing {rname}")
         rprob = rms_workload(rname)
         out["rmsnorm_matmul"] = rms_record(rprob, time_rms(rprob, a.steps, a.warmup, dev), a.steps)
+        if not a.no_cpu:
+            out["rmsnorm_matmul"]["cpu_baseline"] = oracle_rms_baseline(rprob)
         sname = "llama3_8b_swiglu_decode"
         log(f"timing {sname}")
         sprob = swiglu_workload(sname)
         out["swiglu"] = swiglu_record(sprob, time_swiglu(sprob, a.steps, a.warmup, dev), a.steps)
+        if not a.no_cpu:
+            out["swiglu"]["cpu_baseline"] = oracle_swiglu_baseline(sprob)
     line = json.dumps(out)
     print(line, flush=True)
     if a.json_out:

@@ -143,3 +143,15 @@ def test_packed_keys_and_ragged_queries(causal):
     want, worst = np.concatenate(want), np.concatenate(worst)
     report(f"mm packed causal={causal}", got, want)
     assert np.all(np.abs(got - want) <= worst)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_shape(causal):
+    # One query row per request (the decode setting of Cleave §7.3): G = 4 rows
+    # per KV head, key counts from 1 to 3000 (one row tile per (request, KV
+    # head), most of its rows empty); for Lq = 1 the causal flag changes nothing.
+    p = make_problem(dtype="bf16", batch=4, lq=1, hq=32, hkv=8, dqk=128, dv=128,
+                     kv_len=[3000, 1, 517, 64], lcap=3008, seed=58, causal=causal, scale=1.0,
+                     qk_ternary=True)
+    d = DeviceProblem(p, o_dtype="f32", layout="head")
+    _check(f"mm decode causal={causal}", _run(d), p, exact_intermediate=True)

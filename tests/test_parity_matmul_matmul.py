@@ -11,13 +11,15 @@ accumulation remains, a bound tight enough that one dropped or misplaced key
 fails it.  bf16-output O must equal round-to-nearest-even of the fp32-output O
 bit for bit.
 """
+import time
+
 import numpy as np
 import pytest
 import torch
 
 import reduction_attention_gqa_amd as ra
 from gpu_helpers import DeviceProblem, PagedDeviceProblem, report, v_rows
-from oracle import error_bounds, matmul_matmul, matmul_matmul_rows
+from oracle import error_bounds, matmul_matmul
 from synthetic.inputs import make_problem, mm_workload
 
 pytestmark = pytest.mark.gpu
@@ -92,28 +94,19 @@ def test_no_keys_gives_zero():
     _check("mm empty request", got, p)
 
 
-def test_full_size_sampled_rows():
+def test_full_size_whole_output():
+    # The full workload (B=4, 4096 queries and keys, 32/8 heads, D=128, no
+    # mask) in the launch configuration the benchmark times: every output
+    # element within its worst-case bound, the mean error within the mean RMS
+    # bound.
     p = mm_workload("llama3_8b_matmul_matmul_prefill")
     print(f"[case] {p.name}: B={p.batch} Lq={p.lq} L={p.lcap} heads {p.hq}/{p.hkv}", flush=True)
     d = DeviceProblem(p, o_dtype="f32", pad=0.0)
-    out = _run(d)
-    rng = np.random.default_rng(56)
-    rows = [(int(rng.integers(p.batch)), int(rng.integers(p.lq)), int(rng.integers(p.hq)))
-            for _ in range(24)] + [(0, 0, 0), (p.batch - 1, p.lq - 1, p.hq - 1)]
-    want = matmul_matmul_rows(p.q, p.k, v_rows(p), False, p.scale, rows)
-    got = np.stack([out[r] for r in rows])
-    g = p.hq // p.hkv
-    worst = np.zeros_like(want)
-    rms = np.zeros_like(want)
-    for n, (b, i, h) in enumerate(rows):
-        kvh = h // g
-        w_r, r_r = error_bounds(p.q[b:b + 1, i:i + 1, h:h + 1], [p.k[b][:, kvh:kvh + 1]],
-                                [v_rows(p)[b][:, kvh:kvh + 1]], False, p.scale)
-        worst[n], rms[n] = w_r[0, 0, 0], r_r[0, 0, 0]
-    err = np.abs(got - want)
-    report("mm full sampled", got, want)
-    assert np.all(err <= worst)
-    assert err.mean() <= rms.mean()
+    got = _run(d)
+    t0 = time.perf_counter()
+    _check("mm whole output", got, p)
+    print(f"[oracle] {p.name}: whole output and bounds in {time.perf_counter() - t0:.1f} s",
+          flush=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])

@@ -161,7 +161,15 @@ typedef struct attn_plan {
  *              s_max = min(s_request, ceil(Lmax / tile_n)) with
  *              chunk = round_up(ceil(Lmax / s_max), tile_n).
  * kv_lens_host host copy of the B key counts used to size the split (values
- *              clamped to [0, Lcap]), or NULL for "all Lcap".
+ *              clamped to [0, Lcap]), or NULL for "all Lcap".  The device
+ *              counts (problem->kv_lens or kv_indptr) of every call made with
+ *              the plan must not exceed these: the split count, the chunk
+ *              and (GQA family) the grid of work items cover exactly these
+ *              lengths.  Where the device counts need more (a request longer
+ *              than s_max * chunk keys, or more GQA work items than n_items),
+ *              the affected output rows are written as NaN rather than a
+ *              truncated result (all launched rows, in the second case), and
+ *              ws_cnt is left as it was.
  * num_cus      compute units to plan for; <= 0 queries the current device.
  * out          receives the plan.
  * With a page table, the MFMA kernels stage one split's page ids on chip, so

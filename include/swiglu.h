@@ -4,9 +4,9 @@
  *
  *   H = silu(X W_gate^T) * (X W_up^T),  silu(z) = z / (1 + exp(-z))
  *
- * The two MatMuls share their input, so they are fused horizontally (Cleave
- * §7.3: SwiGLU's parallel reduction structure with a common input): each X
- * tile feeds both reductions in one loop and each weight matrix is read once.
+ * Both MatMuls reduce over K and read the same X, so they are fused
+ * horizontally (Cleave §7.3): each X tile feeds both reductions in one loop
+ * and each weight matrix is read once.
  * When there are too few output tiles to fill the GPU (the decode setting:
  * a few tokens) the K axis is split in s parts (Cleave §2.2 "Split-K"); the
  * parts of both MatMuls are added up in a second launch, which then applies

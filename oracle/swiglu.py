@@ -9,9 +9,8 @@ Source: the Cleave paper ("Cleave: Scaling Tensor Program Optimization via
 Decoupled Algebraic Search and Operator Scheduling", paperpeel.com text).
 
 * §7.3: SwiGLU is one of the dense transformer subgraphs evaluated, with
-  Llama-3 8B shapes; it has a parallel reduction structure with a common
-  input, so the two MatMuls can be fused horizontally (both consume the same
-  input tile in one loop).
+  Llama-3 8B shapes.  Both of its MatMuls reduce over K and read the same X,
+  so one loop over K can feed both (horizontal fusion).
 * §2.2 "Split-K": each MatMul's reduction over K is the sum of partial
   reductions over contiguous parts.  The gate is nonlinear, so the parts of
   both MatMuls are added up before it is applied (``swiglu_combine``).

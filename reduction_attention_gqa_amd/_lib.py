@@ -8,7 +8,6 @@ not built, ``load()`` raises: there is no fallback.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from typing import Optional, Sequence
 
@@ -339,10 +338,6 @@ def matmul_matmul(q, k, v, o, *, kv_lens=None, causal=False, scale=0.0, stream=N
     """O = (tau Q K^T) V per (request, query head), no softmax between the products."""
     prob = make_problem(q, k, v, o, kv_lens=kv_lens, causal=causal, scale=scale)
     attn_matmul_matmul(prob, q, k, v, o, stream)
-
-
-def default_scale(dqk: int) -> float:
-    return 1.0 / math.sqrt(dqk)
 
 
 # ------------------------------------------------------ RMSNorm + MatMul

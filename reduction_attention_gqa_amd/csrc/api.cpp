@@ -8,6 +8,8 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <set>
+#include <utility>
 #include <vector>
 
 #include "attn_internal.hpp"
@@ -258,6 +260,20 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 }  // namespace
+
+hipError_t set_lds_limit_once(const void* kernel, int bytes) {
+  static std::mutex mu;
+  static std::set<std::pair<int, const void*>> done;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done.count({dev, kernel})) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done.insert({dev, kernel});
+  return e;
+}
+
 }  // namespace attn
 
 using namespace attn;

@@ -80,6 +80,10 @@ struct SwigluParams {
 };
 hipError_t launch_swiglu(const SwigluParams& p, hipStream_t s);
 
+// Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per (device, kernel); thread-safe.  Launchers call it before every launch.
+hipError_t set_lds_limit_once(const void* kernel, int bytes);
+
 // Launchers (one per kernel family).  Each returns a hipError_t.
 hipError_t launch_generic(const KParams& p, dim3 grid, dim3 block, hipStream_t s);
 hipError_t launch_combine(const KParams& p, hipStream_t s);

@@ -25,13 +25,25 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void combine_kernel(KParams p) 
   const int b = (int)(row / ((int64_t)p.Hq * p.Lq));
   const int L = kv_len_b(p, b);
   int sb = L == 0 ? 0 : (L + p.chunk - 1) / p.chunk;
-  sb = min(sb, p.s_max);
+  const int64_t obase = (int64_t)b * p.os_b + (int64_t)i * p.os_t + (int64_t)h * p.os_h;
+  if (sb > p.s_max) {
+    // More keys on the device than the plan split: some were never reduced.
+    // NaN marks the row instead of a silently truncated result.
+    const float nan = __builtin_nanf("");
+    for (int d = lane; d < p.Dv; d += 64) {
+      if (p.o_bf16)
+        reinterpret_cast<uint16_t*>(p.o)[obase + d] = 0x7fc0;
+      else
+        reinterpret_cast<float*>(p.o)[obase + d] = nan;
+    }
+    if (lane == 0 && p.lse_out) p.lse_out[row] = nan;
+    return;
+  }
 
   float m = kNegInf;
   for (int j = lane; j < sb; j += 64) m = fmaxf(m, p.ws_lse[(int64_t)j * nrows + row]);
   m = wave_max(m);
 
-  const int64_t obase = (int64_t)b * p.os_b + (int64_t)i * p.os_t + (int64_t)h * p.os_h;
   if (m == kNegInf) {  // no split saw a key: O = 0, LSE = -inf
     for (int d = lane; d < p.Dv; d += 64) {
       if (p.o_bf16)

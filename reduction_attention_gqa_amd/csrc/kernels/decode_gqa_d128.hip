@@ -72,8 +72,15 @@ __device__ __forceinline__ int wave_incl_scan(int v, int lane) {
 // The work item of this workgroup: request b, KV head kvh, split j (of sb) and
 // the request's key count L.  Returns false when the workgroup has none.
 // Every wave computes the same answer.
+//
+// `beyond_plan` is set when the device key counts need more than the plan
+// provides: a request longer than s_max * chunk keys, or more work items in
+// total than the grid was sized for (n_items, counted from the host lengths
+// the plan was made from).  Work would then be dropped without a trace, so
+// the caller writes NaN instead of a result.
 __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, int& kvh, int& j,
-                                          int& sb, int& L) {
+                                          int& sb, int& L, bool& beyond_plan) {
+  beyond_plan = false;
   // One split per request: workgroup i is unit i (request i / Hkv, KV head
   // i % Hkv), every request has exactly one item, and only this request's
   // length is needed (a scalar load).
@@ -84,6 +91,7 @@ __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, in
     j = 0;
     sb = 1;
     L = kv_len_b(p, b);
+    beyond_plan = L > p.chunk;
     return true;
   }
   const int64_t N = p.n_items;
@@ -92,10 +100,10 @@ __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, in
   const int64_t s0 = ((int64_t)x * N) >> 3, s1 = ((int64_t)(x + 1) * N) >> 3;
   if (k >= s1 - s0) return false;
   const int64_t item = s0 + k;
+  const int64_t cover = (int64_t)p.s_max * p.chunk;  // keys the plan covers per request
   // Splits per request: s_b = ceil(L_b / chunk), at least 1 (an empty request
   // still owns one item, which writes O = 0 and LSE = -inf), and at most the
-  // plan's s_max (the workspace has s_max slots; keys past s_max * chunk are
-  // outside the plan).
+  // plan's s_max (the workspace has s_max slots).
   if (p.kv_lens == nullptr && p.kv_indptr == nullptr) {
     sb = max(1, min((p.Lcap + p.chunk - 1) / p.chunk, p.s_max));
     const int64_t per = (int64_t)p.Hkv * sb;
@@ -105,10 +113,13 @@ __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, in
     kvh = local / sb;
     j = local - kvh * sb;
     L = p.Lcap;
+    beyond_plan = L > cover || per * p.B > N;
     return true;
   }
-  // Items per request are Hkv * s_b; scan them 64 requests at a time.
+  // Items per request are Hkv * s_b; scan them 64 requests at a time, all the
+  // way to the end (the total is checked against the grid).
   int64_t base = 0;
+  bool found = false;
   for (int c = 0; c < p.B; c += 64) {
     const int bb = c + lane;
     int n = 0;
@@ -116,7 +127,7 @@ __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, in
       n = p.Hkv * max(1, min((kv_len_b(p, bb) + p.chunk - 1) / p.chunk, p.s_max));
     const int incl = wave_incl_scan(n, lane);
     const int total = __shfl(incl, 63, 64);
-    if (item < base + total) {
+    if (!found && item < base + total) {
       const int rel = (int)(item - base);
       const int idx = __builtin_amdgcn_readfirstlane(__popcll(__ballot(incl <= rel)));
       const int excl = __builtin_amdgcn_readfirstlane(__shfl(incl - n, idx, 64));
@@ -127,11 +138,12 @@ __device__ __forceinline__ bool find_item(const KParams& p, int lane, int& b, in
       kvh = local / sb;
       j = local - kvh * sb;
       L = kv_len_b(p, b);
-      return true;
+      found = true;
     }
     base += total;
   }
-  return false;
+  beyond_plan = found && (L > cover || base > N);
+  return found;
 }
 
 
@@ -171,6 +183,32 @@ __device__ __forceinline__ void store_o8(const KParams& p, int64_t off, const f3
   }
 }
 
+// A work item whose device key counts exceed the plan: NaN to its rows of O
+// (one split per request, or the single-launch merge) or to its partial slot
+// (the two-launch split, whose NaN the combine carries into O), and no
+// arrival is counted, so the counters stay zero.
+__device__ void write_beyond_plan(const KParams& p, int b, int kvh, int j, int sb) {
+  const float nan = __builtin_nanf("");
+  const f32x4_t v = {nan, nan, nan, nan};
+  const int t = threadIdx.x;
+  const int orow = t >> 4;
+  const int oc = (t & 15) * 8;
+  if (orow >= p.rows) return;
+  const int i = orow / p.G;
+  const int h = kvh * p.G + orow % p.G;
+  const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
+  if (p.split_mode == 1) {
+    const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + row;
+    float* dst = p.ws_o + slot * D + oc;
+    reinterpret_cast<f32x4_t*>(dst)[0] = v;
+    reinterpret_cast<f32x4_t*>(dst)[1] = v;
+    if (oc == 0) p.ws_lse[slot] = nan;
+    return;
+  }
+  store_o8(p, (int64_t)b * p.os_b + (int64_t)i * p.os_t + (int64_t)h * p.os_h + oc, v, v);
+  if (oc == 0 && p.lse_out) p.lse_out[row] = nan;
+}
+
 // Four waves per workgroup; a workgroup round covers KB * NW keys.  NB
 // register blocks per wave are in flight (four measured slower than two, also
 // with one workgroup per CU).
@@ -194,7 +232,8 @@ void decode_gqa_d128_kernel(KParams p) {
   // Wave index, made visibly wave-uniform so the key loop below is a scalar loop.
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int b, kvh, j, sb, L;
-  if (!find_item(p, lane, b, kvh, j, sb, L)) return;
+  bool beyond_plan;
+  if (!find_item(p, lane, b, kvh, j, sb, L, beyond_plan)) return;
   // The item is the same in every lane; saying so keeps the buffer resources
   // below in scalar registers (otherwise every load is wrapped in a loop over
   // the distinct descriptor values of the wave).
@@ -203,6 +242,10 @@ void decode_gqa_d128_kernel(KParams p) {
   j = __builtin_amdgcn_readfirstlane(j);
   sb = __builtin_amdgcn_readfirstlane(sb);
   L = __builtin_amdgcn_readfirstlane(L);
+  if (__builtin_amdgcn_readfirstlane((int)beyond_plan)) {
+    write_beyond_plan(p, b, kvh, j, sb);
+    return;
+  }
   const int lo = j * p.chunk;
   const int hi = min(lo + p.chunk, L);
 

@@ -370,13 +370,8 @@ void decode_mla_kernel(KParams p) {
 template <bool PAGED>
 hipError_t launch_mla_variant(const KParams& p, dim3 grid, hipStream_t s) {
   constexpr int lds = LDS_BYTES + (PAGED ? 4 * kMlaPageIds : 0);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_mla_kernel<PAGED>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&decode_mla_kernel<PAGED>), lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_mla_kernel<PAGED>, grid, dim3(NT), lds, s, p);
   return hipGetLastError();
 }

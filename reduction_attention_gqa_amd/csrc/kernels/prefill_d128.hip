@@ -513,14 +513,9 @@ void prefill_d128_kernel(KParams p, int nrt) {
 template <int KB, int NS, bool PAGED, bool SOFTMAX>
 hipError_t launch_variant(const KParams& p, int nrt, int64_t nwg, hipStream_t s) {
   constexpr int lds = lds_bytes(KB, NS) + (PAGED ? 4 * kPrefillPageIds : 0);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&prefill_d128_kernel<KB, NS, PAGED, SOFTMAX>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = set_lds_limit_once(
+      reinterpret_cast<const void*>(&prefill_d128_kernel<KB, NS, PAGED, SOFTMAX>), lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((prefill_d128_kernel<KB, NS, PAGED, SOFTMAX>), dim3((unsigned)nwg), dim3(NT), lds, s,
                      p, nrt);
   return hipGetLastError();

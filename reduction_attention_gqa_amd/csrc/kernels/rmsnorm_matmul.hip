@@ -92,7 +92,7 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
   const int hi = min(lo + kcw, hi_j);
 
   // Buffer ranges end at the last valid weight row / token, so rows past N or
-  // M read as zero.  Offsets stay 32-bit: a workgroup's 256 rows, 32 tokens.
+  // M read as zero.  Offsets stay 32-bit: a workgroup's 64 rows, 32 tokens.
   const int wrows = min(ROWS, p.N - n_wg);
   const int xrows = min(32, p.M - m0);
   const uint16_t* wp = reinterpret_cast<const uint16_t*>(p.w) + (int64_t)n_wg * p.w_row;
@@ -107,7 +107,6 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
 
   // k-step at column k: this lane's 8 columns k + 8 kg .. + 7; columns past
   // the split or past K read as zero without a memory access.
-  // Columns past the split or past K read as zero without a memory access.
   auto oob_of = [&](int k) -> uint32_t { return (k < hi && k + 8 * kg < p.K) ? 0u : kOob; };
   auto load_w = [&](WBuf& b, int k0) {
 #pragma unroll

@@ -1,7 +1,7 @@
-// SwiGLU, H = silu(X W_gate^T) * (X W_up^T): two MatMuls on one input,
-// fused horizontally (Cleave §7.3: a parallel reduction structure with a
-// common input), so every X fragment feeds both reductions in the same loop
-// and each weight matrix is streamed once.  With few output tiles (decode: a
+// SwiGLU, H = silu(X W_gate^T) * (X W_up^T): two MatMuls that reduce over K
+// and read the same X, fused horizontally (Cleave §7.3), so every X fragment
+// feeds both reductions in the same loop and each weight matrix is streamed
+// once.  With few output tiles (decode: a
 // few tokens) the K axis is split (Cleave §2.2 "Split-K"); the gate is
 // nonlinear, so the parts of both MatMuls are added up (combine kernel)
 // before silu is applied.

@@ -173,3 +173,46 @@ def test_full_size_decode_whole_output(name, fused, layout):
     print(f"[plan] {name}: kernel={plan.kernel} s_max={plan.s_max} chunk={plan.chunk}", flush=True)
     assert_close(f"{name} whole output", d.out(), o, BF16_MAX, BF16_MEAN)
     assert_lse_close(f"{name} whole output", d.lse_out(), lse)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_device_lengths_beyond_the_plan_write_nan(fused):
+    # The plan is made from host lengths that are shorter than the device's:
+    # request 1 holds 2000 keys on the device but was planned with 1000, so
+    # s_max * chunk (4 x 256) does not cover it.  Its rows come out NaN
+    # instead of a silently truncated result; the other requests are exact;
+    # the arrival counters stay zero.
+    import reduction_attention_gqa_amd as ra
+    p = make_problem(dtype="bf16", batch=3, lq=1, hq=32, hkv=8, dqk=128, dv=128,
+                     kv_len=[1000, 2000, 300], lcap=2048, seed=9)
+    d = DeviceProblem(p)
+    plan = ra.attn_decode_plan(d.problem(), 4, [1000, 1000, 300])
+    assert plan.s_max * plan.chunk < 2000
+    ws = ra.workspace(plan, "cuda")
+    d.decode(plan=plan, ws=ws, fused=fused)
+    out, lse = d.out(), d.lse_out()
+    assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
+    o, lse_want = _oracle(p)
+    keep = [0, 2]
+    assert_close("beyond plan, other requests", out[keep], o[keep], BF16_MAX, BF16_MEAN)
+    assert_lse_close("beyond plan, other requests", lse[keep], lse_want[keep])
+    assert int(ws[2].abs().sum()) == 0
+
+
+def test_more_work_items_than_planned_write_nan():
+    # Host lengths [1000, 100, 300] plan 8 x (4 + 1 + 2) = 56 work items; the
+    # device lengths [1000, 1000, 300] need 80, so the grid is too small for
+    # them.  Every launched item writes NaN (and counts no arrival) instead of
+    # leaving the items past the grid undone without a trace.
+    import reduction_attention_gqa_amd as ra
+    p = make_problem(dtype="bf16", batch=3, lq=1, hq=32, hkv=8, dqk=128, dv=128,
+                     kv_len=[1000, 1000, 300], lcap=1024, seed=10)
+    d = DeviceProblem(p)
+    plan = ra.attn_decode_plan(d.problem(), 4, [1000, 100, 300])
+    assert plan.n_items == 56 and plan.s_max * plan.chunk >= 1000
+    ws = ra.workspace(plan, "cuda")
+    d.o.fill_(0)
+    d.decode(plan=plan, ws=ws, fused=True)
+    out = d.out()
+    assert np.isnan(out[0]).all() and np.isnan(out[1]).all()
+    assert int(ws[2].abs().sum()) == 0

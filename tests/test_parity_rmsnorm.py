@@ -4,21 +4,29 @@ the C ABI.
 The kernel computes the rewritten graph (Cleave §1, Fig. 1: the Matmul on the
 raw input with the rows' sums of squares beside it, the row scale applied
 last), split over K (Cleave §2.2 "Split-K") when the plan says so; the oracle
-is the definition (normalise, then multiply).  Tolerance as for the attention
-path with bf16 inputs and fp32 accumulation: max abs 1e-2, mean abs 1e-3 on the
-fp32 output, and the bf16 output must be the round-to-nearest-even of the fp32
-one.
+is the definition (normalise, then multiply).  Tolerance derived from the
+kernel's arithmetic (below) on the fp32 output, and the bf16 output must be
+the round-to-nearest-even of the fp32 one.
 """
 import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import BF16_MAX, BF16_MEAN, DEV, assert_close
+from gpu_helpers import DEV, assert_close
 import reduction_attention_gqa_amd as ra
 from oracle import rmsnorm_matmul
 from synthetic.inputs import make_rms_problem, rms_workload
 
 pytestmark = pytest.mark.gpu
+
+# Tolerance derived from the kernel's arithmetic.  Its MFMA operands are exact
+# (bf16 inputs, and x g split into an exact bf16 high and low part), so every product is exact in fp32 and the
+# only roundings are fp32 accumulation over K terms and the fp32 epilogue (the row scale from the fp32 sum of squares).
+# With |Y| of order one and K <= 4096 the accumulated error is a random walk
+# of about sqrt(K) fp32 roundings of the running sum, about 1e-6 (measured
+# 5e-7 to 7e-7); the bar sits 100x above that and 100x below the error of a
+# 1% scale mistake (an eps in the wrong place, a division by a padded K).
+TOL_MAX, TOL_MEAN = 1e-4, 1e-5
 
 
 def _dev(a, stride=None):
@@ -45,8 +53,8 @@ def _run(p, s_request=0, y_dtype=torch.float32, x_stride=None, w_stride=None):
 def _check(name, p, **kw):
     want = rmsnorm_matmul(p.x, p.g, p.w, p.eps)
     y32, plan = _run(p, **kw)
-    assert_close(f"{name} (s={plan.s})", y32.cpu().numpy().astype(np.float64), want, BF16_MAX,
-                 BF16_MEAN)
+    assert_close(f"{name} (s={plan.s})", y32.cpu().numpy().astype(np.float64), want, TOL_MAX,
+                 TOL_MEAN)
     y16, _ = _run(p, y_dtype=torch.bfloat16, **kw)
     assert torch.equal(y16, y32.to(torch.bfloat16)), f"{name}: bf16 Y != RNE(fp32 Y)"
     return plan
@@ -116,5 +124,5 @@ def test_workspace_reused_across_calls():
         y.fill_(float("nan"))
         ra.rmsnorm_matmul(prob, plan, x, g, w, y, ws)
         torch.cuda.synchronize()
-        assert_close(f"reuse call {call}", y.cpu().numpy().astype(np.float64), want, BF16_MAX,
-                     BF16_MEAN)
+        assert_close(f"reuse call {call}", y.cpu().numpy().astype(np.float64), want, TOL_MAX,
+                     TOL_MEAN)

@@ -2,20 +2,29 @@
 
 The kernel streams both weight matrices in one loop over K (horizontal
 fusion, Cleave §7.3), split over K when the plan says so (Cleave §2.2
-"Split-K", parts added before the gate).  Tolerance as for the other bf16
-paths: max abs 1e-2, mean abs 1e-3 on the fp32 output; the bf16 output must be
-the round-to-nearest-even of the fp32 one.
+"Split-K", parts added before the gate).  Tolerance derived from the
+kernel's arithmetic (below) on the fp32 output; the bf16 output must be the
+round-to-nearest-even of the fp32 one.
 """
 import numpy as np
 import pytest
 import torch
 
-from gpu_helpers import BF16_MAX, BF16_MEAN, DEV, assert_close
+from gpu_helpers import DEV, assert_close
 import reduction_attention_gqa_amd as ra
 from oracle import swiglu
 from synthetic.inputs import make_swiglu_problem, swiglu_workload
 
 pytestmark = pytest.mark.gpu
+
+# Tolerance derived from the kernel's arithmetic.  Its MFMA operands are exact
+# (bf16 inputs), so every product is exact in fp32 and the
+# only roundings are fp32 accumulation over K terms and the fp32 epilogue (the gate).
+# With |Y| of order one and K <= 4096 the accumulated error is a random walk
+# of about sqrt(K) fp32 roundings of the running sum, about 1e-6 (measured
+# 5e-7 to 7e-7); the bar sits 100x above that and 100x below the error of a
+# 1% scale mistake (an eps in the wrong place, a division by a padded K).
+TOL_MAX, TOL_MEAN = 1e-4, 1e-5
 
 
 def _dev(a, stride=None):
@@ -40,8 +49,8 @@ def _run(p, s_request=0, y_dtype=torch.float32, strides=(None, None, None)):
 def _check(name, p, **kw):
     want = swiglu(p.x, p.w_gate, p.w_up)
     y32, cfg = _run(p, **kw)
-    assert_close(f"{name} (s={cfg.s})", y32.cpu().numpy().astype(np.float64), want, BF16_MAX,
-                 BF16_MEAN)
+    assert_close(f"{name} (s={cfg.s})", y32.cpu().numpy().astype(np.float64), want, TOL_MAX,
+                 TOL_MEAN)
     y16, _ = _run(p, y_dtype=torch.bfloat16, **kw)
     assert torch.equal(y16, y32.to(torch.bfloat16)), f"{name}: bf16 H != RNE(fp32 H)"
     return cfg

@@ -1,14 +1,23 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-Default run (N = 1):
+Default run (N = 1), one JSON line:
   * value: split-K decode throughput in algorithmic HBM GB/s on the
     Llama-3-8B-shaped GQA decode (B=32, 32/8 heads, D=128, 4096 keys, bf16);
     one step = plan + one attn_decode call over the whole batch (for this
     kernel family a single launch: one split per (request, KV head) writes O
     directly; with several splits the last split of each (request, KV head)
-    merges the partials); the two-launch form (split kernel + combine kernel)
-    is timed beside it as an ablation.
+    merges the partials).  Ablations beside it: a paged cache (16-row pages
+    scattered over a pool by a seeded shuffle), the two-launch form (split
+    kernel + combine kernel), the token-major cache and the split-off (s = 1)
+    plan.
+  * ragged_decode: 64 requests with Qwen3-32B heads (64/8, D=128) and
+    log-uniform key counts in [128, 32768], GB/s; with the two-launch,
+    token-major and split-off ablations (the planner splits every long
+    request here).
+  * mla_decode: B=64, 128 heads over one latent head (Dqk=576, Dv=512,
+    V = K[..., :512]), 8192 keys, GB/s; with the split-off ablation.
+  * tiny_decode_f32: fp32, B=1, 8/2 heads, D=64, 256 keys, s = 4: latency.
   * prefill: causal GQA prefill (B=4, L=4096, 32/8 heads, D=128, bf16) in
     algorithmic TFLOP/s; one step = one fused prefill launch.
   * matmul_matmul: MatMul+MatMul, O = (tau Q K^T) V per head with no softmax
@@ -16,30 +25,28 @@ Default run (N = 1):
     TFLOP/s; one step = one launch.
   * rmsnorm_matmul: RMSNorm followed by a MatMul on the Llama-3 8B decode
     shape (32 tokens, K=4096, N=14336, bf16) in algorithmic HBM GB/s (W, X, g
-    read once, Y written once); one step = one call (split launch, plus the
-    combine launch when K is split).
+    read once, Y written once); one step = one call.
   * swiglu: SwiGLU on Llama-3 8B's MLP at 32 tokens (K=4096, N=14336, bf16)
     in algorithmic HBM GB/s (both weight matrices and X read once, H written
     once); one step = one call.
-  * roofline of the dominant kernel of each (per-launch HIP-event times on the
-    launch stream), the split-off (s = 1) ablation, and the fp64 oracle timed
-    on the host cores over a bounded sample of the same workload.
+Every record carries ms_per_step (host wall clock over exactly the timed
+steps), the GPU-side span per step of a second pass with events on the
+launch stream, and the roofline of its dominant kernel (per-launch HIP-event
+times).  After every GPU leg has run, the fp64 oracle is timed on the host
+cores over a bounded sample of each workload (cpu_baseline), and once on a
+single BLAS thread for the Llama decode and the tiny fp32 decode; "host"
+records the CPU model, core count and numpy / BLAS versions.
 Inputs are synthetic (seeded i.i.d. N(0,1), rounded to bf16) and resident in
 HBM before timing.  The decode K/V cache is stored head-major, [B, Hkv, L, D]
 (each (request, KV head) one contiguous stream; the library takes any
-strides), and the token-major [B, L, Hkv, D] cache is timed beside it as an
-ablation (--kv-layout token makes it the measured one).  A paged cache (16-row
-pages scattered over a pool by a seeded shuffle, read through a page table) is
-timed as a further ablation; --paged PS makes a paged cache the measured one.
-Several copies of the inputs are rotated so that a step never finds its K/V in
-the 256 MB Infinity Cache from the previous step.
+strides); --kv-layout token makes the token-major cache the measured one,
+--paged PS a paged one.  Several copies of the inputs are rotated so that a
+step never finds its K/V in the 256 MB Infinity Cache from the previous step.
 
 Algorithmic work: bytes = unique Q, K and V reads + O write (the split
 workspace is not counted); flops = 2 (Dqk + Dv) per visible (query, key) pair.
 
---workload NAME benches one of the other named workloads instead (its own
-JSON line, decode or prefill by shape, llama3_8b_rmsnorm_matmul_decode,
-llama3_8b_swiglu_decode or llama3_8b_matmul_matmul_prefill).
+--workload NAME benches one named workload instead (its own JSON line).
 """
 from __future__ import annotations
 
@@ -322,16 +329,21 @@ def time_decode(prob, steps, warmup, s_request, dev, fused, layout="token", page
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # Per-kernel durations, with events on the launch stream.
+    # Per-kernel durations, with events on the launch stream, and the GPU-side
+    # span of the whole pass (launch gaps included).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    span = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    span[0].record(stream)
     for i in range(steps):
         step(i, evs[i])
+    span[1].record(stream)
     torch.cuda.synchronize()
     split_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     comb_ms = None if fused else sorted(e[1].elapsed_time(e[2]) for e in evs)
     del copies, probs
     return dict(plan=plan, wall_s=wall, split_ms=split_ms, combine_ms=comb_ms,
-                bytes=(qb, kvb, ob), fused=fused)
+                bytes=(qb, kvb, ob), fused=fused,
+                gpu_span_ms_per_step=span[0].elapsed_time(span[1]) / steps)
 
 
 def time_prefill(prob, steps, warmup, dev, mm=False):
@@ -366,12 +378,16 @@ def time_prefill(prob, steps, warmup, dev, mm=False):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    span = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    span[0].record(stream)
     for i in range(steps):
         step(i, evs[i])
+    span[1].record(stream)
     torch.cuda.synchronize()
     k_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     del copies, probs
-    return dict(wall_s=wall, kernel_ms=k_ms, bytes=(qb, kvb, ob))
+    return dict(wall_s=wall, kernel_ms=k_ms, bytes=(qb, kvb, ob),
+                gpu_span_ms_per_step=span[0].elapsed_time(span[1]) / steps)
 
 
 def rms_bytes(prob):
@@ -665,7 +681,7 @@ def mm_record(prob, r, steps):
 
 # ------------------------------------------------------------------------ main
 
-def decode_record(prob, r, steps, warmup, extra_src, key_suffix=""):
+def decode_record(prob, r, steps, extra_src, key_suffix=""):
     qb, kvb, ob = r["bytes"]
     total = qb + kvb + ob
     ms_step = r["wall_s"] * 1e3 / steps
@@ -679,6 +695,7 @@ def decode_record(prob, r, steps, warmup, extra_src, key_suffix=""):
                           + key_suffix)
     return dict(
         value=round(total / (ms_step * 1e-3) / 1e9, 2), ms_per_step=round(ms_step, 5),
+        gpu_span_ms_per_step=round(r["gpu_span_ms_per_step"], 5),
         plan=dict(kernel=plan.kernel, s_max=plan.s_max, chunk=plan.chunk, n_items=plan.n_items,
                   grid=list(plan.grid), ws_bytes=int(plan.ws_o_bytes + plan.ws_lse_bytes)),
         roofline={"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -692,6 +709,159 @@ def decode_record(prob, r, steps, warmup, extra_src, key_suffix=""):
                   "launch_ms": split},
         combine=None if r["combine_ms"] is None else stats(r["combine_ms"]),
         algorithmic_bytes_per_step=total)
+
+
+KERNEL_SRC = {0: "generic.hip", 1: "decode_gqa_d128.hip", 2: "decode_mla.hip"}
+
+
+def single_launch_family(prob):
+    """Does attn_decode run this workload as one launch (the merge inside the
+    split kernel)?  The GQA D=128 family does; the others run split + combine."""
+    return prob.dtype == "bf16" and prob.dqk == 128 and prob.dv == 128
+
+
+def decode_leg(prob, a, dev, ablations=(), layout="head", page_size=0, s_request=0):
+    """Time one decode workload; `ablations` names the extra timings to add
+    ("paged", "two_launch", "token_major", "split_off")."""
+    fused = single_launch_family(prob) and not a.two_launch
+    log(f"timing decode {prob.name} ({'single launch' if fused else 'split + combine'})")
+    r = time_decode(prob, a.steps, a.warmup, s_request, dev, fused, layout, page_size)
+    src = "reduction_attention_gqa_amd/csrc/kernels/" + KERNEL_SRC[r["plan"].kernel]
+    rec = decode_record(prob, r, a.steps, src, f":paged{page_size}" if page_size else "")
+    import reduction_attention_gqa_amd as ra
+    out = {"value": rec["value"], "unit": "GB/s", "ms_per_step": rec["ms_per_step"],
+           "gpu_span_ms_per_step": rec["gpu_span_ms_per_step"],
+           "dtype": "bf16" if prob.dtype == "bf16" else "f32",
+           "config": {"workload": prob.name, "batch": prob.batch, "q_heads": prob.hq,
+                      "kv_heads": prob.hkv, "head_dim_qk": prob.dqk, "head_dim_v": prob.dv,
+                      "kv_len_total": int(prob.lens.sum()), "kv_len_max": int(prob.lens.max()),
+                      "q_len": prob.lq, "kv_layout": layout, "page_size": page_size or None,
+                      "split_s": rec["plan"]["s_max"], "chunk": rec["plan"]["chunk"],
+                      "kernel": ra.KERNEL_NAMES[rec["plan"]["kernel"]]},
+           "roofline": rec["roofline"],
+           "decode_detail": {"plan": rec["plan"], "single_launch": fused,
+                             "combine_launch_ms": rec["combine"],
+                             "algorithmic_bytes_per_step": rec["algorithmic_bytes_per_step"],
+                             "wall_s_timed": round(r["wall_s"], 4)}}
+    n_abl = max(10, a.steps // 2)
+    if "paged" in ablations:
+        log(f"  {prob.name}: paged-cache ablation (16-row pages, shuffled pool)")
+        rp = time_decode(prob, n_abl, 3, 0, dev, fused, layout, 16)
+        recp = decode_record(prob, rp, n_abl, src)
+        out["paged"] = {"page_size": 16, "value": recp["value"], "unit": "GB/s",
+                        "ms_per_step": recp["ms_per_step"],
+                        "launch_ms": recp["roofline"]["launch_ms"]["mean_ms"],
+                        "frac": recp["roofline"]["frac"], "split_s": recp["plan"]["s_max"],
+                        "ratio_to_contiguous": round(recp["value"] / rec["value"], 3)}
+    if "two_launch" in ablations and fused:
+        log(f"  {prob.name}: two-launch ablation (split kernel + combine kernel)")
+        r2 = time_decode(prob, n_abl, 3, s_request, dev, False, layout)
+        rec2 = decode_record(prob, r2, n_abl, src)
+        out["two_launch"] = {"value": rec2["value"], "unit": "GB/s",
+                             "ms_per_step": rec2["ms_per_step"],
+                             "split_launch_ms": rec2["roofline"]["launch_ms"]["mean_ms"],
+                             "combine_launch_ms": rec2["combine"]["mean_ms"],
+                             "speedup_of_single_launch": round(rec["value"] / rec2["value"], 3)}
+    if "token_major" in ablations and layout == "head":
+        log(f"  {prob.name}: token-major cache ablation")
+        r3 = time_decode(prob, n_abl, 3, s_request, dev, fused, "token")
+        rec3 = decode_record(prob, r3, n_abl, src)
+        out["token_major"] = {"value": rec3["value"], "unit": "GB/s",
+                              "ms_per_step": rec3["ms_per_step"],
+                              "launch_ms": rec3["roofline"]["launch_ms"]["mean_ms"],
+                              "frac": rec3["roofline"]["frac"],
+                              "speedup_of_head_major": round(rec["value"] / rec3["value"], 3)}
+    if "split_off" in ablations:
+        log(f"  {prob.name}: split-off ablation (s = 1)")
+        r1 = time_decode(prob, n_abl, 3, 1, dev, fused, layout)
+        rec1 = decode_record(prob, r1, n_abl, src)
+        out["split_off"] = {"value": rec1["value"], "unit": "GB/s",
+                            "ms_per_step": rec1["ms_per_step"],
+                            "split_s_planned": rec["plan"]["s_max"],
+                            "speedup_of_split": round(rec["value"] / rec1["value"], 3)}
+    return out
+
+
+def prefill_leg(prob, a, dev):
+    log(f"timing prefill {prob.name}")
+    r = time_prefill(prob, a.steps, a.warmup, dev)
+    flops = attention_flops(prob)
+    ks = stats(r["kernel_ms"])
+    ms_step = r["wall_s"] * 1e3 / a.steps
+    achieved = flops / (ks["mean_ms"] * 1e-3) / 1e12
+    return {"value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+            "ms_per_step": round(ms_step, 5),
+            "gpu_span_ms_per_step": round(r["gpu_span_ms_per_step"], 5),
+            "config": {"workload": prob.name, "batch": prob.batch, "q_len": prob.lq,
+                       "kv_len": int(prob.lens.max()), "q_heads": prob.hq,
+                       "kv_heads": prob.hkv, "head_dim": prob.dqk, "causal": bool(prob.causal)},
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/"
+                                                "prefill_d128.hip", f"prefill:{prob.name}"),
+                         "kernel": "prefill kernel",
+                         "algorithmic_flops_per_launch": flops, "launch_ms": ks}}
+
+
+# --------------------------------------------------------------- host record
+
+def host_info():
+    """CPU model, usable cores, numpy and BLAS versions of the host that runs
+    the oracle baselines."""
+    import numpy as np
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = []
+    try:
+        from threadpoolctl import threadpool_info
+        for e in threadpool_info():
+            if e.get("user_api") == "blas":
+                blas.append({"library": e.get("internal_api"), "version": e.get("version"),
+                             "threading": e.get("threading_layer"),
+                             "max_threads": e.get("num_threads")})
+    except Exception:  # noqa: BLE001 - metadata only
+        pass
+    return {"cpu_model": model, "cores": cpu_cores(), "logical_cpus": os.cpu_count(),
+            "numpy": np.__version__, "blas": blas}
+
+
+def oracle_decode_single_thread(prob, budget_s=5.0):
+    """The fp64 oracle on one BLAS thread over the whole decode batch: a
+    per-core figure."""
+    from threadpoolctl import threadpool_limits
+    from oracle import attention
+    qb, kvb, ob = decode_bytes(prob)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            attention(prob.q, prob.k, [prob.v_rows(b) for b in range(prob.batch)], prob.causal,
+                      prob.scale)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s or reps >= 1000:
+                break
+    return {"value": round((qb + kvb + ob) * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"whole batch ({prob.batch} requests) x {reps} repetitions, {el:.2f} s, "
+                      f"numpy fp64 on one BLAS thread"}
+
+
+def base_line(a, data):
+    return {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": data}
+
+
+DATA_ATTN = "synthetic (seeded i.i.d. N(0,1), bf16-rounded; no model weights needed)"
 
 
 def main():
@@ -714,7 +884,7 @@ def main():
             family = {128: "gqa_d128", 576: "mla"}.get(prob.dqk, "generic")
             if prob.dtype != "bf16":
                 family = "generic"
-            fused = family == "gqa_d128" and not a.two_launch
+            fused = single_launch_family(prob) and not a.two_launch
             key = ("decode:" if fused else "decode_split:") + name
             if a.paged:
                 key += f":paged{a.paged}"
@@ -733,193 +903,114 @@ def main():
     from synthetic.inputs import (MM_WORKLOADS, RMS_WORKLOADS, SWIGLU_WORKLOADS, WORKLOADS,
                                   mm_workload, rms_workload, swiglu_workload, workload)
     dev = "cuda:0"
-    name = a.workload or "llama3_8b_gqa_decode"
-    if name in MM_WORKLOADS:
-        if a.copy_calibration:
-            log("calibration copy")
-            copy_calibration(dev)
-        log(f"timing {name}")
-        mprob = mm_workload(name)
-        rec = mm_record(mprob, time_prefill(mprob, a.steps, a.warmup, dev, mm=True), a.steps)
-        out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-               "data": "synthetic (seeded i.i.d. N(0,1), bf16-rounded; no model weights needed)"}
-        out.update(rec)
-        if not a.no_cpu:
-            log("timing the fp64 oracle on the host")
-            out["cpu_baseline"] = oracle_mm_baseline(mprob)
-        print(json.dumps(out), flush=True)
-        return
-    if name in SWIGLU_WORKLOADS:
-        if a.copy_calibration:
-            log("calibration copy")
-            copy_calibration(dev)
-        log(f"timing {name}")
-        sprob = swiglu_workload(name)
-        rec = swiglu_record(sprob, time_swiglu(sprob, a.steps, a.warmup, dev, a.s), a.steps)
-        out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-               "data": "synthetic (seeded; X ~ N(0,1), W_gate, W_up ~ N(0,1)/sqrt(K), "
-                       "bf16-rounded; no model weights needed)"}
-        out.update(rec)
-        if not a.no_cpu:
-            log("timing the fp64 oracle on the host")
-            out["cpu_baseline"] = oracle_swiglu_baseline(sprob)
-        print(json.dumps(out), flush=True)
-        return
-    if name in RMS_WORKLOADS:
-        if a.copy_calibration:
-            log("calibration copy")
-            copy_calibration(dev)
-        log(f"timing {name}")
-        rprob = rms_workload(name)
-        rec = rms_record(rprob, time_rms(rprob, a.steps, a.warmup, dev, a.s), a.steps)
-        out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-               "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-               "data": "synthetic (seeded; X ~ N(0,1), g ~ 1 + 0.1 N(0,1), W ~ N(0,1)/sqrt(K), "
-                       "bf16-rounded; no model weights needed)"}
-        out.update(rec)
-        if not a.no_cpu:
-            log("timing the fp64 oracle on the host")
-            out["cpu_baseline"] = oracle_rms_baseline(rprob)
-        print(json.dumps(out), flush=True)
-        return
-    if name not in WORKLOADS:
-        sys.exit(f"unknown workload {name}; choose from "
-                 f"{sorted(WORKLOADS) + sorted(RMS_WORKLOADS) + sorted(SWIGLU_WORKLOADS)}"
-                 f" + {sorted(MM_WORKLOADS)}")
     if a.copy_calibration:
         log("calibration copy")
         copy_calibration(dev)
-    log(f"generating {name}")
-    prob = workload(name)
-    is_prefill = prob.lq > 1
-    out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-           "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "bf16" if prob.dtype == "bf16" else "f32",
-           "data": "synthetic (seeded i.i.d. N(0,1), bf16-rounded; no model weights needed)"}
-    if not is_prefill:
-        # The GQA family runs as one fused launch; the others as split + combine.
-        fused = prob.dtype == "bf16" and prob.dqk == 128 and prob.dv == 128 and not a.two_launch
-        log(f"timing decode ({'single launch' if fused else 'split + combine'})")
-        r = time_decode(prob, a.steps, a.warmup, a.s, dev, fused, a.kv_layout, a.paged)
-        src = ("reduction_attention_gqa_amd/csrc/kernels/"
-               + {0: "generic.hip", 1: "decode_gqa_d128.hip", 2: "decode_mla.hip"}[r["plan"].kernel])
-        rec = decode_record(prob, r, a.steps, a.warmup, src,
-                            f":paged{a.paged}" if a.paged else "")
-        out["unit"] = "GB/s"
-        out["value"] = rec["value"]
-        out["ms_per_step"] = rec["ms_per_step"]
-        out["config"] = {"workload": name, "batch": prob.batch, "q_heads": prob.hq,
-                         "kv_heads": prob.hkv, "head_dim_qk": prob.dqk, "head_dim_v": prob.dv,
-                         "kv_len_total": int(prob.lens.sum()), "kv_len_max": int(prob.lens.max()),
-                         "q_len": prob.lq, "kv_layout": a.kv_layout,
-                         "page_size": a.paged or None,
-                         "split_s": rec["plan"]["s_max"],
-                         "chunk": rec["plan"]["chunk"],
-                         "kernel": ra.KERNEL_NAMES[rec["plan"]["kernel"]]}
-        out["roofline"] = rec["roofline"]
-        out["decode_detail"] = {"plan": rec["plan"], "single_launch": fused,
-                                "combine_launch_ms": rec["combine"],
-                                "algorithmic_bytes_per_step": rec["algorithmic_bytes_per_step"],
-                                "wall_s_timed": round(r["wall_s"], 4)}
-        if not a.no_ablation and a.s == 0 and not a.paged:
-            n_abl = max(10, a.steps // 5)
-            log("timing the paged-cache ablation (16-row pages, shuffled pool)")
-            rp = time_decode(prob, n_abl, 3, 0, dev, fused, a.kv_layout, 16)
-            recp = decode_record(prob, rp, n_abl, 3, src)
-            out["paged"] = {"page_size": 16, "value": recp["value"], "unit": "GB/s",
-                            "ms_per_step": recp["ms_per_step"],
-                            "launch_ms": recp["roofline"]["launch_ms"]["mean_ms"],
-                            "frac": recp["roofline"]["frac"],
-                            "split_s": recp["plan"]["s_max"],
-                            "ratio_to_contiguous": round(recp["value"] / rec["value"], 3)}
-            if fused:
-                log("timing the two-launch ablation (split kernel + combine kernel)")
-                r2 = time_decode(prob, n_abl, 3, 0, dev, False, a.kv_layout)
-                rec2 = decode_record(prob, r2, n_abl, 3, src)
-                out["two_launch"] = {"value": rec2["value"], "unit": "GB/s",
-                                     "ms_per_step": rec2["ms_per_step"],
-                                     "split_launch_ms": rec2["roofline"]["launch_ms"]["mean_ms"],
-                                     "combine_launch_ms": rec2["combine"]["mean_ms"],
-                                     "speedup_of_single_launch":
-                                         round(rec["value"] / rec2["value"], 3)}
-            if a.kv_layout == "head":
-                log("timing the token-major cache ablation")
-                r3 = time_decode(prob, n_abl, 3, 0, dev, fused, "token")
-                rec3 = decode_record(prob, r3, n_abl, 3, src)
-                out["token_major"] = {"value": rec3["value"], "unit": "GB/s",
-                                      "ms_per_step": rec3["ms_per_step"],
-                                      "launch_ms": rec3["roofline"]["launch_ms"]["mean_ms"],
-                                      "speedup_of_head_major":
-                                          round(rec["value"] / rec3["value"], 3)}
-            log("timing split-off ablation (s = 1)")
-            r1 = time_decode(prob, n_abl, 3, 1, dev, fused, a.kv_layout)
-            rec1 = decode_record(prob, r1, n_abl, 3, src)
-            out["split_off"] = {"value": rec1["value"], "unit": "GB/s",
-                                "ms_per_step": rec1["ms_per_step"],
-                                "speedup_of_split": round(rec["value"] / rec1["value"], 3)}
-        if not a.no_cpu:
-            log("timing the fp64 oracle on the host")
-            out["cpu_baseline"] = oracle_decode_baseline(prob)
-    else:
-        out["unit"] = "TFLOP/s"
-    if is_prefill or (a.workload is None and not a.no_prefill):
-        pname = name if is_prefill else "gqa_causal_prefill"
-        pprob = prob if is_prefill else workload(pname)
-        log(f"timing prefill {pname}")
-        steps = a.steps
-        r = time_prefill(pprob, steps, a.warmup, dev)
-        flops = attention_flops(pprob)
-        ks = stats(r["kernel_ms"])
-        ms_step = r["wall_s"] * 1e3 / steps
-        achieved = flops / (ks["mean_ms"] * 1e-3) / 1e12
-        pre = {"value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
-               "ms_per_step": round(ms_step, 5),
-               "config": {"workload": pname, "batch": pprob.batch, "q_len": pprob.lq,
-                          "kv_len": int(pprob.lens.max()), "q_heads": pprob.hq,
-                          "kv_heads": pprob.hkv, "head_dim": pprob.dqk,
-                          "causal": bool(pprob.causal)},
-               "roofline": {"bound": "mfma", "achieved": round(achieved, 3),
-                            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                            "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/"
-                                                   "prefill_d128.hip", f"prefill:{pname}")
-                            if os.path.exists(os.path.join(
-                                ROOT, "reduction_attention_gqa_amd/csrc/kernels/prefill_d128.hip"))
-                            else None,
-                            "kernel": "prefill kernel",
-                            "algorithmic_flops_per_launch": flops, "launch_ms": ks}}
-        if not a.no_cpu:
-            log("timing the fp64 oracle on prefill groups")
-            pre["cpu_baseline"] = oracle_prefill_baseline(pprob)
-        if is_prefill:
-            out.update({k: pre[k] for k in ("value", "ms_per_step", "config", "roofline")})
-            if "cpu_baseline" in pre:
-                out["cpu_baseline"] = pre["cpu_baseline"]
+    cpu_jobs = []   # (record, key, function, args): oracle runs, after every GPU leg
+
+    name = a.workload
+    if name is not None:
+        # One named workload, its own JSON line.
+        if name in MM_WORKLOADS:
+            prob = mm_workload(name)
+            out = base_line(a, DATA_ATTN)
+            out.update(mm_record(prob, time_prefill(prob, a.steps, a.warmup, dev, mm=True),
+                                 a.steps))
+            cpu_jobs.append((out, "cpu_baseline", oracle_mm_baseline, (prob,)))
+        elif name in SWIGLU_WORKLOADS:
+            prob = swiglu_workload(name)
+            out = base_line(a, "synthetic (seeded; X ~ N(0,1), W_gate, W_up ~ N(0,1)/sqrt(K), "
+                               "bf16-rounded; no model weights needed)")
+            log(f"timing {name}")
+            out.update(swiglu_record(prob, time_swiglu(prob, a.steps, a.warmup, dev, a.s),
+                                     a.steps))
+            cpu_jobs.append((out, "cpu_baseline", oracle_swiglu_baseline, (prob,)))
+        elif name in RMS_WORKLOADS:
+            prob = rms_workload(name)
+            out = base_line(a, "synthetic (seeded; X ~ N(0,1), g ~ 1 + 0.1 N(0,1), "
+                               "W ~ N(0,1)/sqrt(K), bf16-rounded; no model weights needed)")
+            log(f"timing {name}")
+            out.update(rms_record(prob, time_rms(prob, a.steps, a.warmup, dev, a.s), a.steps))
+            cpu_jobs.append((out, "cpu_baseline", oracle_rms_baseline, (prob,)))
+        elif name in WORKLOADS:
+            log(f"generating {name}")
+            prob = workload(name)
+            out = base_line(a, DATA_ATTN)
+            if prob.lq > 1:
+                out.update(prefill_leg(prob, a, dev))
+                cpu_jobs.append((out, "cpu_baseline", oracle_prefill_baseline, (prob,)))
+            else:
+                abl = () if a.no_ablation or a.s or a.paged else (
+                    "two_launch", "split_off")
+                leg = decode_leg(prob, a, dev, abl, a.kv_layout, a.paged, a.s)
+                out.update(leg)
+                cpu_jobs.append((out, "cpu_baseline", oracle_decode_baseline, (prob,)))
         else:
-            out["prefill"] = pre
-    if a.workload is None and not a.no_prefill:
-        mname = "llama3_8b_matmul_matmul_prefill"
-        log(f"timing {mname}")
-        mprob = mm_workload(mname)
-        out["matmul_matmul"] = mm_record(mprob, time_prefill(mprob, a.steps, a.warmup, dev,
-                                                             mm=True), a.steps)
-        if not a.no_cpu:
-            log("timing the fp64 oracle on MatMul+MatMul heads")
-            out["matmul_matmul"]["cpu_baseline"] = oracle_mm_baseline(mprob)
+            sys.exit(f"unknown workload {name}; choose from "
+                     f"{sorted(WORKLOADS) + sorted(RMS_WORKLOADS) + sorted(SWIGLU_WORKLOADS)}"
+                     f" + {sorted(MM_WORKLOADS)}")
+    else:
+        # The default run: every workload of the hot path, GPU legs first, then
+        # the oracle on the host.
+        log("generating llama3_8b_gqa_decode")
+        prob2 = workload("llama3_8b_gqa_decode")
+        out = base_line(a, DATA_ATTN)
+        abl = () if a.no_ablation else ("paged", "two_launch", "token_major", "split_off")
+        out.update(decode_leg(prob2, a, dev, abl, a.kv_layout, a.paged, a.s))
+        cpu_jobs.append((out, "cpu_baseline", oracle_decode_baseline, (prob2,)))
+
+        log("generating ragged_decode_qwen3_32b")
+        prob4 = workload("ragged_decode_qwen3_32b")
+        abl = () if a.no_ablation else ("two_launch", "token_major", "split_off")
+        out["ragged_decode"] = decode_leg(prob4, a, dev, abl, a.kv_layout)
+        cpu_jobs.append((out["ragged_decode"], "cpu_baseline", oracle_decode_baseline, (prob4,)))
+        del prob4
+
+        log("generating mla_decode")
+        prob5 = workload("mla_decode")
+        abl = () if a.no_ablation else ("two_launch", "split_off")
+        out["mla_decode"] = decode_leg(prob5, a, dev, abl, "token")
+        cpu_jobs.append((out["mla_decode"], "cpu_baseline", oracle_decode_baseline, (prob5,)))
+
+        prob1 = workload("tiny_gqa_decode_f32")
+        out["tiny_decode_f32"] = decode_leg(prob1, a, dev, (), "token", 0, prob1.s)
+        out["tiny_decode_f32"]["latency_us"] = round(
+            out["tiny_decode_f32"]["ms_per_step"] * 1e3, 2)
+        cpu_jobs.append((out["tiny_decode_f32"], "cpu_baseline", oracle_decode_baseline,
+                         (prob1,)))
+
+        if not a.no_prefill:
+            pprob = workload("gqa_causal_prefill")
+            out["prefill"] = prefill_leg(pprob, a, dev)
+            cpu_jobs.append((out["prefill"], "cpu_baseline", oracle_prefill_baseline, (pprob,)))
+            mname = "llama3_8b_matmul_matmul_prefill"
+            log(f"timing {mname}")
+            mprob = mm_workload(mname)
+            out["matmul_matmul"] = mm_record(mprob, time_prefill(mprob, a.steps, a.warmup, dev,
+                                                                 mm=True), a.steps)
+            cpu_jobs.append((out["matmul_matmul"], "cpu_baseline", oracle_mm_baseline, (mprob,)))
         rname = "llama3_8b_rmsnorm_matmul_decode"
         log(f"timing {rname}")
         rprob = rms_workload(rname)
         out["rmsnorm_matmul"] = rms_record(rprob, time_rms(rprob, a.steps, a.warmup, dev), a.steps)
-        if not a.no_cpu:
-            out["rmsnorm_matmul"]["cpu_baseline"] = oracle_rms_baseline(rprob)
+        cpu_jobs.append((out["rmsnorm_matmul"], "cpu_baseline", oracle_rms_baseline, (rprob,)))
         sname = "llama3_8b_swiglu_decode"
         log(f"timing {sname}")
         sprob = swiglu_workload(sname)
         out["swiglu"] = swiglu_record(sprob, time_swiglu(sprob, a.steps, a.warmup, dev), a.steps)
+        cpu_jobs.append((out["swiglu"], "cpu_baseline", oracle_swiglu_baseline, (sprob,)))
         if not a.no_cpu:
-            out["swiglu"]["cpu_baseline"] = oracle_swiglu_baseline(sprob)
+            cpu_jobs.append((out, "cpu_baseline_one_thread", oracle_decode_single_thread,
+                             (prob2,)))
+            cpu_jobs.append((out["tiny_decode_f32"], "cpu_baseline_one_thread",
+                             oracle_decode_single_thread, (prob1,)))
+
+    if not a.no_cpu:
+        torch.cuda.synchronize()
+        out["host"] = host_info()
+        for rec, key, fn, args in cpu_jobs:
+            log(f"oracle on the host: {key} of {args[0].name}")
+            rec[key] = fn(*args)
     line = json.dumps(out)
     print(line, flush=True)
     if a.json_out:

@@ -227,6 +227,28 @@ int attn_decode(const attn_problem* problem, const attn_plan* plan,
                 void* stream);
 
 /*
+ * attn_decode_noalloc - attn_decode for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same kernels and results as attn_decode, with the
+ * workspace in a device-resident array of the library instead of caller
+ * buffers.  The caller still passes Q, K, V, O and (optionally) lse_out.
+ *
+ * The array is 96 MiB per GPU: 1 MiB of arrival counters (plan->ws_cnt_bytes
+ * must fit) and 95 MiB for ws_lse and ws_o (each rounded up to 256 bytes).
+ * A plan that needs more returns ATTN_ERR_WORKSPACE before anything is
+ * enqueued (e.g. an MLA decode of 64 requests x 128 heads with s = 4 needs
+ * 64 MiB and fits).  Each GPU the library runs on holds its own array until
+ * the process ends; the first call on a GPU looks up its address and clears
+ * its counters on `stream`.  No call allocates (no hipMalloc or allocating
+ * library routine).  Every call on a GPU shares that GPU's array, so calls
+ * that overlap on one GPU (on different streams or threads) race; calls in
+ * one stream are ordered and safe.  Errors as for attn_decode.
+ */
+int attn_decode_noalloc(const attn_problem* problem, const attn_plan* plan,
+                        const void* q, const void* k, const void* v, void* o,
+                        float* lse_out, void* stream);
+
+/*
  * attn_combine - the combine kernel (Cleave §4, Fig. 5(b)): reduces the
  * partials over the s_b splits of each row and divides.  With
  * M = max_j LSE_j and w_j = exp(LSE_j - M):

@@ -9,7 +9,8 @@ is its thin ctypes binding.
 """
 from ._lib import (ATTN_BF16, ATTN_ERR_ARG, ATTN_ERR_HIP, ATTN_ERR_UNSUPPORTED,
                    ATTN_ERR_WORKSPACE, ATTN_F32, ATTN_OK, EXPORTED, KERNEL_NAMES, AttnError,
-                   AttnPlan, AttnProblem, attn_combine, attn_decode, attn_decode_plan,
+                   AttnPlan, AttnProblem, attn_combine, attn_decode, attn_decode_noalloc,
+                   attn_decode_plan,
                    attn_decode_split, attn_matmul_matmul, attn_prefill, decode, load, make_problem, make_rms_problem,
                    matmul_matmul, prefill, rms_workspace, rmsnorm_matmul, rmsnorm_matmul_plan, RmsConfig,
                    RmsProblem, SwigluConfig, SwigluProblem, make_swiglu_problem, swiglu,
@@ -17,7 +18,8 @@ from ._lib import (ATTN_BF16, ATTN_ERR_ARG, ATTN_ERR_HIP, ATTN_ERR_UNSUPPORTED,
 
 __all__ = ["ATTN_BF16", "ATTN_ERR_ARG", "ATTN_ERR_HIP", "ATTN_ERR_UNSUPPORTED",
            "ATTN_ERR_WORKSPACE", "ATTN_F32", "ATTN_OK", "EXPORTED", "KERNEL_NAMES", "AttnError",
-           "AttnPlan", "AttnProblem", "attn_combine", "attn_decode", "attn_decode_plan",
+           "AttnPlan", "AttnProblem", "attn_combine", "attn_decode", "attn_decode_noalloc",
+           "attn_decode_plan",
            "attn_decode_split", "attn_matmul_matmul", "matmul_matmul",
            "attn_prefill", "decode", "load", "make_problem", "make_rms_problem", "prefill",
            "rms_workspace", "rmsnorm_matmul", "rmsnorm_matmul_plan", "RmsConfig", "RmsProblem",

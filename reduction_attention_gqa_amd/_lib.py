@@ -23,7 +23,8 @@ ATTN_ERR_WORKSPACE = 3
 ATTN_ERR_HIP = 4
 KERNEL_NAMES = {0: "generic", 1: "gqa_d128", 2: "mla"}
 
-EXPORTED = ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_decode", "attn_prefill",
+EXPORTED = ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_decode",
+            "attn_decode_noalloc", "attn_prefill",
             "attn_matmul_matmul", "attn_status_str", "attn_last_error", "attn_version", "rmsnorm_matmul_plan",
             "rmsnorm_matmul", "swiglu_plan", "swiglu")
 
@@ -116,6 +117,7 @@ def load() -> ctypes.CDLL:
     lib.attn_combine.argtypes = [P, PL, V, V, V, V, V]
     lib.attn_decode.argtypes = [P, PL, V, V, V, V, ctypes.c_size_t, V, ctypes.c_size_t, V,
                                 ctypes.c_size_t, V, V, V]
+    lib.attn_decode_noalloc.argtypes = [P, PL, V, V, V, V, V, V]
     lib.attn_prefill.argtypes = [P, V, V, V, V, V, V]
     lib.attn_matmul_matmul.argtypes = [P, V, V, V, V, V]
     RP, RC = ctypes.POINTER(RmsProblem), ctypes.POINTER(RmsConfig)
@@ -125,7 +127,7 @@ def load() -> ctypes.CDLL:
     lib.swiglu_plan.argtypes = [SP, ctypes.c_int32, ctypes.c_int32, SC]
     lib.swiglu.argtypes = [SP, SC, V, V, V, V, V, ctypes.c_size_t, V]
     for f in ("attn_decode_plan", "attn_decode_split", "attn_combine", "attn_decode",
-              "attn_prefill", "attn_matmul_matmul", "rmsnorm_matmul_plan", "rmsnorm_matmul",
+              "attn_decode_noalloc", "attn_prefill", "attn_matmul_matmul", "rmsnorm_matmul_plan", "rmsnorm_matmul",
               "swiglu_plan", "swiglu"):
         getattr(lib, f).restype = ctypes.c_int
     lib.attn_status_str.argtypes = [ctypes.c_int]
@@ -286,6 +288,13 @@ def attn_decode(problem: AttnProblem, plan: AttnPlan, q, k, v, ws_o, ws_lse, ws_
                            _ptr(ws_lse), ws_lse.numel() * ws_lse.element_size(),
                            _ptr(ws_cnt), ws_cnt.numel() * ws_cnt.element_size(),
                            _ptr(o), _ptr(lse_out), _stream(stream)))
+
+
+def attn_decode_noalloc(problem: AttnProblem, plan: AttnPlan, q, k, v, o, lse_out=None,
+                        stream=None) -> None:
+    lib = load()
+    _check(lib.attn_decode_noalloc(ctypes.byref(problem), ctypes.byref(plan), _ptr(q), _ptr(k),
+                                   _ptr(v), _ptr(o), _ptr(lse_out), _stream(stream)))
 
 
 def attn_prefill(problem: AttnProblem, q, k, v, o, lse_out=None, stream=None) -> None:

@@ -27,6 +27,7 @@ SOURCES = [
     "kernels/decode_mla.hip",
     "kernels/rmsnorm_matmul.hip",
     "kernels/swiglu.hip",
+    "kernels/scratch.hip",
 ]
 
 # Packed-fp32 VALU forms are switched off for all device code.

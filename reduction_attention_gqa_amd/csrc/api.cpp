@@ -261,6 +261,16 @@ int hip_status(hipError_t e, const char* what) {
 
 }  // namespace
 
+void clear_error() { g_err[0] = 0; }
+
+int report_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
 hipError_t set_lds_limit_once(const void* kernel, int bytes) {
   static std::mutex mu;
   static std::set<std::pair<int, const void*>> done;

@@ -80,6 +80,17 @@ struct SwigluParams {
 };
 hipError_t launch_swiglu(const SwigluParams& p, hipStream_t s);
 
+// Per-thread error reporting of the C ABI (attn_last_error): clear_error()
+// at the start of an entry point, report_error(code, fmt, ...) on failure
+// (returns code).
+void clear_error();
+int report_error(int code, const char* fmt, ...);
+
+// Device-resident workspace of attn_decode_noalloc: arrival counters first,
+// then the split partials.
+constexpr uint64_t kScratchBytes = 96ull << 20;
+constexpr uint64_t kScratchCntBytes = 1ull << 20;
+
 // Raises a kernel's dynamic LDS limit to `bytes` on the current device, once
 // per (device, kernel); thread-safe.  Launchers call it before every launch.
 hipError_t set_lds_limit_once(const void* kernel, int bytes);

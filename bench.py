@@ -16,7 +16,8 @@ Default run (N = 1), one JSON line:
     token-major and split-off ablations (the planner splits every long
     request here).
   * mla_decode: B=64, 128 heads over one latent head (Dqk=576, Dv=512,
-    V = K[..., :512]), 8192 keys, GB/s; with the split-off ablation.
+    V = K[..., :512]), 8192 keys, GB/s; one launch whose last split per
+    request merges; with the two-launch and split-off ablations.
   * tiny_decode_f32: fp32, B=1, 8/2 heads, D=64, 256 keys, s = 4: latency.
   * prefill: causal GQA prefill (B=4, L=4096, 32/8 heads, D=128, bf16) in
     algorithmic TFLOP/s; one step = one fused prefill launch.
@@ -29,8 +30,10 @@ Default run (N = 1), one JSON line:
   * swiglu: SwiGLU on Llama-3 8B's MLP at 32 tokens (K=4096, N=14336, bf16)
     in algorithmic HBM GB/s (both weight matrices and X read once, H written
     once); one step = one call.
-Every record carries ms_per_step (host wall clock over exactly the timed
-steps), the GPU-side span per step of a second pass with events on the
+Each leg first runs its step untimed for about 0.25 s (GPU clocks and
+address translation settle under the new load), then the warm-up steps, then
+exactly the timed steps.  Every record carries ms_per_step (host wall clock
+over exactly the timed steps), the GPU-side span per step of a second pass with events on the
 launch stream, and the roofline of its dominant kernel (per-launch HIP-event
 times).  After every GPU leg has run, the fp64 oracle is timed on the host
 cores over a bounded sample of each workload (cpu_baseline), and once on a
@@ -283,6 +286,25 @@ def traffic_for(kernel_src, launches_key):
 
 # ----------------------------------------------------------------------- timing
 
+SETTLE_S = 0.25
+
+
+def settle(step, seconds=SETTLE_S):
+    """Untimed steps for about `seconds` before the warm-up steps: GPU clocks
+    and address translation reach their steady state under this step's load
+    (the first few dozen launches after a change of load run measurably
+    slower)."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    i = 0
+    while time.perf_counter() < t_end:
+        step(i)
+        i += 1
+        if i % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def time_decode(prob, steps, warmup, s_request, dev, fused, layout="token", page_size=0):
     """Time `steps` decode steps.  fused: one attn_decode call per step (for the
     GQA family a single launch that merges its own splits); otherwise the split
@@ -320,6 +342,7 @@ def time_decode(prob, steps, warmup, s_request, dev, fused, layout="token", page
         if ev is not None:
             ev[2].record(stream)
 
+    settle(step)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -369,6 +392,7 @@ def time_prefill(prob, steps, warmup, dev, mm=False):
         if ev is not None:
             ev[1].record(stream)
 
+    settle(step)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -421,6 +445,7 @@ def time_rms(prob, steps, warmup, dev, s_request=0):
         if ev is not None:
             ev[1].record(stream)
 
+    settle(step)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -510,6 +535,7 @@ def time_swiglu(prob, steps, warmup, dev, s_request=0):
         if ev is not None:
             ev[1].record(stream)
 
+    settle(step)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -716,8 +742,10 @@ KERNEL_SRC = {0: "generic.hip", 1: "decode_gqa_d128.hip", 2: "decode_mla.hip"}
 
 def single_launch_family(prob):
     """Does attn_decode run this workload as one launch (the merge inside the
-    split kernel)?  The GQA D=128 family does; the others run split + combine."""
-    return prob.dtype == "bf16" and prob.dqk == 128 and prob.dv == 128
+    split kernel)?  The GQA D=128 and MLA families do; the generic one runs
+    split + combine."""
+    return prob.dtype == "bf16" and ((prob.dqk == 128 and prob.dv == 128) or
+                                     (prob.dqk == 576 and prob.dv == 512))
 
 
 def decode_leg(prob, a, dev, ablations=(), layout="head", page_size=0, s_request=0):

@@ -206,13 +206,16 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan,
  * family allows.  The result equals attn_decode_split followed by
  * attn_combine (same O and LSE definitions).
  *
- * For the GQA D=128 family this is a single launch: when s_max == 1 each
- * workgroup writes O directly; otherwise every split writes its partial to
- * ws_o / ws_lse, and the last split of each (request, KV head) to finish
- * (counted with an atomic in ws_cnt) merges the partials and writes O -- the
- * combine of Cleave §4 without the second launch (the cost the pages' §7.4
- * attributes to the two-launch design).  Requests with one split write O
- * directly.  Other families run the split launch and then the combine launch.
+ * For the GQA D=128 and MLA families this is a single launch: when
+ * s_max == 1 each workgroup writes O directly; otherwise the splits of each
+ * (request, KV head) coordinate through an atomic counter in ws_cnt, and the
+ * last one to finish merges the partials (read from ws_o / ws_lse) and
+ * writes O -- the combine of Cleave §4 without the second launch (the cost
+ * the pages' §7.4 attributes to the two-launch design).  Requests with one
+ * split write O directly.  The merge sums the splits in split order, so the
+ * result does not depend on which split finishes last.  The generic family
+ * (and an MLA problem whose partials exceed 2 GiB) runs the split launch and
+ * then the combine launch.
  *
  * ws_cnt  DEVICE int32 [B * Hkv] (plan->ws_cnt_bytes).  It must be all zero
  *         before the first call; every call leaves it all zero again.  One

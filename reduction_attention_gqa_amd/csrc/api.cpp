@@ -406,6 +406,15 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
   const uint64_t nrows = (uint64_t)p->batch * p->q_len * p->q_heads;
   out->ws_o_bytes = (uint64_t)s_max * nrows * p->head_dim_v * sizeof(float);
   out->ws_lse_bytes = (uint64_t)s_max * nrows * sizeof(float);
+  if (family == ATTN_KERNEL_MLA) {
+    // The single-launch MLA merge keeps each split's partial in the kernel's
+    // lane order, whole 16-row wave blocks per (request, KV head).
+    const uint64_t rows16 = (uint64_t)ceil_div(rows, 16) * 16;
+    const uint64_t units = (uint64_t)p->batch * p->kv_heads;
+    out->ws_o_bytes = std::max<uint64_t>(out->ws_o_bytes,
+                                         (uint64_t)s_max * units * rows16 * p->head_dim_v * 4);
+    out->ws_lse_bytes = std::max<uint64_t>(out->ws_lse_bytes, (uint64_t)s_max * units * rows16 * 4);
+  }
   out->ws_cnt_bytes = (uint64_t)p->batch * p->kv_heads * sizeof(int32_t);
   out->problem_key = problem_key(p);
   return ATTN_OK;
@@ -479,6 +488,21 @@ int attn_decode(const attn_problem* problem, const attn_plan* plan, const void* 
     kp.n_items = plan->n_items;
     kp.split_mode = plan->s_max == 1 ? 0 : 2;
     return hip_status(launch_decode_gqa_d128(kp, s), "decode_gqa_d128 launch");
+  }
+  // MLA: one launch whose last split per (request, KV head) merges, when the
+  // partials' byte offsets fit the kernel's 31-bit buffer offsets.
+  const uint64_t nrows = (uint64_t)p->batch * p->q_len * p->q_heads;
+  if (plan->kernel == ATTN_KERNEL_MLA && mla_usable(p, plan, q, k, v) &&
+      plan->ws_o_bytes < (1ull << 31)) {
+    KParams kp = base_params(p);
+    kp.q = q; kp.k = k; kp.v = v; kp.o = o;
+    kp.ws_o = ws_o; kp.ws_lse = ws_lse; kp.lse_out = lse_out;
+    kp.counters = ws_cnt;
+    kp.chunk = plan->chunk;
+    kp.s_max = plan->s_max;
+    kp.split_mode = 2;
+    return hip_status(launch_decode_mla(kp, dim3(plan->s_max, p->kv_heads, p->batch), s),
+                      "decode_mla launch");
   }
   // Other kernel families: the split launch, then the combine launch.
   if (int st = attn_decode_split(problem, plan, q, k, v, ws_o, ws_o_bytes, ws_lse, ws_lse_bytes,

@@ -92,6 +92,18 @@ __device__ __forceinline__ void store_dev(float* ptr, float v) {
 __device__ __forceinline__ float load_dev(const float* ptr) {
   return __hip_atomic_load(const_cast<float*>(ptr), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Sixteen-byte versions through a buffer resource, with the same
+// device-coherent cache policy (sc1, cache-policy bit 4 of the buffer
+// instructions).
+constexpr int kCachePolicySc1 = 16;
+__device__ __forceinline__ void store16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4_t v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4_t, v), r, (int)off, 0,
+                                         kCachePolicySc1);
+}
+__device__ __forceinline__ f32x4_t load16_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4_t,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicySc1));
+}
 // s_waitcnt vmcnt(0): every memory operation this wave issued has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

@@ -70,6 +70,43 @@ __device__ __forceinline__ i32x4_t ds_read16_at(uint32_t lds_addr) {
 }
 __device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
+// Four consecutive output values of one row to O (bf16 or f32).
+__device__ __forceinline__ void store_o4(const KParams& p, int64_t off, const f32x4_t& a) {
+  if (p.o_bf16) {
+    uint2 pk;
+    pk.x = pack_bf16x2(a[0], a[1]);
+    pk.y = pack_bf16x2(a[2], a[3]);
+    uint16_t* op = reinterpret_cast<uint16_t*>(p.o) + off;
+    if ((reinterpret_cast<uintptr_t>(op) & 7) == 0) {
+      *reinterpret_cast<uint2*>(op) = pk;
+    } else {
+      op[0] = (uint16_t)(pk.x & 0xffff);
+      op[1] = (uint16_t)(pk.x >> 16);
+      op[2] = (uint16_t)(pk.y & 0xffff);
+      op[3] = (uint16_t)(pk.y >> 16);
+    }
+  } else {
+    float* op = reinterpret_cast<float*>(p.o) + off;
+    if ((reinterpret_cast<uintptr_t>(op) & 15) == 0) {
+      *reinterpret_cast<f32x4_t*>(op) = a;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) op[e] = a[e];
+    }
+  }
+}
+
+// Every output row of (request b, KV head kvh) set to `val`, its LSE to `lse`.
+__device__ void write_rows(const KParams& p, int b, int kvh, float val, float lse) {
+  const f32x4_t v = {val, val, val, val};
+  for (int e = threadIdx.x; e < p.rows * (DV / 4); e += NT) {
+    const int r = e / (DV / 4), c = 4 * (e % (DV / 4));
+    const int qi = r / p.G, qh = kvh * p.G + r % p.G;
+    store_o4(p, (int64_t)b * p.os_b + (int64_t)qi * p.os_t + (int64_t)qh * p.os_h + c, v);
+    if (c == 0 && p.lse_out) p.lse_out[((int64_t)b * p.Lq + qi) * p.Hq + qh] = lse;
+  }
+}
+
 // PAGED: K rows come from a page pool (power-of-two page size).  The split's
 // page ids are staged in LDS after the stages, and each lane copies its
 // 16-byte slot with a 64-bit-addressed global load into LDS (same slot layout).
@@ -84,6 +121,17 @@ void decode_mla_kernel(KParams p) {
   const int b = blockIdx.z;
   const int L = uniform(kv_len_b(p, b));
   const int lo = j * p.chunk;
+  if (p.split_mode == 2) {
+    // Single launch: split 0 answers for a request with no key (O = 0, LSE =
+    // -inf), and for one longer than the plan covers (NaN rather than a
+    // truncated result); no split of such a request counts an arrival.
+    const int sb_all = (L + p.chunk - 1) / p.chunk;
+    if (L == 0 || sb_all > p.s_max) {
+      if (j == 0) write_rows(p, b, kvh, L == 0 ? 0.f : __builtin_nanf(""),
+                             L == 0 ? kNegInf : __builtin_nanf(""));
+      return;
+    }
+  }
   if (lo >= L) return;
   const int hi = min(lo + p.chunk, L);
 
@@ -355,16 +403,147 @@ void decode_mla_kernel(KParams p) {
   int e_lane = threadIdx.x;
   asm volatile("" : "+v"(e_lane));
   const int e_r = 16 * w + (e_lane & 15), e_g = (e_lane >> 4) & 3;
-  if (e_r < R) {
-    const int e_qi = e_r / G, e_qh = kvh * G + e_r % G;
-    const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
-    const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + ((int64_t)b * p.Lq + e_qi) * p.Hq + e_qh;
-    float* dst = p.ws_o + slot * DV + 4 * e_g;
+  const bool e_ok = e_r < R;
+  const int e_qi = e_r / G, e_qh = kvh * G + e_r % G;
+  const float inv = l_row > 0.f ? 1.f / l_row : 0.f;
+  const float lse_own = l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : kNegInf;
+  const int64_t nrows = (int64_t)p.B * p.Lq * p.Hq;
+  const int64_t row = ((int64_t)b * p.Lq + e_qi) * p.Hq + e_qh;
+  const int64_t obase = (int64_t)b * p.os_b + (int64_t)e_qi * p.os_t + (int64_t)e_qh * p.os_h + 4 * e_g;
+  const int sb = (L + p.chunk - 1) / p.chunk;  // splits of this request (>= 1 here)
+
+  if (p.split_mode == 1) {  // partial for the combine kernel
+    if (e_ok) {
+      float* dst = p.ws_o + ((int64_t)j * nrows + row) * DV + 4 * e_g;
 #pragma unroll
-    for (int cb = 0; cb < CBLK; ++cb)
-      *reinterpret_cast<f32x4_t*>(dst + 16 * cb) = oacc[cb] * inv;
-    if (e_g == 0) p.ws_lse[slot] = l_row > 0.f ? (m_ref + fast_log2(l_row)) * kLn2 : kNegInf;
+      for (int cb = 0; cb < CBLK; ++cb)
+        *reinterpret_cast<f32x4_t*>(dst + 16 * cb) = oacc[cb] * inv;
+      if (e_g == 0) p.ws_lse[(int64_t)j * nrows + row] = lse_own;
+    }
+    return;
   }
+  if (sb == 1) {  // the whole request in one split: O directly
+    if (e_ok) {
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) store_o4(p, obase + 16 * cb, oacc[cb] * inv);
+      if (e_g == 0 && p.lse_out) p.lse_out[row] = lse_own;
+    }
+    return;
+  }
+
+  // Single-launch merge (the combine of Cleave §4 inside the split kernel).
+  // The (request, KV head) counter holds tickets in its low 16 bits and
+  // published partials in its high 16 bits.  Every split takes a ticket when
+  // its keys are done; all but the last publish their partial and count it;
+  // the last one (whose ticket is sb - 1) knows that every other split has
+  // already taken its ticket, so it is resident and only has its stores left:
+  // it waits for their count, then merges all sb partials in split order
+  // (its own from registers, with the same arithmetic as a stored one, so the
+  // result is the same bits whichever split comes last) and resets the
+  // counter.
+  //
+  // The partials of this mode are private to the kernel and kept in its lane
+  // order: split j of unit u is a block of ceil(R / 16) wave slabs, slab w
+  // holding for each column block cb the 64 lanes' four values (1 KiB, one
+  // store or load instruction of whole cache lines), plus one LSE per row.
+  //
+  // Ordering on gfx950: partials are written with sc1 (device-coherent)
+  // stores, which write through the XCD's L2 instead of leaving dirty lines
+  // there, and each wave waits for them (vmcnt(0)) before the workgroup
+  // barrier that precedes the counting atomic; the reader's loads are sc1
+  // too, so they are served from the device-coherent level, never from a
+  // stale line of its own L2.  Because no data is left dirty in an L2, the
+  // whole-L2 write-back a device-scope release fence would add is not
+  // needed.
+  int* s_ticket = reinterpret_cast<int*>(smem);
+  const int unit = b * p.Hkv + kvh;
+  int* cnt = p.counters + unit;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    *s_ticket = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff;
+  __syncthreads();
+  const int ticket = *s_ticket;
+  const int nslab = (R + 15) >> 4;                       // wave slabs per block
+  const int64_t nunits = (int64_t)p.B * p.Hkv;
+  const uint32_t slab_bytes = CBLK * 64 * 16;            // 32 KiB
+  const uint32_t block_bytes = (uint32_t)nslab * slab_bytes;
+  // Buffer over the whole partial area; byte offset of (split jj, this lane, cb).
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.ws_o, 0xffffffffu);
+  const uint32_t lane_off = (uint32_t)w * slab_bytes + (uint32_t)lane * 16;
+  auto part_off = [&](int jj, int cb) {
+    return (uint32_t)(((int64_t)jj * nunits + unit) * block_bytes) + lane_off +
+           (uint32_t)(cb * 64 * 16);
+  };
+  auto lse_ptr = [&](int jj) { return p.ws_lse + ((int64_t)jj * nunits + unit) * (nslab * 16) + e_r; };
+  if (ticket < sb - 1) {
+    if (w < nslab) {
+#pragma unroll
+      for (int cb = 0; cb < CBLK; ++cb) store16_dev(wrs, part_off(j, cb), oacc[cb] * inv);
+      if (e_g == 0) store_dev(lse_ptr(j), lse_own);
+    }
+    wait_vmem();
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(cnt, 1 << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if (threadIdx.x == 0) {
+    while ((__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 16) < sb - 1)
+      __builtin_amdgcn_s_sleep(2);
+  }
+  __syncthreads();
+  if (w < nslab) {
+    // Pass 1: the common reference M (base 2) and the weight sum, split order.
+    float M2 = kNegInf;
+    for (int jj = 0; jj < sb; ++jj) {
+      const float lj = jj == j ? lse_own : load_dev(lse_ptr(jj));
+      M2 = vmax(M2, lj * kLog2e);
+    }
+    float wsum = 0.f;
+    if (M2 != kNegInf) {
+      for (int jj = 0; jj < sb; ++jj) {
+        const float lj = jj == j ? lse_own : load_dev(lse_ptr(jj));
+        wsum += fast_exp2(lj * kLog2e - M2);
+      }
+    }
+    const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
+    // Pass 2: four column blocks at a time, the splits in order; the loads of
+    // up to four splits are issued together.
+    constexpr int CB = 4, MB = 4;
+#pragma unroll
+    for (int c0 = 0; c0 < CBLK; c0 += CB) {
+      f32x4_t acc[CB];
+#pragma unroll
+      for (int u = 0; u < CB; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (M2 != kNegInf) {
+        for (int j0 = 0; j0 < sb; j0 += MB) {
+          f32x4_t x[MB][CB];
+#pragma unroll
+          for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int u = 0; u < CB; ++u)
+              x[m][u] = (j0 + m < sb && j0 + m != j) ? load16_dev(wrs, part_off(j0 + m, c0 + u))
+                                                     : oacc[c0 + u] * inv;
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            if (j0 + m < sb) {
+              const float lj = j0 + m == j ? lse_own : load_dev(lse_ptr(j0 + m));
+              const float wj = fast_exp2(lj * kLog2e - M2);
+#pragma unroll
+              for (int u = 0; u < CB; ++u) acc[u] += wj * x[m][u];
+            }
+          }
+        }
+      }
+      if (e_ok) {
+#pragma unroll
+        for (int u = 0; u < CB; ++u) store_o4(p, obase + 16 * (c0 + u), acc[u] * winv);
+      }
+    }
+    if (e_ok && e_g == 0 && p.lse_out)
+      p.lse_out[row] = M2 == kNegInf ? kNegInf : (M2 + fast_log2(wsum)) * kLn2;
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <bool PAGED>

@@ -52,3 +52,47 @@ def test_mla_partial_row_groups_causal_two_queries(s):
     o, lse = attention(p.q, p.k, v_rows(p), True, p.scale)
     assert_close(f"mla causal lq=2 s={s} kernel={plan.kernel}", d.out(), o, BF16_MAX, BF16_MEAN)
     assert_lse_close(f"mla causal lq=2 s={s}", d.lse_out(), lse)
+
+
+def test_mla_single_launch_deterministic_empty_request_and_counters():
+    # One launch (the last split of each request merges): repeated calls agree
+    # bit for bit whichever split finishes last, an empty request gives O = 0
+    # and LSE = -inf, and the arrival counters are zero after every call.
+    import torch
+    import reduction_attention_gqa_amd as ra
+    p = make_problem(dtype="bf16", batch=3, lq=1, hq=128, hkv=1, dqk=576, dv=512,
+                     kv_len=[2000, 513, 0], lcap=2048, seed=44, mla=True)
+    d = DeviceProblem(p)
+    plan = ra.attn_decode_plan(d.problem(), 4, list(p.lens))
+    assert plan.kernel == 2 and plan.s_max == 4
+    ws = ra.workspace(plan, "cuda")
+    d.decode(plan=plan, ws=ws)
+    first = d.o.clone()
+    assert int(ws[2].abs().sum()) == 0
+    o, lse = attention(p.q, p.k, v_rows(p), False, p.scale)
+    assert_close("mla single launch", d.out(), o, BF16_MAX, BF16_MEAN)
+    assert_lse_close("mla single launch", d.lse_out(), lse)
+    assert np.all(d.out()[2] == 0) and np.all(np.isneginf(d.lse_out()[2]))
+    for _ in range(3):
+        d.o.fill_(float("nan"))
+        d.decode(plan=plan, ws=ws)
+        assert torch.equal(first, d.o)
+        assert int(ws[2].abs().sum()) == 0
+
+
+def test_mla_device_length_beyond_the_plan_writes_nan():
+    # Planned with 1000 keys for request 0 (4 splits of 256), which holds 2000
+    # on the device: its rows are NaN, request 1 is exact, counters stay zero.
+    import reduction_attention_gqa_amd as ra
+    p = make_problem(dtype="bf16", batch=2, lq=1, hq=128, hkv=1, dqk=576, dv=512,
+                     kv_len=[2000, 700], lcap=2048, seed=45, mla=True)
+    d = DeviceProblem(p)
+    plan = ra.attn_decode_plan(d.problem(), 4, [1000, 700])
+    assert plan.s_max * plan.chunk < 2000
+    ws = ra.workspace(plan, "cuda")
+    d.decode(plan=plan, ws=ws)
+    out = d.out()
+    assert np.isnan(out[0]).all() and np.isnan(d.lse_out()[0]).all()
+    o, lse = attention(p.q, p.k, v_rows(p), False, p.scale)
+    assert_close("mla beyond plan, request 1", out[1:], o[1:], BF16_MAX, BF16_MEAN)
+    assert int(ws[2].abs().sum()) == 0

@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define ATTN_MI355X_VERSION 4
+#define ATTN_MI355X_VERSION 5
 
 typedef enum attn_dtype {
   ATTN_F32 = 0,   /* IEEE binary32 */
@@ -144,6 +144,13 @@ typedef struct attn_plan {
   uint64_t ws_cnt_bytes;  /* bytes needed for ws_cnt (attn_decode): B*Hkv int32 */
   int64_t n_items;        /* (request, KV head, split) work items from kv_lens_host:
                              Hkv * max(1, s_b) summed over requests */
+  /* attn_decode, GQA family: the keys of every (request, KV head) in rounds of
+   * tile_n keys laid end to end (an empty one counts one round), split into
+   * stream_grid equal runs, one per workgroup; a (request, KV head) is cut
+   * into at most stream_pieces pieces. */
+  int64_t stream_rounds;
+  int32_t stream_grid;
+  int32_t stream_pieces;
   uint64_t problem_key;   /* fingerprint of the planned problem */
 } attn_plan;
 
@@ -206,16 +213,23 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan,
  * family allows.  The result equals attn_decode_split followed by
  * attn_combine (same O and LSE definitions).
  *
- * For the GQA D=128 and MLA families this is a single launch: when
- * s_max == 1 each workgroup writes O directly; otherwise the splits of each
- * (request, KV head) coordinate through an atomic counter in ws_cnt, and the
- * last one to finish merges the partials (read from ws_o / ws_lse) and
- * writes O -- the combine of Cleave §4 without the second launch (the cost
- * the pages' §7.4 attributes to the two-launch design).  Requests with one
- * split write O directly.  The merge sums the splits in split order, so the
- * result does not depend on which split finishes last.  The generic family
- * (and an MLA problem whose partials exceed 2 GiB) runs the split launch and
- * then the combine launch.
+ * For the GQA D=128 and MLA families this is a single launch; the partials
+ * it keeps in ws_o / ws_lse are private to it (their layout is not the one
+ * attn_decode_split documents).
+ *   GQA: the keys of all (request, KV head) units, in rounds of tile_n keys,
+ *   are laid end to end and every workgroup of the plan's stream_grid takes
+ *   an equal run of them (one long stream per compute unit, balanced
+ *   whatever the request lengths; the split of Cleave §2.2 "Split-K" then
+ *   falls where the runs end).  A unit inside one run is written directly;
+ *   the pieces of a unit cut by run boundaries coordinate through an atomic
+ *   counter in ws_cnt and the last one to finish merges them.
+ *   MLA: the plan's s_max splits per request; the last split of each
+ *   (request, KV head) to finish merges them.
+ * Either way this is the combine of Cleave §4 without the second launch (the
+ * cost the pages' §7.4 attributes to the two-launch design), summing the
+ * pieces in order, so the result does not depend on which finishes last.
+ * The generic family (and an MLA problem whose partials exceed 2 GiB) runs
+ * the split launch and then the combine launch.
  *
  * ws_cnt  DEVICE int32 [B * Hkv] (plan->ws_cnt_bytes).  It must be all zero
  *         before the first call; every call leaves it all zero again.  One

@@ -53,7 +53,8 @@ class AttnPlan(ctypes.Structure):
         ("row_tiles", ctypes.c_int32), ("grid", ctypes.c_uint32 * 3), ("block", ctypes.c_uint32),
         ("ws_o_bytes", ctypes.c_uint64), ("ws_lse_bytes", ctypes.c_uint64),
         ("ws_cnt_bytes", ctypes.c_uint64), ("n_items", ctypes.c_int64),
-        ("problem_key", ctypes.c_uint64),
+        ("stream_rounds", ctypes.c_int64), ("stream_grid", ctypes.c_int32),
+        ("stream_pieces", ctypes.c_int32), ("problem_key", ctypes.c_uint64),
     ]
 
 

@@ -403,9 +403,45 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
     out->block = kMlaBlock;
   }
   out->n_items = n_items;
+  if (family == ATTN_KERNEL_GQA_D128) {
+    // attn_decode: rounds of tile_n keys of every unit laid end to end, equal
+    // runs per workgroup (one per compute unit), pieces per unit.
+    int64_t rounds = 0;
+    std::vector<int64_t> unit_rounds((size_t)p->batch);
+    for (int b = 0; b < p->batch; ++b) {
+      int64_t n = kv_lens_host ? kv_lens_host[b] : p->kv_len_max;
+      n = std::min<int64_t>(std::max<int64_t>(n, 0), p->kv_len_max);
+      unit_rounds[(size_t)b] = std::max<int64_t>(1, ceil_div(n, tile_n));
+      rounds += unit_rounds[(size_t)b] * p->kv_heads;
+    }
+    const int64_t grid = std::max<int64_t>(1, std::min<int64_t>((int64_t)cus * kGqaStreamWgsPerCu, rounds));
+    int64_t pieces = 1, u0 = 0;
+    for (int b = 0; b < p->batch; ++b)
+      for (int h = 0; h < p->kv_heads; ++h) {
+        const int64_t u1 = u0 + unit_rounds[(size_t)b];
+        const int64_t g_first = ((u0 + 1) * grid + rounds - 1) / rounds - 1;
+        const int64_t g_last = (u1 * grid + rounds - 1) / rounds - 1;
+        pieces = std::max(pieces, g_last - g_first + 1);
+        u0 = u1;
+      }
+    if (pieces > 65535 || rounds > (1ll << 40))
+      return fail(ATTN_ERR_UNSUPPORTED, "too many pieces or rounds for the stream decode");
+    out->stream_rounds = rounds;
+    out->stream_grid = (int32_t)grid;
+    out->stream_pieces = (int32_t)pieces;
+  }
   const uint64_t nrows = (uint64_t)p->batch * p->q_len * p->q_heads;
   out->ws_o_bytes = (uint64_t)s_max * nrows * p->head_dim_v * sizeof(float);
   out->ws_lse_bytes = (uint64_t)s_max * nrows * sizeof(float);
+  if (family == ATTN_KERNEL_GQA_D128) {
+    // The stream kernel's partials: an 8 KiB block (16 rows x 128 floats in
+    // thread order) and 16 LSEs per (piece, unit).
+    const uint64_t units = (uint64_t)p->batch * p->kv_heads;
+    out->ws_o_bytes = std::max<uint64_t>(out->ws_o_bytes,
+                                         (uint64_t)out->stream_pieces * units * 16 * 128 * 4);
+    out->ws_lse_bytes = std::max<uint64_t>(out->ws_lse_bytes,
+                                           (uint64_t)out->stream_pieces * units * 16 * 4);
+  }
   if (family == ATTN_KERNEL_MLA) {
     // The single-launch MLA merge keeps each split's partial in the kernel's
     // lane order, whole 16-row wave blocks per (request, KV head).
@@ -478,15 +514,19 @@ int attn_decode(const attn_problem* problem, const attn_plan* plan, const void* 
                 (unsigned long long)plan->ws_o_bytes, (unsigned long long)plan->ws_lse_bytes,
                 (unsigned long long)plan->ws_cnt_bytes);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_usable(p, plan, q, k, v)) {
+  if (plan->kernel == ATTN_KERNEL_GQA_D128 && gqa_d128_fits(p, q, k, v) &&
+      plan->ws_o_bytes < (1ull << 31)) {
+    // One launch: equal runs of key rounds per workgroup (paged segments are
+    // staged in LDS piece by piece, so no page-count bound applies).
     KParams kp = base_params(p);
     kp.q = q; kp.k = k; kp.v = v; kp.o = o;
     kp.ws_o = ws_o; kp.ws_lse = ws_lse; kp.lse_out = lse_out;
     kp.counters = ws_cnt;
     kp.chunk = plan->chunk;
     kp.s_max = plan->s_max;
-    kp.n_items = plan->n_items;
-    kp.split_mode = plan->s_max == 1 ? 0 : 2;
+    kp.n_items = plan->stream_rounds;
+    kp.stream_grid = plan->stream_grid;
+    kp.split_mode = 3;
     return hip_status(launch_decode_gqa_d128(kp, s), "decode_gqa_d128 launch");
   }
   // MLA: one launch whose last split per (request, KV head) merges, when the

@@ -27,7 +27,9 @@ struct KParams {
   int32_t ppr;                // page-table row length
   int32_t num_pages;          // page ids are clamped to [0, num_pages)
   int32_t page_shift;         // log2(page_size) when it is a power of two, else -1
-  int64_t n_items;      // (request, KV head, split) work items of the 1-D decode grid
+  int64_t n_items;      // (request, KV head, split) work items of the 1-D decode grid;
+                        // split_mode 3: 128-key rounds of all units laid end to end
+  int32_t stream_grid;  // split_mode 3: workgroups, each taking an equal run of rounds
   int64_t qs_b, qs_t, qs_h;
   int64_t ks_b, ks_t, ks_h;
   int64_t vs_b, vs_t, vs_h;
@@ -40,7 +42,8 @@ struct KParams {
   int32_t s_max;        // split slots
   int32_t rows;         // G * Lq rows per (request, KV head)
   int32_t row_tile;     // rows per workgroup (generic kernel)
-  int32_t split_mode;   // 0: write o (+ lse_out); 1: write ws_o/ws_lse; 2: 1 + in-kernel merge
+  int32_t split_mode;   // 0: write o (+ lse_out); 1: write ws_o/ws_lse; 2: 1 + in-kernel merge;
+                        // 3 (GQA): runs of rounds per workgroup, cut units merged in-kernel
   float scale_log2;     // tau * log2(e): scores are kept in base-2 units (tau itself when no_softmax)
   int32_t no_softmax;   // prefill only: 1 = MatMul+MatMul, O = (tau Q K^T) V
 };
@@ -108,6 +111,7 @@ constexpr int kGenericTileN = 64;      // keys per generic tile
 constexpr int kGenericBlock = 256;
 constexpr int kGqaTileN = 128;         // keys per GQA-D128 workgroup round (4 waves x 32)
 constexpr int kGqaItemsPerCu = 4;      // planner target: work items per compute unit
+constexpr int kGqaStreamWgsPerCu = 1;  // attn_decode: workgroups per compute unit (one run each)
 constexpr int kGqaMinChunk = 256;      // planner floor on keys per split
 constexpr int kGqaBlock = 256;
 constexpr int kGqaMaxRows = 16;

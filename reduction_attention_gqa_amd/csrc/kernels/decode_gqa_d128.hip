@@ -1,23 +1,31 @@
 // Split-K GQA decode for bf16, Dqk = Dv = 128, up to 16 query rows per KV head.
 //
 // Decode has one query row per request, so output tiles are too few to fill
-// the GPU; the key axis is split into chunks that run as separate workgroups
-// (Cleave §2.2 "Split-K", §7.3 decode setting).  A workgroup owns one work
-// item (request, KV head, split) and packs the G query heads that share the KV
-// head into the MFMA column dimension, so every K/V byte is read from HBM once.
+// the GPU; the key axis is split into pieces that run as separate workgroups
+// (Cleave §2.2 "Split-K", §7.3 decode setting).  A workgroup packs the G query
+// heads that share a KV head into the MFMA column dimension, so every K/V
+// byte is read from HBM once.
 //
-// Work items are numbered with the split fastest, then the KV head, then the
-// request.  With several splits per request, XCD x (workgroups x, x + 8, ...)
-// takes one contiguous range of them, so each XCD streams a compact region of
-// the K/V cache; with one split per request, workgroup i takes item i, which
-// spreads the KV heads of a request over the XCDs (measured faster for that
-// case, the other way round for many splits).  The item of a workgroup is
-// found on the device from the per-request key counts, so one compiled kernel
-// serves any mix of lengths.
+// Two kernels share the key streaming below:
 //
-// Within the workgroup the four waves take interleaved 32-key blocks of the
-// split and each keeps its own running max / sum / output (a second, on-chip
-// level of the same split); the waves are merged through LDS at the end.
+// * decode_gqa_d128_items (attn_decode_split): one workgroup per work item
+//   (request, KV head, split j of `chunk` keys), numbered split-fastest; XCD x
+//   (workgroups x, x + 8, ...) takes one contiguous range of items, found on
+//   the device from the per-request key counts, so one compiled kernel serves
+//   any mix of lengths.  Every split writes its partial (O_j = U_j / l_j,
+//   LSE_j) for the combine kernel (Cleave §4, Fig. 5(b)).
+// * decode_gqa_d128_stream (attn_decode, one launch): the keys of every
+//   (request, KV head) unit, in 128-key rounds, laid end to end, and each of
+//   the grid's workgroups (about one per compute unit) takes an equal run of
+//   rounds, whatever the request lengths: a long contiguous stream per
+//   compute unit, balanced by construction.  A unit that lies wholly inside
+//   one run is written to O directly; a unit cut by run boundaries is split
+//   into pieces, each piece's workgroup publishes its partial, and the last
+//   one to finish merges them (the combine of Cleave §4 inside the kernel).
+//
+// Within a workgroup the four waves take interleaved 32-key blocks and each
+// keeps its own running max / sum / output (a second, on-chip level of the
+// same split); the waves are merged through LDS at the end of a piece.
 //
 // Per 32-key block and wave (transposed orientation, keys on the MFMA rows):
 //   S^T[32 x 16] = K[32 x 128] * Q^T[128 x 16]      2 x 4 MFMA 16x16x32
@@ -25,14 +33,6 @@
 //   O^T[128 x 16] += V^T[128 x 32] * P^T[32 x 16]   8 MFMA 16x16x32
 // K arrives from HBM straight in the A-operand layout (16 bytes per lane);
 // V goes row-major into a wave-private LDS tile and comes back transposed.
-//
-// Epilogues (KParams::split_mode):
-//   0  one split per request: O = U / l straight to the output;
-//   1  every split writes its partial (O_j = U_j / l_j, LSE_j) to the
-//      workspace for the combine kernel (Cleave §4, Fig. 5(b));
-//   2  as 1, then the last split of each (request, KV head) to finish merges
-//      the partials itself (single launch); a request with one split writes
-//      O directly.
 #include "../attn_internal.hpp"
 #include "common.hpp"
 #include "layout.hpp"
@@ -44,6 +44,10 @@ constexpr int KB = 32;           // keys per wave block
 constexpr int D = 128;
 constexpr int VROW = 288;        // bytes per V row in LDS (256 + 32 pad)
 constexpr int VTILE = KB * VROW; // one wave's V tile
+constexpr int NW = 4;            // waves per workgroup
+constexpr int NB = 2;            // register blocks in flight per wave
+constexpr int ROUND = KB * NW;   // keys per workgroup round (128)
+static_assert(ROUND == kGqaTileN, "the planner's round is the kernel's");
 
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
@@ -183,11 +187,9 @@ __device__ __forceinline__ void store_o8(const KParams& p, int64_t off, const f3
   }
 }
 
-// A work item whose device key counts exceed the plan: NaN to its rows of O
-// (one split per request, or the single-launch merge) or to its partial slot
-// (the two-launch split, whose NaN the combine carries into O), and no
-// arrival is counted, so the counters stay zero.
-__device__ void write_beyond_plan(const KParams& p, int b, int kvh, int j, int sb) {
+// A work item whose device key counts exceed the plan: NaN to its partial
+// slot, which the combine kernel carries into O.
+__device__ void write_beyond_plan(const KParams& p, int b, int kvh, int j) {
   const float nan = __builtin_nanf("");
   const f32x4_t v = {nan, nan, nan, nan};
   const int t = threadIdx.x;
@@ -196,59 +198,32 @@ __device__ void write_beyond_plan(const KParams& p, int b, int kvh, int j, int s
   if (orow >= p.rows) return;
   const int i = orow / p.G;
   const int h = kvh * p.G + orow % p.G;
-  const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
-  if (p.split_mode == 1) {
-    const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + row;
-    float* dst = p.ws_o + slot * D + oc;
-    reinterpret_cast<f32x4_t*>(dst)[0] = v;
-    reinterpret_cast<f32x4_t*>(dst)[1] = v;
-    if (oc == 0) p.ws_lse[slot] = nan;
-    return;
-  }
-  store_o8(p, (int64_t)b * p.os_b + (int64_t)i * p.os_t + (int64_t)h * p.os_h + oc, v, v);
-  if (oc == 0 && p.lse_out) p.lse_out[row] = nan;
+  const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + ((int64_t)b * p.Lq + i) * p.Hq + h;
+  float* dst = p.ws_o + slot * D + oc;
+  reinterpret_cast<f32x4_t*>(dst)[0] = v;
+  reinterpret_cast<f32x4_t*>(dst)[1] = v;
+  if (oc == 0) p.ws_lse[slot] = nan;
 }
 
-// Four waves per workgroup; a workgroup round covers KB * NW keys.  NB
-// register blocks per wave are in flight (four measured slower than two, also
-// with one workgroup per CU).
-//
-// PAGED: K and V rows are found through the page table (page size a power of
-// two).  The item's page ids are staged in LDS once; each lane then forms the
-// 64-bit address of every row it loads, so pages of any size, down to one
+// One wave's running state over a piece of keys.
+struct WaveState {
+  f32x4_t oacc[8];  // O^T[d = 16 db + 4 h4 + i][row r], relative to m_run
+  float m_run;      // running max of the lane's row (base-2 units)
+  float l_part;     // this lane's share of the row sum
+};
+
+// Streams keys [lo, hi) of (request b, KV head kvh), L_b = L keys, into each
+// wave's state.  Wave w takes blocks lo + 32 w + 128 i (NB in flight).  Every
+// thread of the workgroup calls it.  PAGED: K and V rows are found through
+// the page table (power-of-two page size); the ids of a segment's pages are
+// staged in LDS (at most kGqaPageIds - 1 pages a segment) and every lane forms
+// the 64-bit address of each row it loads, so pages of any size, down to one
 // row, are read with the same 16-byte-per-lane loads as the strided layout.
-constexpr int NW = 4;
-constexpr int NB = 2;
 template <bool PAGED>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void decode_gqa_d128_kernel(KParams p) {
-  constexpr int STEP = KB * NW;
-  __shared__ __attribute__((aligned(16))) char lds_raw[NW * VTILE];  // 36 KiB
-  __shared__ float m_w[NW][16];
-  __shared__ float l_w[NW][16];
-  __shared__ int page_ids[PAGED ? kGqaPageIds : 1];
-
+__device__ __forceinline__ void stream_keys(const KParams& p, int b, int kvh, int lo, int hi,
+                                            int L, char* lds_raw, int* page_ids, WaveState& ws) {
   const int lane = threadIdx.x & 63;
-  // Wave index, made visibly wave-uniform so the key loop below is a scalar loop.
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int b, kvh, j, sb, L;
-  bool beyond_plan;
-  if (!find_item(p, lane, b, kvh, j, sb, L, beyond_plan)) return;
-  // The item is the same in every lane; saying so keeps the buffer resources
-  // below in scalar registers (otherwise every load is wrapped in a loop over
-  // the distinct descriptor values of the wave).
-  b = __builtin_amdgcn_readfirstlane(b);
-  kvh = __builtin_amdgcn_readfirstlane(kvh);
-  j = __builtin_amdgcn_readfirstlane(j);
-  sb = __builtin_amdgcn_readfirstlane(sb);
-  L = __builtin_amdgcn_readfirstlane(L);
-  if (__builtin_amdgcn_readfirstlane((int)beyond_plan)) {
-    write_beyond_plan(p, b, kvh, j, sb);
-    return;
-  }
-  const int lo = j * p.chunk;
-  const int hi = min(lo + p.chunk, L);
-
   const int r = lane & 15;   // MFMA column: query row within the KV group
   const int h4 = lane >> 4;  // lane group
   const int R = p.rows;
@@ -268,7 +243,7 @@ void decode_gqa_d128_kernel(KParams p) {
     }
   }
 
-  // The buffer ranges end at this split's last key: loads past it return zero
+  // The buffer ranges end at the piece's last key: loads past it return zero
   // without touching memory, so every load below is unconditional (which lets
   // the compiler wait only for the block about to be used).
   const uint16_t* kp = reinterpret_cast<const uint16_t*>(p.k) + (int64_t)kvh * p.ks_h;
@@ -282,25 +257,16 @@ void decode_gqa_d128_kernel(KParams p) {
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, PAGED ? 0u : (uint32_t)hi * kst);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(vp, PAGED ? 0u : (uint32_t)hi * vst);
 
-  // Paged: the ids of the pages holding keys [lo, hi), clamped into the pool.
   const int psh = PAGED ? p.page_shift : 0;
   const int pmask = (1 << psh) - 1;
-  const int pg0 = lo >> psh;
-  if constexpr (PAGED) {
-    const int n_ids = hi > lo ? min(((hi - 1) >> psh) - pg0 + 1, kGqaPageIds) : 0;
-    const int32_t* row = p.page_table + (int64_t)b * p.ppr + pg0;
-    for (int e = threadIdx.x; e < n_ids; e += NW * 64) {
-      const int pg = row[e];
-      page_ids[e] = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
-    }
-    __syncthreads();
-  }
   const int64_t kpage = p.ks_b * 2;  // bytes between pages (paged layout)
   const int64_t vpage = p.vs_b * 2;
-  // Address of key `key` in a pool; keys past the split read the split's last
-  // key instead (its scores are masked and its probabilities are zero).
+  int seg_lo = lo, seg_hi = hi;      // the keys whose page ids are staged
+  int pg0 = 0;
+  // Address of key `key` in a pool; keys past the segment read its last key
+  // instead (its scores are masked and its probabilities are zero).
   auto paged_row = [&](const uint16_t* pool, int64_t page_bytes, uint32_t st, int key) {
-    const int kc = min(key, hi - 1);
+    const int kc = min(key, seg_hi - 1);
     const int pg = page_ids[(kc >> psh) - pg0];
     return reinterpret_cast<const char*>(pool) + (int64_t)pg * page_bytes +
            (int64_t)(kc & pmask) * st;
@@ -374,7 +340,7 @@ void decode_gqa_d128_kernel(KParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = kb + 16 * sb + 4 * h4 + i;
-        const bool vis = key < hi && (!p.causal || key <= qlim);
+        const bool vis = key < seg_hi && (!p.causal || key <= qlim);
         const float v = vis ? s[sb][i] * sl2 : kNegInf;
         xs[sb * 4 + i] = v;
         mt = fmaxf(mt, v);
@@ -424,180 +390,377 @@ void decode_gqa_d128_kernel(KParams p) {
   };
 
   // Rotation over NB register blocks: while one block is processed, the next
-  // NB - 1 are in flight.  Wave w takes blocks lo + 32*w + 128*i.  Loads past
-  // the split return zero without touching memory.
-  // A paged item with no keys loads nothing (there is no row to clamp to).
-  Block X[NB];
-  int kb = lo + KB * w;
-  if (!PAGED || hi > lo) {
+  // NB - 1 are in flight.  Loads past the piece return zero without touching
+  // memory.  Paged keys go segment by segment (each segment's page ids staged
+  // in LDS first); a paged piece with no keys loads nothing.
+  constexpr int STEP = KB * NW;
+  const int seg_len = PAGED ? ((kGqaPageIds - 1) << psh) / STEP * STEP : 0;
+  for (seg_lo = lo; seg_lo < hi || (!PAGED && seg_lo == lo); seg_lo += PAGED ? seg_len : hi - lo) {
+    if constexpr (PAGED) {
+      seg_hi = min(hi, seg_lo + seg_len);
+      pg0 = seg_lo >> psh;
+      const int n_ids = min(((seg_hi - 1) >> psh) - pg0 + 1, kGqaPageIds);
+      const int32_t* row = p.page_table + (int64_t)b * p.ppr + pg0;
+      __syncthreads();  // the previous segment's ids are no longer read
+      for (int e = threadIdx.x; e < n_ids; e += NW * 64) {
+        const int pg = row[e];
+        page_ids[e] = pg < 0 ? 0 : (pg >= p.num_pages ? p.num_pages - 1 : pg);
+      }
+      __syncthreads();
+    }
+    Block X[NB];
+    int kb = seg_lo + KB * w;
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i) load_block(X[i], kb + i * STEP);
     // The scheduling barriers keep each block's loads issued before the wait for
     // the block being processed.
-    for (; kb < hi; kb += NB * STEP) {
+    for (; kb < seg_hi; kb += NB * STEP) {
 #pragma unroll
       for (int i = 0; i < NB; ++i) {
         load_block(X[(i + NB - 1) % NB], kb + (i + NB - 1) * STEP);
         __builtin_amdgcn_sched_barrier(0);
-        if (i == 0 || kb + i * STEP < hi) process_block(X[i], kb + i * STEP);
+        if (i == 0 || kb + i * STEP < seg_hi) process_block(X[i], kb + i * STEP);
       }
     }
+    if (!PAGED) break;
   }
+#pragma unroll
+  for (int db = 0; db < 8; ++db) ws.oacc[db] = oacc[db];
+  ws.m_run = m_run;
+  ws.l_part = l_part;
+}
 
-  // Merge the four waves' partial states.
-  float l_row = l_part;
+// One row's result after the waves are merged: thread t holds row t >> 4,
+// columns 8 (t & 15) .. + 7 (threads of rows >= G * Lq hold nothing useful).
+struct RowOut {
+  f32x4_t o0, o1;  // O = U / l, columns oc .. oc + 3 and oc + 4 .. oc + 7
+  float lse;       // natural-log LSE of the piece (-inf without a key)
+};
+
+// Merges the four waves' states through LDS (all threads call it).  The
+// caller must not write lds_raw again before a barrier.
+__device__ __forceinline__ RowOut merge_waves(const WaveState& ws, char* lds_raw,
+                                              float (*m_w)[16], float (*l_w)[16]) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, h4 = lane >> 4;
+  float l_row = ws.l_part;
   l_row += __shfl_xor(l_row, 16, 64);
   l_row += __shfl_xor(l_row, 32, 64);
+  __syncthreads();  // every wave is done with its V tile
   if (h4 == 0) {
-    m_w[w][r] = m_run;
+    m_w[w][r] = ws.m_run;
     l_w[w][r] = l_row;
   }
   __syncthreads();
   float M = kNegInf;
 #pragma unroll
   for (int u = 0; u < NW; ++u) M = fmaxf(M, m_w[u][r]);
-  const float fw = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - M);
+  const float fw = (ws.m_run == kNegInf) ? 0.f : fast_exp2(ws.m_run - M);
   float* osum = reinterpret_cast<float*>(lds_raw);  // [NW][16][128] floats
 #pragma unroll
   for (int db = 0; db < 8; ++db)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) osum[(w * 16 + r) * D + 16 * db + 4 * h4 + i] = oacc[db][i] * fw;
+    for (int i = 0; i < 4; ++i)
+      osum[(w * 16 + r) * D + 16 * db + 4 * h4 + i] = ws.oacc[db][i] * fw;
   __syncthreads();
 
-  // Threads 0..255 write 16 rows x 128 columns: row t/16, columns 8*(t%16) .. +7.
   const int t = threadIdx.x;
   const int orow = t >> 4;
   const int oc = (t & 15) * 8;
-  if (orow < R) {
-    float Mr = kNegInf;
+  float Mr = kNegInf;
 #pragma unroll
-    for (int u = 0; u < NW; ++u) Mr = fmaxf(Mr, m_w[u][orow]);
-    float Lt = 0.f;
-    if (Mr != kNegInf) {
-#pragma unroll
-      for (int u = 0; u < NW; ++u) {
-        const float mu = m_w[u][orow];
-        if (mu != kNegInf) Lt += l_w[u][orow] * fast_exp2(mu - Mr);
-      }
-    }
-    const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-    f32x4_t o0 = {0.f, 0.f, 0.f, 0.f}, o1 = {0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < NW; ++u) Mr = fmaxf(Mr, m_w[u][orow]);
+  float Lt = 0.f;
+  if (Mr != kNegInf) {
 #pragma unroll
     for (int u = 0; u < NW; ++u) {
-      o0 += *reinterpret_cast<const f32x4_t*>(osum + (u * 16 + orow) * D + oc);
-      o1 += *reinterpret_cast<const f32x4_t*>(osum + (u * 16 + orow) * D + oc + 4);
-    }
-    o0 *= inv;
-    o1 *= inv;
-    const int i = orow / p.G;
-    const int h = kvh * p.G + orow % p.G;
-    const float lse = Lt > 0.f ? (Mr + fast_log2(Lt)) * kLn2 : kNegInf;
-    if (p.split_mode == 0 || (p.split_mode == 2 && sb == 1)) {
-      store_o8(p, (int64_t)b * p.os_b + (int64_t)i * p.os_t + (int64_t)h * p.os_h + oc, o0, o1);
-      if (oc == 0 && p.lse_out) p.lse_out[((int64_t)b * p.Lq + i) * p.Hq + h] = lse;
-    } else {
-      const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + ((int64_t)b * p.Lq + i) * p.Hq + h;
-      float* dst = p.ws_o + slot * D + oc;
-      if (p.split_mode == 1) {
-        reinterpret_cast<f32x4_t*>(dst)[0] = o0;
-        reinterpret_cast<f32x4_t*>(dst)[1] = o1;
-        if (oc == 0) p.ws_lse[slot] = lse;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          store_dev(dst + e, o0[e]);
-          store_dev(dst + 4 + e, o1[e]);
-        }
-        if (oc == 0) store_dev(p.ws_lse + slot, lse);
-      }
+      const float mu = m_w[u][orow];
+      if (mu != kNegInf) Lt += l_w[u][orow] * fast_exp2(mu - Mr);
     }
   }
-  if (p.split_mode != 2 || sb == 1) return;
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  RowOut ro;
+  ro.o0 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  ro.o1 = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < NW; ++u) {
+    ro.o0 += *reinterpret_cast<const f32x4_t*>(osum + (u * 16 + orow) * D + oc);
+    ro.o1 += *reinterpret_cast<const f32x4_t*>(osum + (u * 16 + orow) * D + oc + 4);
+  }
+  ro.o0 *= inv;
+  ro.o1 *= inv;
+  ro.lse = Lt > 0.f ? (Mr + fast_log2(Lt)) * kLn2 : kNegInf;
+  return ro;
+}
 
-  // Single-launch merge: the last split of this (request, KV head) to arrive
-  // reduces the sb partials (the combine of Cleave §4, done in place).  Each
-  // wave waits until its device-coherent partial stores have completed, the
-  // barrier gathers the waves, and thread 0 counts the arrival; the last
-  // arrival reads the partials back with device-coherent loads issued after
-  // its counter update returned.
-  __shared__ int s_last;
-  wait_vmem();
-  __syncthreads();
-  const int unit = b * p.Hkv + kvh;
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(p.counters + unit, 1, __ATOMIC_RELAXED,
-                                    __HIP_MEMORY_SCOPE_AGENT) == sb - 1;
-  __syncthreads();
-  if (!s_last) return;
-  if (orow < R) {
+// Work-item kernel (attn_decode_split): every split writes its partial.
+template <bool PAGED>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_gqa_d128_items(KParams p) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[NW * VTILE];  // 36 KiB
+  __shared__ float m_w[NW][16];
+  __shared__ float l_w[NW][16];
+  __shared__ int page_ids[PAGED ? kGqaPageIds : 1];
+
+  const int lane = threadIdx.x & 63;
+  int b, kvh, j, sb, L;
+  bool beyond_plan;
+  if (!find_item(p, lane, b, kvh, j, sb, L, beyond_plan)) return;
+  // The item is the same in every lane; saying so keeps the buffer resources
+  // in scalar registers (otherwise every load is wrapped in a loop over the
+  // distinct descriptor values of the wave).
+  b = __builtin_amdgcn_readfirstlane(b);
+  kvh = __builtin_amdgcn_readfirstlane(kvh);
+  j = __builtin_amdgcn_readfirstlane(j);
+  L = __builtin_amdgcn_readfirstlane(L);
+  if (__builtin_amdgcn_readfirstlane((int)beyond_plan)) {
+    write_beyond_plan(p, b, kvh, j);
+    return;
+  }
+  const int lo = j * p.chunk;
+  const int hi = min(lo + p.chunk, L);
+  WaveState ws;
+  stream_keys<PAGED>(p, b, kvh, lo, hi, L, lds_raw, page_ids, ws);
+  const RowOut ro = merge_waves(ws, lds_raw, m_w, l_w);
+  const int t = threadIdx.x;
+  const int orow = t >> 4;
+  const int oc = (t & 15) * 8;
+  if (orow < p.rows) {
     const int i = orow / p.G;
     const int h = kvh * p.G + orow % p.G;
-    const int64_t nrows = (int64_t)p.B * p.Lq * p.Hq;
-    const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
-    // One pass over the splits in split order, MB at a time: the loads of a
-    // batch are independent (one memory round trip per batch, not two per
-    // split); the running max and weight sum are rescaled per batch.
-    constexpr int MB = 4;
-    float M = kNegInf;  // natural-log units
-    f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
-    for (int j0 = 0; j0 < sb; j0 += MB) {
-      float lse[MB];
-      f32x4_t x0[MB], x1[MB];
-#pragma unroll
-      for (int u = 0; u < MB; ++u) {
-        const int64_t slot = (int64_t)min(j0 + u, sb - 1) * nrows + row;
-        lse[u] = load_dev(p.ws_lse + slot);
-        const float* src = p.ws_o + slot * D + oc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x0[u][e] = load_dev(src + e);
-          x1[u][e] = load_dev(src + 4 + e);
-        }
-      }
-      float mb = M;
-#pragma unroll
-      for (int u = 0; u < MB; ++u)
-        if (j0 + u < sb) mb = fmaxf(mb, lse[u]);
-      if (mb == kNegInf) continue;
-      const float m2 = mb * kLog2e;
-      const float sc = (M == kNegInf) ? 0.f : fast_exp2(M * kLog2e - m2);
-      a0 *= sc;
-      a1 *= sc;
-      wsum *= sc;
-#pragma unroll
-      for (int u = 0; u < MB; ++u) {
-        if (j0 + u < sb) {
-          const float wgt = fast_exp2(lse[u] * kLog2e - m2);
-          a0 += wgt * x0[u];
-          a1 += wgt * x1[u];
-          wsum += wgt;
-        }
-      }
-      M = mb;
-    }
-    if (M != kNegInf) {
-      const float inv = 1.f / wsum;
-      a0 *= inv;
-      a1 *= inv;
-    }
-    store_o8(p, (int64_t)b * p.os_b + (int64_t)i * p.os_t + (int64_t)h * p.os_h + oc, a0, a1);
-    if (oc == 0 && p.lse_out)
-      p.lse_out[row] = M == kNegInf ? kNegInf : M + fast_log2(wsum) * kLn2;
+    const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + ((int64_t)b * p.Lq + i) * p.Hq + h;
+    float* dst = p.ws_o + slot * D + oc;
+    reinterpret_cast<f32x4_t*>(dst)[0] = ro.o0;
+    reinterpret_cast<f32x4_t*>(dst)[1] = ro.o1;
+    if (oc == 0) p.ws_lse[slot] = ro.lse;
   }
-  if (threadIdx.x == 0)  // leave the counter zeroed for the next call
-    __hip_atomic_store(p.counters + unit, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One workgroup's run of rounds [g T / N, (g + 1) T / N) over the units laid
+// end to end (unit u = (request, KV head), max(1, ceil(L_b / 128)) rounds,
+// so an empty unit still has one piece, which writes O = 0).
+//
+// A unit covering global rounds [U0, U1) is cut into the pieces of the
+// workgroups whose runs meet it: g_first = ceil((U0 + 1) N / T) - 1 to
+// g_last = ceil(U1 N / T) - 1, piece index g - g_first.  Every workgroup
+// computes the same numbers, so they agree on the piece count.
+//
+// Merge of a cut unit: the (request, KV head) counter in ws_cnt holds tickets
+// in its low 16 bits and published partials in its high 16 bits.  Each piece
+// takes a ticket when its keys are done; all but the last publish their
+// partial and count it; the last one (ticket = pieces - 1) knows every other
+// piece has already taken its ticket, so that workgroup is resident and has
+// only its stores left: it waits for their count, merges all pieces in piece
+// order (its own from registers, with the same arithmetic as a stored one,
+// so the bits do not depend on which piece finishes last), writes O and
+// resets the counter.  A partial is an 8 KiB block in thread order (thread t's
+// columns oc .. oc + 3 at 16 t, oc + 4 .. oc + 7 at 4096 + 16 t: each store
+// or load instruction moves 1 KiB of whole cache lines) plus one LSE per row.
+//
+// Ordering on gfx950: partials are written with sc1 (device-coherent)
+// stores, which write through the XCD's L2 instead of leaving dirty lines
+// there, and each wave waits for them (vmcnt(0)) before the workgroup barrier
+// that precedes the counting atomic; the reader's loads are sc1 too, so they
+// are served from the device-coherent level, never from a stale line of its
+// own L2.  Because no data is left dirty in an L2, the whole-L2 write-back of
+// a device-scope release fence is not needed.
+template <bool PAGED>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void decode_gqa_d128_stream(KParams p) {
+  __shared__ __attribute__((aligned(16))) char lds_raw[NW * VTILE];  // 36 KiB
+  __shared__ float m_w[NW][16];
+  __shared__ float l_w[NW][16];
+  __shared__ int page_ids[PAGED ? kGqaPageIds : 1];
+  __shared__ int s_ticket;
+
+  const int lane = threadIdx.x & 63;
+  const int64_t T = p.n_items;            // rounds of all units (plan)
+  const int64_t N = gridDim.x;
+  const int64_t g = blockIdx.x;
+  const int64_t r_beg = g * T / N, r_end = (g + 1) * T / N;
+  if (r_beg >= r_end) return;
+
+  // The request holding round r_beg, and the device total of rounds (units
+  // of request b have max(1, ceil(L_b / 128)) rounds each), scanned 64
+  // requests at a time.
+  int64_t base = 0, req_base = 0;
+  int b = -1;
+  for (int c = 0; c < p.B; c += 64) {
+    const int bb = c + lane;
+    int n = 0;
+    if (bb < p.B) n = p.Hkv * max(1, (kv_len_b(p, bb) + ROUND - 1) / ROUND);
+    const int incl = wave_incl_scan(n, lane);
+    const int total = __shfl(incl, 63, 64);
+    if (b < 0 && r_beg < base + total) {
+      const int rel = (int)(r_beg - base);
+      const int idx = __builtin_amdgcn_readfirstlane(__popcll(__ballot(incl <= rel)));
+      b = c + idx;
+      req_base = base + __builtin_amdgcn_readfirstlane(__shfl(incl - n, idx, 64));
+    }
+    base += total;
+  }
+  // More rounds on the device than the plan's T: the rounds past T belong to
+  // no workgroup, so every workgroup writes NaN for the units it meets
+  // instead of results (and counts nothing).
+  const bool beyond_plan = base > T;
+  if (b < 0) {
+    // A run past the device's rounds (device lengths shorter than planned).
+    return;
+  }
+  int L = uniform(kv_len_b(p, b));
+  int nr = max(1, (L + ROUND - 1) / ROUND);
+  int kvh = (int)((r_beg - req_base) / nr);
+  int rin = (int)((r_beg - req_base) - (int64_t)kvh * nr);
+  int64_t cur = r_beg;
+  const int t = threadIdx.x;
+  const int orow = t >> 4;
+  const int oc = (t & 15) * 8;
+  const int64_t nunits = (int64_t)p.B * p.Hkv;
+  while (cur < r_end && b < p.B) {
+    const int take = (int)min((int64_t)(nr - rin), r_end - cur);
+    const int64_t U0 = cur - rin, U1 = U0 + nr;
+    const bool whole = rin == 0 && take == nr;
+    const int lo = rin * ROUND;
+    const int hi = min((rin + take) * ROUND, L);
+    const int qi = orow / p.G;
+    const int qh = kvh * p.G + orow % p.G;
+    const int64_t row = ((int64_t)b * p.Lq + qi) * p.Hq + qh;
+    const int64_t obase = (int64_t)b * p.os_b + (int64_t)qi * p.os_t + (int64_t)qh * p.os_h + oc;
+    if (beyond_plan) {
+      const float nan = __builtin_nanf("");
+      const f32x4_t v = {nan, nan, nan, nan};
+      if (orow < p.rows) {
+        store_o8(p, obase, v, v);
+        if (oc == 0 && p.lse_out) p.lse_out[row] = nan;
+      }
+    } else {
+      WaveState ws;
+      stream_keys<PAGED>(p, b, kvh, lo, hi, L, lds_raw, page_ids, ws);
+      const RowOut ro = merge_waves(ws, lds_raw, m_w, l_w);
+      if (whole) {
+        if (orow < p.rows) {
+          store_o8(p, obase, ro.o0, ro.o1);
+          if (oc == 0 && p.lse_out) p.lse_out[row] = ro.lse;
+        }
+      } else {
+        const int64_t g_first = ((U0 + 1) * N + T - 1) / T - 1;
+        const int64_t g_last = (U1 * N + T - 1) / T - 1;
+        const int pieces = (int)(g_last - g_first + 1);
+        const int pi = (int)(g - g_first);
+        const int unit = b * p.Hkv + kvh;
+        int* cnt = p.counters + unit;
+        if (t == 0)
+          s_ticket = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
+                     0xffff;
+        __syncthreads();
+        const int ticket = s_ticket;
+        const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.ws_o, 0xffffffffu);
+        auto blk = [&](int q) { return (uint32_t)(((int64_t)q * nunits + unit) * (16 * D * 4)); };
+        auto lse_at = [&](int q) { return p.ws_lse + ((int64_t)q * nunits + unit) * 16 + orow; };
+        if (ticket < pieces - 1) {
+          store16_dev(wrs, blk(pi) + 16u * (uint32_t)t, ro.o0);
+          store16_dev(wrs, blk(pi) + 4096u + 16u * (uint32_t)t, ro.o1);
+          if (oc == 0) store_dev(lse_at(pi), ro.lse);
+          wait_vmem();
+          __syncthreads();
+          if (t == 0)
+            __hip_atomic_fetch_add(cnt, 1 << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          if (t == 0) {
+            while ((__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 16) <
+                   pieces - 1)
+              __builtin_amdgcn_s_sleep(2);
+          }
+          __syncthreads();
+          // Pieces in order, four at a time: one memory round trip per batch;
+          // the running reference and weight sum are rescaled per batch.
+          constexpr int MB = 4;
+          float M = kNegInf;  // base-2 units
+          f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+          float wsum = 0.f;
+          for (int q0 = 0; q0 < pieces; q0 += MB) {
+            float lq[MB];
+            f32x4_t x0[MB], x1[MB];
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+              const int q = q0 + u;
+              if (q < pieces && q != pi) {
+                lq[u] = load_dev(lse_at(q));
+                x0[u] = load16_dev(wrs, blk(q) + 16u * (uint32_t)t);
+                x1[u] = load16_dev(wrs, blk(q) + 4096u + 16u * (uint32_t)t);
+              } else {
+                lq[u] = ro.lse;
+                x0[u] = ro.o0;
+                x1[u] = ro.o1;
+              }
+            }
+            float mb = M;
+#pragma unroll
+            for (int u = 0; u < MB; ++u)
+              if (q0 + u < pieces) mb = fmaxf(mb, lq[u] * kLog2e);
+            if (mb == kNegInf) continue;
+            const float sc = (M == kNegInf) ? 0.f : fast_exp2(M - mb);
+            a0 *= sc;
+            a1 *= sc;
+            wsum *= sc;
+#pragma unroll
+            for (int u = 0; u < MB; ++u) {
+              if (q0 + u < pieces) {
+                const float wgt = fast_exp2(lq[u] * kLog2e - mb);
+                a0 += wgt * x0[u];
+                a1 += wgt * x1[u];
+                wsum += wgt;
+              }
+            }
+            M = mb;
+          }
+          if (M != kNegInf) {
+            const float winv = 1.f / wsum;
+            a0 *= winv;
+            a1 *= winv;
+          }
+          if (orow < p.rows) {
+            store_o8(p, obase, a0, a1);
+            if (oc == 0 && p.lse_out)
+              p.lse_out[row] = M == kNegInf ? kNegInf : (M + fast_log2(wsum)) * kLn2;
+          }
+          if (t == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    __syncthreads();  // LDS (wave merge, ticket) is reused by the next piece
+    cur += take;
+    rin = 0;
+    if (++kvh == p.Hkv) {
+      kvh = 0;
+      ++b;
+      if (b < p.B) {
+        L = uniform(kv_len_b(p, b));
+        nr = max(1, (L + ROUND - 1) / ROUND);
+      }
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode_gqa_d128(const KParams& p, hipStream_t s) {
+  if (p.split_mode == 3) {
+    const unsigned nwg = (unsigned)p.stream_grid;
+    if (nwg == 0) return hipSuccess;
+    if (p.page_table)
+      hipLaunchKernelGGL(decode_gqa_d128_stream<true>, dim3(nwg), dim3(NW * 64), 0, s, p);
+    else
+      hipLaunchKernelGGL(decode_gqa_d128_stream<false>, dim3(nwg), dim3(NW * 64), 0, s, p);
+    return hipGetLastError();
+  }
   const int64_t nwg = (p.n_items + 7) / 8 * 8;
   if (nwg == 0) return hipSuccess;
   if (p.page_table)
-    hipLaunchKernelGGL(decode_gqa_d128_kernel<true>, dim3((unsigned)nwg), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL(decode_gqa_d128_items<true>, dim3((unsigned)nwg), dim3(NW * 64), 0, s, p);
   else
-    hipLaunchKernelGGL(decode_gqa_d128_kernel<false>, dim3((unsigned)nwg), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL(decode_gqa_d128_items<false>, dim3((unsigned)nwg), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
 

@@ -244,14 +244,45 @@ def test_empty_batch_is_a_no_op(lib):
 
 # ---------------------------------------------------------------- planner
 
-def _check_plan_invariants(p, plan, lens):
+def _stream_runs(p, lens, cus):
+    """The GQA single-launch decomposition, by brute force: every unit's
+    rounds of 128 keys laid end to end (an empty unit counts one), equal runs
+    [g T / N, (g + 1) T / N) per workgroup, and for every unit the number of
+    runs that meet it."""
+    cap = p.kv_len_max
+    unit_rounds = []
+    for n in lens:
+        r = max(1, math.ceil(min(max(n, 0), cap) / 128))
+        unit_rounds += [r] * p.kv_heads
+    total = sum(unit_rounds)
+    grid = max(1, min(cus, total))
+    owner = []  # owner[round] = the workgroup whose run holds it
+    for g in range(grid):
+        owner += [g] * ((g + 1) * total // grid - g * total // grid)
+    assert len(owner) == total
+    pieces, u0 = 1, 0
+    for r in unit_rounds:
+        pieces = max(pieces, len(set(owner[u0:u0 + r])))
+        u0 += r
+    return total, grid, pieces
+
+
+def _check_plan_invariants(p, plan, lens, cus=256):
     lmax = max(lens) if lens else 0
     assert plan.chunk % plan.tile_n == 0 and plan.chunk >= plan.tile_n
     assert plan.s_max == max(1, math.ceil(lmax / plan.chunk))
     assert plan.s_max * plan.chunk >= lmax
     nrows = p.batch * p.q_len * p.q_heads
-    assert plan.ws_o_bytes == plan.s_max * nrows * p.head_dim_v * 4
-    assert plan.ws_lse_bytes == plan.s_max * nrows * 4
+    ws_o = plan.s_max * nrows * p.head_dim_v * 4
+    ws_lse = plan.s_max * nrows * 4
+    if ra.KERNEL_NAMES[plan.kernel] == "gqa_d128" and p.batch:
+        total, grid, pieces = _stream_runs(p, lens, cus)
+        assert (plan.stream_rounds, plan.stream_grid, plan.stream_pieces) == (total, grid, pieces)
+        units = p.batch * p.kv_heads
+        ws_o = max(ws_o, pieces * units * 16 * 128 * 4)
+        ws_lse = max(ws_lse, pieces * units * 16 * 4)
+    assert plan.ws_o_bytes == ws_o
+    assert plan.ws_lse_bytes == ws_lse
     assert plan.ws_cnt_bytes == p.batch * p.kv_heads * 4
     # Work items (request, KV head, split), counted from the clamped host lengths;
     # an empty request owns one item per KV head.
@@ -290,7 +321,10 @@ def test_plan_llama_decode_uses_gqa_kernel_and_fills_the_gpu(lib):
     # With more compute units than units the key axis is split across workgroups.
     st, plan2 = plan_status(lib, p, num_cus=1024)
     assert st == 0 and plan2.s_max > 1 and plan2.block == 256
-    _check_plan_invariants(p, plan2, [4096] * 32)
+    _check_plan_invariants(p, plan2, [4096] * 32, cus=1024)
+    # The single launch: one run of 32 rounds per compute unit, each exactly
+    # one (request, KV head), so no unit is cut.
+    assert (plan.stream_rounds, plan.stream_grid, plan.stream_pieces) == (8192, 256, 1)
 
 
 def test_plan_unbalanced_lengths_split_across_workgroups(lib):

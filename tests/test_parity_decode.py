@@ -179,9 +179,12 @@ def test_full_size_decode_whole_output(name, fused, layout):
 def test_device_lengths_beyond_the_plan_write_nan(fused):
     # The plan is made from host lengths that are shorter than the device's:
     # request 1 holds 2000 keys on the device but was planned with 1000, so
-    # s_max * chunk (4 x 256) does not cover it.  Its rows come out NaN
-    # instead of a silently truncated result; the other requests are exact;
-    # the arrival counters stay zero.
+    # s_max * chunk (4 x 256) does not cover it.  Two launches: its rows come
+    # out NaN instead of a silently truncated result and the other requests
+    # are exact.  One launch: the runs of rounds per workgroup were cut from
+    # the planned total, which the device's exceeds, so every workgroup writes
+    # NaN for the rows it meets and no row holds a result.  The arrival
+    # counters stay zero either way.
     import reduction_attention_gqa_amd as ra
     p = make_problem(dtype="bf16", batch=3, lq=1, hq=32, hkv=8, dqk=128, dv=128,
                      kv_len=[1000, 2000, 300], lcap=2048, seed=9)
@@ -192,25 +195,28 @@ def test_device_lengths_beyond_the_plan_write_nan(fused):
     d.decode(plan=plan, ws=ws, fused=fused)
     out, lse = d.out(), d.lse_out()
     assert np.isnan(out[1]).all() and np.isnan(lse[1]).all()
-    o, lse_want = _oracle(p)
-    keep = [0, 2]
-    assert_close("beyond plan, other requests", out[keep], o[keep], BF16_MAX, BF16_MEAN)
-    assert_lse_close("beyond plan, other requests", lse[keep], lse_want[keep])
+    if fused:
+        assert np.isnan(out).all()
+    else:
+        o, lse_want = _oracle(p)
+        keep = [0, 2]
+        assert_close("beyond plan, other requests", out[keep], o[keep], BF16_MAX, BF16_MEAN)
+        assert_lse_close("beyond plan, other requests", lse[keep], lse_want[keep])
     assert int(ws[2].abs().sum()) == 0
 
 
 def test_more_work_items_than_planned_write_nan():
-    # Host lengths [1000, 100, 300] plan 8 x (4 + 1 + 2) = 56 work items; the
-    # device lengths [1000, 1000, 300] need 80, so the grid is too small for
-    # them.  Every launched item writes NaN (and counts no arrival); the units
-    # past the grid are never launched and keep what O held (zero here), so
-    # no row holds a result.
+    # Host lengths [1000, 100, 300] plan 8 x (8 + 1 + 3) = 96 rounds of 128
+    # keys; the device lengths [1000, 1000, 300] hold 152, so the runs of the
+    # grid do not cover them.  Every workgroup writes NaN for the rows it meets
+    # (and counts no arrival); rows no run reaches keep what O held (zero
+    # here), so no row holds a result.
     import reduction_attention_gqa_amd as ra
     p = make_problem(dtype="bf16", batch=3, lq=1, hq=32, hkv=8, dqk=128, dv=128,
                      kv_len=[1000, 1000, 300], lcap=1024, seed=10)
     d = DeviceProblem(p)
     plan = ra.attn_decode_plan(d.problem(), 4, [1000, 100, 300])
-    assert plan.n_items == 56 and plan.s_max * plan.chunk >= 1000
+    assert plan.stream_rounds == 96 and plan.s_max * plan.chunk >= 1000
     ws = ra.workspace(plan, "cuda")
     d.o.fill_(0)
     d.decode(plan=plan, ws=ws, fused=True)

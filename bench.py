@@ -742,10 +742,9 @@ KERNEL_SRC = {0: "generic.hip", 1: "decode_gqa_d128.hip", 2: "decode_mla.hip"}
 
 def single_launch_family(prob):
     """Does attn_decode run this workload as one launch (the merge inside the
-    split kernel)?  The GQA D=128 and MLA families do; the generic one runs
-    split + combine."""
-    return prob.dtype == "bf16" and ((prob.dqk == 128 and prob.dv == 128) or
-                                     (prob.dqk == 576 and prob.dv == 512))
+    split kernel)?  Every kernel family does (an MLA problem too large for its
+    single launch aside, which the workloads here are not)."""
+    return True
 
 
 def decode_leg(prob, a, dev, ablations=(), layout="head", page_size=0, s_request=0):

@@ -141,7 +141,7 @@ typedef struct attn_plan {
   uint32_t block;         /* split-kernel threads per workgroup */
   uint64_t ws_o_bytes;    /* bytes needed for ws_o: s_max*B*Lq*Hq*Dv floats */
   uint64_t ws_lse_bytes;  /* bytes needed for ws_lse: s_max*B*Lq*Hq floats */
-  uint64_t ws_cnt_bytes;  /* bytes needed for ws_cnt (attn_decode): B*Hkv int32 */
+  uint64_t ws_cnt_bytes;  /* bytes needed for ws_cnt (attn_decode): B*Hkv*row_tiles int32 */
   int64_t n_items;        /* (request, KV head, split) work items from kv_lens_host:
                              Hkv * max(1, s_b) summed over requests */
   /* attn_decode, GQA family: the keys of every (request, KV head) in rounds of
@@ -216,7 +216,9 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan,
  * For the GQA D=128 and MLA families this is a single launch; the partials
  * it keeps in ws_o / ws_lse are private to it (their layout is not the one
  * attn_decode_split documents).
- *   GQA: the keys of all (request, KV head) units, in rounds of tile_n keys,
+ *   GQA with one split per request (s_max == 1): one workgroup per
+ *   (request, KV head) writes O directly.  GQA with s_max > 1:
+ *   the keys of all (request, KV head) units, in rounds of tile_n keys,
  *   are laid end to end and every workgroup of the plan's stream_grid takes
  *   an equal run of them (one long stream per compute unit, balanced
  *   whatever the request lengths; the split of Cleave §2.2 "Split-K" then
@@ -228,10 +230,14 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan,
  * Either way this is the combine of Cleave §4 without the second launch (the
  * cost the pages' §7.4 attributes to the two-launch design), summing the
  * pieces in order, so the result does not depend on which finishes last.
- * The generic family (and an MLA problem whose partials exceed 2 GiB) runs
- * the split launch and then the combine launch.
+ *   Generic (vector-ALU) family: the plan's s_max splits per (request, KV
+ *   head, row tile); the last one to finish merges them.
+ * An MLA problem whose partials exceed 2 GiB (or whose pointers the MLA
+ * kernel cannot take) runs the split launch and then the combine launch.
  *
- * ws_cnt  DEVICE int32 [B * Hkv] (plan->ws_cnt_bytes).  It must be all zero
+ * ws_cnt  DEVICE int32 arrival counters, plan->ws_cnt_bytes of them (one per
+ *         (request, KV head), times the row tiles for the generic family);
+ *         it must be all zero
  *         before the first call; every call leaves it all zero again.  One
  *         workspace (ws_o, ws_lse, ws_cnt) serves one call at a time: calls
  *         that overlap on the same workspace race.

@@ -111,7 +111,7 @@ constexpr int kGenericTileN = 64;      // keys per generic tile
 constexpr int kGenericBlock = 256;
 constexpr int kGqaTileN = 128;         // keys per GQA-D128 workgroup round (4 waves x 32)
 constexpr int kGqaItemsPerCu = 4;      // planner target: work items per compute unit
-constexpr int kGqaStreamWgsPerCu = 1;  // attn_decode: workgroups per compute unit (one run each)
+constexpr int kGqaStreamWgsPerCu = 2;  // attn_decode when units are cut: runs per compute unit
 constexpr int kGqaMinChunk = 256;      // planner floor on keys per split
 constexpr int kGqaBlock = 256;
 constexpr int kGqaMaxRows = 16;

@@ -8,13 +8,15 @@
 //
 // Two kernels share the key streaming below:
 //
-// * decode_gqa_d128_items (attn_decode_split): one workgroup per work item
-//   (request, KV head, split j of `chunk` keys), numbered split-fastest; XCD x
-//   (workgroups x, x + 8, ...) takes one contiguous range of items, found on
-//   the device from the per-request key counts, so one compiled kernel serves
-//   any mix of lengths.  Every split writes its partial (O_j = U_j / l_j,
-//   LSE_j) for the combine kernel (Cleave §4, Fig. 5(b)).
-// * decode_gqa_d128_stream (attn_decode, one launch): the keys of every
+// * decode_gqa_d128_items (attn_decode_split, and attn_decode with one split
+//   per request): one workgroup per work item (request, KV head, split j of
+//   `chunk` keys), numbered split-fastest; XCD x (workgroups x, x + 8, ...)
+//   takes one contiguous range of items, found on the device from the
+//   per-request key counts, so one compiled kernel serves any mix of lengths.
+//   Every split writes its partial (O_j = U_j / l_j, LSE_j) for the combine
+//   kernel (Cleave §4, Fig. 5(b)); with one split per request O is written
+//   directly.
+// * decode_gqa_d128_stream (attn_decode when the plan splits): the keys of every
 //   (request, KV head) unit, in 128-key rounds, laid end to end, and each of
 //   the grid's workgroups (about one per compute unit) takes an equal run of
 //   rounds, whatever the request lengths: a long contiguous stream per
@@ -529,6 +531,12 @@ void decode_gqa_d128_items(KParams p) {
   if (orow < p.rows) {
     const int i = orow / p.G;
     const int h = kvh * p.G + orow % p.G;
+    if (p.split_mode == 0) {  // one split per request: O directly
+      store_o8(p, (int64_t)b * p.os_b + (int64_t)i * p.os_t + (int64_t)h * p.os_h + oc, ro.o0,
+               ro.o1);
+      if (oc == 0 && p.lse_out) p.lse_out[((int64_t)b * p.Lq + i) * p.Hq + h] = ro.lse;
+      return;
+    }
     const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + ((int64_t)b * p.Lq + i) * p.Hq + h;
     float* dst = p.ws_o + slot * D + oc;
     reinterpret_cast<f32x4_t*>(dst)[0] = ro.o0;

@@ -30,7 +30,12 @@ __device__ __forceinline__ float ld_elem(const void* base, int64_t idx) {
   }
 }
 
-template <bool BF16>
+// STAGE: each key tile's K and V rows are first copied into LDS by all
+// threads with consecutive elements per thread (coalesced, one load per
+// element), and the scores and the V-matmul read them from there; without it
+// (head dims too large for the LDS) every thread reads its K and V elements
+// from memory itself.
+template <bool BF16, bool STAGE>
 __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
   extern __shared__ float smem[];
   float* q_s = smem;                 // [RT][Dqk]
@@ -38,6 +43,10 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
   float* m_s = s_s + RT * TN;        // [RT] running max (base-2 units)
   float* l_s = m_s + RT;             // [RT] running sum
   float* a_s = l_s + RT;             // [RT] rescale factor of this tile
+  const int ks_row = p.Dqk + 1;      // staged K row stride: an odd number of words, so
+                                     // the lanes' different keys fall in different banks
+  float* k_s = a_s + RT;             // [TN][Dqk + 1] staged K rows (STAGE)
+  float* v_s = k_s + TN * ks_row;    // [TN][Dv] staged V rows (STAGE)
 
   const int t = threadIdx.x;
   const int j = blockIdx.x;
@@ -47,15 +56,36 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
   const int L = kv_len_b(p, b);
   const int Lqb = q_len_b(p, b);  // query rows of this request (packed queries: ragged)
 
+  const int r0 = rt * RT;
+  const int nrows = min(RT, p.G * Lqb - r0);
+  if (nrows <= 0) return;  // row tile past this request's queries
+  const int sb_all = (L + p.chunk - 1) / p.chunk;  // splits of this request
+  if (p.split_mode == 2 && (L == 0 || sb_all > p.s_max)) {
+    // Single launch: split 0 answers for a request with no key (O = 0, LSE =
+    // -inf) and for one longer than the plan covers (NaN rather than a
+    // truncated result); no split of such a request counts an arrival.
+    if (j == 0) {
+      const float val = L == 0 ? 0.f : __builtin_nanf("");
+      const float lse = L == 0 ? kNegInf : __builtin_nanf("");
+      for (int e = t; e < nrows * p.Dv; e += NT) {
+        const int r = e / p.Dv, d = e % p.Dv;
+        const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
+        const int64_t oi = o_row_off(p, b, i) + (int64_t)h * p.os_h + d;
+        if (p.o_bf16)
+          reinterpret_cast<uint16_t*>(p.o)[oi] = (uint16_t)f32_to_bf16_bits(val);
+        else
+          reinterpret_cast<float*>(p.o)[oi] = val;
+        if (d == 0 && p.lse_out) p.lse_out[lse_row(p, b, i) * p.Hq + h] = lse;
+      }
+    }
+    return;
+  }
   int lo = 0, hi = L;
   if (p.split_mode) {
     lo = j * p.chunk;
     if (lo >= L) return;  // split j does not exist for this request
     hi = min(lo + p.chunk, L);
   }
-  const int r0 = rt * RT;
-  const int nrows = min(RT, p.G * Lqb - r0);
-  if (nrows <= 0) return;  // row tile past this request's queries
 
   // Causal: rows of this tile see keys j <= i + L - Lq; the tile needs keys
   // up to the largest such bound.
@@ -90,17 +120,40 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
 
   for (int k0 = lo; k0 < hi; k0 += TN) {
     const int nk = min(TN, hi - k0);  // keys of this tile that exist in the range
+    if constexpr (STAGE) {
+      // The previous tile's readers are past the barrier that ends its loop.
+      for (int e = t; e < nk * p.Dqk; e += NT) {
+        const int jj = e / p.Dqk, d = e - jj * p.Dqk;
+        k_s[jj * ks_row + d] =
+            ld_elem<BF16>(p.k, kv_row_off(p, b, k0 + jj, p.ks_b, p.ks_t) + khead + d);
+      }
+      for (int e = t; e < nk * p.Dv; e += NT) {
+        const int jj = e / p.Dv, d = e - jj * p.Dv;
+        v_s[e] = ld_elem<BF16>(p.v, kv_row_off(p, b, k0 + jj, p.vs_b, p.vs_t) + vhead + d);
+      }
+      __syncthreads();
+    }
     // Scores: thread t -> key k0 + t % TN, rows 4*(t / TN) .. +3.
     {
       const int jj = t % TN;
       const int rb = (t / TN) * 4;
       float dot[4] = {0.f, 0.f, 0.f, 0.f};
       if (jj < nk) {
-        const int64_t krow = kv_row_off(p, b, k0 + jj, p.ks_b, p.ks_t) + khead;
-        for (int d = 0; d < p.Dqk; ++d) {
-          const float kv = ld_elem<BF16>(p.k, krow + d);
+        if constexpr (STAGE) {
+          const float* kr = k_s + jj * ks_row;
+#pragma unroll 8
+          for (int d = 0; d < p.Dqk; ++d) {
+            const float kv = kr[d];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) dot[u] = fmaf(q_s[(rb + u) * p.Dqk + d], kv, dot[u]);
+            for (int u = 0; u < 4; ++u) dot[u] = fmaf(q_s[(rb + u) * p.Dqk + d], kv, dot[u]);
+          }
+        } else {
+          const int64_t krow = kv_row_off(p, b, k0 + jj, p.ks_b, p.ks_t) + khead;
+          for (int d = 0; d < p.Dqk; ++d) {
+            const float kv = ld_elem<BF16>(p.k, krow + d);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dot[u] = fmaf(q_s[(rb + u) * p.Dqk + d], kv, dot[u]);
+          }
         }
       }
 #pragma unroll
@@ -160,13 +213,111 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
       if (e < npairs) {
         const int r = e / p.Dv, d = e % p.Dv;
         float a = acc[c] * a_s[r];
-        for (int jj = 0; jj < nk; ++jj)
-          a = fmaf(s_s[r * TN + jj],
-                   ld_elem<BF16>(p.v, kv_row_off(p, b, k0 + jj, p.vs_b, p.vs_t) + vhead + d), a);
+        if constexpr (STAGE) {
+          // Eight independent partial sums keep eight LDS reads in flight.
+          float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          int jj = 0;
+          for (; jj + 8 <= nk; jj += 8) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              part[u] = fmaf(s_s[r * TN + jj + u], v_s[(jj + u) * p.Dv + d], part[u]);
+          }
+          for (; jj < nk; ++jj) part[0] = fmaf(s_s[r * TN + jj], v_s[jj * p.Dv + d], part[0]);
+          a += ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+        } else {
+          for (int jj = 0; jj < nk; ++jj)
+            a = fmaf(s_s[r * TN + jj],
+                     ld_elem<BF16>(p.v, kv_row_off(p, b, k0 + jj, p.vs_b, p.vs_t) + vhead + d), a);
+        }
         acc[c] = a;
       }
     }
     __syncthreads();
+  }
+
+  // Single launch with several splits: the splits of this (request, KV head,
+  // row tile) take tickets (low 16 bits of its counter); all but the last
+  // publish their partial and count it (high 16 bits); the last one, knowing
+  // every other split is resident and has only its stores left, waits for
+  // that count and merges the partials in split order (its own from
+  // registers, computed exactly as a stored one), then resets the counter.
+  // Partials use sc1 (device-coherent) stores and loads, each wave waiting
+  // for its stores before the barrier that precedes the counting atomic, so
+  // no partial is left dirty in, or read stale from, one XCD's L2.
+  if (p.split_mode == 2 && sb_all > 1) {
+    int* cnt = p.counters + ((int64_t)b * p.Hkv + kvh) * gridDim.y + rt;
+    __shared__ int s_ticket;
+    if (t == 0)
+      s_ticket = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff;
+    __syncthreads();
+    const bool last = s_ticket == sb_all - 1;
+    const int64_t nrow_all = (int64_t)p.B * p.Lq * p.Hq;
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int e = t + NT * c;
+      if (e < npairs) {
+        const int r = e / p.Dv, d = e % p.Dv;
+        if (r < nrows && !last) {
+          const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
+          const float l = l_s[r];
+          const int64_t slot = (int64_t)j * nrow_all + ((int64_t)b * p.Lq + i) * p.Hq + h;
+          store_dev(p.ws_o + slot * p.Dv + d, l > 0.f ? acc[c] / l : 0.f);
+          if (d == 0) store_dev(p.ws_lse + slot, l > 0.f ? (m_s[r] + fast_log2(l)) * kLn2 : kNegInf);
+        }
+      }
+    }
+    if (!last) {
+      wait_vmem();
+      __syncthreads();
+      if (t == 0) __hip_atomic_fetch_add(cnt, 1 << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+    if (t == 0) {
+      while ((__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 16) < sb_all - 1)
+        __builtin_amdgcn_s_sleep(2);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < MAXC; ++c) {
+      const int e = t + NT * c;
+      if (e < npairs) {
+        const int r = e / p.Dv, d = e % p.Dv;
+        if (r < nrows) {
+          const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
+          const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
+          const float l = l_s[r];
+          const float o_own = l > 0.f ? acc[c] / l : 0.f;
+          const float lse_own = l > 0.f ? (m_s[r] + fast_log2(l)) * kLn2 : kNegInf;
+          float M2 = kNegInf;
+          for (int jj = 0; jj < sb_all; ++jj) {
+            const float lj = jj == j ? lse_own : load_dev(p.ws_lse + (int64_t)jj * nrow_all + row);
+            M2 = fmaxf(M2, lj * kLog2e);
+          }
+          float num = 0.f, den = 0.f;
+          if (M2 != kNegInf) {
+            for (int jj = 0; jj < sb_all; ++jj) {
+              const int64_t slot = (int64_t)jj * nrow_all + row;
+              const float lj = jj == j ? lse_own : load_dev(p.ws_lse + slot);
+              const float oj = jj == j ? o_own : load_dev(p.ws_o + slot * p.Dv + d);
+              const float wj = fast_exp2(lj * kLog2e - M2);
+              num += wj * oj;
+              den += wj;
+            }
+          }
+          const float o = den > 0.f ? num / den : 0.f;
+          const int64_t oi = o_row_off(p, b, i) + (int64_t)h * p.os_h + d;
+          if (p.o_bf16)
+            reinterpret_cast<uint16_t*>(p.o)[oi] = (uint16_t)f32_to_bf16_bits(o);
+          else
+            reinterpret_cast<float*>(p.o)[oi] = o;
+          if (d == 0 && p.lse_out)
+            p.lse_out[lse_row(p, b, i) * p.Hq + h] =
+                M2 == kNegInf ? kNegInf : (M2 + fast_log2(den)) * kLn2;
+        }
+      }
+    }
+    if (t == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
   }
 
   // Epilogue: divide by the row sum after the V-matmul (Cleave §2.2, Fig. 2).
@@ -180,7 +331,7 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
         const float l = l_s[r];
         const float o = l > 0.f ? acc[c] / l : 0.f;
         const float lse = l > 0.f ? (m_s[r] + fast_log2(l)) * kLn2 : kNegInf;
-        if (p.split_mode) {
+        if (p.split_mode == 1) {
           const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
           const int64_t slot = (int64_t)j * p.B * p.Lq * p.Hq + row;
           p.ws_o[slot * p.Dv + d] = o;
@@ -201,11 +352,30 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
 }  // namespace
 
 hipError_t launch_generic(const KParams& p, dim3 grid, dim3 block, hipStream_t s) {
-  const size_t shmem = sizeof(float) * ((size_t)RT * p.Dqk + RT * TN + 3 * RT);
-  if (p.in_bf16)
-    hipLaunchKernelGGL(generic_attn_kernel<true>, grid, block, shmem, s, p);
-  else
-    hipLaunchKernelGGL(generic_attn_kernel<false>, grid, block, shmem, s, p);
+  const size_t base = sizeof(float) * ((size_t)RT * p.Dqk + RT * TN + 3 * RT);
+  // Stage K/V tiles when they fit in 64 KiB (head dims Dqk + Dv < 256).
+  const size_t tiles = sizeof(float) * (size_t)TN * (p.Dqk + 1 + p.Dv);
+  const bool stage = tiles <= (64u << 10);
+  const size_t shmem = base + (stage ? tiles : 0);
+  if (p.in_bf16) {
+    if (stage) {
+      if (hipError_t e = set_lds_limit_once(
+              reinterpret_cast<const void*>(&generic_attn_kernel<true, true>), (int)shmem))
+        return e;
+      hipLaunchKernelGGL((generic_attn_kernel<true, true>), grid, block, shmem, s, p);
+    } else {
+      hipLaunchKernelGGL((generic_attn_kernel<true, false>), grid, block, shmem, s, p);
+    }
+  } else {
+    if (stage) {
+      if (hipError_t e = set_lds_limit_once(
+              reinterpret_cast<const void*>(&generic_attn_kernel<false, true>), (int)shmem))
+        return e;
+      hipLaunchKernelGGL((generic_attn_kernel<false, true>), grid, block, shmem, s, p);
+    } else {
+      hipLaunchKernelGGL((generic_attn_kernel<false, false>), grid, block, shmem, s, p);
+    }
+  }
   return hipGetLastError();
 }
 

@@ -255,16 +255,23 @@ def _stream_runs(p, lens, cus):
         r = max(1, math.ceil(min(max(n, 0), cap) / 128))
         unit_rounds += [r] * p.kv_heads
     total = sum(unit_rounds)
+
+    def pieces_for(grid):
+        owner = []  # owner[round] = the workgroup whose run holds it
+        for g in range(grid):
+            owner += [g] * ((g + 1) * total // grid - g * total // grid)
+        assert len(owner) == total
+        pieces, u0 = 1, 0
+        for r in unit_rounds:
+            pieces = max(pieces, len(set(owner[u0:u0 + r])))
+            u0 += r
+        return pieces
+
+    # One run per compute unit when that cuts no unit, else two.
     grid = max(1, min(cus, total))
-    owner = []  # owner[round] = the workgroup whose run holds it
-    for g in range(grid):
-        owner += [g] * ((g + 1) * total // grid - g * total // grid)
-    assert len(owner) == total
-    pieces, u0 = 1, 0
-    for r in unit_rounds:
-        pieces = max(pieces, len(set(owner[u0:u0 + r])))
-        u0 += r
-    return total, grid, pieces
+    if pieces_for(grid) > 1:
+        grid = max(1, min(2 * cus, total))
+    return total, grid, pieces_for(grid)
 
 
 def _check_plan_invariants(p, plan, lens, cus=256):
@@ -283,7 +290,7 @@ def _check_plan_invariants(p, plan, lens, cus=256):
         ws_lse = max(ws_lse, pieces * units * 16 * 4)
     assert plan.ws_o_bytes == ws_o
     assert plan.ws_lse_bytes == ws_lse
-    assert plan.ws_cnt_bytes == p.batch * p.kv_heads * 4
+    assert plan.ws_cnt_bytes == p.batch * p.kv_heads * plan.row_tiles * 4
     # Work items (request, KV head, split), counted from the clamped host lengths;
     # an empty request owns one item per KV head.
     cap = p.kv_len_max

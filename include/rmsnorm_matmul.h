@@ -54,13 +54,19 @@ typedef struct rmsnorm_matmul_config {
   int32_t k_chunk;      /* columns per part, a multiple of 32 */
   uint32_t grid[3];     /* split-kernel grid: 64-column tiles of n, s, 32-row tiles of m */
   uint32_t block;       /* split-kernel threads per workgroup */
-  uint64_t ws_bytes;    /* fp32 workspace: (s*m*n + s*m) * 4 bytes when s > 1, else 0 */
+  int32_t kernel;       /* 0: split-K streaming kernel (decode setting); 1: tiled GEMM
+                           (prefill setting, m >= 256 and k a multiple of 32) */
+  uint64_t ws_bytes;    /* workspace bytes: kernel 0: (s*m*n + s*m) * 4 when s > 1, else 0;
+                           kernel 1: m*k*4 (X * g as bf16 pairs) rounded up to 256,
+                           plus m*4 */
   uint64_t problem_key; /* fingerprint of the planned problem */
 } rmsnorm_matmul_config;
 
 /*
  * rmsnorm_matmul_plan - choose s (Cleave §2.2 "Split-K"; §7.3 decode setting).
  *
+ * With m >= 256 tokens and k a multiple of 32 the plan is the tiled GEMM
+ * (kernel 1; s = 1, s_request is ignored); otherwise kernel 0:
  * s_request  <= 0: the planner picks the largest s whose workgroups (one
  *            per 64 x 32 output tile and part; the four waves of a workgroup
  *            split the part's columns among themselves) fit on num_cus compute
@@ -74,10 +80,16 @@ int rmsnorm_matmul_plan(const rmsnorm_matmul_problem* problem, int32_t s_request
                         int32_t num_cus, rmsnorm_matmul_config* out);
 
 /*
- * rmsnorm_matmul - Y = RMSNorm(X) W^T.  With plan->s == 1 one launch writes Y;
+ * rmsnorm_matmul - Y = RMSNorm(X) W^T.
+ * Kernel 0 (decode setting): with plan->s == 1 one launch writes Y;
  * otherwise the split launch writes each part's dot products U_j [m, n] and
  * sums of squares SSQ_j [m] to ws, and the combine launch writes
  * Y = (sum_j U_j) / sqrt(sum_j SSQ_j / k + eps).
+ * Kernel 1 (prefill setting, Cleave §7.3): a first pass writes X * g,
+ * exactly, as a pair of bf16 matrices hi + lo, and every row's scale
+ * 1 / sqrt(mean(x^2) + eps) to ws; the tiled MFMA GEMM then computes
+ * (hi + lo) W^T and multiplies each row by its scale in its epilogue (the
+ * division after the MatMul, Cleave §1).
  * ws may be NULL when plan->ws_bytes == 0.  x, g and w must be 16-byte
  * aligned (ATTN_ERR_UNSUPPORTED otherwise).  Calls sharing one workspace must
  * not overlap.

@@ -71,7 +71,8 @@ class RmsConfig(ctypes.Structure):
     """rmsnorm_matmul_config (include/rmsnorm_matmul.h)."""
     _fields_ = [
         ("s", ctypes.c_int32), ("k_chunk", ctypes.c_int32), ("grid", ctypes.c_uint32 * 3),
-        ("block", ctypes.c_uint32), ("ws_bytes", ctypes.c_uint64), ("problem_key", ctypes.c_uint64),
+        ("block", ctypes.c_uint32), ("kernel", ctypes.c_int32), ("ws_bytes", ctypes.c_uint64),
+        ("problem_key", ctypes.c_uint64),
     ]
 
 
@@ -89,7 +90,8 @@ class SwigluConfig(ctypes.Structure):
     """swiglu_config (include/swiglu.h)."""
     _fields_ = [
         ("s", ctypes.c_int32), ("k_chunk", ctypes.c_int32), ("grid", ctypes.c_uint32 * 3),
-        ("block", ctypes.c_uint32), ("ws_bytes", ctypes.c_uint64), ("problem_key", ctypes.c_uint64),
+        ("block", ctypes.c_uint32), ("kernel", ctypes.c_int32), ("ws_bytes", ctypes.c_uint64),
+        ("problem_key", ctypes.c_uint64),
     ]
 
 
@@ -383,11 +385,12 @@ def rmsnorm_matmul_plan(problem: RmsProblem, s_request: int = 0, num_cus: int = 
 
 
 def rms_workspace(plan: RmsConfig, device):
-    """The fp32 workspace a plan asks for (torch owns the memory), or None."""
+    """The workspace a plan asks for, as float32 elements (torch owns the
+    memory), or None."""
     import torch
     if plan.ws_bytes == 0:
         return None
-    return torch.empty(plan.ws_bytes // 4, dtype=torch.float32, device=device)
+    return torch.empty((plan.ws_bytes + 3) // 4, dtype=torch.float32, device=device)
 
 
 def rmsnorm_matmul(problem: RmsProblem, plan: RmsConfig, x, g, w, y, ws=None, stream=None) -> None:

@@ -27,6 +27,7 @@ SOURCES = [
     "kernels/decode_mla.hip",
     "kernels/rmsnorm_matmul.hip",
     "kernels/swiglu.hip",
+    "kernels/gemm_nt.hip",
     "kernels/scratch.hip",
 ]
 

@@ -693,6 +693,13 @@ int check_rms(const rmsnorm_matmul_problem* p) {
   return ATTN_OK;
 }
 
+// The prefill setting (Cleave §7.3: at least 256 tokens) on the tiled GEMM:
+// whole 32-column k-steps and row strides one buffer resource spans.
+bool rms_gemm_fits(const rmsnorm_matmul_problem* p) {
+  return p->m >= kGemmMinTokens && p->k % 32 == 0 && p->w_stride <= kGemmMaxStride &&
+         2 * (int64_t)p->k <= kGemmMaxStride;
+}
+
 uint64_t rms_key(const rmsnorm_matmul_problem* p) {
   const int32_t f[] = {0x524d53, p->dtype, p->m, p->k, p->n};
   uint64_t h = 1469598103934665603ull;
@@ -720,6 +727,20 @@ int rmsnorm_matmul_plan(const rmsnorm_matmul_problem* problem, int32_t s_request
   if (cus <= 0 && device_cu_count(&cus) != 0)
     return fail(ATTN_ERR_HIP, "cannot query the compute-unit count of the current device");
   const int64_t steps = ceil_div(p->k, 32);   // 32-column k-steps
+  if (rms_gemm_fits(p)) {
+    // Prefill setting: the tiled GEMM (256 x 256 output tiles), after a pass
+    // that forms X * g (exact, as bf16 pairs) and the row scales in the
+    // workspace.
+    out->s = 1;
+    out->k_chunk = p->k;
+    out->grid[0] = (uint32_t)(ceil_div(p->m, 256) * ceil_div(p->n, 256));
+    out->grid[1] = out->grid[2] = 1;
+    out->block = 512;
+    out->kernel = 1;
+    out->ws_bytes = (((uint64_t)p->m * p->k * 4 + 255) & ~uint64_t(255)) + (uint64_t)p->m * 4;
+    out->problem_key = rms_key(p);
+    return ATTN_OK;
+  }
   const int64_t tiles = ceil_div(p->n, kRmsTileN) * ceil_div(p->m, kRmsTileM);
   int64_t s = 1;
   if (s_request > 0) {
@@ -761,6 +782,35 @@ int rmsnorm_matmul(const rmsnorm_matmul_problem* problem, const rmsnorm_matmul_c
   if (!x || !g || !w || !y) return fail(ATTN_ERR_ARG, "x, g, w and y must not be NULL");
   if (!aligned16(x) || !aligned16(g) || !aligned16(w))
     return fail(ATTN_ERR_UNSUPPORTED, "x, g and w must be 16-byte aligned");
+  if (plan->kernel == 1) {
+    if (p->m < kGemmMinTokens || p->k % 32 != 0) return fail(ATTN_ERR_ARG, "corrupt plan");
+    if (!rms_gemm_fits(p)) return fail(ATTN_ERR_UNSUPPORTED, "row stride beyond %lld elements",
+                                       (long long)kGemmMaxStride);
+    const uint64_t xg_bytes = ((uint64_t)p->m * p->k * 4 + 255) & ~uint64_t(255);
+    const uint64_t need = xg_bytes + (uint64_t)p->m * 4;
+    if (!ws || ws_bytes < need)
+      return fail(ATTN_ERR_WORKSPACE, "workspace too small: need %llu bytes",
+                  (unsigned long long)need);
+    if (reinterpret_cast<uintptr_t>(ws) & 15) return fail(ATTN_ERR_ARG, "workspace must be 16-byte aligned");
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    RmsPrepParams rp;
+    std::memset(&rp, 0, sizeof(rp));
+    rp.x = x; rp.g = g;
+    rp.xg = ws;
+    rp.row_scale = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + xg_bytes);
+    rp.x_row = p->x_stride; rp.xg_row = 2 * (int64_t)p->k;
+    rp.M = p->m; rp.K = p->k; rp.eps = p->eps;
+    if (int st = hip_status(launch_rms_prep(rp, hs), "rms_prep launch")) return st;
+    GemmParams gp;
+    std::memset(&gp, 0, sizeof(gp));
+    gp.a = ws; gp.b0 = w; gp.y = y; gp.row_scale = rp.row_scale;
+    gp.a_row = 2 * (int64_t)p->k; gp.b0_row = p->w_stride; gp.y_row = p->y_stride;
+    gp.M = p->m; gp.N = p->n; gp.K = 2 * p->k;
+    gp.y_bf16 = p->y_dtype == ATTN_BF16;
+    gp.mode = 0;
+    gp.b_shift = 1;
+    return hip_status(launch_gemm_nt(gp, hs), "gemm launch");
+  }
   const uint64_t need = plan->s > 1 ? (uint64_t)plan->s * p->m * ((uint64_t)p->n + 1) * sizeof(float) : 0;
   if (need && (!ws || ws_bytes < need))
     return fail(ATTN_ERR_WORKSPACE, "workspace too small: need %llu bytes", (unsigned long long)need);
@@ -811,6 +861,11 @@ int check_swiglu(const swiglu_problem* p) {
   return ATTN_OK;
 }
 
+bool swiglu_gemm_fits(const swiglu_problem* p) {
+  return p->m >= kGemmMinTokens && p->k % 32 == 0 && p->x_stride <= kGemmMaxStride &&
+         p->wg_stride <= kGemmMaxStride && p->wu_stride <= kGemmMaxStride;
+}
+
 uint64_t swiglu_key(const swiglu_problem* p) {
   const int32_t f[] = {0x535747, p->dtype, p->m, p->k, p->n};
   uint64_t h = 1469598103934665603ull;
@@ -838,6 +893,19 @@ int swiglu_plan(const swiglu_problem* problem, int32_t s_request, int32_t num_cu
   if (cus <= 0 && device_cu_count(&cus) != 0)
     return fail(ATTN_ERR_HIP, "cannot query the compute-unit count of the current device");
   const int64_t steps = ceil_div(p->k, 32);
+  if (swiglu_gemm_fits(p)) {
+    // Prefill setting: the tiled GEMM of both MatMuls (256-token x 128-column
+    // output tiles, gate and up side by side).
+    out->s = 1;
+    out->k_chunk = p->k;
+    out->grid[0] = (uint32_t)(ceil_div(p->m, 256) * ceil_div(p->n, 128));
+    out->grid[1] = out->grid[2] = 1;
+    out->block = 512;
+    out->kernel = 1;
+    out->ws_bytes = 0;
+    out->problem_key = swiglu_key(p);
+    return ATTN_OK;
+  }
   const int64_t tiles = ceil_div(p->n, kSwTileN) * ceil_div(p->m, kSwTileM);
   int64_t s = 1;
   if (s_request > 0) {
@@ -876,6 +944,20 @@ int swiglu(const swiglu_problem* problem, const swiglu_config* config, const voi
   if (!x || !w_gate || !w_up || !y) return fail(ATTN_ERR_ARG, "x, w_gate, w_up and y must not be NULL");
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up))
     return fail(ATTN_ERR_UNSUPPORTED, "x, w_gate and w_up must be 16-byte aligned");
+  if (config->kernel == 1) {
+    if (p->m < kGemmMinTokens || p->k % 32 != 0) return fail(ATTN_ERR_ARG, "corrupt config");
+    if (!swiglu_gemm_fits(p)) return fail(ATTN_ERR_UNSUPPORTED, "row stride beyond %lld elements",
+                                          (long long)kGemmMaxStride);
+    GemmParams gp;
+    std::memset(&gp, 0, sizeof(gp));
+    gp.a = x; gp.b0 = w_gate; gp.b1 = w_up; gp.y = y;
+    gp.a_row = p->x_stride; gp.b0_row = p->wg_stride; gp.b1_row = p->wu_stride;
+    gp.y_row = p->y_stride;
+    gp.M = p->m; gp.N = p->n; gp.K = p->k;
+    gp.y_bf16 = p->y_dtype == ATTN_BF16;
+    gp.mode = 1;
+    return hip_status(launch_gemm_nt(gp, reinterpret_cast<hipStream_t>(stream)), "gemm launch");
+  }
   const uint64_t need = config->s > 1 ? 2ull * (uint64_t)config->s * p->m * p->n * sizeof(float) : 0;
   if (need && (!ws || ws_bytes < need))
     return fail(ATTN_ERR_WORKSPACE, "workspace too small: need %llu bytes", (unsigned long long)need);

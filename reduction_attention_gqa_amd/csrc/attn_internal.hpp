@@ -83,6 +83,41 @@ struct SwigluParams {
 };
 hipError_t launch_swiglu(const SwigluParams& p, hipStream_t s);
 
+// Tiled bf16 GEMM of the prefill setting: A [M, K], B0 (and B1) [N, K], row
+// strides in elements, K a multiple of 32.  mode 0: Y = row_scale[m] *
+// (A B0^T)[m, n] (RMSNorm + MatMul, A = X * g); mode 1: Y = silu(A B0^T) *
+// (A B1^T) (SwiGLU).
+struct GemmParams {
+  const void* a;
+  const void* b0;
+  const void* b1;
+  void* y;
+  const float* row_scale;
+  int64_t a_row, b0_row, b1_row, y_row;
+  int32_t M, N, K;   // K: columns of A (a multiple of 32)
+  int32_t y_bf16;
+  int32_t mode;      // 0: Y = row_scale * (A B0^T); 1: Y = silu(A B0^T) * (A B1^T)
+  int32_t b_shift;   // A step t (32 columns) meets B step t >> b_shift
+};
+hipError_t launch_gemm_nt(const GemmParams& p, hipStream_t s);
+
+// Prefill RMSNorm's first pass: X * g as bf16 pairs [M, 2K] (per 32-column
+// step: the step's hi parts, then its lo parts) and row_scale [M].
+struct RmsPrepParams {
+  const void* x;
+  const void* g;
+  void* xg;
+  float* row_scale;
+  int64_t x_row, xg_row;
+  int32_t M, K;
+  float eps;
+};
+hipError_t launch_rms_prep(const RmsPrepParams& p, hipStream_t s);
+constexpr int kGemmMinTokens = 256;   // token count from which the tiled GEMM is planned
+// Largest row stride (elements) of a GEMM operand: a workgroup's 256 rows
+// then span under 2^32 bytes, the reach of one buffer resource.
+constexpr int64_t kGemmMaxStride = int64_t(1) << 22;
+
 // Per-thread error reporting of the C ABI (attn_last_error): clear_error()
 // at the start of an entry point, report_error(code, fmt, ...) on failure
 // (returns code).

@@ -47,6 +47,7 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
                                      // the lanes' different keys fall in different banks
   float* k_s = a_s + RT;             // [TN][Dqk + 1] staged K rows (STAGE)
   float* v_s = k_s + TN * ks_row;    // [TN][Dv] staged V rows (STAGE)
+  __shared__ int64_t row_k[TN], row_v[TN];  // element offsets of the tile's K and V rows
 
   const int t = threadIdx.x;
   const int j = blockIdx.x;
@@ -122,14 +123,36 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
     const int nk = min(TN, hi - k0);  // keys of this tile that exist in the range
     if constexpr (STAGE) {
       // The previous tile's readers are past the barrier that ends its loop.
-      for (int e = t; e < nk * p.Dqk; e += NT) {
-        const int jj = e / p.Dqk, d = e - jj * p.Dqk;
-        k_s[jj * ks_row + d] =
-            ld_elem<BF16>(p.k, kv_row_off(p, b, k0 + jj, p.ks_b, p.ks_t) + khead + d);
+      // Row offsets once per key, then consecutive elements per thread (the
+      // element index advances by NT: a fixed step in columns and rows).
+      if (t < nk) {
+        row_k[t] = kv_row_off(p, b, k0 + t, p.ks_b, p.ks_t) + khead;
+        row_v[t] = kv_row_off(p, b, k0 + t, p.vs_b, p.vs_t) + vhead;
       }
-      for (int e = t; e < nk * p.Dv; e += NT) {
-        const int jj = e / p.Dv, d = e - jj * p.Dv;
-        v_s[e] = ld_elem<BF16>(p.v, kv_row_off(p, b, k0 + jj, p.vs_b, p.vs_t) + vhead + d);
+      __syncthreads();
+      {
+        const int dj = NT / p.Dqk, dd = NT - dj * p.Dqk;
+        int jj = t / p.Dqk, d = t - jj * p.Dqk;
+        for (; jj < nk; jj += dj, d += dd) {
+          if (d >= p.Dqk) {
+            d -= p.Dqk;
+            ++jj;
+            if (jj >= nk) break;
+          }
+          k_s[jj * ks_row + d] = ld_elem<BF16>(p.k, row_k[jj] + d);
+        }
+      }
+      {
+        const int dj = NT / p.Dv, dd = NT - dj * p.Dv;
+        int jj = t / p.Dv, d = t - jj * p.Dv;
+        for (; jj < nk; jj += dj, d += dd) {
+          if (d >= p.Dv) {
+            d -= p.Dv;
+            ++jj;
+            if (jj >= nk) break;
+          }
+          v_s[jj * p.Dv + d] = ld_elem<BF16>(p.v, row_v[jj] + d);
+        }
       }
       __syncthreads();
     }

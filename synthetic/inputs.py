@@ -46,12 +46,14 @@ Recipe (stated once, used by tests, smoke and bench):
   initialisation scale, so Y stays of order one), each fp32 and rounded to
   bf16 like the attention inputs.  Workloads:
   ``llama3_8b_rmsnorm_matmul_decode`` M=32 tokens, K=4096 (hidden size),
-  N=14336 (MLP projection width), eps 1e-5; ``tiny_rmsnorm_matmul`` M=5,
-  K=256, N=200.
+  N=14336 (MLP projection width), eps 1e-5;
+  ``llama3_8b_rmsnorm_matmul_prefill`` the same with M=4096 tokens (one
+  4096-token prompt); ``tiny_rmsnorm_matmul`` M=5, K=256, N=200.
 * SwiGLU (``make_swiglu_problem``): draw X [M, K] ~ N(0, 1), then W_gate and
   W_up [N, K] ~ N(0, 1) / sqrt(K), bf16-rounded.  Workloads:
   ``llama3_8b_swiglu_decode`` M=32, K=4096, N=14336 (Llama-3 8B's MLP);
-  ``tiny_swiglu`` M=5, K=256, N=200.
+  ``llama3_8b_swiglu_prefill`` the same with M=4096; ``tiny_swiglu`` M=5,
+  K=256, N=200.
 """
 from __future__ import annotations
 
@@ -266,6 +268,7 @@ class RmsProblem:
 RMS_WORKLOADS = {
     "tiny_rmsnorm_matmul": dict(m=5, k=256, n=200),
     "llama3_8b_rmsnorm_matmul_decode": dict(m=32, k=4096, n=14336),
+    "llama3_8b_rmsnorm_matmul_prefill": dict(m=4096, k=4096, n=14336),
 }
 
 
@@ -313,6 +316,7 @@ class SwigluProblem:
 SWIGLU_WORKLOADS = {
     "tiny_swiglu": dict(m=5, k=256, n=200),
     "llama3_8b_swiglu_decode": dict(m=32, k=4096, n=14336),
+    "llama3_8b_swiglu_prefill": dict(m=4096, k=4096, n=14336),
 }
 
 

@@ -517,11 +517,12 @@ def test_rms_invalid_problem(lib, edit, code):
 
 
 @pytest.mark.parametrize("m,k,n,s_req", [(32, 4096, 14336, 0), (32, 4096, 4096, 0), (1, 4096, 6144, 0),
-                                         (300, 4096, 4096, 0), (5, 256, 200, 0), (5, 264, 70, 0),
-                                         (32, 4096, 14336, 3), (32, 4096, 14336, 1000)])
+                                         (255, 4096, 4096, 0), (300, 4104, 4096, 0), (5, 256, 200, 0),
+                                         (5, 264, 70, 0), (32, 4096, 14336, 3), (32, 4096, 14336, 1000)])
 def test_rms_plan_invariants(lib, m, k, n, s_req):
     st, cfg = rms_plan(lib, rms_problem(m=m, k=k, n=n, x_stride=k, w_stride=k, y_stride=n), s_req)
     assert st == 0
+    assert cfg.kernel == 0      # fewer than 256 tokens, or k not a multiple of 32
     steps = -(-k // 32)
     assert cfg.k_chunk % 32 == 0 and cfg.s >= 1
     assert cfg.s * cfg.k_chunk >= k and (cfg.s - 1) * cfg.k_chunk < k   # no empty part
@@ -537,6 +538,19 @@ def test_rms_plan_invariants(lib, m, k, n, s_req):
         # four k-steps per wave
         tiles = cfg.grid[0] * cfg.grid[2]
         assert cfg.s <= max(1, min(256 // tiles, steps // 16))
+
+
+@pytest.mark.parametrize("m,k,n,s_req", [(256, 4096, 14336, 0), (300, 4096, 4096, 0),
+                                         (4096, 4096, 14336, 5), (300, 288, 300, 0)])
+def test_rms_plan_prefill_gemm(lib, m, k, n, s_req):
+    # From 256 tokens on with k % 32 == 0: the tiled GEMM, one 256 x 256 output
+    # tile per workgroup of 512 threads, s = 1 whatever was requested, and a
+    # workspace for X * g as bf16 pairs (256-byte aligned) and the row scales.
+    st, cfg = rms_plan(lib, rms_problem(m=m, k=k, n=n, x_stride=k, w_stride=k, y_stride=n), s_req)
+    assert st == 0 and cfg.kernel == 1
+    assert cfg.s == 1 and cfg.k_chunk == k and cfg.block == 512
+    assert tuple(cfg.grid) == ((-(-m // 256)) * (-(-n // 256)), 1, 1)
+    assert cfg.ws_bytes == (m * k * 4 + 255) // 256 * 256 + m * 4
 
 
 def test_rms_workspace_and_plan_checks(lib):
@@ -605,10 +619,11 @@ def test_swiglu_invalid_problem(lib, edit, code):
 
 
 @pytest.mark.parametrize("m,k,n,s_req", [(32, 4096, 14336, 0), (1, 4096, 14336, 0),
-                                         (5, 256, 200, 0), (33, 264, 70, 3), (32, 4096, 14336, 999)])
+                                         (5, 256, 200, 0), (33, 264, 70, 3), (32, 4096, 14336, 999),
+                                         (255, 4096, 14336, 0), (300, 4104, 200, 0)])
 def test_swiglu_plan_invariants(lib, m, k, n, s_req):
     st, cfg = sw_plan(lib, sw_problem(m=m, k=k, n=n), s_req)
-    assert st == 0
+    assert st == 0 and cfg.kernel == 0
     assert cfg.k_chunk % 32 == 0 and cfg.s * cfg.k_chunk >= k and (cfg.s - 1) * cfg.k_chunk < k
     # 64 output columns x 32 tokens per workgroup; each part's columns are
     # split over the two waves of a column group.
@@ -616,6 +631,18 @@ def test_swiglu_plan_invariants(lib, m, k, n, s_req):
     assert cfg.ws_bytes == (2 * cfg.s * m * n * 4 if cfg.s > 1 else 0)
     if s_req == 0:
         assert cfg.grid[0] * cfg.grid[1] * cfg.grid[2] <= max(256, cfg.grid[0] * cfg.grid[2])
+
+
+@pytest.mark.parametrize("m,k,n,s_req", [(256, 4096, 14336, 0), (4096, 4096, 14336, 7),
+                                         (300, 288, 200, 0)])
+def test_swiglu_plan_prefill_gemm(lib, m, k, n, s_req):
+    # From 256 tokens on with k % 32 == 0: one GEMM of both MatMuls, a
+    # 256-token x 128-column output tile (gate and up) per workgroup, no
+    # workspace.
+    st, cfg = sw_plan(lib, sw_problem(m=m, k=k, n=n), s_req)
+    assert st == 0 and cfg.kernel == 1
+    assert cfg.s == 1 and cfg.k_chunk == k and cfg.block == 512 and cfg.ws_bytes == 0
+    assert tuple(cfg.grid) == ((-(-m // 256)) * (-(-n // 128)), 1, 1)
 
 
 def test_swiglu_workspace_and_config_checks(lib):

@@ -3,11 +3,14 @@ the C ABI.
 
 The kernel computes the rewritten graph (Cleave §1, Fig. 1: the Matmul on the
 raw input with the rows' sums of squares beside it, the row scale applied
-last), split over K (Cleave §2.2 "Split-K") when the plan says so; the oracle
-is the definition (normalise, then multiply).  Tolerance derived from the
+last), split over K (Cleave §2.2 "Split-K") when the plan says so, and from
+256 tokens on (the prefill setting of Cleave §7.3) as a tiled MFMA GEMM; the
+oracle is the definition (normalise, then multiply).  Tolerance derived from the
 kernel's arithmetic (below) on the fp32 output, and the bf16 output must be
 the round-to-nearest-even of the fp32 one.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -20,7 +23,8 @@ from synthetic.inputs import make_rms_problem, rms_workload
 pytestmark = pytest.mark.gpu
 
 # Tolerance derived from the kernel's arithmetic.  Its MFMA operands are exact
-# (bf16 inputs, and x g split into an exact bf16 high and low part), so every product is exact in fp32 and the
+# (bf16 inputs, and x g split into an exact bf16 high and low part, in both
+# kernels), so every product is exact in fp32 and the
 # only roundings are fp32 accumulation over K terms and the fp32 epilogue (the row scale from the fp32 sum of squares).
 # With |Y| of order one and K <= 4096 the accumulated error is a random walk
 # of about sqrt(K) fp32 roundings of the running sum, about 1e-6 (measured
@@ -50,11 +54,15 @@ def _run(p, s_request=0, y_dtype=torch.float32, x_stride=None, w_stride=None):
     return y, plan
 
 
-def _check(name, p, **kw):
-    want = rmsnorm_matmul(p.x, p.g, p.w, p.eps)
+def _check(name, p, rows=None, **kw):
+    """Y against the oracle (on the given rows only, when ``rows`` is set:
+    the oracle's rows are independent), and bf16 Y == RNE(fp32 Y) everywhere."""
+    rows = np.arange(p.m) if rows is None else np.asarray(rows)
+    want = rmsnorm_matmul(p.x[rows], p.g, p.w, p.eps)
     y32, plan = _run(p, **kw)
-    assert_close(f"{name} (s={plan.s})", y32.cpu().numpy().astype(np.float64), want, TOL_MAX,
-                 TOL_MEAN)
+    assert_close(f"{name} (kernel {plan.kernel}, s={plan.s})",
+                 y32[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64), want,
+                 TOL_MAX, TOL_MEAN)
     y16, _ = _run(p, y_dtype=torch.bfloat16, **kw)
     assert torch.equal(y16, y32.to(torch.bfloat16)), f"{name}: bf16 Y != RNE(fp32 Y)"
     return plan
@@ -126,3 +134,51 @@ def test_workspace_reused_across_calls():
         torch.cuda.synchronize()
         assert_close(f"reuse call {call}", y.cpu().numpy().astype(np.float64), want, TOL_MAX,
                      TOL_MEAN)
+
+
+# The prefill setting (m >= 256 tokens, k a multiple of 32): the tiled GEMM.
+
+def test_prefill_gemm_ragged_tiles():
+    # m = 300 and n = 300 end inside the second 256-row / 256-column tile;
+    # k = 288 is 9 steps of 32 columns, so the 4-stage ring wraps mid-way.
+    p = make_rms_problem(m=300, k=288, n=300, seed=36)
+    plan = _check("prefill ragged", p)
+    assert plan.kernel == 1 and plan.s == 1
+
+
+def test_prefill_gemm_xcd_tile_order():
+    # 8 column tiles: the grid is ordered XCD by XCD (column tiles x, x + 8, ..).
+    p = make_rms_problem(m=512, k=256, n=8 * 256, seed=37)
+    assert _check("prefill xcd order", p).kernel == 1
+
+
+def test_prefill_gemm_strided_and_zero_rows():
+    # Padded rows (NaN past k) and a zero row (Y = 0) through the GEMM path.
+    p = make_rms_problem(m=260, k=320, n=96, seed=38)
+    p.x[7] = 0.0
+    y, plan = _run(p, x_stride=328, w_stride=352)
+    assert plan.kernel == 1 and torch.all(y[7] == 0)
+    _check("prefill strided", p, x_stride=328, w_stride=352)
+
+
+def test_prefill_gemm_equals_split_kernel():
+    # The two kernels compute the same exact products; only the fp32 summation
+    # order differs.  The first 128 rows alone are planned on the streaming
+    # kernel (m < 256).
+    p = make_rms_problem(m=256, k=512, n=200, seed=39)
+    y_gemm, plan = _run(p)
+    half = dataclasses.replace(p, x=np.ascontiguousarray(p.x[:128]))
+    y_half, plan_half = _run(half)
+    assert plan.kernel == 1 and plan_half.kernel == 0
+    np.testing.assert_allclose(y_gemm[:128].cpu().numpy(), y_half.cpu().numpy(), rtol=0, atol=2e-5)
+
+
+def test_full_size_prefill_sampled_rows():
+    # Llama-3 8B's projection at 4096 tokens (K = 4096, N = 14336), in the
+    # launch configuration the benchmark times; every column of 96 rows: the
+    # first and last row of each 256-row tile and 64 drawn rows.
+    p = rms_workload("llama3_8b_rmsnorm_matmul_prefill")
+    edges = [r for t in range(0, p.m, 256) for r in (t, t + 255)]
+    drawn = np.random.default_rng(7).choice(p.m, 64, replace=False)
+    rows = np.unique(np.concatenate([edges, drawn]))
+    assert _check("llama3_8b prefill", p, rows=rows).kernel == 1

@@ -2,10 +2,14 @@
 
 The kernel streams both weight matrices in one loop over K (horizontal
 fusion, Cleave §7.3), split over K when the plan says so (Cleave §2.2
-"Split-K", parts added before the gate).  Tolerance derived from the
+"Split-K", parts added before the gate); from 256 tokens on (the prefill
+setting of Cleave §7.3) both MatMuls run as one tiled MFMA GEMM whose
+workgroups hold a gate and an up tile of the same columns.  Tolerance derived from the
 kernel's arithmetic (below) on the fp32 output; the bf16 output must be the
 round-to-nearest-even of the fp32 one.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -46,11 +50,15 @@ def _run(p, s_request=0, y_dtype=torch.float32, strides=(None, None, None)):
     return y, cfg
 
 
-def _check(name, p, **kw):
-    want = swiglu(p.x, p.w_gate, p.w_up)
+def _check(name, p, rows=None, **kw):
+    """H against the oracle (on the given rows only, when ``rows`` is set:
+    the oracle's rows are independent), and bf16 H == RNE(fp32 H) everywhere."""
+    rows = np.arange(p.m) if rows is None else np.asarray(rows)
+    want = swiglu(p.x[rows], p.w_gate, p.w_up)
     y32, cfg = _run(p, **kw)
-    assert_close(f"{name} (s={cfg.s})", y32.cpu().numpy().astype(np.float64), want, TOL_MAX,
-                 TOL_MEAN)
+    assert_close(f"{name} (kernel {cfg.kernel}, s={cfg.s})",
+                 y32[torch.from_numpy(rows).to(DEV)].cpu().numpy().astype(np.float64), want,
+                 TOL_MAX, TOL_MEAN)
     y16, _ = _run(p, y_dtype=torch.bfloat16, **kw)
     assert torch.equal(y16, y32.to(torch.bfloat16)), f"{name}: bf16 H != RNE(fp32 H)"
     return cfg
@@ -84,3 +92,44 @@ def test_one_part_equals_many_parts():
     y1, _ = _run(p, s_request=1)
     y8, _ = _run(p, s_request=8)
     np.testing.assert_allclose(y1.cpu().numpy(), y8.cpu().numpy(), rtol=0, atol=5e-5)
+
+
+# The prefill setting (m >= 256 tokens, k a multiple of 32): the tiled GEMM.
+
+def test_prefill_gemm_ragged_tiles():
+    # m = 300 ends inside the second 256-row tile, n = 200 inside the second
+    # 128-column tile; k = 288 is 9 steps, so the 4-stage ring wraps mid-way.
+    cfg = _check("prefill ragged", make_swiglu_problem(m=300, k=288, n=200, seed=44))
+    assert cfg.kernel == 1 and cfg.s == 1
+
+
+def test_prefill_gemm_xcd_tile_order():
+    # 16 column tiles of 128: the grid is ordered XCD by XCD.
+    assert _check("prefill xcd order", make_swiglu_problem(m=512, k=256, n=16 * 128,
+                                                           seed=45)).kernel == 1
+
+
+def test_prefill_gemm_strided_rows():
+    _check("prefill strided", make_swiglu_problem(m=270, k=320, n=150, seed=46),
+           strides=(328, 352, 336))
+
+
+def test_prefill_gemm_equals_split_kernel():
+    # Same exact products as the streaming kernel; fp32 summation order differs.
+    p = make_swiglu_problem(m=256, k=512, n=200, seed=47)
+    y_gemm, cfg = _run(p)
+    half = dataclasses.replace(p, x=np.ascontiguousarray(p.x[:128]))
+    y_half, cfg_half = _run(half)
+    assert cfg.kernel == 1 and cfg_half.kernel == 0
+    np.testing.assert_allclose(y_gemm[:128].cpu().numpy(), y_half.cpu().numpy(), rtol=0, atol=5e-5)
+
+
+def test_full_size_prefill_sampled_rows():
+    # Llama-3 8B's MLP at 4096 tokens (K = 4096, N = 14336), in the launch
+    # configuration the benchmark times; every column of the first and last
+    # row of each 256-row tile and of 64 drawn rows.
+    p = swiglu_workload("llama3_8b_swiglu_prefill")
+    edges = [r for t in range(0, p.m, 256) for r in (t, t + 255)]
+    drawn = np.random.default_rng(8).choice(p.m, 64, replace=False)
+    rows = np.unique(np.concatenate([edges, drawn]))
+    assert _check("llama3_8b prefill", p, rows=rows).kernel == 1

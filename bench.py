@@ -30,6 +30,10 @@ Default run (N = 1), one JSON line:
   * swiglu: SwiGLU on Llama-3 8B's MLP at 32 tokens (K=4096, N=14336, bf16)
     in algorithmic HBM GB/s (both weight matrices and X read once, H written
     once); one step = one call.
+  * rmsnorm_matmul_prefill, swiglu_prefill: the same two subgraphs in the
+    prefill setting, 4096 tokens, in algorithmic TFLOP/s (2 m k n per
+    MatMul); one step = one call (the X * g pre-pass and the tiled GEMM, or
+    the one GEMM launch of both SwiGLU MatMuls).
 Each leg first runs its step untimed for about 0.25 s (GPU clocks and
 address translation settle under the new load), then the warm-up steps, then
 exactly the timed steps.  Every record carries ms_per_step (host wall clock
@@ -209,7 +213,9 @@ KERNEL_OF = {
     "rms": ("rmsnorm_matmul_split_kernel",
             "reduction_attention_gqa_amd/csrc/kernels/rmsnorm_matmul.hip"),
     "swiglu": ("swiglu_split_kernel", "reduction_attention_gqa_amd/csrc/kernels/swiglu.hip"),
+    "gemm": ("gemm_nt_kernel", "reduction_attention_gqa_amd/csrc/kernels/gemm_nt.hip"),
 }
+GEMM_SRC = KERNEL_OF["gemm"][1]
 
 
 def copy_calibration(dev):
@@ -463,6 +469,16 @@ def time_rms(prob, steps, warmup, dev, s_request=0):
     return dict(plan=plan, wall_s=wall, call_ms=call_ms, bytes=(rd, wr))
 
 
+def gemm_roofline(flops, r, traffic_key, kernel):
+    """MFMA roofline of a prefill-setting call: algorithmic flops / mean call time."""
+    call = stats(r["call_ms"])
+    achieved = flops / (call["mean_ms"] * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+            "traffic": traffic_for(GEMM_SRC, traffic_key), "kernel": kernel,
+            "algorithmic_flops_per_launch": flops, "launch_ms": call}
+
+
 def rms_record(prob, r, steps):
     rd, wr = r["bytes"]
     total = rd + wr
@@ -470,11 +486,19 @@ def rms_record(prob, r, steps):
     call = stats(r["call_ms"])
     achieved = total / (call["mean_ms"] * 1e-3) / 1e9
     plan = r["plan"]
+    config = {"workload": prob.name, "m": prob.m, "k": prob.k, "n": prob.n, "eps": prob.eps,
+              "split_s": plan.s, "k_chunk": plan.k_chunk, "kernel": plan.kernel}
+    if plan.kernel == 1:
+        # Prefill setting: compute-bound; 2 m k n flops of the MatMul (the
+        # hi/lo halves of X * g are one exact operand, not extra work).
+        flops = 2.0 * prob.m * prob.k * prob.n
+        return {"value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "ms_per_step": round(ms_step, 5), "config": config,
+                "roofline": gemm_roofline(flops, r, f"rms:{prob.name}",
+                                          "X*g pre-pass + tiled MFMA GEMM (timed together)")}
     return {
         "value": round(total / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
-        "ms_per_step": round(ms_step, 5),
-        "config": {"workload": prob.name, "m": prob.m, "k": prob.k, "n": prob.n, "eps": prob.eps,
-                   "split_s": plan.s, "k_chunk": plan.k_chunk},
+        "ms_per_step": round(ms_step, 5), "config": config,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/"
@@ -484,24 +508,38 @@ def rms_record(prob, r, steps):
                      "algorithmic_bytes_per_launch": total, "launch_ms": call}}
 
 
-def oracle_rms_baseline(prob):
-    """The fp64 oracle on the whole RMSNorm + MatMul workload (one call)."""
+def oracle_rows(prob, rows_cap):
+    """The first rows of a workload (all of them if there are at most rows_cap):
+    the oracle's rows are independent, so a row sample is a bounded sample of
+    the same work."""
+    return min(prob.m, rows_cap)
+
+
+def oracle_rms_baseline(prob, rows_cap=256):
+    """The fp64 oracle on the RMSNorm + MatMul workload (at most rows_cap token
+    rows of it), in the unit of the GPU leg."""
     from threadpoolctl import threadpool_limits
     from oracle import rmsnorm_matmul
     cores = cpu_cores()
-    rd, wr = rms_bytes(prob)
+    rows = oracle_rows(prob, rows_cap)
+    x = prob.x[:rows]
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         reps = 0
         while True:
-            rmsnorm_matmul(prob.x, prob.g, prob.w, prob.eps)
+            rmsnorm_matmul(x, prob.g, prob.w, prob.eps)
             reps += 1
             el = time.perf_counter() - t0
             if el > 5.0 or reps >= 20:
                 break
-    return {"value": round((rd + wr) * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"the whole workload, {reps} call(s) in {el:.1f} s, numpy fp64"}
+    sample = (f"the whole workload, {reps} call(s) in {el:.1f} s, numpy fp64" if rows == prob.m
+              else f"{rows} of {prob.m} token rows, {reps} call(s) in {el:.1f} s, numpy fp64")
+    if prob.m >= 256:
+        value, unit = round(2.0 * rows * prob.k * prob.n * reps / el / 1e12, 6), "TFLOP/s"
+    else:
+        rd, wr = rms_bytes(prob)
+        value, unit = round((rd + wr) * reps / el / 1e9, 4), "GB/s"
+    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle", "sample": sample}
 
 
 def swiglu_bytes(prob):
@@ -560,11 +598,17 @@ def swiglu_record(prob, r, steps):
     call = stats(r["call_ms"])
     achieved = total / (call["mean_ms"] * 1e-3) / 1e9
     cfg = r["plan"]
+    config = {"workload": prob.name, "m": prob.m, "k": prob.k, "n": prob.n,
+              "split_s": cfg.s, "k_chunk": cfg.k_chunk, "kernel": cfg.kernel}
+    if cfg.kernel == 1:
+        flops = 4.0 * prob.m * prob.k * prob.n   # both MatMuls
+        return {"value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+                "ms_per_step": round(ms_step, 5), "config": config,
+                "roofline": gemm_roofline(flops, r, f"swiglu:{prob.name}",
+                                          "tiled MFMA GEMM of both MatMuls, one launch")}
     return {
         "value": round(total / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
-        "ms_per_step": round(ms_step, 5),
-        "config": {"workload": prob.name, "m": prob.m, "k": prob.k, "n": prob.n,
-                   "split_s": cfg.s, "k_chunk": cfg.k_chunk},
+        "ms_per_step": round(ms_step, 5), "config": config,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/swiglu.hip",
@@ -574,24 +618,31 @@ def swiglu_record(prob, r, steps):
                      "algorithmic_bytes_per_launch": total, "launch_ms": call}}
 
 
-def oracle_swiglu_baseline(prob):
-    """The fp64 oracle on the whole SwiGLU workload."""
+def oracle_swiglu_baseline(prob, rows_cap=256):
+    """The fp64 oracle on the SwiGLU workload (at most rows_cap token rows of
+    it), in the unit of the GPU leg."""
     from threadpoolctl import threadpool_limits
     from oracle import swiglu
     cores = cpu_cores()
-    rd, wr = swiglu_bytes(prob)
+    rows = oracle_rows(prob, rows_cap)
+    x = prob.x[:rows]
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         reps = 0
         while True:
-            swiglu(prob.x, prob.w_gate, prob.w_up)
+            swiglu(x, prob.w_gate, prob.w_up)
             reps += 1
             el = time.perf_counter() - t0
             if el > 5.0 or reps >= 20:
                 break
-    return {"value": round((rd + wr) * reps / el / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"the whole workload, {reps} call(s) in {el:.1f} s, numpy fp64"}
+    sample = (f"the whole workload, {reps} call(s) in {el:.1f} s, numpy fp64" if rows == prob.m
+              else f"{rows} of {prob.m} token rows, {reps} call(s) in {el:.1f} s, numpy fp64")
+    if prob.m >= 256:
+        value, unit = round(4.0 * rows * prob.k * prob.n * reps / el / 1e12, 6), "TFLOP/s"
+    else:
+        rd, wr = swiglu_bytes(prob)
+        value, unit = round((rd + wr) * reps / el / 1e9, 4), "GB/s"
+    return {"value": value, "unit": unit, "cores": cores, "kind": "oracle", "sample": sample}
 
 
 def stats(ms):
@@ -902,9 +953,11 @@ def main():
         if name in MM_NAMES:
             family, key = "prefill", f"mm:{name}"
         elif name in SW_NAMES:
-            family, key = "swiglu", f"swiglu:{name}"
+            family = "gemm" if SW_NAMES[name]["m"] >= 256 else "swiglu"
+            key = f"swiglu:{name}"
         elif name in RMS_WORKLOADS_NAMES:
-            family, key = "rms", f"rms:{name}"
+            family = "gemm" if RMS_WORKLOADS_NAMES[name]["m"] >= 256 else "rms"
+            key = f"rms:{name}"
         elif prob.lq > 1:
             family, key = "prefill", f"prefill:{name}"
         else:
@@ -1026,6 +1079,21 @@ def main():
         sprob = swiglu_workload(sname)
         out["swiglu"] = swiglu_record(sprob, time_swiglu(sprob, a.steps, a.warmup, dev), a.steps)
         cpu_jobs.append((out["swiglu"], "cpu_baseline", oracle_swiglu_baseline, (sprob,)))
+        if not a.no_prefill:
+            for rname in ("llama3_8b_rmsnorm_matmul_prefill",):
+                log(f"timing {rname}")
+                rprob = rms_workload(rname)
+                out["rmsnorm_matmul_prefill"] = rms_record(
+                    rprob, time_rms(rprob, a.steps, a.warmup, dev), a.steps)
+                cpu_jobs.append((out["rmsnorm_matmul_prefill"], "cpu_baseline",
+                                 oracle_rms_baseline, (rprob,)))
+            for sname in ("llama3_8b_swiglu_prefill",):
+                log(f"timing {sname}")
+                sprob = swiglu_workload(sname)
+                out["swiglu_prefill"] = swiglu_record(
+                    sprob, time_swiglu(sprob, a.steps, a.warmup, dev), a.steps)
+                cpu_jobs.append((out["swiglu_prefill"], "cpu_baseline", oracle_swiglu_baseline,
+                                 (sprob,)))
         if not a.no_cpu:
             cpu_jobs.append((out, "cpu_baseline_one_thread", oracle_decode_single_thread,
                              (prob2,)))

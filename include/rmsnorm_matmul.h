@@ -55,7 +55,7 @@ typedef struct rmsnorm_matmul_config {
   uint32_t grid[3];     /* split-kernel grid: 64-column tiles of n, s, 32-row tiles of m */
   uint32_t block;       /* split-kernel threads per workgroup */
   int32_t kernel;       /* 0: split-K streaming kernel (decode setting); 1: tiled GEMM
-                           (prefill setting, m >= 256 and k a multiple of 32) */
+                           (prefill setting, m >= 256 and k a multiple of 64) */
   uint64_t ws_bytes;    /* workspace bytes: kernel 0: (s*m*n + s*m) * 4 when s > 1, else 0;
                            kernel 1: m*k*4 (X * g as bf16 pairs) rounded up to 256,
                            plus m*4 */
@@ -65,7 +65,7 @@ typedef struct rmsnorm_matmul_config {
 /*
  * rmsnorm_matmul_plan - choose s (Cleave §2.2 "Split-K"; §7.3 decode setting).
  *
- * With m >= 256 tokens and k a multiple of 32 the plan is the tiled GEMM
+ * With m >= 256 tokens and k a multiple of 64 the plan is the tiled GEMM
  * (kernel 1; s = 1, s_request is ignored); otherwise kernel 0:
  * s_request  <= 0: the planner picks the largest s whose workgroups (one
  *            per 64 x 32 output tile and part; the four waves of a workgroup

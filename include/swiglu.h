@@ -56,14 +56,14 @@ typedef struct swiglu_config {
   uint32_t block;       /* split-kernel threads per workgroup */
   int32_t kernel;       /* 0: split-K streaming kernel (decode setting); 1: tiled GEMM
                            of both MatMuls at once (prefill setting, m >= 256 and k a
-                           multiple of 32; no workspace) */
+                           multiple of 64; no workspace) */
   uint64_t ws_bytes;    /* fp32 workspace: 2 * s * m * n * 4 bytes when s > 1, else 0 */
   uint64_t problem_key; /* fingerprint of the planned problem */
 } swiglu_config;
 
 /*
  * swiglu_plan - choose s (Cleave §2.2 "Split-K"; §7.3 decode and prefill).
- * With m >= 256 tokens and k a multiple of 32 the plan is the tiled GEMM
+ * With m >= 256 tokens and k a multiple of 64 the plan is the tiled GEMM
  * (kernel 1; s = 1, s_request is ignored); otherwise kernel 0:
  * s_request  <= 0: the largest s whose workgroups (one per 64 x 32 output
  *            tile and part; two waves split each part's columns) fit on

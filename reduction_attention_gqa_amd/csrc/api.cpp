@@ -694,9 +694,9 @@ int check_rms(const rmsnorm_matmul_problem* p) {
 }
 
 // The prefill setting (Cleave §7.3: at least 256 tokens) on the tiled GEMM:
-// whole 32-column k-steps and row strides one buffer resource spans.
+// whole 64-column k-steps and row strides one buffer resource spans.
 bool rms_gemm_fits(const rmsnorm_matmul_problem* p) {
-  return p->m >= kGemmMinTokens && p->k % 32 == 0 && p->w_stride <= kGemmMaxStride &&
+  return p->m >= kGemmMinTokens && p->k % kGemmKStep == 0 && p->w_stride <= kGemmMaxStride &&
          2 * (int64_t)p->k <= kGemmMaxStride;
 }
 
@@ -783,7 +783,7 @@ int rmsnorm_matmul(const rmsnorm_matmul_problem* problem, const rmsnorm_matmul_c
   if (!aligned16(x) || !aligned16(g) || !aligned16(w))
     return fail(ATTN_ERR_UNSUPPORTED, "x, g and w must be 16-byte aligned");
   if (plan->kernel == 1) {
-    if (p->m < kGemmMinTokens || p->k % 32 != 0) return fail(ATTN_ERR_ARG, "corrupt plan");
+    if (p->m < kGemmMinTokens || p->k % kGemmKStep != 0) return fail(ATTN_ERR_ARG, "corrupt plan");
     if (!rms_gemm_fits(p)) return fail(ATTN_ERR_UNSUPPORTED, "row stride beyond %lld elements",
                                        (long long)kGemmMaxStride);
     const uint64_t xg_bytes = ((uint64_t)p->m * p->k * 4 + 255) & ~uint64_t(255);
@@ -862,7 +862,7 @@ int check_swiglu(const swiglu_problem* p) {
 }
 
 bool swiglu_gemm_fits(const swiglu_problem* p) {
-  return p->m >= kGemmMinTokens && p->k % 32 == 0 && p->x_stride <= kGemmMaxStride &&
+  return p->m >= kGemmMinTokens && p->k % kGemmKStep == 0 && p->x_stride <= kGemmMaxStride &&
          p->wg_stride <= kGemmMaxStride && p->wu_stride <= kGemmMaxStride;
 }
 
@@ -945,7 +945,7 @@ int swiglu(const swiglu_problem* problem, const swiglu_config* config, const voi
   if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up))
     return fail(ATTN_ERR_UNSUPPORTED, "x, w_gate and w_up must be 16-byte aligned");
   if (config->kernel == 1) {
-    if (p->m < kGemmMinTokens || p->k % 32 != 0) return fail(ATTN_ERR_ARG, "corrupt config");
+    if (p->m < kGemmMinTokens || p->k % kGemmKStep != 0) return fail(ATTN_ERR_ARG, "corrupt config");
     if (!swiglu_gemm_fits(p)) return fail(ATTN_ERR_UNSUPPORTED, "row stride beyond %lld elements",
                                           (long long)kGemmMaxStride);
     GemmParams gp;

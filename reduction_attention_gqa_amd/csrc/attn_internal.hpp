@@ -94,14 +94,14 @@ struct GemmParams {
   void* y;
   const float* row_scale;
   int64_t a_row, b0_row, b1_row, y_row;
-  int32_t M, N, K;   // K: columns of A (a multiple of 32)
+  int32_t M, N, K;   // K: columns of A (a multiple of kGemmKStep)
   int32_t y_bf16;
   int32_t mode;      // 0: Y = row_scale * (A B0^T); 1: Y = silu(A B0^T) * (A B1^T)
-  int32_t b_shift;   // A step t (32 columns) meets B step t >> b_shift
+  int32_t b_shift;   // A step t (kGemmKStep columns) meets B step t >> b_shift
 };
 hipError_t launch_gemm_nt(const GemmParams& p, hipStream_t s);
 
-// Prefill RMSNorm's first pass: X * g as bf16 pairs [M, 2K] (per 32-column
+// Prefill RMSNorm's first pass: X * g as bf16 pairs [M, 2K] (per 64-column
 // step: the step's hi parts, then its lo parts) and row_scale [M].
 struct RmsPrepParams {
   const void* x;
@@ -114,6 +114,7 @@ struct RmsPrepParams {
 };
 hipError_t launch_rms_prep(const RmsPrepParams& p, hipStream_t s);
 constexpr int kGemmMinTokens = 256;   // token count from which the tiled GEMM is planned
+constexpr int kGemmKStep = 64;        // the tiled GEMM's K step: k must be a multiple
 // Largest row stride (elements) of a GEMM operand: a workgroup's 256 rows
 // then span under 2^32 bytes, the reach of one buffer resource.
 constexpr int64_t kGemmMaxStride = int64_t(1) << 22;

@@ -8,8 +8,8 @@
 // * RMSNorm + MatMul (mode 0).  A first pass over X (rms_prep_kernel) forms
 //   x * g exactly, as a bf16 pair hi + lo, and each token's row scale
 //   1 / sqrt(mean(x^2) + eps) from the same read of X; the GEMM then
-//   multiplies the un-normalised X * g by W (A steps alternate hi and lo
-//   columns against the same W step: b_shift = 1) and applies the row scale
+//   multiplies the un-normalised X * g by W (A steps alternate the hi and
+//   the lo parts of 64 columns against the same W step: b_shift = 1) and applies the row scale
 //   to the finished dot products -- the division moved after the MatMul
 //   (Cleave §1, Fig. 1).  The normalised input is never formed, and the
 //   gain costs no precision (at twice the MFMA work of a rounded x * g).
@@ -22,14 +22,17 @@
 // (w & 1, w >> 1) computes rows 128 wm .. + 127 and B rows 64 wn .. + 63 (for
 // SwiGLU: gate rows 32 wn .. + 31 and the up rows beside them) as 4 x 2 MFMA
 // tiles of 32 x 32 (mfma_f32_32x32x16_bf16), 128 accumulators per lane.
-// K goes in steps of 32 columns: the A and B tiles of a step (16 KiB each)
-// are copied HBM -> LDS by buffer loads that write LDS directly, into a
-// 4-stage ring (three steps in flight).  A tile row is 64 bytes; 16-byte chunk
-// c of row r sits at chunk c ^ ((r >> 2) & 3), which keeps the fragment reads
-// (32 rows, two chunks per instruction) free of bank conflicts.
+// K goes in steps of 64 columns, so that each tile row of a step is one
+// whole 128-byte line (the L2 serves whole lines at twice the rate of half
+// lines): the A and B tiles of a step (32 KiB each) are copied HBM -> LDS by
+// buffer loads that write LDS directly, into a 2-stage ring (the next step's
+// copy in flight during a step).  16-byte chunk c of tile row r sits at chunk
+// c ^ (r % 8), which keeps the fragment reads (32 rows, two chunks per
+// instruction) free of bank conflicts.
 // Workgroups are ordered so that the eight XCDs each own every eighth column
-// tile and run through all row tiles of it: a weight tile is fetched from HBM
-// once per XCD and reused from that XCD's L2 by every row tile.
+// tile (a weight tile is fetched by one XCD only) and walk their tiles in
+// bands of GROUP_M row tiles, so that the workgroups an XCD runs at once
+// share their A and B tiles through its L2.
 #include "../attn_internal.hpp"
 #include "common.hpp"
 
@@ -40,22 +43,30 @@ constexpr int NW = 8;
 constexpr int NT = NW * 64;
 constexpr int BM = 256;              // A rows per workgroup
 constexpr int BB = 256;              // B rows per workgroup
-constexpr int BK = 32;               // columns of K per step
-constexpr int ROWB = BK * 2;         // bytes per tile row
-constexpr int TILE = BM * ROWB;      // 16 KiB per operand and stage
+constexpr int BK = 64;               // columns of K per step
+constexpr int ROWB = BK * 2;         // bytes per tile row: one 128-byte line
+constexpr int CH = ROWB / 16;        // 16-byte chunks per tile row
+constexpr int SUBS = BK / 16;        // MFMA k-steps (16 columns) per step
+constexpr int TILE = BM * ROWB;      // 32 KiB per operand and stage
 constexpr int STAGE = 2 * TILE;      // A tile then B tile
-constexpr int NS = 4;                // ring stages
+constexpr int NS = 2;                // ring stages
 constexpr int LOOK = NS - 1;         // steps in flight
+constexpr int GROUP_M = 8;           // row tiles per band of the tile order
 constexpr int LDS_BYTES = NS * STAGE;  // 128 KiB
-constexpr int DMA_PER_OP = TILE / 1024;        // 16 one-KiB copies per operand and stage
-constexpr int DMA_PER_WAVE = DMA_PER_OP / NW;  // 2 per operand and wave
-static_assert(DMA_PER_WAVE == 2, "vmcnt values below assume 4 copies per wave and stage");
+constexpr int DMA_PER_OP = TILE / 1024;        // one-KiB copies per operand and stage
+constexpr int DMA_PER_WAVE = DMA_PER_OP / NW;  // per operand and wave
+constexpr int LOADS_PER_STEP = 2 * DMA_PER_WAVE;  // copy instructions per wave and step
+static_assert(LOOK <= 2, "wait_steps_but covers at most one newer step");
 
 typedef __attribute__((address_space(3))) const i32x4_t lds_i32x4_t;
 __device__ __forceinline__ i32x4_t ds_read16_at(uint32_t lds_addr) {
   return *reinterpret_cast<lds_i32x4_t*>((uintptr_t)lds_addr);
 }
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// Chunk c of tile row r sits at chunk c ^ (r % CH): the fragment reads (32
+// rows, two chunks per instruction) then fall on distinct banks.
+__device__ __forceinline__ int swz(int r) { return r & (CH - 1); }
+// s_waitcnt immediate: lgkmcnt(0), vmcnt and expcnt at their maxima (no wait).
+constexpr int kWaitLgkm0 = 0xC07F;
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // Y[m, n] (bf16 rounded to nearest even, or fp32) when inside the matrix.
@@ -75,8 +86,14 @@ void gemm_nt_kernel(GemmParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = w & 1, wn = w >> 1;
 
-  // Tile order: XCD x = id % 8 takes column tiles x, x + 8, ... and all row
-  // tiles of each (row tiles fastest), when the column tiles split evenly.
+  // Tile order.  When the column tiles split evenly over the eight XCDs, XCD
+  // x = id % 8 takes column tiles x, x + 8, ... (so each weight tile is
+  // fetched by one XCD only); its k-th workgroup takes local tile k of a grid
+  // of row tiles x owned column tiles walked in bands of GROUP_M row tiles,
+  // down a column of the band first.  The workgroups an XCD runs at once
+  // (32) then cover GROUP_M rows x 32 / GROUP_M columns, and a k-step of
+  // them needs GROUP_M + 32 / GROUP_M operand tiles from outside the XCD
+  // rather than one per workgroup.
   constexpr int NOUT = MODE == 0 ? BB : BB / 2;  // output columns per workgroup
   const int tiles_m = (p.M + BM - 1) / BM;
   const int tiles_n = (p.N + NOUT - 1) / NOUT;
@@ -84,8 +101,13 @@ void gemm_nt_kernel(GemmParams p) {
   int mt, nt;
   if ((tiles_n & 7) == 0) {
     const int x = id & 7, k = id >> 3;
-    nt = x + 8 * (k / tiles_m);
-    mt = k % tiles_m;
+    const int cols = tiles_n >> 3;                 // column tiles of this XCD
+    const int band = k / (GROUP_M * cols);
+    const int r0 = band * GROUP_M;
+    const int rows = min(GROUP_M, tiles_m - r0);   // rows of this band
+    const int kb = k - band * GROUP_M * cols;
+    mt = r0 + kb % rows;
+    nt = x + 8 * (kb / rows);
   } else {
     nt = id / tiles_m;
     mt = id % tiles_m;
@@ -104,16 +126,17 @@ void gemm_nt_kernel(GemmParams p) {
   const __amdgpu_buffer_rsrc_t b1rs = MODE == 0 ? b0rs :
       make_rsrc(reinterpret_cast<const uint16_t*>(p.b1) + (int64_t)n0 * p.b1_row, (uint32_t)brows * b1st);
 
-  // Copies of a stage: wave w fills A slots 64 (2w + u) + lane and B slots
-  // likewise (u = 0, 1): slot s holds row s / 4, physical chunk s % 4, i.e.
-  // logical chunk (s % 4) ^ swz(row).  For SwiGLU, B rows 0..127 are gate rows
-  // and 128..255 up rows (waves 0-3 copy the former, 4-7 the latter).
+  // Copies of a stage: wave w fills A slots 64 (DMA_PER_WAVE w + u) + lane and
+  // B slots likewise: slot s holds row s / CH, physical chunk s % CH, i.e.
+  // logical chunk (s % CH) ^ swz(row); eight lanes copy one whole row (a
+  // 128-byte line).  For SwiGLU, B rows 0..127 are gate rows and 128..255 up
+  // rows (waves 0-3 copy the former, 4-7 the latter).
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(smem);
   uint32_t a_off[DMA_PER_WAVE], b_off[DMA_PER_WAVE];
 #pragma unroll
   for (int u = 0; u < DMA_PER_WAVE; ++u) {
     const int slot = 64 * (DMA_PER_WAVE * w + u) + lane;
-    const int row = slot >> 2, c = (slot & 3) ^ swz(row);
+    const int row = slot / CH, c = (slot % CH) ^ swz(row);
     a_off[u] = (uint32_t)row * ast + 16u * (uint32_t)c;
     const int brow = MODE == 0 ? row : (row & 127);
     b_off[u] = (uint32_t)brow * (MODE == 0 || row < 128 ? b0st : b1st) + 16u * (uint32_t)c;
@@ -136,24 +159,23 @@ void gemm_nt_kernel(GemmParams p) {
     }
   };
   // All copies of a step have landed once at most `later` newer steps' copies
-  // (4 instructions each) are outstanding.
+  // are outstanding.
   auto wait_steps_but = [&](int later) {
-    switch (later) {
-      case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-      case 1: asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); break;
-      default: asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); break;
-    }
+    if (later <= 0)
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LOADS_PER_STEP) : "memory");
   };
 
   // Per-lane fragment addresses (loop invariant): A block i row 128 wm + 32 i
   // + lane % 32, B block j row (mode 0) 64 wn + 32 j + lane % 32, (mode 1)
-  // 32 wn + lane % 32 + 128 j; chunk 2 * sub + lane / 32, swizzled.
+  // 32 wn + lane % 32 + 128 j; chunk 2 sub + lane / 32, swizzled.
   const int lr = lane & 31, lh = lane >> 5;
-  uint32_t a_rd[4][2], b_rd[2][2];
+  uint32_t a_rd[4][SUBS], b_rd[2][SUBS];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < SUBS; ++sub) {
       const int row = 128 * wm + 32 * i + lr;
       a_rd[i][sub] = smem_lds + (uint32_t)(row * ROWB + 16 * ((2 * sub + lh) ^ swz(row)));
       asm volatile("" : "+v"(a_rd[i][sub]));
@@ -161,7 +183,7 @@ void gemm_nt_kernel(GemmParams p) {
 #pragma unroll
   for (int j = 0; j < 2; ++j)
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
+    for (int sub = 0; sub < SUBS; ++sub) {
       const int row = MODE == 0 ? 64 * wn + 32 * j + lr : 32 * wn + lr + 128 * j;
       b_rd[j][sub] = smem_lds + (uint32_t)(TILE + row * ROWB + 16 * ((2 * sub + lh) ^ swz(row)));
       asm volatile("" : "+v"(b_rd[j][sub]));
@@ -182,26 +204,49 @@ void gemm_nt_kernel(GemmParams p) {
   wait_steps_but(min(LOOK - 1, nsteps - 1));
   asm volatile("s_barrier" ::: "memory");
 
-  // Step t reads stage t % NS; the copy of step t + LOOK refills the stage step
-  // t - 1 read, which every wave left at the barrier ending step t - 1.
+  // Fragments of one 16-column k-step: A blocks i and B blocks j.
+  struct Frags { i32x4_t a[4], b[2]; };
+  auto read_frags = [&](Frags& f, uint32_t so, int sub) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = ds_read16_at(a_rd[i][sub] + so);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) f.b[j] = ds_read16_at(b_rd[j][sub] + so);
+  };
+  auto mfmas = [&](const Frags& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = mfma32x32x16(as_bf16x8(f.a[i]), as_bf16x8(f.b[j]), acc[i][j]);
+  };
+
+  // Step t reads stage t % NS, SUBS k-steps of 16 columns; the fragments of
+  // k-step s + 1 are read while the MFMAs of k-step s run.  The first
+  // k-step's fragments are read right after the barrier that makes the
+  // stage visible, and that barrier comes before the last k-step's MFMAs of
+  // the step before, which then cover the reads.  The copy of step t + LOOK,
+  // issued at the start of step t, refills the stage of step t - 1, which
+  // every wave finished reading before the barrier that ended step t - 1.
+  Frags f[2];
+  read_frags(f[0], 0u, 0);
   for (int t = 0; t < nsteps; ++t) {
-    if (t + LOOK < nsteps) dma(t + LOOK, (t + LOOK) & (NS - 1));
-    const uint32_t so = (uint32_t)((t & (NS - 1)) * STAGE);
+    if (t + LOOK < nsteps) dma(t + LOOK, (t + LOOK) % NS);
+    const uint32_t so = (uint32_t)((t % NS) * STAGE);
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      i32x4_t a[4], b[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = ds_read16_at(a_rd[i][sub] + so);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = ds_read16_at(b_rd[j][sub] + so);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = mfma32x32x16(as_bf16x8(a[i]), as_bf16x8(b[j]), acc[i][j]);
+    for (int sub = 0; sub + 1 < SUBS; ++sub) {
+      read_frags(f[(sub + 1) & 1], so, sub + 1);
+      mfmas(f[sub & 1]);
     }
     wait_steps_but(max(0, min(LOOK - 1, nsteps - 2 - t)));
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // The compiler's own wait and barrier: it then knows that the fragments
+    // read before the barrier have arrived.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");   // no LDS access moves across the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < nsteps) read_frags(f[0], (uint32_t)(((t + 1) % NS) * STAGE), 0);
+    mfmas(f[(SUBS - 1) & 1]);
   }
 
   // Epilogue.  Lane holds, for A block i and B block j, rows
@@ -223,7 +268,7 @@ void gemm_nt_kernel(GemmParams p) {
 
 // The exact product x * g (two bf16 significands fit in fp32's) as a bf16
 // pair hi + lo, hi = RNE(x g) and lo = x g - hi (at most 8 significant bits,
-// so exact in bf16), stored per 32-column step as [hi of the step | lo of the
+// so exact in bf16), stored per 64-column step as [hi of the step | lo of the
 // step], and the row scale 1 / sqrt(mean(x^2) + eps); one read of the row,
 // one workgroup per token row.
 __global__ __launch_bounds__(256) void rms_prep_kernel(RmsPrepParams p) {

@@ -517,12 +517,13 @@ def test_rms_invalid_problem(lib, edit, code):
 
 
 @pytest.mark.parametrize("m,k,n,s_req", [(32, 4096, 14336, 0), (32, 4096, 4096, 0), (1, 4096, 6144, 0),
-                                         (255, 4096, 4096, 0), (300, 4104, 4096, 0), (5, 256, 200, 0),
+                                         (255, 4096, 4096, 0), (300, 4104, 4096, 0), (300, 288, 300, 0),
+                                         (5, 256, 200, 0),
                                          (5, 264, 70, 0), (32, 4096, 14336, 3), (32, 4096, 14336, 1000)])
 def test_rms_plan_invariants(lib, m, k, n, s_req):
     st, cfg = rms_plan(lib, rms_problem(m=m, k=k, n=n, x_stride=k, w_stride=k, y_stride=n), s_req)
     assert st == 0
-    assert cfg.kernel == 0      # fewer than 256 tokens, or k not a multiple of 32
+    assert cfg.kernel == 0      # fewer than 256 tokens, or k not a multiple of 64
     steps = -(-k // 32)
     assert cfg.k_chunk % 32 == 0 and cfg.s >= 1
     assert cfg.s * cfg.k_chunk >= k and (cfg.s - 1) * cfg.k_chunk < k   # no empty part
@@ -541,9 +542,9 @@ def test_rms_plan_invariants(lib, m, k, n, s_req):
 
 
 @pytest.mark.parametrize("m,k,n,s_req", [(256, 4096, 14336, 0), (300, 4096, 4096, 0),
-                                         (4096, 4096, 14336, 5), (300, 288, 300, 0)])
+                                         (4096, 4096, 14336, 5), (300, 320, 300, 0)])
 def test_rms_plan_prefill_gemm(lib, m, k, n, s_req):
-    # From 256 tokens on with k % 32 == 0: the tiled GEMM, one 256 x 256 output
+    # From 256 tokens on with k % 64 == 0: the tiled GEMM, one 256 x 256 output
     # tile per workgroup of 512 threads, s = 1 whatever was requested, and a
     # workspace for X * g as bf16 pairs (256-byte aligned) and the row scales.
     st, cfg = rms_plan(lib, rms_problem(m=m, k=k, n=n, x_stride=k, w_stride=k, y_stride=n), s_req)
@@ -620,7 +621,7 @@ def test_swiglu_invalid_problem(lib, edit, code):
 
 @pytest.mark.parametrize("m,k,n,s_req", [(32, 4096, 14336, 0), (1, 4096, 14336, 0),
                                          (5, 256, 200, 0), (33, 264, 70, 3), (32, 4096, 14336, 999),
-                                         (255, 4096, 14336, 0), (300, 4104, 200, 0)])
+                                         (255, 4096, 14336, 0), (300, 4104, 200, 0), (300, 288, 200, 0)])
 def test_swiglu_plan_invariants(lib, m, k, n, s_req):
     st, cfg = sw_plan(lib, sw_problem(m=m, k=k, n=n), s_req)
     assert st == 0 and cfg.kernel == 0
@@ -634,9 +635,9 @@ def test_swiglu_plan_invariants(lib, m, k, n, s_req):
 
 
 @pytest.mark.parametrize("m,k,n,s_req", [(256, 4096, 14336, 0), (4096, 4096, 14336, 7),
-                                         (300, 288, 200, 0)])
+                                         (300, 320, 200, 0)])
 def test_swiglu_plan_prefill_gemm(lib, m, k, n, s_req):
-    # From 256 tokens on with k % 32 == 0: one GEMM of both MatMuls, a
+    # From 256 tokens on with k % 64 == 0: one GEMM of both MatMuls, a
     # 256-token x 128-column output tile (gate and up) per workgroup, no
     # workspace.
     st, cfg = sw_plan(lib, sw_problem(m=m, k=k, n=n), s_req)

@@ -136,12 +136,12 @@ def test_workspace_reused_across_calls():
                      TOL_MEAN)
 
 
-# The prefill setting (m >= 256 tokens, k a multiple of 32): the tiled GEMM.
+# The prefill setting (m >= 256 tokens, k a multiple of 64): the tiled GEMM.
 
 def test_prefill_gemm_ragged_tiles():
     # m = 300 and n = 300 end inside the second 256-row / 256-column tile;
-    # k = 288 is 9 steps of 32 columns, so the 4-stage ring wraps mid-way.
-    p = make_rms_problem(m=300, k=288, n=300, seed=36)
+    # k = 320 is 5 steps of 64 columns, so the 2-stage ring ends mid-cycle.
+    p = make_rms_problem(m=300, k=320, n=300, seed=36)
     plan = _check("prefill ragged", p)
     assert plan.kernel == 1 and plan.s == 1
 

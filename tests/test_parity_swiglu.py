@@ -94,12 +94,13 @@ def test_one_part_equals_many_parts():
     np.testing.assert_allclose(y1.cpu().numpy(), y8.cpu().numpy(), rtol=0, atol=5e-5)
 
 
-# The prefill setting (m >= 256 tokens, k a multiple of 32): the tiled GEMM.
+# The prefill setting (m >= 256 tokens, k a multiple of 64): the tiled GEMM.
 
 def test_prefill_gemm_ragged_tiles():
     # m = 300 ends inside the second 256-row tile, n = 200 inside the second
-    # 128-column tile; k = 288 is 9 steps, so the 4-stage ring wraps mid-way.
-    cfg = _check("prefill ragged", make_swiglu_problem(m=300, k=288, n=200, seed=44))
+    # 128-column tile; k = 320 is 5 steps of 64 columns, so the 2-stage ring
+    # ends mid-cycle.
+    cfg = _check("prefill ragged", make_swiglu_problem(m=300, k=320, n=200, seed=44))
     assert cfg.kernel == 1 and cfg.s == 1
 
 

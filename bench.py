@@ -206,7 +206,7 @@ COPY_CALIBRATION_BYTES = 256 << 20  # bytes read (and written) by the calibratio
 # Kernel-name substring and source file of the dominant kernel of each workload
 # family, for the PMC summary.
 KERNEL_OF = {
-    "gqa_d128": ("decode_gqa_d128_kernel", "reduction_attention_gqa_amd/csrc/kernels/decode_gqa_d128.hip"),
+    "gqa_d128": ("decode_gqa_d128_", "reduction_attention_gqa_amd/csrc/kernels/decode_gqa_d128.hip"),
     "mla": ("decode_mla_kernel", "reduction_attention_gqa_amd/csrc/kernels/decode_mla.hip"),
     "generic": ("generic", "reduction_attention_gqa_amd/csrc/kernels/generic.hip"),
     "prefill": ("prefill_d128_kernel", "reduction_attention_gqa_amd/csrc/kernels/prefill_d128.hip"),
@@ -515,7 +515,7 @@ def oracle_rows(prob, rows_cap):
     return min(prob.m, rows_cap)
 
 
-def oracle_rms_baseline(prob, rows_cap=256):
+def oracle_rms_baseline(prob, rows_cap=512):
     """The fp64 oracle on the RMSNorm + MatMul workload (at most rows_cap token
     rows of it), in the unit of the GPU leg."""
     from threadpoolctl import threadpool_limits
@@ -530,7 +530,7 @@ def oracle_rms_baseline(prob, rows_cap=256):
             rmsnorm_matmul(x, prob.g, prob.w, prob.eps)
             reps += 1
             el = time.perf_counter() - t0
-            if el > 5.0 or reps >= 20:
+            if el > 10.0 or reps >= 200:
                 break
     sample = (f"the whole workload, {reps} call(s) in {el:.1f} s, numpy fp64" if rows == prob.m
               else f"{rows} of {prob.m} token rows, {reps} call(s) in {el:.1f} s, numpy fp64")
@@ -618,7 +618,7 @@ def swiglu_record(prob, r, steps):
                      "algorithmic_bytes_per_launch": total, "launch_ms": call}}
 
 
-def oracle_swiglu_baseline(prob, rows_cap=256):
+def oracle_swiglu_baseline(prob, rows_cap=512):
     """The fp64 oracle on the SwiGLU workload (at most rows_cap token rows of
     it), in the unit of the GPU leg."""
     from threadpoolctl import threadpool_limits
@@ -633,7 +633,7 @@ def oracle_swiglu_baseline(prob, rows_cap=256):
             swiglu(x, prob.w_gate, prob.w_up)
             reps += 1
             el = time.perf_counter() - t0
-            if el > 5.0 or reps >= 20:
+            if el > 10.0 or reps >= 200:
                 break
     sample = (f"the whole workload, {reps} call(s) in {el:.1f} s, numpy fp64" if rows == prob.m
               else f"{rows} of {prob.m} token rows, {reps} call(s) in {el:.1f} s, numpy fp64")
@@ -674,7 +674,7 @@ def oracle_decode_baseline(prob, budget_s=10.0):
                       prob.scale)
             reps += 1
             el = time.perf_counter() - t0
-            if el >= budget_s or reps >= 1000:
+            if el >= budget_s or reps >= 200000:
                 break
     gbs = (qb + kvb + ob) * reps / el / 1e9
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
@@ -925,7 +925,7 @@ def oracle_decode_single_thread(prob, budget_s=5.0):
                       prob.scale)
             reps += 1
             el = time.perf_counter() - t0
-            if el >= budget_s or reps >= 1000:
+            if el >= budget_s or reps >= 200000:
                 break
     return {"value": round((qb + kvb + ob) * reps / el / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",

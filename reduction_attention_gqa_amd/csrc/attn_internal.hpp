@@ -151,7 +151,8 @@ constexpr int kGqaStreamWgsPerCu = 2;  // attn_decode when units are cut: runs p
 constexpr int kGqaMinChunk = 256;      // planner floor on keys per split
 constexpr int kGqaBlock = 256;
 constexpr int kGqaMaxRows = 16;
-constexpr int kPrefillStages = 4;     // prefill K/V ring depth (tiles)
+constexpr int kPrefillStages = 6;     // prefill K/V ring depth (tiles)
+constexpr int kPrefillBarrierTiles = 2;  // prefill key tiles per workgroup barrier
 constexpr int kMlaTileN = 32;          // keys per MLA tile
 constexpr int kMlaBlock = 512;         // 8 waves of 16 query rows
 constexpr int kMlaRows = 128;          // query rows per MLA workgroup

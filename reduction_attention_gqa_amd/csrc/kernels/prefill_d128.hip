@@ -24,8 +24,10 @@
 // accumulator always share one reference, so O = U / l is unchanged.
 //
 // K/V tiles go HBM -> LDS by buffer loads that write LDS directly, into an
-// NS-stage K ring and an NS-stage V ring (tile i + NS - 1 is in flight while
-// tile i is consumed; four stages measure as fast as eight).  A tile row is 256 bytes, and the 16-byte chunk c of
+// NS-stage K ring and an NS-stage V ring.  The workgroup meets at a barrier
+// once per group of BAR = 2 tiles (NS = 6: the group's tiles, the next
+// group's, and two in flight), which publishes the next group's tiles and
+// frees the group's stages; a barrier per tile cost 1-4 %.  A tile row is 256 bytes, and the 16-byte chunk c of
 // row r sits at chunk c ^ swz(r), which keeps both the K operand reads (16
 // keys, one chunk each) and the transposed V reads (4 keys, 4 chunks each)
 // free of bank conflicts.  Every LDS read is a per-lane base register plus an
@@ -90,17 +92,20 @@ __device__ __forceinline__ float row_sum(float v) { const f32x2_t h = row_halves
 // Byte offset of (row, 16-byte chunk c) inside a K or V tile.
 __device__ __forceinline__ int tile_off(int row, int c) { return row * RB + 16 * (c ^ swz(row)); }
 
-// KB key blocks of 32 per tile; NS ring stages, tile i + NS - 1 loaded while
-// tile i is consumed.  PAGED: K/V rows come from a page pool (power-of-two
+// KB key blocks of 32 per tile; NS ring stages; BAR tiles per barrier group,
+// whose successors' copies are issued when the group starts.  PAGED: K/V rows come from a page pool (power-of-two
 // page size); the request's page ids are staged in LDS after the rings and
 // each lane copies its row with a 64-bit-addressed global load into LDS.
-template <int KB, int NS, bool PAGED, bool SOFTMAX>
+template <int KB, int NS, int BAR, bool PAGED, bool SOFTMAX>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_d128_kernel(KParams p, int nrt) {
   constexpr int TK = 32 * KB;         // keys per tile
   constexpr int KT = TK * RB;         // bytes of one K (or V) tile
   constexpr int VRING = NS * KT;      // the V ring follows the K ring
-  constexpr int LOOK = NS - 1;        // DMA lookahead in tiles
+  constexpr int LOOK = NS - BAR;      // DMA lookahead in tiles
+  // A group reads tiles g .. g + BAR and the next one up to g + 2 BAR; stage
+  // arithmetic is compile-time only when groups tile the ring.
+  static_assert(BAR >= 1 && NS % BAR == 0 && NS >= 2 * BAR + 1, "ring stages per barrier group");
   constexpr int NDMA = KB;            // 1 KiB DMA blocks per wave per K (or V) tile
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int lane = threadIdx.x & 63;
@@ -333,8 +338,9 @@ void prefill_d128_kernel(KParams p, int nrt) {
 #pragma unroll
     for (int t = 0; t < LOOK; ++t)
       if (t < ntiles) dma_tile(t * TK, t);
-    // Tiles 0 and 1 landed (step 0 reads K of tile 1); later ones may stay in flight.
-    wait_tiles_but(max(0, min(LOOK - 1, ntiles - 1) - 1));
+    // Tiles 0 .. BAR landed (steps 0 .. BAR - 1 read K of tiles 1 .. BAR);
+    // later ones may stay in flight.
+    wait_tiles_but(max(0, min(LOOK - 1, ntiles - 1) - BAR));
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -361,7 +367,14 @@ void prefill_d128_kernel(KParams p, int nrt) {
   auto step = [&](const int it, const int st, const bool next, const bool mask_next)
       __attribute__((always_inline)) {
     const int k0 = it * TK;
-    if (it + LOOK < ntiles) dma_tile(k0 + LOOK * TK, (st + LOOK) % NS);
+    // A group of BAR steps starts: copy its successors' tiles it + LOOK ..
+    // it + LOOK + BAR - 1 into the stages of tiles it - BAR .. it - 1, which
+    // every wave finished with before the barrier that ended the last group.
+    if (st % BAR == 0) {
+#pragma unroll
+      for (int j = 0; j < BAR; ++j)
+        if (it + LOOK + j < ntiles) dma_tile(k0 + (LOOK + j) * TK, (st + LOOK + j) % NS);
+    }
 
     // Lazy rescale (rare).
     if (SOFTMAX && __builtin_amdgcn_ballot_w64(mt_cur > m_ref + kRescaleThreshold) != 0) {
@@ -442,31 +455,32 @@ void prefill_d128_kernel(KParams p, int nrt) {
       for (int kb = 0; kb < KB; ++kb) s_cur[kb] = s_nxt[kb];
     }
 
-    // Tile it + 2 must have landed before the next step reads its K; later
-    // tiles may stay in flight.  The barrier also frees stage st.
-    wait_tiles_but(max(0, min(it + LOOK, ntiles - 1) - (it + 2)));
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // The last step of a group: tiles up to it + BAR + 1 must have landed
+    // before the next group reads them (K of it + 2 .. it + BAR + 1, V of
+    // it + 1 .. it + BAR); later tiles may stay in flight.  The barrier also
+    // frees the group's stages.  The last step waits for every copy.
+    if (!next) {
+      wait_tiles_but(0);
+    } else if (st % BAR == BAR - 1) {
+      wait_tiles_but(max(0, min(it + LOOK, ntiles - 1) - (it + BAR + 1)));
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
   };
   // A step whose ring stage is only known at run time.
+  // A step whose ring stage is only known at run time (the masked steps near
+  // the diagonal and the last one): one copy of the step, stage offsets added
+  // at run time.
   auto step_any = [&](const int it, const bool next, const bool mask_next)
       __attribute__((always_inline)) {
-    static_assert(NS == 4 || NS == 8, "ring stages");
-    switch (it % NS) {
-      case 0: step(it, 0, next, mask_next); break;
-      case 1: step(it, 1, next, mask_next); break;
-      case 2: step(it, 2, next, mask_next); break;
-      case 3: step(it, 3, next, mask_next); break;
-      case 4: step(it, 4 % NS, next, mask_next); break;
-      case 5: step(it, 5 % NS, next, mask_next); break;
-      case 6: step(it, 6 % NS, next, mask_next); break;
-      default: step(it, 7 % NS, next, mask_next); break;
-    }
+    step(it, it % NS, next, mask_next);
   };
 
   // Tiles below n_clean need no mask; step it masks tile it + 1 when that
-  // tile needs it.  Every wave runs ntiles steps (one barrier each).  The
-  // unmasked run starts at tile 0 and goes in groups of NS (stages 0..NS-1),
-  // then a remainder of at most NS - 1 with known stages.
+  // tile needs it.  Every wave runs ntiles steps (a barrier every BAR).  The
+  // unmasked run starts at tile 0 and goes in groups of NS (stages 0..NS-1,
+  // known at compile time), then a remainder of at most NS - 1 steps and the
+  // masked ones with the stage known at run time (one copy of the step: six
+  // unrolled masked copies spilled registers and ran 4 % slower).
   const int n1 = max(0, min(n_clean, ntiles - 1));
   const int clean_end = max(0, n1 - 1);
   int it = 0;
@@ -474,9 +488,7 @@ void prefill_d128_kernel(KParams p, int nrt) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) step(it + u, u, true, false);
   }
-#pragma unroll
-  for (int u = 0; u < NS - 1; ++u)
-    if (it < clean_end) step(it++, u, true, false);
+  for (; it < clean_end; ++it) step_any(it, true, false);
   for (; it < ntiles - 1; ++it) step_any(it, true, true);
   if (ntiles > 0) step_any(ntiles - 1, false, false);
 
@@ -510,13 +522,14 @@ void prefill_d128_kernel(KParams p, int nrt) {
   }
 }
 
-template <int KB, int NS, bool PAGED, bool SOFTMAX>
+template <int KB, int NS, int BAR, bool PAGED, bool SOFTMAX>
 hipError_t launch_variant(const KParams& p, int nrt, int64_t nwg, hipStream_t s) {
   constexpr int lds = lds_bytes(KB, NS) + (PAGED ? 4 * kPrefillPageIds : 0);
+  static_assert(lds <= 160 * 1024, "LDS per workgroup");
   hipError_t e = set_lds_limit_once(
-      reinterpret_cast<const void*>(&prefill_d128_kernel<KB, NS, PAGED, SOFTMAX>), lds);
+      reinterpret_cast<const void*>(&prefill_d128_kernel<KB, NS, BAR, PAGED, SOFTMAX>), lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((prefill_d128_kernel<KB, NS, PAGED, SOFTMAX>), dim3((unsigned)nwg), dim3(NT), lds, s,
+  hipLaunchKernelGGL((prefill_d128_kernel<KB, NS, BAR, PAGED, SOFTMAX>), dim3((unsigned)nwg), dim3(NT), lds, s,
                      p, nrt);
   return hipGetLastError();
 }
@@ -528,11 +541,11 @@ hipError_t launch_prefill_d128(const KParams& p, hipStream_t s) {
   const int64_t nwg = (int64_t)p.B * p.Hkv * nrt;
   if (nwg == 0) return hipSuccess;
   if (p.no_softmax) {
-    if (p.page_table) return launch_variant<1, kPrefillStages, true, false>(p, nrt, nwg, s);
-    return launch_variant<1, kPrefillStages, false, false>(p, nrt, nwg, s);
+    if (p.page_table) return launch_variant<1, kPrefillStages, kPrefillBarrierTiles, true, false>(p, nrt, nwg, s);
+    return launch_variant<1, kPrefillStages, kPrefillBarrierTiles, false, false>(p, nrt, nwg, s);
   }
-  if (p.page_table) return launch_variant<1, kPrefillStages, true, true>(p, nrt, nwg, s);
-  return launch_variant<1, kPrefillStages, false, true>(p, nrt, nwg, s);
+  if (p.page_table) return launch_variant<1, kPrefillStages, kPrefillBarrierTiles, true, true>(p, nrt, nwg, s);
+  return launch_variant<1, kPrefillStages, kPrefillBarrierTiles, false, true>(p, nrt, nwg, s);
 }
 
 }  // namespace attn

@@ -10,8 +10,10 @@
 // row strides in elements, bf16 inputs.  A workgroup is four waves and owns
 // 64 output columns and up to 32 tokens on the MFMA columns; waves 2c and
 // 2c + 1 share columns 32c .. 32c + 31 (two 16-row blocks of each weight
-// matrix, the same rows in both) and take the two halves of the part's K
-// range (a second, on-chip level of the same split-K):
+// matrix, the same rows in both) and take alternate super-steps of the part's
+// K range (a second, on-chip level of the same split-K; alternating, rather
+// than a half each, keeps the pair's reads of a weight row 512 contiguous
+// bytes at a time: 6 % faster):
 //   G^T[16 x 16] += W_gate[16 x 32] X^T[32 x 16],  U^T likewise   16x16x32 MFMA
 // The weights move a super-step (four 32-column k-steps, 256 contiguous
 // bytes per row) ahead of use, double-buffered; X (a few KB, through the
@@ -90,12 +92,12 @@ __global__ __launch_bounds__(NW * 64) void swiglu_split_kernel(SwigluParams p) {
   const int n_wg = blockIdx.x * COLS;
   const int j = blockIdx.y;
   const int m0 = blockIdx.z * 32;
-  // This wave's half of the part's columns (a multiple of 32 wide).
+  // This wave's super-steps of the part's columns: every other one, from
+  // the (w & 1)-th on.
   const int lo_j = j * p.k_chunk;
   const int hi_j = min(lo_j + p.k_chunk, p.K);
-  const int kch = (p.k_chunk + 63) / 64 * 32;
-  const int lo = min(lo_j + (w & 1) * kch, hi_j);
-  const int hi = min(lo + kch, hi_j);
+  const int lo = lo_j + (w & 1) * 32 * SS;
+  const int hi = hi_j;
 
   // Buffer ranges end at the last valid weight row / token, so rows past N or
   // M read as zero.  Offsets stay 32-bit: a workgroup's 64 rows, 32 tokens.
@@ -143,8 +145,9 @@ __global__ __launch_bounds__(NW * 64) void swiglu_split_kernel(SwigluParams p) {
     for (int mg = 0; mg < 2; ++mg) acc_g[b][mg] = acc_u[b][mg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Double-buffered super-steps; scheduling barriers keep the issue order
-  // (each super-step's X first, then the next super-step's weights).
-  constexpr int STEP = 32 * SS;
+  // (each super-step's X first, then the next super-step's weights).  STEP:
+  // from one of this wave's super-steps to its next.
+  constexpr int STEP = 32 * SS * 2;
   WBuf wb[2];
   XBuf xb;
   load_w(wb[0], lo);

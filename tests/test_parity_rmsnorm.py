@@ -42,10 +42,10 @@ def _dev(a, stride=None):
     return wide[:, : a.shape[1]]
 
 
-def _run(p, s_request=0, y_dtype=torch.float32, x_stride=None, w_stride=None):
+def _run(p, s_request=0, y_dtype=torch.float32, x_stride=None, w_stride=None, y_stride=None):
     x, w = _dev(p.x, x_stride), _dev(p.w, w_stride)
     g = _dev(p.g[None, :])[0]
-    y = torch.full((p.m, p.n), float("nan"), dtype=y_dtype, device=DEV)
+    y = torch.full((p.m, y_stride or p.n), float("nan"), dtype=y_dtype, device=DEV)[:, : p.n]
     prob = ra.make_rms_problem(x, g, w, y, eps=p.eps)
     plan = ra.rmsnorm_matmul_plan(prob, s_request)
     ws = ra.rms_workspace(plan, DEV)
@@ -182,3 +182,23 @@ def test_full_size_prefill_sampled_rows():
     drawn = np.random.default_rng(7).choice(p.m, 64, replace=False)
     rows = np.unique(np.concatenate([edges, drawn]))
     assert _check("llama3_8b prefill", p, rows=rows).kernel == 1
+
+
+@pytest.mark.parametrize("m,k,n", [(256, 64, 1), (256, 64, 257), (257, 128, 3), (512, 192, 515)])
+def test_prefill_gemm_edges(m, k, n):
+    # One 64-column step (k = 64) and odd ones, exactly one row tile and one
+    # row past it, a single output column and ragged column counts (odd n:
+    # the bf16 output is written element by element at the tile's edge).
+    p = make_rms_problem(m=m, k=k, n=n, seed=40 + m + n)
+    assert _check(f"edges {m}x{k}x{n}", p).kernel == 1
+
+
+def test_prefill_gemm_padded_output_rows():
+    # Y with a row stride past n (NaN in the padding): the padding stays NaN.
+    p = make_rms_problem(m=300, k=128, n=200, seed=49)
+    y, plan = _run(p, y_stride=232)
+    assert plan.kernel == 1
+    full = y.as_strided((p.m, 232), (232, 1))
+    assert torch.isnan(full[:, 200:]).all() and not torch.isnan(y).any()
+    want = rmsnorm_matmul(p.x, p.g, p.w, p.eps)
+    assert_close("padded y", y.cpu().numpy().astype(np.float64), want, TOL_MAX, TOL_MEAN)

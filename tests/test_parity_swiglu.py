@@ -40,9 +40,9 @@ def _dev(a, stride=None):
     return wide[:, : a.shape[1]]
 
 
-def _run(p, s_request=0, y_dtype=torch.float32, strides=(None, None, None)):
+def _run(p, s_request=0, y_dtype=torch.float32, strides=(None, None, None), y_stride=None):
     x, wg, wu = _dev(p.x, strides[0]), _dev(p.w_gate, strides[1]), _dev(p.w_up, strides[2])
-    y = torch.full((p.m, p.n), float("nan"), dtype=y_dtype, device=DEV)
+    y = torch.full((p.m, y_stride or p.n), float("nan"), dtype=y_dtype, device=DEV)[:, : p.n]
     prob = ra.make_swiglu_problem(x, wg, wu, y)
     cfg = ra.swiglu_plan(prob, s_request)
     ra.swiglu(prob, cfg, x, wg, wu, y, ra.swiglu_workspace(cfg, DEV))
@@ -134,3 +134,21 @@ def test_full_size_prefill_sampled_rows():
     drawn = np.random.default_rng(8).choice(p.m, 64, replace=False)
     rows = np.unique(np.concatenate([edges, drawn]))
     assert _check("llama3_8b prefill", p, rows=rows).kernel == 1
+
+
+@pytest.mark.parametrize("m,k,n", [(256, 64, 1), (256, 64, 129), (257, 128, 3), (512, 192, 259)])
+def test_prefill_gemm_edges(m, k, n):
+    # One 64-column step and odd step counts, exactly one row tile and one row
+    # past it, a single output column and ragged column counts.
+    cfg = _check(f"edges {m}x{k}x{n}", make_swiglu_problem(m=m, k=k, n=n, seed=50 + m + n))
+    assert cfg.kernel == 1
+
+
+def test_prefill_gemm_padded_output_rows():
+    p = make_swiglu_problem(m=300, k=128, n=200, seed=59)
+    y, cfg = _run(p, y_stride=232)
+    assert cfg.kernel == 1
+    full = y.as_strided((p.m, 232), (232, 1))
+    assert torch.isnan(full[:, 200:]).all() and not torch.isnan(y).any()
+    assert_close("padded y", y.cpu().numpy().astype(np.float64), swiglu(p.x, p.w_gate, p.w_up),
+                 TOL_MAX, TOL_MEAN)

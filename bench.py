@@ -37,9 +37,12 @@ Default run (N = 1), one JSON line:
 Each leg first runs its step untimed for about 0.25 s (GPU clocks and
 address translation settle under the new load), then the warm-up steps, then
 exactly the timed steps.  Every record carries ms_per_step (host wall clock
-over exactly the timed steps), the GPU-side span per step of a second pass with events on the
-launch stream, and the roofline of its dominant kernel (per-launch HIP-event
-times).  After every GPU leg has run, the fp64 oracle is timed on the host
+over exactly the timed steps), gpu_span_ms_per_step (the GPU time between two
+HIP events recorded on the launch stream around the same timed steps, per
+step) and the roofline of its dominant kernel: achieved = algorithmic work
+per launch / that span per launch (for the two-launch decode ablation, the
+split kernel's own event pairs); a second pass with an event pair around
+every launch gives the per-launch statistics in launch_ms.  After every GPU leg has run, the fp64 oracle is timed on the host
 cores over a bounded sample of each workload (cpu_baseline), and once on a
 single BLAS thread for the Llama decode and the tiny fp32 decode; "host"
 records the CPU model, core count and numpy / BLAS versions.
@@ -311,6 +314,23 @@ def settle(step, seconds=SETTLE_S):
     torch.cuda.synchronize()
 
 
+def timed_region(step, steps, stream):
+    """Exactly `steps` steps, synchronised on both sides: the host wall clock
+    over them, and the GPU time between two events recorded on the launch
+    stream around them (no event between the steps), per step."""
+    import torch
+    reg = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    reg[0].record(stream)
+    for i in range(steps):
+        step(i)
+    reg[1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, reg[0].elapsed_time(reg[1]) / steps
+
+
 def time_decode(prob, steps, warmup, s_request, dev, fused, layout="token", page_size=0):
     """Time `steps` decode steps.  fused: one attn_decode call per step (for the
     GQA family a single launch that merges its own splits); otherwise the split
@@ -351,28 +371,19 @@ def time_decode(prob, steps, warmup, s_request, dev, fused, layout="token", page
     settle(step)
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
-    # Timed region: exactly `steps` steps, synchronised on both sides.
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    # Per-kernel durations, with events on the launch stream, and the GPU-side
-    # span of the whole pass (launch gaps included).
+    wall, region_ms = timed_region(step, steps, stream)
+    # Per-kernel durations of a second pass, an event pair around each launch
+    # (the pair adds its own overhead; the two-launch form needs it to tell
+    # the kernels apart).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    span = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    span[0].record(stream)
     for i in range(steps):
         step(i, evs[i])
-    span[1].record(stream)
     torch.cuda.synchronize()
     split_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     comb_ms = None if fused else sorted(e[1].elapsed_time(e[2]) for e in evs)
     del copies, probs
     return dict(plan=plan, wall_s=wall, split_ms=split_ms, combine_ms=comb_ms,
-                bytes=(qb, kvb, ob), fused=fused,
-                gpu_span_ms_per_step=span[0].elapsed_time(span[1]) / steps)
+                bytes=(qb, kvb, ob), fused=fused, region_ms=region_ms)
 
 
 def time_prefill(prob, steps, warmup, dev, mm=False):
@@ -401,23 +412,14 @@ def time_prefill(prob, steps, warmup, dev, mm=False):
     settle(step)
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall, region_ms = timed_region(step, steps, stream)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    span = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    span[0].record(stream)
     for i in range(steps):
         step(i, evs[i])
-    span[1].record(stream)
     torch.cuda.synchronize()
     k_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     del copies, probs
-    return dict(wall_s=wall, kernel_ms=k_ms, bytes=(qb, kvb, ob),
-                gpu_span_ms_per_step=span[0].elapsed_time(span[1]) / steps)
+    return dict(wall_s=wall, kernel_ms=k_ms, bytes=(qb, kvb, ob), region_ms=region_ms)
 
 
 def rms_bytes(prob):
@@ -454,29 +456,26 @@ def time_rms(prob, steps, warmup, dev, s_request=0):
     settle(step)
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall, region_ms = timed_region(step, steps, stream)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     call_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     del ws_copies
-    return dict(plan=plan, wall_s=wall, call_ms=call_ms, bytes=(rd, wr))
+    return dict(plan=plan, wall_s=wall, call_ms=call_ms, bytes=(rd, wr), region_ms=region_ms)
 
 
 def gemm_roofline(flops, r, traffic_key, kernel):
-    """MFMA roofline of a prefill-setting call: algorithmic flops / mean call time."""
-    call = stats(r["call_ms"])
-    achieved = flops / (call["mean_ms"] * 1e-3) / 1e12
+    """MFMA roofline of a prefill-setting call: algorithmic flops / the call's
+    average GPU time over the timed region."""
+    achieved = flops / (r["region_ms"] * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
             "traffic": traffic_for(GEMM_SRC, traffic_key), "kernel": kernel,
-            "algorithmic_flops_per_launch": flops, "launch_ms": call}
+            "algorithmic_flops_per_launch": flops,
+            "region_ms_per_launch": round(r["region_ms"], 6),
+            "launch_ms": stats(r["call_ms"])}
 
 
 def rms_record(prob, r, steps):
@@ -484,7 +483,7 @@ def rms_record(prob, r, steps):
     total = rd + wr
     ms_step = r["wall_s"] * 1e3 / steps
     call = stats(r["call_ms"])
-    achieved = total / (call["mean_ms"] * 1e-3) / 1e9
+    achieved = total / (r["region_ms"] * 1e-3) / 1e9
     plan = r["plan"]
     config = {"workload": prob.name, "m": prob.m, "k": prob.k, "n": prob.n, "eps": prob.eps,
               "split_s": plan.s, "k_chunk": plan.k_chunk, "kernel": plan.kernel}
@@ -493,19 +492,22 @@ def rms_record(prob, r, steps):
         # hi/lo halves of X * g are one exact operand, not extra work).
         flops = 2.0 * prob.m * prob.k * prob.n
         return {"value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                "ms_per_step": round(ms_step, 5), "config": config,
+                "ms_per_step": round(ms_step, 5), "gpu_span_ms_per_step": round(r["region_ms"], 5),
+        "config": config,
                 "roofline": gemm_roofline(flops, r, f"rms:{prob.name}",
                                           "X*g pre-pass + tiled MFMA GEMM (timed together)")}
     return {
         "value": round(total / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
-        "ms_per_step": round(ms_step, 5), "config": config,
+        "ms_per_step": round(ms_step, 5), "gpu_span_ms_per_step": round(r["region_ms"], 5),
+        "config": config,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/"
                                             "rmsnorm_matmul.hip", f"rms:{prob.name}"),
                      "kernel": ("RMSNorm+MatMul kernel, one launch" if plan.s == 1 else
                                 "RMSNorm+MatMul split kernel + combine kernel (timed together)"),
-                     "algorithmic_bytes_per_launch": total, "launch_ms": call}}
+                     "algorithmic_bytes_per_launch": total,
+                     "region_ms_per_launch": round(r["region_ms"], 6), "launch_ms": call}}
 
 
 def oracle_rows(prob, rows_cap):
@@ -576,19 +578,14 @@ def time_swiglu(prob, steps, warmup, dev, s_request=0):
     settle(step)
     for i in range(warmup):
         step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall, region_ms = timed_region(step, steps, stream)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     for i in range(steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     call_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     del weights
-    return dict(plan=cfg, wall_s=wall, call_ms=call_ms, bytes=(rd, wr))
+    return dict(plan=cfg, wall_s=wall, call_ms=call_ms, bytes=(rd, wr), region_ms=region_ms)
 
 
 def swiglu_record(prob, r, steps):
@@ -596,26 +593,29 @@ def swiglu_record(prob, r, steps):
     total = rd + wr
     ms_step = r["wall_s"] * 1e3 / steps
     call = stats(r["call_ms"])
-    achieved = total / (call["mean_ms"] * 1e-3) / 1e9
+    achieved = total / (r["region_ms"] * 1e-3) / 1e9
     cfg = r["plan"]
     config = {"workload": prob.name, "m": prob.m, "k": prob.k, "n": prob.n,
               "split_s": cfg.s, "k_chunk": cfg.k_chunk, "kernel": cfg.kernel}
     if cfg.kernel == 1:
         flops = 4.0 * prob.m * prob.k * prob.n   # both MatMuls
         return {"value": round(flops / (ms_step * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
-                "ms_per_step": round(ms_step, 5), "config": config,
+                "ms_per_step": round(ms_step, 5), "gpu_span_ms_per_step": round(r["region_ms"], 5),
+        "config": config,
                 "roofline": gemm_roofline(flops, r, f"swiglu:{prob.name}",
                                           "tiled MFMA GEMM of both MatMuls, one launch")}
     return {
         "value": round(total / (ms_step * 1e-3) / 1e9, 2), "unit": "GB/s",
-        "ms_per_step": round(ms_step, 5), "config": config,
+        "ms_per_step": round(ms_step, 5), "gpu_span_ms_per_step": round(r["region_ms"], 5),
+        "config": config,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/swiglu.hip",
                                             f"swiglu:{prob.name}"),
                      "kernel": ("SwiGLU kernel, one launch" if cfg.s == 1 else
                                 "SwiGLU split kernel + combine kernel (timed together)"),
-                     "algorithmic_bytes_per_launch": total, "launch_ms": call}}
+                     "algorithmic_bytes_per_launch": total,
+                     "region_ms_per_launch": round(r["region_ms"], 6), "launch_ms": call}}
 
 
 def oracle_swiglu_baseline(prob, rows_cap=512):
@@ -741,9 +741,10 @@ def mm_record(prob, r, steps):
     flops = attention_flops(prob)
     ks = stats(r["kernel_ms"])
     ms_step = r["wall_s"] * 1e3 / steps
-    achieved = flops / (ks["mean_ms"] * 1e-3) / 1e12
+    achieved = flops / (r["region_ms"] * 1e-3) / 1e12
     return {"value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
             "ms_per_step": round(ms_step, 5),
+            "gpu_span_ms_per_step": round(r["region_ms"], 5),
             "config": {"workload": prob.name, "batch": prob.batch, "q_len": prob.lq,
                        "kv_len": int(prob.lens.max()), "q_heads": prob.hq,
                        "kv_heads": prob.hkv, "head_dim": prob.dqk, "causal": bool(prob.causal)},
@@ -753,7 +754,8 @@ def mm_record(prob, r, steps):
                          "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/"
                                                 "prefill_d128.hip", f"mm:{prob.name}"),
                          "kernel": "MatMul+MatMul kernel (prefill kernel without the softmax)",
-                         "algorithmic_flops_per_launch": flops, "launch_ms": ks}}
+                         "algorithmic_flops_per_launch": flops,
+                         "region_ms_per_launch": round(r["region_ms"], 6), "launch_ms": ks}}
 
 
 # ------------------------------------------------------------------------ main
@@ -763,16 +765,18 @@ def decode_record(prob, r, steps, extra_src, key_suffix=""):
     total = qb + kvb + ob
     ms_step = r["wall_s"] * 1e3 / steps
     split = stats(r["split_ms"])
-    # The dominant kernel: the single fused launch (Q, K, V read + O written) or
-    # the split launch of the two-launch path (Q, K, V read).
+    # The dominant kernel: the single fused launch (Q, K, V read + O written),
+    # timed over the timed region, or the split launch of the two-launch path
+    # (Q, K, V read), timed by its own event pairs.
     kern_bytes = total if r["fused"] else qb + kvb
-    achieved = kern_bytes / (split["mean_ms"] * 1e-3) / 1e9
+    launch_ms = r["region_ms"] if r["fused"] else split["mean_ms"]
+    achieved = kern_bytes / (launch_ms * 1e-3) / 1e9
     plan = r["plan"]
     traffic = traffic_for(extra_src, ("decode:" if r["fused"] else "decode_split:") + prob.name
                           + key_suffix)
     return dict(
         value=round(total / (ms_step * 1e-3) / 1e9, 2), ms_per_step=round(ms_step, 5),
-        gpu_span_ms_per_step=round(r["gpu_span_ms_per_step"], 5),
+        gpu_span_ms_per_step=round(r["region_ms"], 5),
         plan=dict(kernel=plan.kernel, s_max=plan.s_max, chunk=plan.chunk, n_items=plan.n_items,
                   grid=list(plan.grid), ws_bytes=int(plan.ws_o_bytes + plan.ws_lse_bytes)),
         roofline={"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
@@ -783,6 +787,7 @@ def decode_record(prob, r, steps, extra_src, key_suffix=""):
                               "decode kernel, single launch with in-kernel merge")
                              if r["fused"] else "decode split kernel"),
                   "algorithmic_bytes_per_launch": kern_bytes,
+                  "region_ms_per_launch": round(launch_ms, 6),
                   "launch_ms": split},
         combine=None if r["combine_ms"] is None else stats(r["combine_ms"]),
         algorithmic_bytes_per_step=total)
@@ -866,10 +871,10 @@ def prefill_leg(prob, a, dev):
     flops = attention_flops(prob)
     ks = stats(r["kernel_ms"])
     ms_step = r["wall_s"] * 1e3 / a.steps
-    achieved = flops / (ks["mean_ms"] * 1e-3) / 1e12
+    achieved = flops / (r["region_ms"] * 1e-3) / 1e12
     return {"value": round(flops / (ms_step * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
             "ms_per_step": round(ms_step, 5),
-            "gpu_span_ms_per_step": round(r["gpu_span_ms_per_step"], 5),
+            "gpu_span_ms_per_step": round(r["region_ms"], 5),
             "config": {"workload": prob.name, "batch": prob.batch, "q_len": prob.lq,
                        "kv_len": int(prob.lens.max()), "q_heads": prob.hq,
                        "kv_heads": prob.hkv, "head_dim": prob.dqk, "causal": bool(prob.causal)},
@@ -879,7 +884,8 @@ def prefill_leg(prob, a, dev):
                          "traffic": traffic_for("reduction_attention_gqa_amd/csrc/kernels/"
                                                 "prefill_d128.hip", f"prefill:{prob.name}"),
                          "kernel": "prefill kernel",
-                         "algorithmic_flops_per_launch": flops, "launch_ms": ks}}
+                         "algorithmic_flops_per_launch": flops,
+                         "region_ms_per_launch": round(r["region_ms"], 6), "launch_ms": ks}}
 
 
 # --------------------------------------------------------------- host record

@@ -142,20 +142,19 @@ void gemm_nt_kernel(GemmParams p) {
     b_off[u] = (uint32_t)brow * (MODE == 0 || row < 128 ? b0st : b1st) + 16u * (uint32_t)c;
   }
   const bool b_up = MODE == 1 && w >= NW / 2;
+  const __amdgpu_buffer_rsrc_t brs = b_up ? b1rs : b0rs;
+  // The compiler's own buffer-to-LDS load (it sets M0 itself and knows that
+  // the fragment reads do not use it, so it does not drain them first).
+  typedef __attribute__((address_space(3))) void lds_void_t;
   auto dma = [&](int step, int stage) {
     const uint32_t kb = (uint32_t)step * BK * 2, kbb = (uint32_t)(step >> p.b_shift) * BK * 2;
 #pragma unroll
     for (int u = 0; u < DMA_PER_WAVE; ++u) {
-      const uint32_t m0a = smem_lds + (uint32_t)(stage * STAGE + (DMA_PER_WAVE * w + u) * 1024);
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                   :: "s"(m0a), "v"(a_off[u] + kb), "s"(ars) : "memory", "m0");
-      const uint32_t m0b = m0a + TILE;
-      if (b_up)
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :: "s"(m0b), "v"(b_off[u] + kbb), "s"(b1rs) : "memory", "m0");
-      else
-        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                     :: "s"(m0b), "v"(b_off[u] + kbb), "s"(b0rs) : "memory", "m0");
+      const int slot0 = stage * STAGE + (DMA_PER_WAVE * w + u) * 1024;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ars, (lds_void_t*)(smem + slot0), 16,
+                                               (int)(a_off[u] + kb), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs, (lds_void_t*)(smem + slot0 + TILE), 16,
+                                               (int)(b_off[u] + kbb), 0, 0, 0);
     }
   };
   // All copies of a step have landed once at most `later` newer steps' copies
@@ -234,8 +233,12 @@ void gemm_nt_kernel(GemmParams p) {
     const uint32_t so = (uint32_t)((t % NS) * STAGE);
 #pragma unroll
     for (int sub = 0; sub + 1 < SUBS; ++sub) {
+      // Scheduling barriers keep the next k-step's reads ahead of this
+      // k-step's MFMAs (left alone, the compiler sinks each read to its use).
       read_frags(f[(sub + 1) & 1], so, sub + 1);
+      __builtin_amdgcn_sched_barrier(0);
       mfmas(f[sub & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     wait_steps_but(max(0, min(LOOK - 1, nsteps - 2 - t)));
     // The compiler's own wait and barrier: it then knows that the fragments

@@ -355,11 +355,18 @@ int attn_decode_plan(const attn_problem* problem, int32_t s_request, const int32
       chunk = ceil_div(ceil_div(lmax, s_max), tile_n) * tile_n;
     } else {
       // Aim for a family-specific number of workgroups per compute unit, with at
-      // least two tiles per split so the per-split prologue and epilogue stay small.
+      // least two tiles per split so the per-split prologue and epilogue stay
+      // small.  The generic family takes one tile per split when its work does
+      // not fill the GPU anyway (a small problem's latency is that of its
+      // longest split), and at most kGenericTileN splits, the most its
+      // single-launch merge tabulates in LDS.
       const int64_t target_wgs = (int64_t)cus * target_wgs_per_cu(family);
       const int64_t work_tiles = tiles_total * units_per_req;
       int64_t chunk_tiles = ceil_div(work_tiles, target_wgs);
-      chunk_tiles = std::max<int64_t>(chunk_tiles, 2);
+      if (family != ATTN_KERNEL_GENERIC || work_tiles > target_wgs)
+        chunk_tiles = std::max<int64_t>(chunk_tiles, 2);
+      if (family == ATTN_KERNEL_GENERIC)
+        chunk_tiles = std::max<int64_t>(chunk_tiles, ceil_div(max_tiles, kGenericTileN));
       chunk_tiles = std::min<int64_t>(chunk_tiles, max_tiles);
       chunk = chunk_tiles * tile_n;
     }

@@ -27,7 +27,7 @@
 // lines): the A and B tiles of a step (32 KiB each) are copied HBM -> LDS by
 // buffer loads that write LDS directly, into a 2-stage ring (the next step's
 // copy in flight during a step).  16-byte chunk c of tile row r sits at chunk
-// c ^ (r % 8), which keeps the fragment reads (32 rows, two chunks per
+// c ^ ((r / 2) % 8), which keeps the fragment reads (32 rows, two chunks per
 // instruction) free of bank conflicts.
 // Workgroups are ordered so that the eight XCDs each own every eighth column
 // tile (a weight tile is fetched by one XCD only) and walk their tiles in
@@ -62,9 +62,12 @@ typedef __attribute__((address_space(3))) const i32x4_t lds_i32x4_t;
 __device__ __forceinline__ i32x4_t ds_read16_at(uint32_t lds_addr) {
   return *reinterpret_cast<lds_i32x4_t*>((uintptr_t)lds_addr);
 }
-// Chunk c of tile row r sits at chunk c ^ (r % CH): the fragment reads (32
-// rows, two chunks per instruction) then fall on distinct banks.
-__device__ __forceinline__ int swz(int r) { return r & (CH - 1); }
+// Chunk c of tile row r sits at chunk c ^ ((r / 2) % CH).  The LDS serves a
+// 16-byte read sixteen lanes at a time over 64 four-byte banks (256 bytes),
+// and a 128-byte tile row covers half of them, its parity choosing the half:
+// sixteen consecutive rows, one chunk each, then cover all 64 banks once.
+// (c ^ (r % CH) would map rows r and r + 8 onto the same banks.)
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & (CH - 1); }
 // s_waitcnt immediate: lgkmcnt(0), vmcnt and expcnt at their maxima (no wait).
 constexpr int kWaitLgkm0 = 0xC07F;
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }

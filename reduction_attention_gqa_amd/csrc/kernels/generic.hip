@@ -19,7 +19,7 @@ namespace {
 constexpr int RT = kGenericRowTile;
 constexpr int TN = kGenericTileN;
 constexpr int NT = kGenericBlock;
-constexpr int MAXC = 32;  // output (row, d) pairs per thread: RT * Dv <= NT * MAXC, Dv <= 512
+constexpr int NB = 8;     // elements per thread and operand loaded before any is stored
 
 template <bool BF16>
 __device__ __forceinline__ float ld_elem(const void* base, int64_t idx) {
@@ -30,12 +30,57 @@ __device__ __forceinline__ float ld_elem(const void* base, int64_t idx) {
   }
 }
 
+// Copies a tile of nk rows of `wk` elements (row jj of `ka` at element offset
+// rk[jj]) into LDS rows of stride `sk`, and likewise a tile of `wv`-element
+// rows of `va` into rows of stride `sv`.  Thread t takes elements t, t + NT,
+// ... of each tile (consecutive threads, consecutive elements: coalesced);
+// each round issues NB loads of each tile before it stores any of them, so
+// their latencies overlap instead of adding up.
+template <bool BF16>
+__device__ __forceinline__ void stage_kv(const void* ka, const int64_t* rk, int wk, float* dk_s, int sk,
+                                         const void* va, const int64_t* rv, int wv, float* dv_s, int sv,
+                                         int nk, int t) {
+  const int djk = NT / wk, ddk = NT - djk * wk;
+  const int djv = NT / wv, ddv = NT - djv * wv;
+  int jk = t / wk, ck = t - jk * wk;
+  int jv = t / wv, cv = t - jv * wv;
+  while (jk < nk || jv < nk) {
+    float xk[NB], xv[NB];
+    int ok[NB], ov[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      // Past the tile: element 0 of row 0 is read (it exists) and dropped.
+      ok[u] = jk < nk ? jk * sk + ck : -1;
+      xk[u] = ld_elem<BF16>(ka, jk < nk ? rk[jk] + ck : rk[0]);
+      ov[u] = jv < nk ? jv * sv + cv : -1;
+      xv[u] = ld_elem<BF16>(va, jv < nk ? rv[jv] + cv : rv[0]);
+      jk += djk;
+      ck += ddk;
+      if (ck >= wk) {
+        ck -= wk;
+        ++jk;
+      }
+      jv += djv;
+      cv += ddv;
+      if (cv >= wv) {
+        cv -= wv;
+        ++jv;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      if (ok[u] >= 0) dk_s[ok[u]] = xk[u];
+      if (ov[u] >= 0) dv_s[ov[u]] = xv[u];
+    }
+  }
+}
+
 // STAGE: each key tile's K and V rows are first copied into LDS by all
-// threads with consecutive elements per thread (coalesced, one load per
-// element), and the scores and the V-matmul read them from there; without it
-// (head dims too large for the LDS) every thread reads its K and V elements
-// from memory itself.
-template <bool BF16, bool STAGE>
+// threads (stage_kv), and the scores and the V-matmul read them from there;
+// without it (head dims too large for the LDS) every thread reads its K and V
+// elements from memory itself.  CP: output (row, d) pairs per thread, a power
+// of two with RT * Dv <= NT * CP.
+template <bool BF16, bool STAGE, int CP>
 __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
   extern __shared__ float smem[];
   float* q_s = smem;                 // [RT][Dqk]
@@ -95,28 +140,45 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
     hi = min(hi, i_last + L - Lqb + 1);
   }
 
-  // Q tile (hoisted out of the key loop: Cleave §6.1, loop-invariant input).
-  for (int e = t; e < RT * p.Dqk; e += NT) {
-    const int r = e / p.Dqk, d = e % p.Dqk;
-    float val = 0.f;
-    if (r < nrows) {
+  // Q tile (hoisted out of the key loop: Cleave §6.1, loop-invariant input);
+  // NB loads per thread in flight before their stores.  The request's first
+  // query row (an offset-array read when packed) is looked up once, so no
+  // wait for it separates the loads.
+  const int64_t q0 = q_row_off(p, b, 0);
+  for (int e0 = t; e0 < RT * p.Dqk; e0 += NB * NT) {
+    float qv[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      // Every load is issued; one past the tile or its rows reads element 0
+      // of row 0 (which exists) and is dropped, so no branch holds the
+      // loads apart.
+      const int e = e0 + u * NT;
+      const bool ok = e < RT * p.Dqk && e / p.Dqk < nrows;
+      const int ec = ok ? e : 0;
+      const int r = ec / p.Dqk, d = ec - r * p.Dqk;
       const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
-      val = ld_elem<BF16>(p.q, q_row_off(p, b, i) + (int64_t)h * p.qs_h + d);
+      const float x = ld_elem<BF16>(p.q, q0 + (int64_t)i * p.qs_t + (int64_t)h * p.qs_h + d);
+      qv[u] = ok ? x : 0.f;
     }
-    q_s[e] = val;
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (e0 + u * NT < RT * p.Dqk) q_s[e0 + u * NT] = qv[u];
   }
   if (t < RT) {
     m_s[t] = kNegInf;
     l_s[t] = 0.f;
   }
 
-  float acc[MAXC];
+  float acc[CP];
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) acc[c] = 0.f;
+  for (int c = 0; c < CP; ++c) acc[c] = 0.f;
   const int npairs = RT * p.Dv;
 
   const int64_t khead = (int64_t)kvh * p.ks_h;
   const int64_t vhead = (int64_t)kvh * p.vs_h;
+  // Contiguous (plain or packed) K/V: key 0 of this request and KV head.
+  const int64_t kbase = p.page_table ? 0 : kv_base_off(p, b, p.ks_b, p.ks_t) + khead;
+  const int64_t vbase = p.page_table ? 0 : kv_base_off(p, b, p.vs_b, p.vs_t) + vhead;
   __syncthreads();
 
   for (int k0 = lo; k0 < hi; k0 += TN) {
@@ -126,34 +188,18 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
       // Row offsets once per key, then consecutive elements per thread (the
       // element index advances by NT: a fixed step in columns and rows).
       if (t < nk) {
-        row_k[t] = kv_row_off(p, b, k0 + t, p.ks_b, p.ks_t) + khead;
-        row_v[t] = kv_row_off(p, b, k0 + t, p.vs_b, p.vs_t) + vhead;
+        const int key = k0 + t;
+        if (p.page_table) {
+          const int64_t pg = page_of(p, b, key), kr = key % p.page_size;
+          row_k[t] = pg * p.ks_b + kr * p.ks_t + khead;
+          row_v[t] = pg * p.vs_b + kr * p.vs_t + vhead;
+        } else {
+          row_k[t] = kbase + (int64_t)key * p.ks_t;
+          row_v[t] = vbase + (int64_t)key * p.vs_t;
+        }
       }
       __syncthreads();
-      {
-        const int dj = NT / p.Dqk, dd = NT - dj * p.Dqk;
-        int jj = t / p.Dqk, d = t - jj * p.Dqk;
-        for (; jj < nk; jj += dj, d += dd) {
-          if (d >= p.Dqk) {
-            d -= p.Dqk;
-            ++jj;
-            if (jj >= nk) break;
-          }
-          k_s[jj * ks_row + d] = ld_elem<BF16>(p.k, row_k[jj] + d);
-        }
-      }
-      {
-        const int dj = NT / p.Dv, dd = NT - dj * p.Dv;
-        int jj = t / p.Dv, d = t - jj * p.Dv;
-        for (; jj < nk; jj += dj, d += dd) {
-          if (d >= p.Dv) {
-            d -= p.Dv;
-            ++jj;
-            if (jj >= nk) break;
-          }
-          v_s[jj * p.Dv + d] = ld_elem<BF16>(p.v, row_v[jj] + d);
-        }
-      }
+      stage_kv<BF16>(p.k, row_k, p.Dqk, k_s, ks_row, p.v, row_v, p.Dv, v_s, p.Dv, nk, t);
       __syncthreads();
     }
     // Scores: thread t -> key k0 + t % TN, rows 4*(t / TN) .. +3.
@@ -231,7 +277,7 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
     __syncthreads();
     // Output accumulator: thread t owns pairs e = t + NT*c -> (r = e / Dv, d = e % Dv).
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
+    for (int c = 0; c < CP; ++c) {
       const int e = t + NT * c;
       if (e < npairs) {
         const int r = e / p.Dv, d = e % p.Dv;
@@ -276,7 +322,7 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
     const bool last = s_ticket == sb_all - 1;
     const int64_t nrow_all = (int64_t)p.B * p.Lq * p.Hq;
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
+    for (int c = 0; c < CP; ++c) {
       const int e = t + NT * c;
       if (e < npairs) {
         const int r = e / p.Dv, d = e % p.Dv;
@@ -300,8 +346,93 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
         __builtin_amdgcn_s_sleep(2);
     }
     __syncthreads();
+    if (sb_all <= TN) {
+      // Merge through a table in the (now free) score tile: tab[jj][r] holds
+      // split jj's LSE of row r, then its weight 2^(LSE log2 e - M).  Every
+      // partial is fetched in batches of NB loads (not one dependent load at
+      // a time); the sums run in split order, as below.
+      float* tab = s_s;
+      const int nent = sb_all * nrows;
+      for (int e0 = t; e0 < nent; e0 += NB * NT) {
+        float lv[NB];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
+        for (int u = 0; u < NB; ++u) {
+          const int e = e0 + u * NT;
+          const int ec = e < nent ? e : 0;
+          const int jj = ec / nrows, r = ec - jj * nrows;
+          const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
+          const int64_t slot = (int64_t)jj * nrow_all + ((int64_t)b * p.Lq + i) * p.Hq + h;
+          const float x = load_dev(p.ws_lse + slot);  // split j's own slot is unused
+          const float l = l_s[r];
+          lv[u] = jj == j ? (l > 0.f ? (m_s[r] + fast_log2(l)) * kLn2 : kNegInf) : x;
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+          const int e = e0 + u * NT;
+          if (e < nent) {
+            const int jj = e / nrows, r = e - jj * nrows;
+            tab[jj * RT + r] = lv[u];
+          }
+        }
+      }
+      __syncthreads();
+      // Per row: M (base 2), the weights and their sum (a_s), M itself (m_s;
+      // the row's own m and l are no longer needed but l_s is).
+      if (t < nrows) {
+        float M2 = kNegInf;
+        for (int jj = 0; jj < sb_all; ++jj) M2 = fmaxf(M2, tab[jj * RT + t] * kLog2e);
+        float den = 0.f;
+        for (int jj = 0; jj < sb_all; ++jj) {
+          const float wj = M2 == kNegInf ? 0.f : fast_exp2(tab[jj * RT + t] * kLog2e - M2);
+          tab[jj * RT + t] = wj;
+          den += wj;
+        }
+        a_s[t] = den;
+        m_s[t] = M2;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int c = 0; c < CP; ++c) {
+        const int e = t + NT * c;
+        if (e < npairs) {
+          const int r = e / p.Dv, d = e % p.Dv;
+          if (r < nrows) {
+            const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
+            const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
+            const float l = l_s[r];
+            const float o_own = l > 0.f ? acc[c] / l : 0.f;
+            float num = 0.f;
+            for (int jj0 = 0; jj0 < sb_all; jj0 += NB) {
+              float ov[NB];
+#pragma unroll
+              for (int u = 0; u < NB; ++u) {
+                const int jj = jj0 + u < sb_all ? jj0 + u : 0;
+                ov[u] = load_dev(p.ws_o + ((int64_t)jj * nrow_all + row) * p.Dv + d);
+              }
+#pragma unroll
+              for (int u = 0; u < NB; ++u) {
+                const int jj = jj0 + u;
+                if (jj < sb_all) num += tab[jj * RT + r] * (jj == j ? o_own : ov[u]);
+              }
+            }
+            const float den = a_s[r], M2 = m_s[r];
+            const float o = den > 0.f ? num / den : 0.f;
+            const int64_t oi = o_row_off(p, b, i) + (int64_t)h * p.os_h + d;
+            if (p.o_bf16)
+              reinterpret_cast<uint16_t*>(p.o)[oi] = (uint16_t)f32_to_bf16_bits(o);
+            else
+              reinterpret_cast<float*>(p.o)[oi] = o;
+            if (d == 0 && p.lse_out)
+              p.lse_out[lse_row(p, b, i) * p.Hq + h] =
+                  M2 == kNegInf ? kNegInf : (M2 + fast_log2(den)) * kLn2;
+          }
+        }
+      }
+      if (t == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return;
+    }
+#pragma unroll
+    for (int c = 0; c < CP; ++c) {
       const int e = t + NT * c;
       if (e < npairs) {
         const int r = e / p.Dv, d = e % p.Dv;
@@ -345,7 +476,7 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
 
   // Epilogue: divide by the row sum after the V-matmul (Cleave §2.2, Fig. 2).
 #pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
+  for (int c = 0; c < CP; ++c) {
     const int e = t + NT * c;
     if (e < npairs) {
       const int r = e / p.Dv, d = e % p.Dv;
@@ -372,34 +503,38 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
   }
 }
 
+template <bool BF16, bool STAGE, int CP>
+hipError_t launch_generic_variant(const KParams& p, dim3 grid, dim3 block, size_t shmem, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(&generic_attn_kernel<BF16, STAGE, CP>);
+  if (STAGE)
+    if (hipError_t e = set_lds_limit_once(fn, (int)shmem)) return e;
+  hipLaunchKernelGGL((generic_attn_kernel<BF16, STAGE, CP>), grid, block, shmem, s, p);
+  return hipGetLastError();
+}
+
+template <bool BF16, bool STAGE>
+hipError_t launch_generic_cp(const KParams& p, dim3 grid, dim3 block, size_t shmem, hipStream_t s) {
+  const int pairs = RT * p.Dv;  // output (row, d) pairs of a workgroup
+  if (pairs <= NT * 4) return launch_generic_variant<BF16, STAGE, 4>(p, grid, block, shmem, s);
+  if (pairs <= NT * 8) return launch_generic_variant<BF16, STAGE, 8>(p, grid, block, shmem, s);
+  if (pairs <= NT * 16) return launch_generic_variant<BF16, STAGE, 16>(p, grid, block, shmem, s);
+  return launch_generic_variant<BF16, STAGE, 32>(p, grid, block, shmem, s);
+}
+
 }  // namespace
 
 hipError_t launch_generic(const KParams& p, dim3 grid, dim3 block, hipStream_t s) {
+  if (RT * p.Dv > NT * 32) return hipErrorInvalidValue;  // Dv <= 512
   const size_t base = sizeof(float) * ((size_t)RT * p.Dqk + RT * TN + 3 * RT);
   // Stage K/V tiles when they fit in 64 KiB (head dims Dqk + Dv < 256).
   const size_t tiles = sizeof(float) * (size_t)TN * (p.Dqk + 1 + p.Dv);
   const bool stage = tiles <= (64u << 10);
   const size_t shmem = base + (stage ? tiles : 0);
-  if (p.in_bf16) {
-    if (stage) {
-      if (hipError_t e = set_lds_limit_once(
-              reinterpret_cast<const void*>(&generic_attn_kernel<true, true>), (int)shmem))
-        return e;
-      hipLaunchKernelGGL((generic_attn_kernel<true, true>), grid, block, shmem, s, p);
-    } else {
-      hipLaunchKernelGGL((generic_attn_kernel<true, false>), grid, block, shmem, s, p);
-    }
-  } else {
-    if (stage) {
-      if (hipError_t e = set_lds_limit_once(
-              reinterpret_cast<const void*>(&generic_attn_kernel<false, true>), (int)shmem))
-        return e;
-      hipLaunchKernelGGL((generic_attn_kernel<false, true>), grid, block, shmem, s, p);
-    } else {
-      hipLaunchKernelGGL((generic_attn_kernel<false, false>), grid, block, shmem, s, p);
-    }
-  }
-  return hipGetLastError();
+  if (p.in_bf16)
+    return stage ? launch_generic_cp<true, true>(p, grid, block, shmem, s)
+                 : launch_generic_cp<true, false>(p, grid, block, shmem, s);
+  return stage ? launch_generic_cp<false, true>(p, grid, block, shmem, s)
+               : launch_generic_cp<false, false>(p, grid, block, shmem, s);
 }
 
 }  // namespace attn

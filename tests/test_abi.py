@@ -658,3 +658,29 @@ def test_swiglu_workspace_and_config_checks(lib):
                       1 << 40, None) == ra.ATTN_ERR_ARG
     assert lib.swiglu(ctypes.byref(p), ctypes.byref(cfg), fake, ctypes.c_void_p(0x1004), fake, fake,
                       fake, 1 << 40, None) == ra.ATTN_ERR_UNSUPPORTED
+
+
+def test_plan_generic_small_problem_one_tile_per_split(lib):
+    # 256 keys (four 64-key tiles) x 2 KV heads do not fill 256 CUs: one tile
+    # per split, so the latency is one tile's.
+    p = problem(dtype=ra.ATTN_F32, o_dtype=ra.ATTN_F32, batch=1, q_heads=8, kv_heads=2,
+                head_dim_qk=64, head_dim_v=64, kv_len_max=256)
+    st, plan = plan_status(lib, p)
+    assert st == 0 and plan.kernel == 0 and plan.s_max == 4 and plan.chunk == 64
+    _check_plan_invariants(p, plan, [256])
+
+
+def test_plan_generic_caps_splits_at_the_merge_table(lib):
+    # 32768 keys = 512 tiles on one KV head: at most 64 splits (the most the
+    # single-launch merge tabulates), whatever the GPU size.
+    for cus in (256, 4096):
+        p = problem(dtype=ra.ATTN_F32, o_dtype=ra.ATTN_F32, batch=1, q_heads=4, kv_heads=1,
+                    head_dim_qk=64, head_dim_v=64, kv_len_max=32768)
+        st, plan = plan_status(lib, p, num_cus=cus)
+        assert st == 0 and plan.kernel == 0 and plan.s_max <= 64
+        _check_plan_invariants(p, plan, [32768])
+    # A problem that fills the GPU keeps at least two tiles per split.
+    p = problem(dtype=ra.ATTN_F32, o_dtype=ra.ATTN_F32, batch=64, q_heads=8, kv_heads=2,
+                head_dim_qk=64, head_dim_v=64, kv_len_max=4096)
+    st, plan = plan_status(lib, p)
+    assert st == 0 and plan.kernel == 0 and plan.chunk >= 128

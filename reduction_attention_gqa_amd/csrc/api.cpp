@@ -145,6 +145,9 @@ KParams base_params(const attn_problem* p) {
   k.rows = k.G * k.Lq;
   k.row_tile = kGenericRowTile;
   k.scale_log2 = scale_of(p) * 1.44269504088896340736f;
+  k.div_dqk = make_fastdiv(std::max(k.Dqk, 1));
+  k.div_dv = make_fastdiv(std::max(k.Dv, 1));
+  k.div_g = make_fastdiv(std::max(k.G, 1));
   return k;
 }
 

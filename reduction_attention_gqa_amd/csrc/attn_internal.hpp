@@ -9,6 +9,23 @@
 namespace attn {
 
 // Everything a kernel needs, passed by value.  Strides are in elements.
+// Division by a divisor fixed for the whole launch as a multiply-high and a
+// shift (Granlund and Montgomery, "Division by Invariant Integers using
+// Multiplication", PLDI 1994, section 4): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (umulhi(m, n) + n) >> l for
+// 0 <= n < 2^31 (umulhi(m, n) <= n, so the sum fits in 32 bits).
+struct FastDiv {
+  uint32_t m, l;
+};
+inline FastDiv make_fastdiv(int32_t d) {
+  FastDiv f;
+  uint32_t l = 0;
+  while (l < 31 && (1u << l) < (uint32_t)d) ++l;
+  f.l = l;
+  f.m = (uint32_t)((((uint64_t)1 << l) - (uint64_t)d) * ((uint64_t)1 << 32) / (uint64_t)d) + 1u;
+  return f;
+}
+
 struct KParams {
   const void* q;
   const void* k;
@@ -46,6 +63,7 @@ struct KParams {
                         // 3 (GQA): runs of rounds per workgroup, cut units merged in-kernel
   float scale_log2;     // tau * log2(e): scores are kept in base-2 units (tau itself when no_softmax)
   int32_t no_softmax;   // prefill only: 1 = MatMul+MatMul, O = (tau Q K^T) V
+  FastDiv div_dqk, div_dv, div_g;  // divisions by Dqk, Dv and G (generic kernel)
 };
 
 // RMSNorm followed by a MatMul: X [M, K], g [K], W [N, K], Y [M, N] (bf16

@@ -21,6 +21,10 @@ constexpr int TN = kGenericTileN;
 constexpr int NT = kGenericBlock;
 constexpr int NB = 8;     // elements per thread and operand loaded before any is stored
 
+__device__ __forceinline__ int fdiv(int n, FastDiv f) {
+  return (int)((__umulhi(f.m, (uint32_t)n) + (uint32_t)n) >> f.l);
+}
+
 template <bool BF16>
 __device__ __forceinline__ float ld_elem(const void* base, int64_t idx) {
   if constexpr (BF16) {
@@ -105,6 +109,36 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
   const int r0 = rt * RT;
   const int nrows = min(RT, p.G * Lqb - r0);
   if (nrows <= 0) return;  // row tile past this request's queries
+
+  // Q tile (hoisted out of the key loop: Cleave §6.1, loop-invariant input);
+  // NB loads per thread in flight before their stores, issued before the
+  // key count is first used so that the two reads overlap.  The request's first
+  // query row (an offset-array read when packed) is looked up once, so no
+  // wait for it separates the loads.
+  const int64_t q0 = q_row_off(p, b, 0);
+  for (int e0 = t; e0 < RT * p.Dqk; e0 += NB * NT) {
+    float qv[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      // Every load is issued; one past the tile or its rows reads element 0
+      // of row 0 (which exists) and is dropped, so no branch holds the
+      // loads apart.
+      const int e = e0 + u * NT;
+      const bool ok = e < nrows * p.Dqk;  // rows past the tile's read as zero
+      const int ec = ok ? e : 0;
+      const int r = fdiv(ec, p.div_dqk), d = ec - r * p.Dqk;
+      const int rr = r0 + r, i = fdiv(rr, p.div_g), h = kvh * p.G + rr - i * p.G;
+      const float x = ld_elem<BF16>(p.q, q0 + (int64_t)i * p.qs_t + (int64_t)h * p.qs_h + d);
+      qv[u] = ok ? x : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u)
+      if (e0 + u * NT < RT * p.Dqk) q_s[e0 + u * NT] = qv[u];
+  }
+  if (t < RT) {
+    m_s[t] = kNegInf;
+    l_s[t] = 0.f;
+  }
   const int sb_all = (L + p.chunk - 1) / p.chunk;  // splits of this request
   if (p.split_mode == 2 && (L == 0 || sb_all > p.s_max)) {
     // Single launch: split 0 answers for a request with no key (O = 0, LSE =
@@ -114,8 +148,8 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
       const float val = L == 0 ? 0.f : __builtin_nanf("");
       const float lse = L == 0 ? kNegInf : __builtin_nanf("");
       for (int e = t; e < nrows * p.Dv; e += NT) {
-        const int r = e / p.Dv, d = e % p.Dv;
-        const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
+        const int r = fdiv(e, p.div_dv), d = e - r * p.Dv;
+        const int rr = r0 + r, i = fdiv(rr, p.div_g), h = kvh * p.G + rr - i * p.G;
         const int64_t oi = o_row_off(p, b, i) + (int64_t)h * p.os_h + d;
         if (p.o_bf16)
           reinterpret_cast<uint16_t*>(p.o)[oi] = (uint16_t)f32_to_bf16_bits(val);
@@ -136,38 +170,10 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
   // Causal: rows of this tile see keys j <= i + L - Lq; the tile needs keys
   // up to the largest such bound.
   if (p.causal) {
-    const int i_last = (r0 + nrows - 1) / p.G;
+    const int i_last = fdiv(r0 + nrows - 1, p.div_g);
     hi = min(hi, i_last + L - Lqb + 1);
   }
 
-  // Q tile (hoisted out of the key loop: Cleave §6.1, loop-invariant input);
-  // NB loads per thread in flight before their stores.  The request's first
-  // query row (an offset-array read when packed) is looked up once, so no
-  // wait for it separates the loads.
-  const int64_t q0 = q_row_off(p, b, 0);
-  for (int e0 = t; e0 < RT * p.Dqk; e0 += NB * NT) {
-    float qv[NB];
-#pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      // Every load is issued; one past the tile or its rows reads element 0
-      // of row 0 (which exists) and is dropped, so no branch holds the
-      // loads apart.
-      const int e = e0 + u * NT;
-      const bool ok = e < RT * p.Dqk && e / p.Dqk < nrows;
-      const int ec = ok ? e : 0;
-      const int r = ec / p.Dqk, d = ec - r * p.Dqk;
-      const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
-      const float x = ld_elem<BF16>(p.q, q0 + (int64_t)i * p.qs_t + (int64_t)h * p.qs_h + d);
-      qv[u] = ok ? x : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < NB; ++u)
-      if (e0 + u * NT < RT * p.Dqk) q_s[e0 + u * NT] = qv[u];
-  }
-  if (t < RT) {
-    m_s[t] = kNegInf;
-    l_s[t] = 0.f;
-  }
 
   float acc[CP];
 #pragma unroll
@@ -202,12 +208,13 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
       stage_kv<BF16>(p.k, row_k, p.Dqk, k_s, ks_row, p.v, row_v, p.Dv, v_s, p.Dv, nk, t);
       __syncthreads();
     }
-    // Scores: thread t -> key k0 + t % TN, rows 4*(t / TN) .. +3.
+    // Scores: thread t -> key k0 + t % TN, rows 4*(t / TN) .. +3 (a wave
+    // whose rows are all past the tile's rows skips the dot products).
     {
       const int jj = t % TN;
       const int rb = (t / TN) * 4;
       float dot[4] = {0.f, 0.f, 0.f, 0.f};
-      if (jj < nk) {
+      if (jj < nk && rb < nrows) {
         if constexpr (STAGE) {
           const float* kr = k_s + jj * ks_row;
 #pragma unroll 8
@@ -231,15 +238,16 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
         const int key = k0 + jj;
         bool vis = (jj < nk) && (r < nrows);
         if (vis && p.causal) {
-          const int i = (r0 + r) / p.G;
+          const int i = fdiv(r0 + r, p.div_g);
           vis = key <= i + L - Lqb;
         }
         s_s[r * TN + jj] = vis ? dot[u] * p.scale_log2 : kNegInf;
       }
     }
     __syncthreads();
-    // Online softmax: 16 threads per row, 4 keys each.
-    {
+    // Online softmax: 16 threads per row, 4 keys each; rows past the tile's
+    // rows are never read.
+    if (t / 16 < nrows) {
       const int r = t / 16;
       const int c0 = (t % 16) * 4;
       float sv[4];
@@ -279,8 +287,8 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
 #pragma unroll
     for (int c = 0; c < CP; ++c) {
       const int e = t + NT * c;
-      if (e < npairs) {
-        const int r = e / p.Dv, d = e % p.Dv;
+      if (e < nrows * p.Dv) {  // rows of the tile only
+        const int r = fdiv(e, p.div_dv), d = e - r * p.Dv;
         float a = acc[c] * a_s[r];
         if constexpr (STAGE) {
           // Eight independent partial sums keep eight LDS reads in flight.
@@ -325,9 +333,9 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
     for (int c = 0; c < CP; ++c) {
       const int e = t + NT * c;
       if (e < npairs) {
-        const int r = e / p.Dv, d = e % p.Dv;
+        const int r = fdiv(e, p.div_dv), d = e - r * p.Dv;
         if (r < nrows && !last) {
-          const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
+          const int rr = r0 + r, i = fdiv(rr, p.div_g), h = kvh * p.G + rr - i * p.G;
           const float l = l_s[r];
           const int64_t slot = (int64_t)j * nrow_all + ((int64_t)b * p.Lq + i) * p.Hq + h;
           store_dev(p.ws_o + slot * p.Dv + d, l > 0.f ? acc[c] / l : 0.f);
@@ -351,29 +359,25 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
       // split jj's LSE of row r, then its weight 2^(LSE log2 e - M).  Every
       // partial is fetched in batches of NB loads (not one dependent load at
       // a time); the sums run in split order, as below.
+      // Entry e = jj * RT + r; rows past the tile's are not loaded.
       float* tab = s_s;
-      const int nent = sb_all * nrows;
+      const int nent = sb_all * RT;
       for (int e0 = t; e0 < nent; e0 += NB * NT) {
         float lv[NB];
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
           const int e = e0 + u * NT;
-          const int ec = e < nent ? e : 0;
-          const int jj = ec / nrows, r = ec - jj * nrows;
-          const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
-          const int64_t slot = (int64_t)jj * nrow_all + ((int64_t)b * p.Lq + i) * p.Hq + h;
+          const int jj = e / RT, r = e % RT;
+          const bool ok = e < nent && r < nrows;
+          const int rr = r0 + (ok ? r : 0), i = fdiv(rr, p.div_g), h = kvh * p.G + rr - i * p.G;
+          const int64_t slot = (int64_t)(ok ? jj : 0) * nrow_all + ((int64_t)b * p.Lq + i) * p.Hq + h;
           const float x = load_dev(p.ws_lse + slot);  // split j's own slot is unused
           const float l = l_s[r];
           lv[u] = jj == j ? (l > 0.f ? (m_s[r] + fast_log2(l)) * kLn2 : kNegInf) : x;
         }
 #pragma unroll
-        for (int u = 0; u < NB; ++u) {
-          const int e = e0 + u * NT;
-          if (e < nent) {
-            const int jj = e / nrows, r = e - jj * nrows;
-            tab[jj * RT + r] = lv[u];
-          }
-        }
+        for (int u = 0; u < NB; ++u)
+          if (e0 + u * NT < nent) tab[e0 + u * NT] = lv[u];
       }
       __syncthreads();
       // Per row: M (base 2), the weights and their sum (a_s), M itself (m_s;
@@ -395,9 +399,9 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
       for (int c = 0; c < CP; ++c) {
         const int e = t + NT * c;
         if (e < npairs) {
-          const int r = e / p.Dv, d = e % p.Dv;
+          const int r = fdiv(e, p.div_dv), d = e - r * p.Dv;
           if (r < nrows) {
-            const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
+            const int rr = r0 + r, i = fdiv(rr, p.div_g), h = kvh * p.G + rr - i * p.G;
             const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
             const float l = l_s[r];
             const float o_own = l > 0.f ? acc[c] / l : 0.f;
@@ -435,9 +439,9 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
     for (int c = 0; c < CP; ++c) {
       const int e = t + NT * c;
       if (e < npairs) {
-        const int r = e / p.Dv, d = e % p.Dv;
+        const int r = fdiv(e, p.div_dv), d = e - r * p.Dv;
         if (r < nrows) {
-          const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
+          const int rr = r0 + r, i = fdiv(rr, p.div_g), h = kvh * p.G + rr - i * p.G;
           const int64_t row = ((int64_t)b * p.Lq + i) * p.Hq + h;
           const float l = l_s[r];
           const float o_own = l > 0.f ? acc[c] / l : 0.f;
@@ -479,9 +483,9 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
   for (int c = 0; c < CP; ++c) {
     const int e = t + NT * c;
     if (e < npairs) {
-      const int r = e / p.Dv, d = e % p.Dv;
+      const int r = fdiv(e, p.div_dv), d = e - r * p.Dv;
       if (r < nrows) {
-        const int rr = r0 + r, i = rr / p.G, h = kvh * p.G + rr % p.G;
+        const int rr = r0 + r, i = fdiv(rr, p.div_g), h = kvh * p.G + rr - i * p.G;
         const float l = l_s[r];
         const float o = l > 0.f ? acc[c] / l : 0.f;
         const float lse = l > 0.f ? (m_s[r] + fast_log2(l)) * kLn2 : kNegInf;

@@ -5,27 +5,11 @@
 #include <stdint.h>
 
 #include "attn_mi355x.h"
+#include "fastdiv.hpp"
 
 namespace attn {
 
 // Everything a kernel needs, passed by value.  Strides are in elements.
-// Division by a divisor fixed for the whole launch as a multiply-high and a
-// shift (Granlund and Montgomery, "Division by Invariant Integers using
-// Multiplication", PLDI 1994, section 4): with l = ceil(log2 d) and
-// m = floor(2^32 (2^l - d) / d) + 1, n / d = (umulhi(m, n) + n) >> l for
-// 0 <= n < 2^31 (umulhi(m, n) <= n, so the sum fits in 32 bits).
-struct FastDiv {
-  uint32_t m, l;
-};
-inline FastDiv make_fastdiv(int32_t d) {
-  FastDiv f;
-  uint32_t l = 0;
-  while (l < 31 && (1u << l) < (uint32_t)d) ++l;
-  f.l = l;
-  f.m = (uint32_t)((((uint64_t)1 << l) - (uint64_t)d) * ((uint64_t)1 << 32) / (uint64_t)d) + 1u;
-  return f;
-}
-
 struct KParams {
   const void* q;
   const void* k;

@@ -33,14 +33,15 @@ constexpr int NW = 4;      // waves per workgroup
 constexpr int NRB = 4;     // 16-row weight blocks per wave
 constexpr int ROWS = NRB * 16;  // weight rows per workgroup (shared by its waves)
 static_assert(NRB == NW, "wave w finishes row block w");
-constexpr int NBUF = 4;    // k-steps in flight per wave
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every range: loads read zero
 
 // One super-step: SS consecutive 32-column k-steps.  Its W loads for one
-// weight row cover SS * 64 contiguous bytes and are issued back to back, so
-// the memory sees whole row segments rather than 64-byte pieces spread over
-// time.
-constexpr int SS = 4;
+// weight row cover SS * 64 contiguous bytes, one 128-byte line, and are
+// issued back to back, so the memory sees whole lines rather than 64-byte
+// pieces spread over time.  (Two-line super-steps, or two super-steps in
+// flight, measured 7 % slower: more rows in flight at once cost more than
+// the deeper queue gains.)
+constexpr int SS = 2;
 struct WBuf {
   i32x4_t w[SS][NRB];
 };

@@ -12,11 +12,11 @@
 // 2c + 1 share columns 32c .. 32c + 31 (two 16-row blocks of each weight
 // matrix, the same rows in both) and take alternate super-steps of the part's
 // K range (a second, on-chip level of the same split-K; alternating, rather
-// than a half each, keeps the pair's reads of a weight row 512 contiguous
-// bytes at a time: 6 % faster):
+// than a half each, keeps the pair's reads of a weight row contiguous:
+// 6 % faster):
 //   G^T[16 x 16] += W_gate[16 x 32] X^T[32 x 16],  U^T likewise   16x16x32 MFMA
-// The weights move a super-step (four 32-column k-steps, 256 contiguous
-// bytes per row) ahead of use, double-buffered; X (a few KB, through the
+// The weights move a super-step (two 32-column k-steps, 128 contiguous
+// bytes per row: one line) ahead of use, double-buffered; X (a few KB, through the
 // caches) is issued first so in-order completion never holds it behind W.
 // The two halves are added through LDS and each wave of the pair finishes
 // one row block: with the whole K range in one part (s = 1) it applies the
@@ -32,7 +32,7 @@ constexpr int NW = 4;       // waves per workgroup
 constexpr int NRB = 2;      // 16-row blocks per wave and weight matrix
 constexpr int COLS = NW / 2 * NRB * 16;  // output columns per workgroup (64)
 static_assert(NW == 4 && NRB == 2, "a wave pair covers one column group; each wave finishes one block");
-constexpr int SS = 4;       // k-steps per super-step
+constexpr int SS = 2;       // k-steps per super-step
 constexpr uint32_t kOob = 0x80000000u;  // a buffer offset past every range: loads read zero
 
 struct WBuf {

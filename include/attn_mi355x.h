@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define ATTN_MI355X_VERSION 6
+#define ATTN_MI355X_VERSION 7
 
 typedef enum attn_dtype {
   ATTN_F32 = 0,   /* IEEE binary32 */

@@ -52,10 +52,12 @@ typedef struct rmsnorm_matmul_problem {
 typedef struct rmsnorm_matmul_config {
   int32_t s;            /* K parts, >= 1 */
   int32_t k_chunk;      /* columns per part, a multiple of 32 */
-  uint32_t grid[3];     /* split-kernel grid: 64-column tiles of n, s, 32-row tiles of m */
+  uint32_t grid[3];     /* split-kernel grid: tile_n-column tiles of n, s, 32-row tiles of m */
   uint32_t block;       /* split-kernel threads per workgroup */
   int32_t kernel;       /* 0: split-K streaming kernel (decode setting); 1: tiled GEMM
                            (prefill setting, m >= 256 and k a multiple of 64) */
+  int32_t tile_n;       /* kernel 0: output columns (rows of W) per workgroup, a multiple
+                           of 4 in [4, 64], grid[0] = ceil(n / tile_n); kernel 1: 0 */
   uint64_t ws_bytes;    /* workspace bytes: kernel 0: (s*m*n + s*m) * 4 when s > 1, else 0;
                            kernel 1: m*k*4 (X * g as bf16 pairs) rounded up to 256,
                            plus m*4 */

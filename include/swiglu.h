@@ -52,11 +52,13 @@ typedef struct swiglu_problem {
 typedef struct swiglu_config {
   int32_t s;            /* K parts, >= 1 */
   int32_t k_chunk;      /* columns per part, a multiple of 32 */
-  uint32_t grid[3];     /* split-kernel grid: 64-column tiles of n, s, 32-row tiles of m */
+  uint32_t grid[3];     /* split-kernel grid: tile_n-column tiles of n, s, 32-row tiles of m */
   uint32_t block;       /* split-kernel threads per workgroup */
   int32_t kernel;       /* 0: split-K streaming kernel (decode setting); 1: tiled GEMM
                            of both MatMuls at once (prefill setting, m >= 256 and k a
                            multiple of 64; no workspace) */
+  int32_t tile_n;       /* kernel 0: output columns (rows of each W) per workgroup, a
+                           multiple of 4 in [4, 64], grid[0] = ceil(n / tile_n); kernel 1: 0 */
   uint64_t ws_bytes;    /* fp32 workspace: 2 * s * m * n * 4 bytes when s > 1, else 0 */
   uint64_t problem_key; /* fingerprint of the planned problem */
 } swiglu_config;

@@ -71,8 +71,8 @@ class RmsConfig(ctypes.Structure):
     """rmsnorm_matmul_config (include/rmsnorm_matmul.h)."""
     _fields_ = [
         ("s", ctypes.c_int32), ("k_chunk", ctypes.c_int32), ("grid", ctypes.c_uint32 * 3),
-        ("block", ctypes.c_uint32), ("kernel", ctypes.c_int32), ("ws_bytes", ctypes.c_uint64),
-        ("problem_key", ctypes.c_uint64),
+        ("block", ctypes.c_uint32), ("kernel", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+        ("ws_bytes", ctypes.c_uint64), ("problem_key", ctypes.c_uint64),
     ]
 
 
@@ -90,8 +90,8 @@ class SwigluConfig(ctypes.Structure):
     """swiglu_config (include/swiglu.h)."""
     _fields_ = [
         ("s", ctypes.c_int32), ("k_chunk", ctypes.c_int32), ("grid", ctypes.c_uint32 * 3),
-        ("block", ctypes.c_uint32), ("kernel", ctypes.c_int32), ("ws_bytes", ctypes.c_uint64),
-        ("problem_key", ctypes.c_uint64),
+        ("block", ctypes.c_uint32), ("kernel", ctypes.c_int32), ("tile_n", ctypes.c_int32),
+        ("ws_bytes", ctypes.c_uint64), ("problem_key", ctypes.c_uint64),
     ]
 
 

@@ -678,9 +678,41 @@ int attn_matmul_matmul(const attn_problem* problem, const void* q, const void* k
 namespace attn {
 namespace {
 
-constexpr int kRmsTileN = 64;   // weight rows per split-kernel workgroup
+constexpr int kRmsTileN = 64;   // most weight rows per split-kernel workgroup
 constexpr int kRmsTileM = 32;   // tokens per split-kernel workgroup
 constexpr int kRmsBlock = 256;
+
+// Output columns per workgroup (tile_n) and K parts (s) of the decode-setting
+// streaming kernels.  For each tile width from 64 down to 16 columns in steps
+// of 4: the most parts (at least min_steps k-steps each) whose workgroups fit
+// on the compute units at once, or the requested s.  The pair that leaves the
+// fewest compute units idle in the last round of workgroups wins, the wider
+// tile on a tie (a narrower tile reads the same bytes; its rows past the tile
+// read as zero without a memory access).
+constexpr int kStreamTileMax = 64;  // the streaming kernels' four 16-row MFMA blocks
+void plan_stream_split(int64_t n, int64_t tiles_m, int64_t steps, int64_t min_steps, int cus,
+                       int32_t s_request, int32_t* tile_out, int64_t* s_out) {
+  double best = -1.0;
+  *tile_out = kStreamTileMax;
+  *s_out = 1;
+  for (int tile = kStreamTileMax; tile >= 16; tile -= 4) {
+    const int64_t tiles = ceil_div(n, tile) * tiles_m;
+    int64_t s = 1;
+    if (s_request > 0)
+      s = std::min<int64_t>(s_request, steps);
+    else if (tiles > 0)
+      s = std::max<int64_t>(1, std::min<int64_t>((int64_t)cus / tiles, steps / min_steps));
+    const int64_t chunk_steps = ceil_div(steps, s);
+    s = ceil_div(steps, chunk_steps);
+    const int64_t wgs = tiles * s;
+    const double fill = wgs > 0 ? (double)wgs / (double)(ceil_div(wgs, cus) * cus) : 0.0;
+    if (fill > best + 1e-9) {
+      best = fill;
+      *tile_out = tile;
+      *s_out = s;
+    }
+  }
+}
 
 int check_rms(const rmsnorm_matmul_problem* p) {
   if (!p) return fail(ATTN_ERR_ARG, "problem is NULL");
@@ -751,24 +783,19 @@ int rmsnorm_matmul_plan(const rmsnorm_matmul_problem* problem, int32_t s_request
     out->problem_key = rms_key(p);
     return ATTN_OK;
   }
-  const int64_t tiles = ceil_div(p->n, kRmsTileN) * ceil_div(p->m, kRmsTileM);
+  // Parts of at least four k-steps per wave (a part is split over the four
+  // waves of a workgroup).
+  int32_t tile_n = kRmsTileN;
   int64_t s = 1;
-  if (s_request > 0) {
-    s = std::min<int64_t>(s_request, steps);
-  } else if (tiles > 0) {
-    // The most parts whose workgroups still run in one round (one per compute
-    // unit; each of its four waves keeps a 16 KiB super-step of W in flight),
-    // at least four k-steps per wave (a part is split over the four waves).
-    s = (int64_t)cus / tiles;
-    s = std::max<int64_t>(1, std::min<int64_t>(s, steps / 16));
-  }
+  plan_stream_split(p->n, ceil_div(p->m, kRmsTileM), steps, 16, cus, s_request, &tile_n, &s);
   const int64_t chunk_steps = ceil_div(steps, s);
   s = ceil_div(steps, chunk_steps);
   if (s > 65535 || ceil_div(p->m, kRmsTileM) > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, "too many parts or token tiles for the grid");
   out->s = (int32_t)s;
   out->k_chunk = (int32_t)(chunk_steps * 32);
-  out->grid[0] = (uint32_t)ceil_div(p->n, kRmsTileN);
+  out->tile_n = tile_n;
+  out->grid[0] = (uint32_t)ceil_div(p->n, tile_n);
   out->grid[1] = (uint32_t)s;
   out->grid[2] = (uint32_t)ceil_div(p->m, kRmsTileM);
   out->block = kRmsBlock;
@@ -821,6 +848,8 @@ int rmsnorm_matmul(const rmsnorm_matmul_problem* problem, const rmsnorm_matmul_c
     gp.b_shift = 1;
     return hip_status(launch_gemm_nt(gp, hs), "gemm launch");
   }
+  if (plan->tile_n < 4 || plan->tile_n > kStreamTileMax || plan->tile_n % 4)
+    return fail(ATTN_ERR_ARG, "corrupt plan");
   const uint64_t need = plan->s > 1 ? (uint64_t)plan->s * p->m * ((uint64_t)p->n + 1) * sizeof(float) : 0;
   if (need && (!ws || ws_bytes < need))
     return fail(ATTN_ERR_WORKSPACE, "workspace too small: need %llu bytes", (unsigned long long)need);
@@ -835,6 +864,7 @@ int rmsnorm_matmul(const rmsnorm_matmul_problem* problem, const rmsnorm_matmul_c
   k.M = p->m; k.K = p->k; k.N = p->n;
   k.s = plan->s;
   k.k_chunk = plan->k_chunk;
+  k.tile_n = plan->tile_n;
   k.y_bf16 = p->y_dtype == ATTN_BF16;
   k.eps = p->eps;
   return hip_status(launch_rmsnorm_matmul(k, reinterpret_cast<hipStream_t>(stream)),
@@ -916,21 +946,19 @@ int swiglu_plan(const swiglu_problem* problem, int32_t s_request, int32_t num_cu
     out->problem_key = swiglu_key(p);
     return ATTN_OK;
   }
-  const int64_t tiles = ceil_div(p->n, kSwTileN) * ceil_div(p->m, kSwTileM);
+  // Parts of at least four k-steps per wave (a part is split over each pair
+  // of waves).
+  int32_t tile_n = kSwTileN;
   int64_t s = 1;
-  if (s_request > 0) {
-    s = std::min<int64_t>(s_request, steps);
-  } else if (tiles > 0) {
-    s = (int64_t)cus / tiles;
-    s = std::max<int64_t>(1, std::min<int64_t>(s, steps / 8));  // >= 4 k-steps per wave
-  }
+  plan_stream_split(p->n, ceil_div(p->m, kSwTileM), steps, 8, cus, s_request, &tile_n, &s);
   const int64_t chunk_steps = ceil_div(steps, s);
   s = ceil_div(steps, chunk_steps);
   if (s > 65535 || ceil_div(p->m, kSwTileM) > 65535)
     return fail(ATTN_ERR_UNSUPPORTED, "too many parts or token tiles for the grid");
   out->s = (int32_t)s;
   out->k_chunk = (int32_t)(chunk_steps * 32);
-  out->grid[0] = (uint32_t)ceil_div(p->n, kSwTileN);
+  out->tile_n = tile_n;
+  out->grid[0] = (uint32_t)ceil_div(p->n, tile_n);
   out->grid[1] = (uint32_t)s;
   out->grid[2] = (uint32_t)ceil_div(p->m, kSwTileM);
   out->block = 256;
@@ -968,6 +996,8 @@ int swiglu(const swiglu_problem* problem, const swiglu_config* config, const voi
     gp.mode = 1;
     return hip_status(launch_gemm_nt(gp, reinterpret_cast<hipStream_t>(stream)), "gemm launch");
   }
+  if (config->tile_n < 4 || config->tile_n > kStreamTileMax || config->tile_n % 4)
+    return fail(ATTN_ERR_ARG, "corrupt config");
   const uint64_t need = config->s > 1 ? 2ull * (uint64_t)config->s * p->m * p->n * sizeof(float) : 0;
   if (need && (!ws || ws_bytes < need))
     return fail(ATTN_ERR_WORKSPACE, "workspace too small: need %llu bytes", (unsigned long long)need);
@@ -984,6 +1014,7 @@ int swiglu(const swiglu_problem* problem, const swiglu_config* config, const voi
   k.M = p->m; k.K = p->k; k.N = p->n;
   k.s = config->s;
   k.k_chunk = config->k_chunk;
+  k.tile_n = config->tile_n;
   k.y_bf16 = p->y_dtype == ATTN_BF16;
   return hip_status(launch_swiglu(k, reinterpret_cast<hipStream_t>(stream)), "swiglu launch");
 }

@@ -63,6 +63,7 @@ struct RmsParams {
   int32_t M, K, N;
   int32_t s;            // K splits
   int32_t k_chunk;      // columns per split, a multiple of 32
+  int32_t tile_n;       // weight rows per workgroup, a multiple of 4 in [4, 64]
   int32_t y_bf16;
   float eps;
 };
@@ -81,6 +82,7 @@ struct SwigluParams {
   int32_t M, K, N;
   int32_t s;            // K splits
   int32_t k_chunk;      // columns per split, a multiple of 32
+  int32_t tile_n;       // output columns per workgroup, a multiple of 4 in [4, 64]
   int32_t y_bf16;
 };
 hipError_t launch_swiglu(const SwigluParams& p, hipStream_t s);

@@ -10,9 +10,11 @@
 //
 // Layout: X [M, K], g [K], W [N, K] (linear-layer weights), Y [M, N], row
 // strides in elements, bf16 inputs.  A workgroup is four waves that share the
-// workgroup's 64 weight rows (four MFMA row blocks) and up to 32 tokens (two
-// MFMA column groups) and split the part's K range four ways, wave w taking
-// the w-th quarter (a second, on-chip level of the same split-K):
+// workgroup's tile of up to 64 weight rows (four MFMA row blocks; the planner
+// narrows the tile, in steps of 4 rows, so that the tiles fill the compute
+// units: 56 rows for N = 14336 on 256 of them) and up to 32 tokens (two MFMA
+// column groups) and split the part's K range four ways, wave w taking the
+// w-th quarter (a second, on-chip level of the same split-K):
 //   U^T[16 x 16] += W[16 x 32] (X * g)^T[32 x 16]     16x16x32 bf16 MFMA
 // W streams from HBM straight into the A operand (16 bytes per lane and row
 // block, four k-steps in flight); X and g come through the caches (a few KB,
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;   // MFMA row (weight row) / column (token) index
   const int kg = lane >> 4;  // 8-column group of a 32-column k-step
-  const int n_wg = blockIdx.x * ROWS;
+  const int n_wg = blockIdx.x * p.tile_n;  // tile_n <= ROWS, a multiple of 4
   const int j = blockIdx.y;
   const int m0 = blockIdx.z * 32;
   // This wave's quarter of the part's columns (a multiple of 32 wide).
@@ -92,9 +94,10 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
   const int lo = min(lo_j + w * kcw, hi_j);
   const int hi = min(lo + kcw, hi_j);
 
-  // Buffer ranges end at the last valid weight row / token, so rows past N or
-  // M read as zero.  Offsets stay 32-bit: a workgroup's 64 rows, 32 tokens.
-  const int wrows = min(ROWS, p.N - n_wg);
+  // Buffer ranges end at the tile's last valid weight row and token, so rows
+  // past the tile, N or M read as zero without a memory access.  Offsets stay
+  // 32-bit: a workgroup's 64 rows, 32 tokens.
+  const int wrows = min(p.tile_n, p.N - n_wg);
   const int xrows = min(32, p.M - m0);
   const uint16_t* wp = reinterpret_cast<const uint16_t*>(p.w) + (int64_t)n_wg * p.w_row;
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(p.x) + (int64_t)m0 * p.x_row;
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) void rmsnorm_matmul_split_kernel(RmsParams
 #pragma unroll
   for (int mg = 0; mg < 2; ++mg) {
     const int m = m0 + 16 * mg + r;
-    if (m >= p.M) continue;
+    if (m >= p.M || 16 * w + 4 * kg >= wrows) continue;  // rows past the tile: the next one's
     if (p.s == 1) {
       // The whole K range is here: apply the row scale after the Matmul.
       const float scale = 1.0f / sqrtf(ssq_tot[mg] / (float)p.K + p.eps);
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(256) void rmsnorm_matmul_combine_kernel(RmsParams p
 
 hipError_t launch_rmsnorm_matmul(const RmsParams& p, hipStream_t s) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  const dim3 grid((unsigned)((p.N + ROWS - 1) / ROWS), (unsigned)p.s,
+  const dim3 grid((unsigned)((p.N + p.tile_n - 1) / p.tile_n), (unsigned)p.s,
                   (unsigned)((p.M + 31) / 32));
   hipLaunchKernelGGL(rmsnorm_matmul_split_kernel, grid, dim3(NW * 64), 0, s, p);
   hipError_t e = hipGetLastError();

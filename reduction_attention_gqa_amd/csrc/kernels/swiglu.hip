@@ -8,7 +8,9 @@
 //
 // Layout: X [M, K], W_gate and W_up [N, K] (linear-layer weights), H [M, N],
 // row strides in elements, bf16 inputs.  A workgroup is four waves and owns
-// 64 output columns and up to 32 tokens on the MFMA columns; waves 2c and
+// up to 64 output columns (the planner narrows the tile, in steps of 4, so
+// that the tiles fill the compute units) and up to 32 tokens on the MFMA
+// columns; waves 2c and
 // 2c + 1 share columns 32c .. 32c + 31 (two 16-row blocks of each weight
 // matrix, the same rows in both) and take alternate super-steps of the part's
 // K range (a second, on-chip level of the same split-K; alternating, rather
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(NW * 64) void swiglu_split_kernel(SwigluParams p) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;   // MFMA row (weight row) / column (token) index
   const int kg = lane >> 4;  // 8-column group of a 32-column k-step
-  const int n_wg = blockIdx.x * COLS;
+  const int n_wg = blockIdx.x * p.tile_n;  // tile_n <= COLS, a multiple of 4
   const int j = blockIdx.y;
   const int m0 = blockIdx.z * 32;
   // This wave's super-steps of the part's columns: every other one, from
@@ -99,9 +101,10 @@ __global__ __launch_bounds__(NW * 64) void swiglu_split_kernel(SwigluParams p) {
   const int lo = lo_j + (w & 1) * 32 * SS;
   const int hi = hi_j;
 
-  // Buffer ranges end at the last valid weight row / token, so rows past N or
-  // M read as zero.  Offsets stay 32-bit: a workgroup's 64 rows, 32 tokens.
-  const int wrows = min(COLS, p.N - n_wg);
+  // Buffer ranges end at the tile's last valid weight row and token, so rows
+  // past the tile, N or M read as zero without a memory access.  Offsets stay
+  // 32-bit: a workgroup's 64 rows, 32 tokens.
+  const int wrows = min(p.tile_n, p.N - n_wg);
   const int xrows = min(32, p.M - m0);
   const uint16_t* gp = reinterpret_cast<const uint16_t*>(p.wg) + (int64_t)n_wg * p.wg_row;
   const uint16_t* up = reinterpret_cast<const uint16_t*>(p.wu) + (int64_t)n_wg * p.wu_row;
@@ -194,7 +197,7 @@ __global__ __launch_bounds__(NW * 64) void swiglu_split_kernel(SwigluParams p) {
 #pragma unroll
   for (int mg = 0; mg < 2; ++mg) {
     const int m = m0 + 16 * mg + r;
-    if (m >= p.M) continue;
+    if (m >= p.M || n_lane - n_wg >= wrows) continue;  // columns past the tile: the next one's
     const f32x4_t g = red[w0][0][blk][mg][lane] + red[w0 + 1][0][blk][mg][lane];
     const f32x4_t u = red[w0][1][blk][mg][lane] + red[w0 + 1][1][blk][mg][lane];
     if (p.s == 1) {
@@ -243,7 +246,8 @@ __global__ __launch_bounds__(256) void swiglu_combine_kernel(SwigluParams p) {
 
 hipError_t launch_swiglu(const SwigluParams& p, hipStream_t s) {
   if (p.M == 0 || p.N == 0) return hipSuccess;
-  const dim3 grid((unsigned)((p.N + COLS - 1) / COLS), (unsigned)p.s, (unsigned)((p.M + 31) / 32));
+  const dim3 grid((unsigned)((p.N + p.tile_n - 1) / p.tile_n), (unsigned)p.s,
+                  (unsigned)((p.M + 31) / 32));
   hipLaunchKernelGGL(swiglu_split_kernel, grid, dim3(NW * 64), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.s == 1) return e;

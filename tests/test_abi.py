@@ -530,15 +530,37 @@ def test_rms_plan_invariants(lib, m, k, n, s_req):
     assert cfg.s <= steps
     if s_req > 0:
         assert cfg.s <= s_req
-    # 64 weight rows x 32 tokens per workgroup; the part's columns are split
-    # over its four waves.
-    assert tuple(cfg.grid) == (-(-n // 64), cfg.s, -(-m // 32)) and cfg.block == 256
+    # tile_n weight rows (at most 64, a multiple of 4) x 32 tokens per
+    # workgroup; the part's columns are split over its four waves.
+    assert 16 <= cfg.tile_n <= 64 and cfg.tile_n % 4 == 0
+    assert tuple(cfg.grid) == (-(-n // cfg.tile_n), cfg.s, -(-m // 32)) and cfg.block == 256
     assert cfg.ws_bytes == (cfg.s * m * (n + 1) * 4 if cfg.s > 1 else 0)
     if s_req == 0:
         # planner's choice: the most parts that still fit one round, at least
-        # four k-steps per wave
+        # four k-steps per wave, and the tile that fills the compute units best
         tiles = cfg.grid[0] * cfg.grid[2]
         assert cfg.s <= max(1, min(256 // tiles, steps // 16))
+        wgs = tiles * cfg.s
+        fill = wgs / (-(-wgs // 256) * 256)
+        for t in range(64, 15, -4):
+            tt = -(-n // t) * -(-m // 32)
+            s2 = max(1, min(256 // tt, steps // 16))
+            s2 = -(-steps // -(-steps // s2))
+            w2 = tt * s2
+            assert fill >= w2 / (-(-w2 // 256) * 256) - 1e-9
+
+
+def test_rms_plan_decode_shape_fills_the_gpu(lib):
+    # N = 14336 weight rows on 256 CUs: 56-row tiles, 256 workgroups, one part
+    # (64-row tiles would leave 32 CUs idle).
+    st, cfg = rms_plan(lib, rms_problem(m=32, k=4096, n=14336, x_stride=4096, w_stride=4096,
+                                        y_stride=14336))
+    assert st == 0 and cfg.kernel == 0 and cfg.tile_n == 56 and cfg.s == 1
+    assert tuple(cfg.grid) == (256, 1, 1)
+    # 4096 rows: 64-row tiles and four parts fill the GPU as well.
+    st, cfg = rms_plan(lib, rms_problem(m=32, k=4096, n=4096, x_stride=4096, w_stride=4096,
+                                        y_stride=4096))
+    assert st == 0 and cfg.tile_n == 64 and cfg.s == 4 and tuple(cfg.grid) == (64, 4, 1)
 
 
 @pytest.mark.parametrize("m,k,n,s_req", [(256, 4096, 14336, 0), (300, 4096, 4096, 0),
@@ -570,6 +592,11 @@ def test_rms_workspace_and_plan_checks(lib):
     bad.k_chunk = 100                                     # not a multiple of 32
     assert lib.rmsnorm_matmul(ctypes.byref(p), ctypes.byref(bad), fake, fake, fake, fake, fake,
                               1 << 40, None) == ra.ATTN_ERR_ARG
+    for tile in (0, 2, 30, 68):                           # not a multiple of 4 in [4, 64]
+        bad = _lib.RmsConfig.from_buffer_copy(cfg)
+        bad.tile_n = tile
+        assert lib.rmsnorm_matmul(ctypes.byref(p), ctypes.byref(bad), fake, fake, fake, fake, fake,
+                                  1 << 40, None) == ra.ATTN_ERR_ARG
     unaligned = ctypes.c_void_p(0x1008)
     assert lib.rmsnorm_matmul(ctypes.byref(p), ctypes.byref(cfg), unaligned, fake, fake, fake, fake,
                               1 << 40, None) == ra.ATTN_ERR_UNSUPPORTED
@@ -626,9 +653,11 @@ def test_swiglu_plan_invariants(lib, m, k, n, s_req):
     st, cfg = sw_plan(lib, sw_problem(m=m, k=k, n=n), s_req)
     assert st == 0 and cfg.kernel == 0
     assert cfg.k_chunk % 32 == 0 and cfg.s * cfg.k_chunk >= k and (cfg.s - 1) * cfg.k_chunk < k
-    # 64 output columns x 32 tokens per workgroup; each part's columns are
-    # split over the two waves of a column group.
-    assert tuple(cfg.grid) == (-(-n // 64), cfg.s, -(-m // 32)) and cfg.block == 256
+    # tile_n output columns (at most 64, a multiple of 4) x 32 tokens per
+    # workgroup; each part's columns are split over the two waves of a column
+    # group.
+    assert 16 <= cfg.tile_n <= 64 and cfg.tile_n % 4 == 0
+    assert tuple(cfg.grid) == (-(-n // cfg.tile_n), cfg.s, -(-m // 32)) and cfg.block == 256
     assert cfg.ws_bytes == (2 * cfg.s * m * n * 4 if cfg.s > 1 else 0)
     if s_req == 0:
         assert cfg.grid[0] * cfg.grid[1] * cfg.grid[2] <= max(256, cfg.grid[0] * cfg.grid[2])
@@ -658,6 +687,14 @@ def test_swiglu_workspace_and_config_checks(lib):
                       1 << 40, None) == ra.ATTN_ERR_ARG
     assert lib.swiglu(ctypes.byref(p), ctypes.byref(cfg), fake, ctypes.c_void_p(0x1004), fake, fake,
                       fake, 1 << 40, None) == ra.ATTN_ERR_UNSUPPORTED
+    for tile in (0, 2, 30, 68):                           # not a multiple of 4 in [4, 64]
+        bad = _lib.SwigluConfig.from_buffer_copy(cfg)
+        bad.tile_n = tile
+        assert lib.swiglu(ctypes.byref(p), ctypes.byref(bad), fake, fake, fake, fake, fake,
+                          1 << 40, None) == ra.ATTN_ERR_ARG
+    # The decode shape: 56-column tiles fill 256 CUs with one part.
+    st, cfg1 = sw_plan(lib, p)
+    assert st == 0 and cfg1.tile_n == 56 and cfg1.s == 1 and tuple(cfg1.grid) == (256, 1, 1)
 
 
 def test_plan_generic_small_problem_one_tile_per_split(lib):

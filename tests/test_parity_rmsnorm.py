@@ -42,12 +42,17 @@ def _dev(a, stride=None):
     return wide[:, : a.shape[1]]
 
 
-def _run(p, s_request=0, y_dtype=torch.float32, x_stride=None, w_stride=None, y_stride=None):
+def _run(p, s_request=0, y_dtype=torch.float32, x_stride=None, w_stride=None, y_stride=None,
+         tile_n=None):
     x, w = _dev(p.x, x_stride), _dev(p.w, w_stride)
     g = _dev(p.g[None, :])[0]
     y = torch.full((p.m, y_stride or p.n), float("nan"), dtype=y_dtype, device=DEV)[:, : p.n]
     prob = ra.make_rms_problem(x, g, w, y, eps=p.eps)
     plan = ra.rmsnorm_matmul_plan(prob, s_request)
+    if tile_n is not None:  # a tile width of the caller's choosing
+        assert plan.kernel == 0
+        plan.tile_n = tile_n
+        plan.grid[0] = -(-p.n // tile_n)
     ws = ra.rms_workspace(plan, DEV)
     ra.rmsnorm_matmul(prob, plan, x, g, w, y, ws)
     torch.cuda.synchronize()
@@ -107,7 +112,9 @@ def test_full_size_decode():
     # planner's split; every output checked.
     p = rms_workload("llama3_8b_rmsnorm_matmul_decode")
     plan = _check("llama3_8b decode", p)
-    assert plan.s >= 1
+    # 56-row tiles on 256 workgroups: every tile boundary but every fourth
+    # falls inside a 16-row MFMA block.
+    assert plan.kernel == 0 and plan.s == 1 and plan.tile_n == 56 and plan.grid[0] == 256
 
 
 def test_one_part_equals_many_parts():
@@ -202,3 +209,16 @@ def test_prefill_gemm_padded_output_rows():
     assert torch.isnan(full[:, 200:]).all() and not torch.isnan(y).any()
     want = rmsnorm_matmul(p.x, p.g, p.w, p.eps)
     assert_close("padded y", y.cpu().numpy().astype(np.float64), want, TOL_MAX, TOL_MEAN)
+
+
+@pytest.mark.parametrize("s", [1, 3])
+@pytest.mark.parametrize("tile", [4, 20, 36, 56, 64])
+def test_tile_widths(tile, s):
+    # Workgroup tiles of 4 to 64 weight rows: tiles that end inside a 16-row
+    # MFMA block, and n = 203 ending inside a tile and inside a quad of rows
+    # (the rows past each tile belong to the next workgroup and must not be
+    # written by this one).
+    p = make_rms_problem(m=5, k=320, n=203, seed=41)
+    plan = _check(f"tile {tile} s={s}", p, s_request=s, tile_n=tile)
+    assert plan.tile_n == tile and plan.s == s
+

@@ -40,11 +40,16 @@ def _dev(a, stride=None):
     return wide[:, : a.shape[1]]
 
 
-def _run(p, s_request=0, y_dtype=torch.float32, strides=(None, None, None), y_stride=None):
+def _run(p, s_request=0, y_dtype=torch.float32, strides=(None, None, None), y_stride=None,
+         tile_n=None):
     x, wg, wu = _dev(p.x, strides[0]), _dev(p.w_gate, strides[1]), _dev(p.w_up, strides[2])
     y = torch.full((p.m, y_stride or p.n), float("nan"), dtype=y_dtype, device=DEV)[:, : p.n]
     prob = ra.make_swiglu_problem(x, wg, wu, y)
     cfg = ra.swiglu_plan(prob, s_request)
+    if tile_n is not None:  # a tile width of the caller's choosing
+        assert cfg.kernel == 0
+        cfg.tile_n = tile_n
+        cfg.grid[0] = -(-p.n // tile_n)
     ra.swiglu(prob, cfg, x, wg, wu, y, ra.swiglu_workspace(cfg, DEV))
     torch.cuda.synchronize()
     return y, cfg
@@ -83,8 +88,10 @@ def test_strided_rows():
 
 
 def test_full_size_decode():
-    # Llama-3 8B's MLP at 32 tokens: K = 4096, N = 14336; every output checked.
-    _check("llama3_8b decode", swiglu_workload("llama3_8b_swiglu_decode"))
+    # Llama-3 8B's MLP at 32 tokens: K = 4096, N = 14336; every output checked,
+    # with the planner's 56-column tiles on 256 workgroups.
+    cfg = _check("llama3_8b decode", swiglu_workload("llama3_8b_swiglu_decode"))
+    assert cfg.kernel == 0 and cfg.s == 1 and cfg.tile_n == 56 and cfg.grid[0] == 256
 
 
 def test_one_part_equals_many_parts():
@@ -152,3 +159,15 @@ def test_prefill_gemm_padded_output_rows():
     assert torch.isnan(full[:, 200:]).all() and not torch.isnan(y).any()
     assert_close("padded y", y.cpu().numpy().astype(np.float64), swiglu(p.x, p.w_gate, p.w_up),
                  TOL_MAX, TOL_MEAN)
+
+
+@pytest.mark.parametrize("s", [1, 3])
+@pytest.mark.parametrize("tile", [4, 20, 36, 56, 64])
+def test_tile_widths(tile, s):
+    # Workgroup tiles of 4 to 64 output columns: tiles that end inside a
+    # 16-row MFMA block, and n = 203 ending inside a tile and inside a quad of
+    # columns (columns past each tile belong to the next workgroup).
+    p = make_swiglu_problem(m=5, k=320, n=203, seed=42)
+    cfg = _check(f"tile {tile} s={s}", p, s_request=s, tile_n=tile)
+    assert cfg.tile_n == tile and cfg.s == s
+

@@ -48,6 +48,7 @@ struct KParams {
   float scale_log2;     // tau * log2(e): scores are kept in base-2 units (tau itself when no_softmax)
   int32_t no_softmax;   // prefill only: 1 = MatMul+MatMul, O = (tau Q K^T) V
   FastDiv div_dqk, div_dv, div_g;  // divisions by Dqk, Dv and G (generic kernel)
+  int32_t kv_vec;       // generic kernel: K/V rows load as 16-byte chunks (set at launch)
 };
 
 // RMSNorm followed by a MatMul: X [M, K], g [K], W [N, K], Y [M, N] (bf16

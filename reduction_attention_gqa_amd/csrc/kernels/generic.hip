@@ -34,47 +34,79 @@ __device__ __forceinline__ float ld_elem(const void* base, int64_t idx) {
   }
 }
 
-// Copies a tile of nk rows of `wk` elements (row jj of `ka` at element offset
-// rk[jj]) into LDS rows of stride `sk`, and likewise a tile of `wv`-element
-// rows of `va` into rows of stride `sv`.  Thread t takes elements t, t + NT,
-// ... of each tile (consecutive threads, consecutive elements: coalesced);
-// each round issues NB loads of each tile before it stores any of them, so
-// their latencies overlap instead of adding up.
-template <bool BF16>
-__device__ __forceinline__ void stage_kv(const void* ka, const int64_t* rk, int wk, float* dk_s, int sk,
-                                         const void* va, const int64_t* rv, int wv, float* dv_s, int sv,
-                                         int nk, int t) {
-  const int djk = NT / wk, ddk = NT - djk * wk;
-  const int djv = NT / wv, ddv = NT - djv * wv;
-  int jk = t / wk, ck = t - jk * wk;
-  int jv = t / wv, cv = t - jv * wv;
-  while (jk < nk || jv < nk) {
-    float xk[NB], xv[NB];
-    int ok[NB], ov[NB];
+// VE consecutive elements of a row (VE = 1, or 16 bytes: 4 fp32 / 8 bf16) as
+// fp32; `idx` is a multiple of VE when VE > 1.
+template <bool BF16, int VE>
+__device__ __forceinline__ void ld_chunk(const void* base, int64_t idx, float* out) {
+  if constexpr (VE == 1) {
+    out[0] = ld_elem<BF16>(base, idx);
+  } else if constexpr (BF16) {
+    static_assert(VE == 8, "16-byte bf16 chunks");
+    const uint4 v = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      // Past the tile: element 0 of row 0 is read (it exists) and dropped.
-      ok[u] = jk < nk ? jk * sk + ck : -1;
-      xk[u] = ld_elem<BF16>(ka, jk < nk ? rk[jk] + ck : rk[0]);
-      ov[u] = jv < nk ? jv * sv + cv : -1;
-      xv[u] = ld_elem<BF16>(va, jv < nk ? rv[jv] + cv : rv[0]);
+    for (int e = 0; e < 4; ++e) {
+      out[2 * e] = bf16_bits_to_f32((uint16_t)(w[e] & 0xffff));
+      out[2 * e + 1] = bf16_bits_to_f32((uint16_t)(w[e] >> 16));
+    }
+  } else {
+    static_assert(VE == 4, "16-byte fp32 chunks");
+    const float4 v = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+    out[0] = v.x;
+    out[1] = v.y;
+    out[2] = v.z;
+    out[3] = v.w;
+  }
+}
+
+// Copies a tile of nk rows of `wk` elements (row jj of `ka` at element offset
+// rk(jj)) into LDS rows of stride `sk`, and likewise a tile of `wv`-element
+// rows of `va` into rows of stride `sv`, in chunks of VE elements (16-byte
+// loads when VE > 1: every row offset and width is then a multiple of VE).
+// Thread t takes chunks t, t + NT, ... of each tile (consecutive threads,
+// consecutive chunks: coalesced); each round issues NC loads of each tile
+// before it stores any of them, so their latencies overlap instead of adding
+// up.
+template <bool BF16, int VE, class RowK, class RowV>
+__device__ __forceinline__ void stage_kv(const void* ka, RowK rk, int wk, float* dk_s, int sk,
+                                         const void* va, RowV rv, int wv, float* dv_s, int sv,
+                                         int nk, int t) {
+  constexpr int NC = VE == 1 ? NB : 16 / VE;  // chunks per round and tile
+  const int nck = wk / VE, ncv = wv / VE;      // chunks per row
+  const int djk = NT / nck, ddk = NT - djk * nck;
+  const int djv = NT / ncv, ddv = NT - djv * ncv;
+  int jk = t / nck, ck = t - jk * nck;
+  int jv = t / ncv, cv = t - jv * ncv;
+  while (jk < nk || jv < nk) {
+    float xk[NC][VE], xv[NC][VE];
+    int ok[NC], ov[NC];
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      // Past the tile: the first chunk of row 0 is read (it exists) and dropped.
+      ok[u] = jk < nk ? jk * sk + ck * VE : -1;
+      ld_chunk<BF16, VE>(ka, jk < nk ? rk(jk) + ck * VE : rk(0), xk[u]);
+      ov[u] = jv < nk ? jv * sv + cv * VE : -1;
+      ld_chunk<BF16, VE>(va, jv < nk ? rv(jv) + cv * VE : rv(0), xv[u]);
       jk += djk;
       ck += ddk;
-      if (ck >= wk) {
-        ck -= wk;
+      if (ck >= nck) {
+        ck -= nck;
         ++jk;
       }
       jv += djv;
       cv += ddv;
-      if (cv >= wv) {
-        cv -= wv;
+      if (cv >= ncv) {
+        cv -= ncv;
         ++jv;
       }
     }
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      if (ok[u] >= 0) dk_s[ok[u]] = xk[u];
-      if (ov[u] >= 0) dv_s[ov[u]] = xv[u];
+    for (int u = 0; u < NC; ++u) {
+#pragma unroll
+      for (int e = 0; e < VE; ++e) {
+        if (ok[u] >= 0) dk_s[ok[u] + e] = xk[u][e];
+        if (ov[u] >= 0) dv_s[ov[u] + e] = xv[u][e];
+      }
     }
   }
 }
@@ -86,6 +118,7 @@ __device__ __forceinline__ void stage_kv(const void* ka, const int64_t* rk, int 
 // of two with RT * Dv <= NT * CP.
 template <bool BF16, bool STAGE, int CP>
 __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
+  constexpr int VEC = BF16 ? 8 : 4;  // elements per 16-byte chunk
   extern __shared__ float smem[];
   float* q_s = smem;                 // [RT][Dqk]
   float* s_s = q_s + RT * p.Dqk;     // [RT][TN]  scores, then exp tile
@@ -191,21 +224,32 @@ __global__ __launch_bounds__(NT) void generic_attn_kernel(KParams p) {
     const int nk = min(TN, hi - k0);  // keys of this tile that exist in the range
     if constexpr (STAGE) {
       // The previous tile's readers are past the barrier that ends its loop.
-      // Row offsets once per key, then consecutive elements per thread (the
-      // element index advances by NT: a fixed step in columns and rows).
-      if (t < nk) {
-        const int key = k0 + t;
-        if (p.page_table) {
+      // Paged: each key's row offsets once (a page-table read), through LDS;
+      // contiguous layouts compute them where they are used.  16-byte
+      // chunks when the layout allows (p.kv_vec), else single elements.
+      if (p.page_table) {
+        if (t < nk) {
+          const int key = k0 + t;
           const int64_t pg = page_of(p, b, key), kr = key % p.page_size;
           row_k[t] = pg * p.ks_b + kr * p.ks_t + khead;
           row_v[t] = pg * p.vs_b + kr * p.vs_t + vhead;
-        } else {
-          row_k[t] = kbase + (int64_t)key * p.ks_t;
-          row_v[t] = vbase + (int64_t)key * p.vs_t;
         }
+        __syncthreads();
+        auto rk = [&](int jj) { return row_k[jj]; };
+        auto rv = [&](int jj) { return row_v[jj]; };
+        if (p.kv_vec)
+          stage_kv<BF16, VEC>(p.k, rk, p.Dqk, k_s, ks_row, p.v, rv, p.Dv, v_s, p.Dv, nk, t);
+        else
+          stage_kv<BF16, 1>(p.k, rk, p.Dqk, k_s, ks_row, p.v, rv, p.Dv, v_s, p.Dv, nk, t);
+      } else {
+        const int64_t kb0 = kbase + (int64_t)k0 * p.ks_t, vb0 = vbase + (int64_t)k0 * p.vs_t;
+        auto rk = [&](int jj) { return kb0 + (int64_t)jj * p.ks_t; };
+        auto rv = [&](int jj) { return vb0 + (int64_t)jj * p.vs_t; };
+        if (p.kv_vec)
+          stage_kv<BF16, VEC>(p.k, rk, p.Dqk, k_s, ks_row, p.v, rv, p.Dv, v_s, p.Dv, nk, t);
+        else
+          stage_kv<BF16, 1>(p.k, rk, p.Dqk, k_s, ks_row, p.v, rv, p.Dv, v_s, p.Dv, nk, t);
       }
-      __syncthreads();
-      stage_kv<BF16>(p.k, row_k, p.Dqk, k_s, ks_row, p.v, row_v, p.Dv, v_s, p.Dv, nk, t);
       __syncthreads();
     }
     // Scores: thread t -> key k0 + t % TN, rows 4*(t / TN) .. +3 (a wave
@@ -527,8 +571,16 @@ hipError_t launch_generic_cp(const KParams& p, dim3 grid, dim3 block, size_t shm
 
 }  // namespace
 
-hipError_t launch_generic(const KParams& p, dim3 grid, dim3 block, hipStream_t s) {
-  if (RT * p.Dv > NT * 32) return hipErrorInvalidValue;  // Dv <= 512
+hipError_t launch_generic(const KParams& kp, dim3 grid, dim3 block, hipStream_t s) {
+  if (RT * kp.Dv > NT * 32) return hipErrorInvalidValue;  // Dv <= 512
+  // K/V staging in 16-byte chunks when every row offset and row width is a
+  // whole number of chunks and the base pointers are 16-byte aligned.
+  KParams p = kp;
+  const int64_t ve = p.in_bf16 ? 8 : 4;
+  const auto al16 = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0; };
+  p.kv_vec = al16(p.k) && al16(p.v) && p.Dqk % ve == 0 && p.Dv % ve == 0 && p.ks_b % ve == 0 &&
+             p.ks_t % ve == 0 && p.ks_h % ve == 0 && p.vs_b % ve == 0 && p.vs_t % ve == 0 &&
+             p.vs_h % ve == 0;
   const size_t base = sizeof(float) * ((size_t)RT * p.Dqk + RT * TN + 3 * RT);
   // Stage K/V tiles when they fit in 64 KiB (head dims Dqk + Dv < 256).
   const size_t tiles = sizeof(float) * (size_t)TN * (p.Dqk + 1 + p.Dv);

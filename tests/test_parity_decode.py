@@ -175,6 +175,21 @@ def test_full_size_decode_whole_output(name, fused, layout):
     assert_lse_close(f"{name} whole output", d.lse_out(), lse)
 
 
+@pytest.mark.parametrize("layout", ["head", "token"])
+@pytest.mark.parametrize("s", [2, 4, 8])
+def test_full_size_llama_forced_splits(s, layout):
+    # The Llama decode shape with the key axis split s ways (the planner takes
+    # s = 1 here): the single-launch merge of every (request, KV head) at full
+    # size, every output element against the oracle.
+    print(f"[case] llama s={s} layout={layout}", flush=True)
+    p, o, lse = _full_oracle("llama3_8b_gqa_decode")
+    d = DeviceProblem(p, layout=layout)
+    plan = d.decode(s_request=s)
+    assert plan.s_max == s
+    assert_close(f"llama s={s} {layout}", d.out(), o, BF16_MAX, BF16_MEAN)
+    assert_lse_close(f"llama s={s} {layout}", d.lse_out(), lse)
+
+
 @pytest.mark.parametrize("fused", [False, True])
 def test_device_lengths_beyond_the_plan_write_nan(fused):
     # The plan is made from host lengths that are shorter than the device's:

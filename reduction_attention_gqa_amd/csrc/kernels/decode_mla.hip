@@ -46,6 +46,7 @@ constexpr int LDS_BYTES = NSTAGE * STAGE;  // 147,456
 constexpr int NBLK = TK * CHUNKS / 64;     // 36 one-KiB DMA blocks per tile
 constexpr int BLK_ROUNDS = (NBLK + NW - 1) / NW;  // 5: waves 0-3 issue 5, waves 4-7 issue 4
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr int kFastMerge = 4;          // split counts the pipelined merge takes
 static_assert(NBLK * 64 == TK * CHUNKS, "a tile is a whole number of DMA blocks");
 static_assert(NBLK - (BLK_ROUNDS - 1) * NW == 4, "waves 0-3 own the last round");
 
@@ -279,9 +280,10 @@ void decode_mla_kernel(KParams p) {
 
   // Operand fetches of a tile, in MFMA order: f = 0..35 the K fragments
   // (f = 2*ks + kb), f = 36..67 the V^T fragments (column block f - 36).  One
-  // rolling window of FD fetches runs across the whole tile and on into the
-  // next tile's K fragments, so V is already in flight during the softmax and
-  // the next scores' K during the V-matmul.
+  // rolling window of FD fetches runs across the tile, so V is already in
+  // flight during the softmax.  It stops at the tile's end: a window running
+  // on into the next tile would need that tile landed one barrier earlier,
+  // which leaves one tile fewer in flight (measured 2 % slower).
   constexpr int NF = 2 * KSTEPS + CBLK;  // 68
   constexpr int FD = 3;                  // fetches in flight
   auto fetch = [&](int f, uint32_t soff) -> i32x4_t {
@@ -301,22 +303,23 @@ void decode_mla_kernel(KParams p) {
     return va;
   };
 
-  // Prologue: tiles 0..2 in flight, tile 0 landed, its first K fetches issued.
+  // Prologue: tiles 0..2 in flight.
 #pragma unroll
   for (int t = 0; t < NSTAGE - 1; ++t)
     if (t < ntiles) dma_tile(t, t);
-  wait_tiles_but(min(ntiles - 1, NSTAGE - 2));
-  asm volatile("s_barrier" ::: "memory");
-  i32x4_t fr[NF + FD];
-#pragma unroll
-  for (int f = 0; f < FD; ++f) fr[f] = fetch(f, 0);
+  i32x4_t fr[NF];
 
   for (int it = 0; it < ntiles; ++it) {
     const int st = it & (NSTAGE - 1);
     const uint32_t soff = (uint32_t)(st * STAGE);
-    // The next tile's stage; on the last tile the fetches into it read stale
-    // (in-bounds) LDS and are dropped.
-    const uint32_t soff_next = (uint32_t)(((it + 1) & (NSTAGE - 1)) * STAGE);
+    // Hand-over: tile it has landed for every wave, and every wave has
+    // finished tile it - 1 (its last reads fed the previous V-matmul), whose
+    // stage the DMA of tile it + 3 now refills: three tiles stay in flight.
+    wait_tiles_but(min(ntiles - it - 1, NSTAGE - 2));
+    asm volatile("s_barrier" ::: "memory");
+    if (it + NSTAGE - 1 < ntiles) dma_tile(it + NSTAGE - 1, (it + NSTAGE - 1) & (NSTAGE - 1));
+#pragma unroll
+    for (int f = 0; f < FD; ++f) fr[f] = fetch(f, soff);
 
     // S^T = K Q^T: two chains (key blocks).
     f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -375,24 +378,14 @@ void decode_mla_kernel(KParams p) {
     pk[3] = (int)pack_bf16x2(pv[6], pv[7]);
     const bf16x8_t pb = as_bf16x8(pk);
 
-    // Hand-over: tile it + 1 has landed for every wave (the V-matmul below
-    // starts reading its K), and every wave has finished tile it - 1, whose
-    // stage the DMA of tile it + 3 now refills.  Reads of tile it issued
-    // before the barrier are all consumed before the next one.
-    wait_tiles_but(min(ntiles - it - 2, 1));
-    asm volatile("s_barrier" ::: "memory");
-    if (it + NSTAGE - 1 < ntiles) dma_tile(it + NSTAGE - 1, (it + NSTAGE - 1) & (NSTAGE - 1));
-
-    // O^T += V^T P^T; the window runs on into the next tile's K fragments.
+    // O^T += V^T P^T.
 #pragma unroll
     for (int f = 2 * KSTEPS; f < NF; ++f) {
-      fr[f + FD] = f + FD < NF ? fetch(f + FD, soff) : fetch(f + FD - NF, soff_next);
+      if (f + FD < NF) fr[f + FD] = fetch(f + FD, soff);
       const int cb = f - 2 * KSTEPS;
       oacc[cb] = mfma16x16x32(as_bf16x8(fr[f]), pb, oacc[cb]);
       __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int f = 0; f < FD; ++f) fr[f] = fr[NF + f];
   }
 
   // Split epilogue: O_j = U / l (fp32), LSE_j = (m_ref + log2 l) ln 2.  Lane
@@ -446,6 +439,12 @@ void decode_mla_kernel(KParams p) {
   // order: split j of unit u is a block of ceil(R / 16) wave slabs, slab w
   // holding for each column block cb the 64 lanes' four values (1 KiB, one
   // store or load instruction of whole cache lines), plus one LSE per row.
+  // With at most kFastMerge splits they are stored as bf16 (round to nearest
+  // even), the lane's values of column blocks 2q and 2q + 1 side by side in
+  // one 16-byte slot of 1 KiB row q: the splits of every request finish
+  // together, so the partial traffic (written, then read back by the merging
+  // split) is not hidden behind other work and halving it shortens the
+  // launch's tail.  The merging split rounds its own partial the same way.
   //
   // Ordering on gfx950: partials are written with sc1 (device-coherent)
   // stores, which write through the XCD's L2 instead of leaving dirty lines
@@ -475,10 +474,35 @@ void decode_mla_kernel(KParams p) {
            (uint32_t)(cb * 64 * 16);
   };
   auto lse_ptr = [&](int jj) { return p.ws_lse + ((int64_t)jj * nunits + unit) * (nslab * 16) + e_r; };
+  // bf16 partials: byte offset of (split jj, this lane, column blocks 2q,
+  // 2q + 1).  They fill the first half of the same per-(split, unit) blocks
+  // as fp32 ones, since requests with more splits share the area in fp32.
+  const bool half_parts = sb <= kFastMerge;
+  const uint32_t lane_off16 = (uint32_t)w * (slab_bytes / 2) + (uint32_t)lane * 16;
+  auto part16_off = [&](int jj, int q) {
+    return (uint32_t)(((int64_t)jj * nunits + unit) * block_bytes) + lane_off16 +
+           (uint32_t)(q * 64 * 16);
+  };
+  // Column blocks 2q and 2q + 1 of this split's O_j, rounded to bf16 and packed.
+  auto own16 = [&](int q) {
+    const f32x4_t a = oacc[2 * q] * inv, c = oacc[2 * q + 1] * inv;
+    i32x4_t v;
+    v[0] = (int)pack_bf16x2(a[0], a[1]);
+    v[1] = (int)pack_bf16x2(a[2], a[3]);
+    v[2] = (int)pack_bf16x2(c[0], c[1]);
+    v[3] = (int)pack_bf16x2(c[2], c[3]);
+    return v;
+  };
   if (ticket < sb - 1) {
     if (w < nslab) {
+      if (half_parts) {
 #pragma unroll
-      for (int cb = 0; cb < CBLK; ++cb) store16_dev(wrs, part_off(j, cb), oacc[cb] * inv);
+        for (int q = 0; q < CBLK / 2; ++q)
+          store16_dev(wrs, part16_off(j, q), __builtin_bit_cast(f32x4_t, own16(q)));
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < CBLK; ++cb) store16_dev(wrs, part_off(j, cb), oacc[cb] * inv);
+      }
       if (e_g == 0) store_dev(lse_ptr(j), lse_own);
     }
     wait_vmem();
@@ -492,7 +516,77 @@ void decode_mla_kernel(KParams p) {
       __builtin_amdgcn_s_sleep(2);
   }
   __syncthreads();
-  if (w < nslab) {
+  if (w < nslab && half_parts) {
+    // Up to four splits: every load of the merge is issued ahead of its use.
+    // The LSEs first (one round trip; a split index past sb is clamped to a
+    // slot inside the area and its value dropped), then the other splits'
+    // bf16 partials, MD steps of two column blocks ahead.
+    float lb[kFastMerge];
+#pragma unroll
+    for (int jj = 0; jj < kFastMerge; ++jj) lb[jj] = load_dev(lse_ptr(min(jj, sb - 1)));
+    int jo[kFastMerge - 1];  // the other splits in split order
+#pragma unroll
+    for (int k = 0; k < kFastMerge - 1; ++k) jo[k] = min(k < j ? k : k + 1, sb - 1);
+    constexpr int MCB = 2, MD = 4, NSTEP = CBLK / MCB;
+    i32x4_t xb[MD][kFastMerge - 1];
+    auto issue = [&](int step, int slot) {
+#pragma unroll
+      for (int k = 0; k < kFastMerge - 1; ++k)
+        xb[slot][k] = __builtin_bit_cast(i32x4_t, load16_dev(wrs, part16_off(jo[k], step)));
+    };
+    // Values 4u .. 4u + 3 of a packed slot (column block 2q + u) as fp32.
+    auto unpack = [](const i32x4_t& v, int u) {
+      f32x4_t r;
+      r[0] = __builtin_bit_cast(float, (uint32_t)v[2 * u] << 16);
+      r[1] = __builtin_bit_cast(float, (uint32_t)v[2 * u] & 0xffff0000u);
+      r[2] = __builtin_bit_cast(float, (uint32_t)v[2 * u + 1] << 16);
+      r[3] = __builtin_bit_cast(float, (uint32_t)v[2 * u + 1] & 0xffff0000u);
+      return r;
+    };
+#pragma unroll
+    for (int st = 0; st < MD; ++st) issue(st, st);
+    // Pass 1: the common reference M (base 2), the weights and their sum in
+    // split order.
+#pragma unroll
+    for (int jj = 0; jj < kFastMerge; ++jj)
+      lb[jj] = jj >= sb ? kNegInf : (jj == j ? lse_own : lb[jj]) * kLog2e;
+    float M2 = kNegInf;
+#pragma unroll
+    for (int jj = 0; jj < kFastMerge; ++jj) M2 = vmax(M2, lb[jj]);
+    float wt[kFastMerge];
+    float wsum = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < kFastMerge; ++jj) {
+      wt[jj] = M2 == kNegInf ? 0.f : fast_exp2(lb[jj] - M2);
+      wsum += wt[jj];
+    }
+    const float winv = wsum > 0.f ? 1.f / wsum : 0.f;
+    // Pass 2: two column blocks per step, the splits in order (this split's
+    // own partial from registers, rounded as a stored one).
+#pragma unroll
+    for (int step = 0; step < NSTEP; ++step) {
+      const int slot = step % MD;
+      const i32x4_t own_pk = own16(step);
+#pragma unroll
+      for (int u = 0; u < MCB; ++u) {
+        const int cb = MCB * step + u;
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < kFastMerge; ++jj) {
+          const i32x4_t xp = jj == j ? own_pk
+                                     : (jj < j ? xb[slot][jj < kFastMerge - 1 ? jj : 0]
+                                               : xb[slot][jj > 0 ? jj - 1 : 0]);
+          const f32x4_t xv = unpack(xp, u);
+          const f32x4_t t = acc + wt[jj] * xv;
+          acc = jj < sb ? t : acc;
+        }
+        if (e_ok) store_o4(p, obase + 16 * cb, acc * winv);
+      }
+      if (step + MD < NSTEP) issue(step + MD, slot);
+    }
+    if (e_ok && e_g == 0 && p.lse_out)
+      p.lse_out[row] = M2 == kNegInf ? kNegInf : (M2 + fast_log2(wsum)) * kLn2;
+  } else if (w < nslab) {
     // Pass 1: the common reference M (base 2) and the weight sum, split order.
     float M2 = kNegInf;
     for (int jj = 0; jj < sb; ++jj) {

@@ -11,8 +11,9 @@ from synthetic.inputs import make_problem, workload
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("s", [0, 1, 3])
+@pytest.mark.parametrize("s", [0, 1, 3, 4, 6])
 def test_mla_small(s):
+    # s <= 4: the merge with every load issued ahead; more splits: the general merge.
     p = make_problem(dtype="bf16", batch=2, lq=1, hq=128, hkv=1, dqk=576, dv=512,
                      kv_len=[300, 1000], lcap=1024, seed=41, mla=True)
     d = DeviceProblem(p)

@@ -285,7 +285,7 @@ void decode_mla_kernel(KParams p) {
   // on into the next tile would need that tile landed one barrier earlier,
   // which leaves one tile fewer in flight (measured 2 % slower).
   constexpr int NF = 2 * KSTEPS + CBLK;  // 68
-  constexpr int FD = 3;                  // fetches in flight
+  constexpr int FD = 4;                  // fetches in flight (5 spills)
   auto fetch = [&](int f, uint32_t soff) -> i32x4_t {
     if (f < 2 * KSTEPS) {
       const int ks = f >> 1, kb = f & 1;

@@ -575,10 +575,11 @@ void decode_gqa_d128_items(KParams p) {
 //
 // Merge of a cut unit: the (request, KV head) counter in ws_cnt holds tickets
 // in its low 16 bits and published partials in its high 16 bits.  Each piece
-// takes a ticket when its keys are done; all but the last publish their
-// partial and count it; the last one (ticket = pieces - 1) knows every other
-// piece has already taken its ticket, so that workgroup is resident and has
-// only its stores left: it waits for their count, merges all pieces in piece
+// takes a ticket as it starts; all but the last publish their partial when
+// their keys are done and count it; the last one (ticket = pieces - 1) knows
+// every other piece has already taken its ticket, so that workgroup is
+// resident and has nothing left to wait for (a piece that does not merge
+// never waits): it waits for their count, merges all pieces in piece
 // order (its own from registers, with the same arithmetic as a stored one,
 // so the bits do not depend on which piece finishes last), writes O and
 // resets the counter.  A partial is an 8 KiB block in thread order (thread t's
@@ -662,6 +663,12 @@ void decode_gqa_d128_stream(KParams p) {
         if (oc == 0 && p.lse_out) p.lse_out[row] = nan;
       }
     } else {
+      // A piece of a cut unit takes its ticket as it starts, so the atomic's
+      // round trip runs under the piece's key stream.
+      int early_ticket = 0;
+      if (!whole && t == 0)
+        early_ticket = __hip_atomic_fetch_add(p.counters + b * p.Hkv + kvh, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
       WaveState ws;
       stream_keys<PAGED>(p, b, kvh, lo, hi, L, lds_raw, page_ids, ws);
       const RowOut ro = merge_waves(ws, lds_raw, m_w, l_w);
@@ -677,9 +684,7 @@ void decode_gqa_d128_stream(KParams p) {
         const int pi = (int)(g - g_first);
         const int unit = b * p.Hkv + kvh;
         int* cnt = p.counters + unit;
-        if (t == 0)
-          s_ticket = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) &
-                     0xffff;
+        if (t == 0) s_ticket = early_ticket & 0xffff;
         __syncthreads();
         const int ticket = s_ticket;
         const __amdgpu_buffer_rsrc_t wrs = make_rsrc(p.ws_o, 0xffffffffu);

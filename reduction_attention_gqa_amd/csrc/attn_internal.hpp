@@ -156,8 +156,15 @@ constexpr int kGqaStreamWgsPerCu = 2;  // attn_decode when units are cut: runs p
 constexpr int kGqaMinChunk = 256;      // planner floor on keys per split
 constexpr int kGqaBlock = 256;
 constexpr int kGqaMaxRows = 16;
-constexpr int kPrefillStages = 6;     // prefill K/V ring depth (tiles)
-constexpr int kPrefillBarrierTiles = 2;  // prefill key tiles per workgroup barrier
+// Prefill K/V rings: contiguous caches take 64-key tiles (two 32-key blocks)
+// in a 4-stage ring with a barrier per tile; paged pools 32-key tiles in a
+// 6-stage ring with a barrier per two tiles (their per-lane copy moves one
+// block per wave).
+constexpr int kPrefillKeyBlocks = 2;      // contiguous: 32-key blocks per tile
+constexpr int kPrefillStages = 4;         // contiguous: ring depth (tiles)
+constexpr int kPrefillBarrierTiles = 1;   // contiguous: tiles per workgroup barrier
+constexpr int kPrefillPagedStages = 6;    // paged: ring depth (32-key tiles)
+constexpr int kPrefillPagedBarrierTiles = 2;  // paged: tiles per workgroup barrier
 constexpr int kMlaTileN = 32;          // keys per MLA tile
 constexpr int kMlaBlock = 512;         // 8 waves of 16 query rows
 constexpr int kMlaRows = 128;          // query rows per MLA workgroup

@@ -215,7 +215,9 @@ int attn_decode_split(const attn_problem* problem, const attn_plan* plan,
  *
  * For the GQA D=128 and MLA families this is a single launch; the partials
  * it keeps in ws_o / ws_lse are private to it (their layout is not the one
- * attn_decode_split documents).
+ * attn_decode_split documents; an MLA request of at most four splits keeps
+ * its partial outputs rounded to bf16, so the result then differs from the
+ * two-launch one by that rounding, well inside the bf16 output tolerance).
  *   GQA with one split per request (s_max == 1): one workgroup per
  *   (request, KV head) writes O directly.  GQA with s_max > 1:
  *   the keys of all (request, KV head) units, in rounds of tile_n keys,

@@ -239,3 +239,26 @@ def test_more_work_items_than_planned_write_nan():
     assert np.isnan(out[0]).all() and np.isnan(out).any()
     assert np.all(np.isnan(out) | (out == 0))
     assert int(ws[2].abs().sum()) == 0
+
+
+@pytest.mark.parametrize("layout", ["head", "token"])
+def test_full_size_ragged_single_launch_bitwise_and_counters(layout):
+    # The full ragged workload in one launch (the stream schedule: hundreds of
+    # cut units whose pieces take their merge tickets as they start): repeated
+    # calls agree bit for bit, and every arrival counter is back at zero.
+    import reduction_attention_gqa_amd as ra
+    p = workload("ragged_decode_qwen3_32b")
+    print(f"[case] ragged_decode_qwen3_32b bitwise layout={layout}", flush=True)
+    d = DeviceProblem(p, layout=layout)
+    plan = ra.attn_decode_plan(d.problem(), 0, list(p.lens))
+    assert plan.kernel == 1 and plan.s_max > 1 and plan.stream_pieces > 1
+    ws = ra.workspace(plan, "cuda")
+    d.decode(plan=plan, ws=ws)
+    first, first_lse = d.o.clone(), d.lse.clone()
+    assert int(ws[2].abs().sum()) == 0
+    for _ in range(3):
+        d.o.fill_(float("nan"))
+        d.lse.fill_(float("nan"))
+        d.decode(plan=plan, ws=ws)
+        assert torch.equal(first, d.o) and torch.equal(first_lse, d.lse)
+        assert int(ws[2].abs().sum()) == 0

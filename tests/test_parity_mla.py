@@ -97,3 +97,26 @@ def test_mla_device_length_beyond_the_plan_writes_nan():
     o, lse = attention(p.q, p.k, v_rows(p), False, p.scale)
     assert_close("mla beyond plan, request 1", out[1:], o[1:], BF16_MAX, BF16_MEAN)
     assert int(ws[2].abs().sum()) == 0
+
+
+def test_mla_full_size_single_launch_bitwise_and_counters():
+    # The full MLA workload in one launch (four splits per request, bf16
+    # partials, the last split merging): repeated calls agree bit for bit,
+    # and every arrival counter is back at zero.
+    import torch
+    import reduction_attention_gqa_amd as ra
+    p = workload("mla_decode")
+    print("[case] mla_decode bitwise", flush=True)
+    d = DeviceProblem(p)
+    plan = ra.attn_decode_plan(d.problem(), 0, list(p.lens))
+    assert plan.kernel == 2 and plan.s_max == 4
+    ws = ra.workspace(plan, "cuda")
+    d.decode(plan=plan, ws=ws)
+    first, first_lse = d.o.clone(), d.lse.clone()
+    assert int(ws[2].abs().sum()) == 0
+    for _ in range(3):
+        d.o.fill_(float("nan"))
+        d.lse.fill_(float("nan"))
+        d.decode(plan=plan, ws=ws)
+        assert torch.equal(first, d.o) and torch.equal(first_lse, d.lse)
+        assert int(ws[2].abs().sum()) == 0
